@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the fused NVFP4 W4A4 operator.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and
+benchmark. It only draws random bytes and numbers in the layouts the operator
+takes; it holds none of the operator's arithmetic (no E2M1/E4M3 decode, no
+products, no sums). Every array it returns is a plain numpy array on the host;
+callers copy it to the device themselves.
+
+Layouts (all dense, row-major, no padding):
+  act          uint8  [M, K/2]   two E2M1 codes per byte, low nibble = even k
+  ascales      uint8  [K/16, M]  FP8-E4M3 (OCP E4M3FN) bytes, one per 16 k
+  wgt          uint8  [N, K/2]
+  wscales      uint8  [K/16, N]
+  wcscale      float32 [N]
+  bias         float32 [N]
+  lora_act_in  uint16 [M, R]     bfloat16 bit patterns
+  lora_up      uint16 [R, N]     bfloat16 bit patterns
+
+The operator, its packing ([rows, K/2] bytes of two E2M1 codes, [K/16, rows]
+E4M3 scales) and the rank-R LoRA residual follow the SVDQuant W4A4 on
+Blackwell page ("Blackwell 上的 SVDQuant W4A4 算子实现"), section 2. The
+value distributions and shapes below are the workloads this repository
+measures: diffusion-transformer linear layers with hidden size 3072 and MLP
+width 12288.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "bf16_bits_from_f32",
+           "e4m3_scale_byte"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shape plus the distribution knobs that differ."""
+    name: str
+    M: int
+    N: int
+    K: int
+    R: int
+    seed: int
+    lora_act_std: float = 0.1
+    lora_up_std: float = 0.1
+    zero_scale_frac: float = 0.0   # fraction of E4M3 scale bytes forced to 0x00
+    zero_bias_frac: float = 0.0    # fraction of bias entries forced to 0.0
+    notes: str = field(default="", compare=False)
+
+    @property
+    def shape(self):
+        return (self.M, self.N, self.K, self.R)
+
+    def flops(self) -> int:
+        """Algorithmic flops of one call: 2MNK for the main product + 2MRN for LoRA."""
+        return 2 * self.M * self.N * self.K + 2 * self.M * self.R * self.N
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 256, 256, 512, 32, seed=1000,
+                     notes="small case, several tiles"),
+    "qkv": Workload("qkv", 4096, 3072, 3072, 32, seed=1001,
+                    notes="QKV-like linear, 4096 tokens, hidden 3072"),
+    "mlp_up": Workload("mlp_up", 4096, 12288, 3072, 32, seed=1002,
+                       notes="MLP-up linear 3072 -> 12288"),
+    "mlp_down": Workload("mlp_down", 4096, 3072, 12288, 128, seed=1003, lora_act_std=0.05,
+                         notes="MLP-down linear 12288 -> 3072 at LoRA rank 128"),
+    "ragged": Workload("ragged", 1000, 3072, 3072, 16, seed=1004, zero_scale_frac=0.10,
+                       zero_bias_frac=0.01,
+                       notes="M not a tile multiple; 10% zero scale blocks, 1% zero bias"),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (input recipe only).
+
+    Used to turn normal samples into the bf16 LoRA inputs. NaN never occurs here.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def e4m3_scale_byte(exp: np.ndarray, mant: np.ndarray) -> np.ndarray:
+    """Byte of a positive normal E4M3FN number 2**exp * (1 + mant/8).
+
+    exp in [-6, 8], mant in [0, 7] (exp 8 with mant 7 is the NaN code and is
+    rejected). This writes the bit fields only; it never evaluates the value.
+    """
+    exp = np.asarray(exp, dtype=np.int64)
+    mant = np.asarray(mant, dtype=np.int64)
+    if np.any(exp < -6) or np.any(exp > 8) or np.any(mant < 0) or np.any(mant > 7):
+        raise ValueError("exponent/mantissa out of the E4M3 normal range")
+    if np.any((exp == 8) & (mant == 7)):
+        raise ValueError("0x7F/0xFF is the E4M3FN NaN code")
+    return (((exp + 7) << 3) | mant).astype(np.uint8)
+
+
+def _packed_codes(rng: np.random.Generator, rows: int, K: int) -> np.ndarray:
+    lo = rng.integers(0, 16, size=(rows, K // 2), dtype=np.uint8)  # even k
+    hi = rng.integers(0, 16, size=(rows, K // 2), dtype=np.uint8)  # odd k
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def _scales(rng: np.random.Generator, kblocks: int, rows: int, zero_frac: float) -> np.ndarray:
+    # random power of two in [2^-4, 2^2] times a mantissa 1 + m/8, m uniform in 0..7
+    e = rng.integers(-4, 3, size=(kblocks, rows))
+    m = rng.integers(0, 8, size=(kblocks, rows))
+    s = e4m3_scale_byte(e, m)
+    if zero_frac > 0.0:
+        s[rng.random(size=s.shape) < zero_frac] = 0x00
+    return s
+
+
+def make_inputs(wl: Workload | str, seed: int | None = None) -> dict:
+    """Draw one seeded input set for a workload; returns a dict of numpy arrays."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    M, N, K, R = wl.shape
+    if K % 16 != 0:
+        raise ValueError("K must be a multiple of 16")
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    act = _packed_codes(rng, M, K)
+    ascales = _scales(rng, K // 16, M, wl.zero_scale_frac)
+    wgt = _packed_codes(rng, N, K)
+    wscales = _scales(rng, K // 16, N, wl.zero_scale_frac)
+    wcscale = rng.uniform(0.5, 1.5, size=N).astype(np.float32)
+    bias = rng.standard_normal(size=N).astype(np.float32)
+    if wl.zero_bias_frac > 0.0:
+        bias[rng.random(size=N) < wl.zero_bias_frac] = 0.0
+    lora_act_in = bf16_bits_from_f32(
+        (rng.standard_normal(size=(M, R)) * wl.lora_act_std).astype(np.float32))
+    lora_up = bf16_bits_from_f32(
+        (rng.standard_normal(size=(R, N)) * wl.lora_up_std).astype(np.float32))
+    return dict(act=act, ascales=ascales, wgt=wgt, wscales=wscales, wcscale=wcscale,
+                bias=bias, lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R)
+
+
+def custom_inputs(M: int, N: int, K: int, R: int, seed: int, **kw) -> dict:
+    """Inputs for an arbitrary shape with the standard distributions."""
+    wl = Workload("custom", M, N, K, R, seed=seed, **kw)
+    return make_inputs(wl)

@@ -1,0 +1,508 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each pin ties the oracle to something it does not compute itself: golden values
+derived by hand from the format definitions (tests/golden/), an independent
+E4M3 decoder (torch.float8_e4m3fn), exact rational brute force on tiny inputs,
+closed forms for structured inputs, and algebraic invariants. A mutation test
+at the end plants plausible mistakes in the oracle and checks that at least one
+pin fails for every one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.w4a4_ref as ref
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ARG_ORDER = ("act", "ascales", "wgt", "wscales", "wcscale", "bias", "lora_act_in", "lora_up")
+
+
+def _args(x):
+    return [x[k] for k in ARG_ORDER]
+
+
+def _y(x):
+    return ref.gemm_w4a4_ref(*_args(x))
+
+
+# ------------------------------------------------------------ independent decoders
+
+def _golden_e2m1():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e2m1_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                parts = line.split()
+                vals[int(parts[0])] = float(parts[4])
+    return vals
+
+
+def _torch_e4m3():
+    b = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    return b.to(torch.float64).numpy()
+
+
+_E2M1_GOLD = _golden_e2m1()
+_E4M3_TORCH = _torch_e4m3()
+
+
+def _frac(x: float) -> Fraction:
+    return Fraction(x)  # exact for every finite float
+
+
+def brute_force(x) -> np.ndarray:
+    """Exact y from element loops over rational numbers.
+
+    Decodes with the golden E2M1 table and torch's E4M3 decoder, never with the
+    oracle's tables, and walks every (m, n, k) and (m, n, r) one at a time.
+    """
+    M, N, K, R = x["M"], x["N"], x["K"], x["R"]
+    act, wgt = x["act"], x["wgt"]
+    asc, wsc = x["ascales"], x["wscales"]
+    la = x["lora_act_in"].astype(np.uint32) << 16
+    lu = x["lora_up"].astype(np.uint32) << 16
+    la = la.view(np.float32)
+    lu = lu.view(np.float32)
+    y = np.empty((M, N), dtype=object)
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                byte_a = int(act[m, k // 2])
+                byte_w = int(wgt[n, k // 2])
+                ca = (byte_a >> 4) if (k % 2) else (byte_a & 15)
+                cw = (byte_w >> 4) if (k % 2) else (byte_w & 15)
+                a = _frac(_E2M1_GOLD[ca]) * _frac(_E4M3_TORCH[asc[k // 16, m]])
+                w = _frac(_E2M1_GOLD[cw]) * _frac(_E4M3_TORCH[wsc[k // 16, n]])
+                s += a * w
+            lora = Fraction(0)
+            for r in range(R):
+                lora += _frac(float(la[m, r])) * _frac(float(lu[r, n]))
+            y[m, n] = _frac(float(x["wcscale"][n])) * s + _frac(float(x["bias"][n])) + lora
+    return y
+
+
+def _small(M, N, K, R, seed, **kw):
+    return synthetic.custom_inputs(M, N, K, R, seed=seed, **kw)
+
+
+def _const_inputs(M, N, K, R, a_code, w_code, a_scale, w_scale, la_bits, lu_bits, seed=5):
+    """Structured inputs: every nibble / scale / LoRA entry the same; wcscale, bias random."""
+    rng = np.random.default_rng(seed)
+    byte = lambda c: np.uint8(c | (c << 4))
+    return dict(
+        act=np.full((M, K // 2), byte(a_code), np.uint8),
+        ascales=np.full((K // 16, M), a_scale, np.uint8),
+        wgt=np.full((N, K // 2), byte(w_code), np.uint8),
+        wscales=np.full((K // 16, N), w_scale, np.uint8),
+        wcscale=rng.uniform(0.5, 1.5, N).astype(np.float32),
+        bias=rng.standard_normal(N).astype(np.float32),
+        lora_act_in=np.full((M, R), la_bits, np.uint16),
+        lora_up=np.full((R, N), lu_bits, np.uint16),
+        M=M, N=N, K=K, R=R)
+
+
+# ------------------------------------------------------------ pins (return None or raise)
+
+def pin_e2m1_golden():
+    for c in range(16):
+        v = ref.E2M1_TABLE[c]
+        g = _E2M1_GOLD[c]
+        assert v == g and math.copysign(1, v) == math.copysign(1, g), (c, v, g)
+
+
+def pin_e4m3_torch():
+    t = _E4M3_TORCH
+    o = ref.E4M3_TABLE
+    nan_t, nan_o = np.isnan(t), np.isnan(o)
+    assert np.array_equal(nan_t, nan_o)
+    assert np.array_equal(t[~nan_t], o[~nan_o])
+    assert np.array_equal(np.signbit(t[~nan_t]), np.signbit(o[~nan_o]))
+
+
+def pin_e4m3_golden():
+    with open(os.path.join(GOLDEN, "e4m3_spot_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            b, v = line.split()
+            b, v = int(b, 16), float(v)
+            o = ref.E4M3_TABLE[b]
+            if math.isnan(v):
+                assert math.isnan(o), b
+            else:
+                assert o == v and math.copysign(1, o) == math.copysign(1, v), (hex(b), o, v)
+
+
+def pin_bruteforce_tiny():
+    """Vectorised oracle == exact rational loops on tiny random shapes (R in {0, 1, 3})."""
+    for (M, N, K, R, seed) in [(3, 2, 16, 0, 1), (2, 3, 32, 1, 2), (4, 3, 48, 3, 3),
+                               (1, 5, 32, 3, 4)]:
+        x = _small(M, N, K, R, seed)
+        y = _y(x)
+        exact = brute_force(x)
+        for m in range(M):
+            for n in range(N):
+                # float64 LoRA sums may round (random bf16 exponents); the main sum cannot
+                assert abs(Fraction(y[m, n]) - exact[m, n]) <= Fraction(2) ** -40 * (
+                    1 + abs(exact[m, n])), (M, N, K, R, m, n)
+
+
+def pin_bruteforce_full_e4m3_range():
+    """Scales drawn from every finite E4M3 byte (subnormals, 448, negative) still match."""
+    rng = np.random.default_rng(11)
+    x = _small(3, 4, 48, 2, 12)
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+    x["ascales"] = rng.choice(finite, size=x["ascales"].shape).astype(np.uint8)
+    x["wscales"] = rng.choice(finite, size=x["wscales"].shape).astype(np.uint8)
+    y = _y(x)
+    exact = brute_force(x)
+    for m in range(3):
+        for n in range(4):
+            assert abs(Fraction(y[m, n]) - exact[m, n]) <= Fraction(2) ** -44 * (
+                1 + abs(exact[m, n])), (m, n)
+
+
+def pin_exact_integer_accumulation():
+    """Under the workload scales every product is a multiple of 2^-16, so the
+    float64 main sum equals an int64 accumulation of (A*2^8)(W*2^8) exactly."""
+    for name, rows in [("tiny", slice(0, 64)), ("qkv", slice(0, 16)), ("mlp_down", slice(0, 8))]:
+        x = synthetic.make_inputs(name)
+        act, asc = x["act"][rows], x["ascales"][:, rows]
+        wgt, wsc = x["wgt"][:32], x["wscales"][:, :32]
+        S = ref.main_product(act, asc, wgt, wsc)
+        # integer decode straight from the bytes via the golden/torch tables
+        def as_int(packed, scales):
+            lo = packed & 15
+            hi = packed >> 4
+            codes = np.stack([lo, hi], axis=-1).reshape(packed.shape[0], -1)
+            e2 = np.array([_E2M1_GOLD[c] for c in range(16)])[codes]
+            sc = _E4M3_TORCH[scales].T.repeat(16, axis=1)
+            v = e2 * sc * 256.0
+            assert np.all(v == np.round(v))
+            return v.astype(np.int64)
+        ia = as_int(act, asc)
+        iw = as_int(wgt, wsc)
+        acc = ia @ iw.T                      # int64 matmul: exact
+        assert np.array_equal(S * 65536.0, acc.astype(np.float64))
+        assert np.all(np.abs(acc) < 2 ** 52)
+
+
+def pin_closed_form_constant():
+    """All nibbles and scales constant: y = K * a * sa * w * sw * wc[n] + bias[n] + R * la * lu."""
+    cases = [
+        # (a_code, w_code, a_scale, w_scale, a*sa*w*sw)
+        (2, 2, 0x38, 0x38, 1.0),          # 1.0 * 1.0
+        (5, 12, 0x40, 0x30, -6.0),        # (3 * 2) * (-2 * 0.5)
+        (7, 9, 0x3F, 0x01, -6 * 1.875 * 0.5 * 2.0 ** -9),
+    ]
+    for (ac, wc_, asb, wsb, prod) in cases:
+        M, N, K, R = 3, 5, 64, 4
+        x = _const_inputs(M, N, K, R, ac, wc_, asb, wsb, 0x3F00, 0x3E80)   # 0.5, 0.25
+        y = _y(x)
+        wc = x["wcscale"].astype(np.float64)
+        b = x["bias"].astype(np.float64)
+        want = K * prod * wc + b + R * 0.5 * 0.25
+        assert np.array_equal(y, np.broadcast_to(want, (M, N))), (ac, wc_)
+
+
+def pin_nibble_order():
+    """One nonzero act nibble: its byte's low half is k even, the high half k odd."""
+    M, N, K, R = 4, 6, 64, 2
+    rng = np.random.default_rng(21)
+    for k0 in (18, 19, 0, 63):
+        x = _const_inputs(M, N, K, R, 0, 0, 0x38, 0x38, 0x3F00, 0x3E80)
+        m0, code = 2, 13                                   # -3.0
+        x["act"][m0, k0 // 2] = code << (4 * (k0 % 2))
+        # wgt: low nibbles 2.0, high nibbles 1.0, so the parity of k shows
+        x["wgt"][:] = np.uint8(4 | (2 << 4))
+        x["wscales"] = rng.choice([0x30, 0x38, 0x40, 0x48], size=x["wscales"].shape).astype(
+            np.uint8)
+        y = _y(x)
+        sw = _E4M3_TORCH[x["wscales"][k0 // 16]]
+        wparity = 2.0 if k0 % 2 == 0 else 1.0
+        base = x["bias"].astype(np.float64) + R * 0.125
+        want = np.tile(base, (M, 1))
+        want[m0] += -3.0 * 1.0 * wparity * sw * x["wcscale"].astype(np.float64)
+        assert np.array_equal(y, want), k0
+
+
+def pin_scale_layout():
+    """ascales is [K/16, M] and wscales [K/16, N]: a distinct scale moves one row / column only."""
+    M, N, K, R = 5, 7, 96, 0
+    for (kb0, m0, kb1, n1) in [(1, 3, 4, 2), (2, 0, 2, 6), (5, 4, 0, 0)]:
+        x = _const_inputs(M, N, K, R, 2, 2, 0x38, 0x38, 0, 0)
+        x["ascales"][kb0, m0] = 0x48     # 4.0
+        x["wscales"][kb1, n1] = 0x30     # 0.5
+        y = _y(x)
+        sa = np.ones((K // 16, M))
+        sa[kb0, m0] = 4.0
+        sw = np.ones((K // 16, N))
+        sw[kb1, n1] = 0.5
+        S = 16.0 * (sa.T @ sw)           # sum over blocks of 16 * sa * sw
+        want = S * x["wcscale"].astype(np.float64) + x["bias"].astype(np.float64)
+        assert np.array_equal(y, want), (kb0, m0, kb1, n1)
+
+
+def pin_r0_invariant():
+    """R = 0 gives wc*S + bias; R > 0 with lora_up == 0 gives the very same values."""
+    x = _small(6, 5, 64, 0, 31)
+    y0 = _y(x)
+    x1 = dict(x)
+    x1["R"] = 3
+    rng = np.random.default_rng(3)
+    x1["lora_act_in"] = rng.integers(0, 0x7F00, size=(6, 3)).astype(np.uint16)
+    x1["lora_up"] = np.zeros((3, 5), np.uint16)
+    assert np.array_equal(_y(x1), y0)
+    exact = brute_force(x)
+    assert all(Fraction(y0[m, n]) == exact[m, n] for m in range(6) for n in range(5))
+
+
+def pin_zero_main_term():
+    """All act scales zero (or all act codes zero): y = bias + L, L from exact loops."""
+    for mode in ("scales", "codes"):
+        x = _small(4, 6, 32, 5, 41)
+        if mode == "scales":
+            x["ascales"][:] = 0
+        else:
+            x["act"][:] = 0
+        y = _y(x)
+        exact = brute_force(x)
+        for m in range(4):
+            for n in range(6):
+                assert abs(Fraction(y[m, n]) - exact[m, n]) <= Fraction(2) ** -48, (mode, m, n)
+        # and the LoRA term is visible: without it the result would differ
+        assert not np.allclose(y, x["bias"].astype(np.float64)[None, :], atol=1e-6)
+
+
+def pin_block_deletion():
+    """Zeroing the scales of one k-block equals removing its 16 columns of k."""
+    x = _small(5, 4, 80, 2, 51)
+    for kb in (0, 2, 4):
+        xz = dict(x)
+        xz["ascales"] = x["ascales"].copy()
+        xz["ascales"][kb] = 0
+        keep_bytes = np.r_[0:kb * 8, (kb + 1) * 8:40]
+        keep_blocks = np.r_[0:kb, kb + 1:5]
+        xr = dict(x)
+        xr["act"] = x["act"][:, keep_bytes].copy()
+        xr["wgt"] = x["wgt"][:, keep_bytes].copy()
+        xr["ascales"] = x["ascales"][keep_blocks].copy()
+        xr["wscales"] = x["wscales"][keep_blocks].copy()
+        xr["K"] = 64
+        assert np.array_equal(_y(xz), _y(xr)), kb
+
+
+def pin_linearity():
+    """Doubling wcscale doubles the main term; raising every act scale exponent by one
+    doubles S; adding c to bias adds c."""
+    x = _small(6, 7, 64, 3, 61)
+    y = _y(x)
+    L = ref.lora_product(x["lora_act_in"], x["lora_up"])
+    b = x["bias"].astype(np.float64)
+    main = y - b - L
+    x2 = dict(x)
+    x2["wcscale"] = (x["wcscale"] * 2).astype(np.float32)
+    assert np.allclose(_y(x2) - b - L, 2 * main, rtol=0, atol=1e-9 * np.abs(main).max())
+    x3 = dict(x)
+    x3["ascales"] = (x["ascales"] + 8).astype(np.uint8)      # exponent field + 1
+    assert np.allclose(_y(x3) - b - L, 2 * main, rtol=0, atol=1e-9 * np.abs(main).max())
+    x4 = dict(x)
+    x4["bias"] = (x["bias"] + np.float32(0.75)).astype(np.float32)
+    delta = x4["bias"].astype(np.float64) - b          # the fp32 sum rounds; use its real step
+    assert np.allclose(_y(x4), y + delta[None, :], rtol=0, atol=1e-12 * np.abs(y).max())
+
+
+def pin_transpose_symmetry():
+    """With wc = 1, bias = 0, R = 0, swapping the two operands transposes y."""
+    x = _small(5, 3, 48, 0, 71)
+    x["wcscale"][:] = 1.0
+    x["bias"][:] = 0.0
+    y = _y(x)
+    xt = dict(x)
+    xt.update(act=x["wgt"], ascales=x["wscales"], wgt=x["act"], wscales=x["ascales"],
+              wcscale=np.ones(5, np.float32), bias=np.zeros(5, np.float32),
+              lora_act_in=np.zeros((3, 0), np.uint16), lora_up=np.zeros((0, 5), np.uint16),
+              M=3, N=5)
+    assert np.array_equal(_y(xt), y.T)
+
+
+def pin_subnormal_scales():
+    """Subnormal E4M3 scales (0x01..0x07): small main term, still exact."""
+    x = _small(3, 4, 64, 2, 81)
+    rng = np.random.default_rng(82)
+    x["ascales"] = rng.integers(1, 8, size=x["ascales"].shape).astype(np.uint8)
+    x["wscales"] = rng.integers(1, 8, size=x["wscales"].shape).astype(np.uint8)
+    y = _y(x)
+    exact = brute_force(x)
+    for m in range(3):
+        for n in range(4):
+            assert abs(Fraction(y[m, n]) - exact[m, n]) <= Fraction(2) ** -48, (m, n)
+
+
+def pin_bf16_rounding():
+    with open(os.path.join(GOLDEN, "bf16_rounding.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            expr, bits, _ = [p.strip() for p in line.split(";")]
+            v = eval(expr, {"__builtins__": {}})
+            got = int(ref.bf16_rne_bits(np.array([v]))[0])
+            assert got == int(bits, 16), (expr, hex(got), bits)
+    # values exactly representable in float32 round the same way as torch's RNE cast
+    rng = np.random.default_rng(91)
+    f32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    tb = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ref.bf16_rne_bits(f32.astype(np.float64)), tb)
+
+
+def pin_ulp():
+    u = ref.ulp_bf16(np.array([1.0, 1.5, 2.0, -3.0, 2.0 ** -126, 2.0 ** -130, 0.0, 255.0]))
+    want = [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -133, 2.0 ** -133, 2.0 ** -133,
+            2.0 ** 0]
+    assert list(u) == want
+
+
+def pin_checker():
+    """The acceptance check passes the rounded reference and catches a dropped LoRA or bias
+    term on a case whose main term is zero."""
+    x = _small(8, 8, 32, 4, 101)
+    x["ascales"][:] = 0
+    y = _y(x)
+    T = ref.term_magnitude(*_args(x))
+    assert ref.check_output(ref.bf16_rne_bits(y), y, T)["ok"]
+    no_bias = y - x["bias"].astype(np.float64)[None, :]
+    assert not ref.check_output(ref.bf16_rne_bits(no_bias), y, T)["ok"]
+    no_lora = y - ref.lora_product(x["lora_act_in"], x["lora_up"])
+    assert not ref.check_output(ref.bf16_rne_bits(no_lora), y, T)["ok"]
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ------------------------------------------------------------ mutation test
+
+def _mut_nibble_swap_act_only(mp):
+    # Swapping the nibble order in *both* operands permutes k the same way on
+    # both sides and leaves y unchanged; the real mistake is a mismatch.
+    orig = ref.unpack_codes
+    def swapped(p):
+        c = orig(p)
+        return c.reshape(c.shape[0], -1, 2)[:, :, ::-1].reshape(c.shape)
+    def bad(act, asc, wgt, wsc):
+        codes = swapped(act)
+        A = ref.E2M1_TABLE[codes] * np.repeat(ref.E4M3_TABLE[np.asarray(asc)].T, 16, axis=1)
+        return A @ ref.dequantize(wgt, wsc).T
+    mp.setattr(ref, "main_product", bad)
+
+
+def _mut_scale_rows_as_blocks(mp):
+    def bad(packed, scales):
+        codes = ref.unpack_codes(packed)
+        rows, K = codes.shape
+        s = np.asarray(scales).reshape(-1)[: rows * (K // 16)].reshape(rows, K // 16)
+        return ref.E2M1_TABLE[codes] * np.repeat(ref.E4M3_TABLE[s], 16, axis=1)
+    mp.setattr(ref, "dequantize", bad)
+
+
+def _mut_block32(mp):
+    def bad(packed, scales):
+        codes = ref.unpack_codes(packed)
+        rows, K = codes.shape
+        idx = np.minimum(np.arange(K) // 32, K // 16 - 1)
+        return ref.E2M1_TABLE[codes] * ref.E4M3_TABLE[np.asarray(scales)[idx, :].T]
+    mp.setattr(ref, "dequantize", bad)
+
+
+def _mut_lora_scaled(mp):
+    def bad(*a):
+        S = ref.main_product(*a[:4])
+        wc = np.asarray(a[4], np.float64)
+        return wc * (S + ref.lora_product(a[6], a[7])) + np.asarray(a[5], np.float64)
+    mp.setattr(ref, "gemm_w4a4_ref", bad)
+
+
+def _mut_drop_bias(mp):
+    def bad(*a):
+        S = ref.main_product(*a[:4])
+        return np.asarray(a[4], np.float64) * S + ref.lora_product(a[6], a[7])
+    mp.setattr(ref, "gemm_w4a4_ref", bad)
+
+
+def _mut_e2m1_unsigned(mp):
+    mp.setattr(ref, "E2M1_TABLE", np.abs(ref.E2M1_TABLE))
+
+
+def _mut_e2m1_subnormal(mp):
+    t = ref.E2M1_TABLE.copy()
+    t[1], t[9] = 0.75, -0.75
+    mp.setattr(ref, "E2M1_TABLE", t)
+
+
+def _mut_e4m3_bias8(mp):
+    mp.setattr(ref, "E4M3_TABLE", ref.E4M3_TABLE / 2)
+
+
+def _mut_e4m3_subnormal_as_normal(mp):
+    t = ref.E4M3_TABLE.copy()
+    for m in range(1, 8):
+        t[m] = (1 + m / 8) * 2.0 ** -7
+    mp.setattr(ref, "E4M3_TABLE", t)
+
+
+def _mut_lora_up_transposed(mp):
+    def bad(la, lu):
+        a = ref.bf16_bits_to_f64(la)
+        u = ref.bf16_bits_to_f64(lu)
+        if a.shape[1] == 0:
+            return np.zeros((a.shape[0], u.shape[1]))
+        # reads lora_up as if it were stored [N, R]
+        ut = u.reshape(-1)[: u.size].reshape(u.shape[1], u.shape[0]).T
+        return a @ ut
+    mp.setattr(ref, "lora_product", bad)
+
+
+def _mut_wgt_transposed_scales(mp):
+    orig = ref.main_product
+    def bad(act, asc, wgt, wsc):
+        A = ref.dequantize(act, asc)
+        wflip = np.asarray(wsc)[::-1].copy()    # blocks in reverse order
+        W = ref.dequantize(wgt, wflip)
+        return A @ W.T
+    mp.setattr(ref, "main_product", bad)
+
+
+def _mut_bf16_truncate(mp):
+    def bad(y):
+        y32 = np.asarray(y, np.float64).astype(np.float32)
+        return (y32.view(np.uint32) >> 16).astype(np.uint16)
+    mp.setattr(ref, "bf16_rne_bits", bad)
+
+
+MUTANTS = [v for k, v in sorted(globals().items()) if k.startswith("_mut_")]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
+def test_pins_catch_planted_mistake(mutant, monkeypatch):
+    with monkeypatch.context() as mp:
+        mutant(mp)
+        failed = []
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError, IndexError):
+                failed.append(pin.__name__)
+        assert failed, f"no pin caught {mutant.__name__}"
