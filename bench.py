@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Throughput of the fused NVFP4 W4A4 GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload qkv] [--gpus 1]
+
+One step is one call of gemm_w4a4 (the whole operator: loader, decode, MFMA
+K-loop, wcscale, LoRA-up, bias, bf16 store) on inputs already resident in HBM.
+Prints one JSON line. TFLOP/s counts the algorithmic 2MNK + 2MRN flops.
+
+The JSON carries:
+  roofline      achieved TFLOP/s of the kernel (per-launch HIP events on the
+                launch stream) against the dense fp16 MFMA peak of MI355X
+                (2.5 PFLOP/s), plus the fraction of the dense FP4 peak; traffic
+                = HBM bytes per launch from the committed rocprofv3 counter
+                summary when it was taken on the current kernel source, else null
+  cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on a bounded row
+                sample of the same workload on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", f)
+                  for f in ("gemm_w4a4.hip", "w4a4_layout.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_traffic.txt, if that
+    summary was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"gemm_w4a4_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inputs: dict, rows: int) -> dict:
+    """Time the CPU oracle (as it stands) on the first `rows` output rows."""
+    import numpy as np
+
+    import oracle.w4a4_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    sel = np.arange(rows)
+    args = (inputs["act"][sel], inputs["ascales"][:, sel], inputs["wgt"], inputs["wscales"],
+            inputs["wcscale"], inputs["bias"], inputs["lora_act_in"][sel], inputs["lora_up"])
+    t0 = time.perf_counter()
+    ref.gemm_w4a4_ref(*args)
+    dt = time.perf_counter() - t0
+    M, N, K, R = inputs["M"], inputs["N"], inputs["K"], inputs["R"]
+    flops = 2 * rows * N * K + 2 * rows * R * N
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of M={M} (all N={N}, K={K}, R={R}); "
+                      f"{dt:.2f} s; decode single-threaded numpy, dgemm on {threads} BLAS threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qkv")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of the CPU-oracle baseline sample (0 skips it)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter scale probe)")
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this operator needs no cross-GPU work and "
+              "this build runs on a single MI355X (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_gemm_amd as w4
+    import synthetic
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    wl = synthetic.workload(a.workload)
+    x = synthetic.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(x[k]).to(dev) for k in ("act", "ascales", "wgt", "wscales",
+                                                     "wcscale", "bias")}
+    la = torch.from_numpy(x["lora_act_in"].view(np.int16)).view(torch.bfloat16).to(dev)
+    lu = torch.from_numpy(x["lora_up"].view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        w4.gemm_w4a4(t["act"], t["ascales"], t["wgt"], t["wscales"], t["wcscale"], t["bias"],
+                     la, lu, out=out, stream=stream)
+
+    if a.copy_probe_mb > 0:
+        src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    region_ms = starts[0].elapsed_time(ends[-1])
+
+    # a sampled parity check of the timed output (first rows) against the oracle
+    import oracle.w4a4_ref as ref
+    rows = np.arange(min(16, wl.M))
+    y, T = ref.reference_rows(x, rows)
+    got = out[:len(rows)].view(torch.int16).cpu().numpy().view(np.uint16)
+    chk = ref.check_output(got, y, T)
+
+    flops = wl.flops()
+    ms_per_step = region_ms / a.steps
+    avg_launch_ms = float(np.mean(per_launch_ms))
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    value = flops * a.steps / (region_ms * 1e-3) / 1e12
+    traffic = committed_traffic(a.workload)
+    plan = w4.plan(*wl.shape)
+    res = {
+        "metric": "W4A4 GEMM TFLOP/s + % of used-MFMA/FP4 peak, M=4096 N=K=3072 R=32",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
+                   "operands": "NVFP4 (E2M1 + E4M3 per 16 k), LoRA bf16, out bf16",
+                   "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_MFMA_TFLOPS, 4),
+                     "traffic": traffic,
+                     "frac_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "min_launch_us": round(min(per_launch_ms) * 1e3, 2),
+                     "kernel_source_sha256": kernel_source_hash()},
+        "parity_sample": {"rows": int(len(rows)), "max_err_over_bound": round(chk["max_ratio"], 4),
+                          "ok": chk["ok"]},
+        "wall_s": round(wall, 3),
+    }
+    if a.cpu_rows > 0:
+        res["cpu_baseline"] = cpu_baseline(x, min(a.cpu_rows, wl.M))
+    print(json.dumps(res), flush=True)
+    return 0 if chk["ok"] else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,89 @@
+"""Fused NVFP4 W4A4 GEMM for AMD Instinct MI355X (gfx950).
+
+    y = scaled_mma(act4, wgt4) * wcscale + bias + lora_act_in @ lora_up
+
+Python binding over the C ABI of libgemm_w4a4.so (include/gemm_w4a4.h).
+PyTorch supplies device memory and the stream; every step of the operator runs
+in the library's HIP kernels. If the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+from . import _native
+from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, MAX_R, OK, gemm_w4a4_raw,
+                      library_path, plan, strerror, variants)
+
+__all__ = ["gemm_w4a4", "gemm_w4a4_raw", "plan", "variants", "strerror", "library_path",
+           "GemmError", "OK", "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R"]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"gemm_w4a4 failed: {strerror(code)} ({code})")
+        self.code = code
+
+
+def _check(t, name, dtype, shape, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_up=None,
+              out=None, stream=None):
+    """Enqueue the fused operator on `stream` (default: torch's current stream).
+
+    act uint8 [M, K/2]; ascales uint8 (or float8_e4m3fn) [K/16, M];
+    wgt uint8 [N, K/2]; wscales uint8 (or float8_e4m3fn) [K/16, N];
+    wcscale, bias float32 [N]; lora_act_in bfloat16 [M, R]; lora_up bfloat16 [R, N]
+    (both None for R = 0). Returns out, bfloat16 [M, N] (allocated if None).
+    """
+    import torch
+    if act.dim() != 2 or wgt.dim() != 2:
+        raise ValueError("act and wgt must be 2-D")
+    device = act.device
+    if device.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    M, half = act.shape
+    N = wgt.shape[0]
+    K = 2 * half
+    if ascales.dtype == torch.float8_e4m3fn:
+        ascales = ascales.view(torch.uint8)
+    if wscales.dtype == torch.float8_e4m3fn:
+        wscales = wscales.view(torch.uint8)
+    _check(act, "act", torch.uint8, (M, half), device)
+    _check(wgt, "wgt", torch.uint8, (N, half), device)
+    _check(ascales, "ascales", torch.uint8, (K // 16, M), device)
+    _check(wscales, "wscales", torch.uint8, (K // 16, N), device)
+    _check(wcscale, "wcscale", torch.float32, (N,), device)
+    _check(bias, "bias", torch.float32, (N,), device)
+    if (lora_act_in is None) != (lora_up is None):
+        raise ValueError("lora_act_in and lora_up go together")
+    if lora_act_in is None:
+        R = 0
+        la_ptr = lu_ptr = 0
+    else:
+        R = lora_act_in.shape[1]
+        _check(lora_act_in, "lora_act_in", torch.bfloat16, (M, R), device)
+        _check(lora_up, "lora_up", torch.bfloat16, (R, N), device)
+        la_ptr, lu_ptr = lora_act_in.data_ptr(), lora_up.data_ptr()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _check(out, "out", torch.bfloat16, (M, N), device)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(device):
+        rc = gemm_w4a4_raw(act.data_ptr(), ascales.data_ptr(), wgt.data_ptr(),
+                           wscales.data_ptr(), wcscale.data_ptr(), bias.data_ptr(), la_ptr,
+                           lu_ptr, out.data_ptr(), M, N, K, R, handle)
+    if rc != OK:
+        raise GemmError(rc)
+    return out

@@ -1,0 +1,96 @@
+"""ctypes view of the C ABI declared in include/gemm_w4a4.h.
+
+Only argument marshalling lives here: every step of the operator runs in the
+HIP kernels of libgemm_w4a4.so. There is no fallback; if the library is
+missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+OK = 0
+EINVAL = -1
+EALIGN = -2
+ELAUNCH = -3
+EOVERLAP = -4
+EDEVICE = -5
+MAX_R = 1024
+
+_PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n",
+                "threads", "lds_bytes", "lds_stage_bytes", "lds_limit", "tiles_m", "tiles_n",
+                "grid", "k_stages", "lora_steps")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in _PLAN_FIELDS]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f in _PLAN_FIELDS}
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libgemm_w4a4.so (once). Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m bit_quantized_gemm_amd.build "
+                "or __graft_entry__.build()); there is no non-HIP fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        lib.gemm_w4a4.argtypes = [vp] * 9 + [i, i, i, i, vp]
+        lib.gemm_w4a4.restype = i
+        lib.gemm_w4a4_plan.argtypes = [i, i, i, i, ctypes.POINTER(Plan)]
+        lib.gemm_w4a4_plan.restype = i
+        lib.gemm_w4a4_num_variants.argtypes = []
+        lib.gemm_w4a4_num_variants.restype = i
+        lib.gemm_w4a4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
+        lib.gemm_w4a4_variant_info.restype = i
+        lib.gemm_w4a4_strerror.argtypes = [i]
+        lib.gemm_w4a4_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def strerror(code: int) -> str:
+    return load().gemm_w4a4_strerror(code).decode()
+
+
+def gemm_w4a4_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                  M, N, K, R, stream) -> int:
+    """Direct call of the C entry point with integer addresses; returns its code."""
+    return load().gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                            out, M, N, K, R, stream)
+
+
+def plan(M: int, N: int, K: int, R: int) -> dict:
+    p = Plan()
+    rc = load().gemm_w4a4_plan(M, N, K, R, ctypes.byref(p))
+    if rc != OK:
+        raise ValueError(f"gemm_w4a4_plan: {strerror(rc)} ({rc})")
+    return p.as_dict()
+
+
+def variants() -> list:
+    lib = load()
+    out = []
+    for v in range(lib.gemm_w4a4_num_variants()):
+        p = Plan()
+        if lib.gemm_w4a4_variant_info(v, ctypes.byref(p)) != OK:
+            raise RuntimeError("variant_info failed")
+        out.append(p.as_dict())
+    return out

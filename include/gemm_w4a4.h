@@ -1,0 +1,120 @@
+/*
+ * gemm_w4a4.h — C ABI of the fused NVFP4 W4A4 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (section 2 of the SVDQuant W4A4 on Blackwell page,
+ * "Blackwell 上的 SVDQuant W4A4 算子实现"):
+ *
+ *     y[m,n] = wcscale[n] * sum_k A[m,k] * W[n,k] + bias[n]
+ *              + sum_r lora_act_in[m,r] * lora_up[r,n]
+ *
+ * where A and W are NVFP4: E2M1 codes (two per byte) times one FP8-E4M3 block
+ * scale per 16 consecutive k (same page, section 3.1: single-level block
+ * scaling, no per-tensor factor). The per-column affine is the page's
+ * section 6.6 epilogue; the LoRA residual is added after the wcscale product,
+ * as the section 2 formula writes it. The result is rounded to bfloat16
+ * (nearest, ties to even).
+ *
+ * Layouts: every tensor is dense and row-major, without padding or strides.
+ *   act          uint8   [M, K/2]   byte j of row m holds k = 2j (low nibble)
+ *                                   and k = 2j+1 (high nibble)
+ *   ascales      uint8   [K/16, M]  OCP E4M3FN bytes; scale of (m,k) is
+ *                                   ascales[k/16][m]
+ *   wgt          uint8   [N, K/2]   as act, one row per output column n
+ *   wscales      uint8   [K/16, N]
+ *   wcscale      float   [N]
+ *   bias         float   [N]
+ *   lora_act_in  uint16  [M, R]     bfloat16 bit patterns
+ *   lora_up      uint16  [R, N]     bfloat16 bit patterns
+ *   out          uint16  [M, N]     bfloat16 bit patterns (written)
+ *
+ * Ownership: every tensor pointer is a device pointer owned by the caller.
+ * The library allocates and frees nothing, keeps no per-call state, and never
+ * synchronizes: a successful call only enqueues work on `stream`.
+ */
+#ifndef GEMM_W4A4_H
+#define GEMM_W4A4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. Validation runs before any HIP call, so on a negative code
+ * nothing has been enqueued. No C++ exception crosses this boundary. */
+enum {
+  GEMM_W4A4_OK = 0,
+  GEMM_W4A4_EINVAL = -1,      /* bad size (M<1, N<1, K<16, K%16, R<0, R>GEMM_W4A4_MAX_R,
+                                 or any tensor of 2^31 bytes or more) or a required
+                                 NULL pointer */
+  GEMM_W4A4_EALIGN = -2,      /* act/wgt not 16-byte aligned, wcscale/bias not 4-byte,
+                                 lora/out not 2-byte aligned */
+  GEMM_W4A4_ELAUNCH = -3,     /* the HIP launch itself failed */
+  GEMM_W4A4_EOVERLAP = -4,    /* out overlaps an input */
+  GEMM_W4A4_EDEVICE = -5      /* the current device is not gfx950 */
+};
+
+#define GEMM_W4A4_MAX_R 1024
+
+/*
+ * gemm_w4a4 — enqueue y = scaled_mma(act, wgt) * wcscale + bias + lora_act_in @ lora_up.
+ *
+ * act, ascales, wgt, wscales, wcscale, bias, out: required (non-NULL).
+ * lora_act_in, lora_up: may be NULL only when R == 0 (no LoRA term).
+ * M, N >= 1; K >= 16 with K % 16 == 0; 0 <= R <= GEMM_W4A4_MAX_R.
+ * stream: a hipStream_t passed as void*; NULL selects the null stream.
+ *
+ * Every out[m][n] with m < M, n < N is overwritten; nothing else is written
+ * and no input is modified. Results are deterministic: the same inputs give
+ * the same bytes on every call (no atomics, no split-K). E4M3 NaN scale bytes
+ * (0x7F, 0xFF) propagate NaN into every output their block touches.
+ * Returns GEMM_W4A4_OK or one of the negative codes above.
+ */
+int gemm_w4a4(const uint8_t* act, const uint8_t* ascales,
+              const uint8_t* wgt, const uint8_t* wscales,
+              const float* wcscale, const float* bias,
+              const uint16_t* lora_act_in, const uint16_t* lora_up,
+              uint16_t* out, int M, int N, int K, int R, void* stream);
+
+/*
+ * Launch plan chosen by the LDS/register budget solver for one problem size.
+ * Filled by gemm_w4a4_plan; pure host arithmetic (no HIP call), so it also
+ * runs on a machine without a GPU.
+ */
+typedef struct {
+  int variant;        /* index of the compiled kernel instance */
+  int block_m;        /* output rows per workgroup tile */
+  int block_n;        /* output columns per workgroup tile */
+  int block_k;        /* k per pipeline stage */
+  int stages;         /* LDS stages of the operand ring */
+  int waves_m;        /* wave grid inside a workgroup */
+  int waves_n;
+  int threads;        /* threads per workgroup */
+  int lds_bytes;      /* LDS the instance uses, from the same layout the kernel carves */
+  int lds_stage_bytes;/* bytes of one ring stage (packed A + packed B) */
+  int lds_limit;      /* LDS available to one workgroup on gfx950 */
+  int tiles_m;
+  int tiles_n;
+  int grid;           /* workgroups launched */
+  int k_stages;       /* pipeline iterations over K */
+  int lora_steps;     /* 16-deep LoRA MFMA steps (ceil(R/16)) */
+} gemm_w4a4_plan_t;
+
+/* Fill *plan for (M, N, K, R). Returns GEMM_W4A4_OK or GEMM_W4A4_EINVAL
+ * (same size rules as gemm_w4a4; plan may not be NULL). */
+int gemm_w4a4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan);
+
+/* Number of compiled kernel instances, and the plan fields fixed by instance
+ * `variant` (problem-size fields are zero). Returns GEMM_W4A4_EINVAL for an
+ * unknown index. Used to check the solver against the compiled code objects. */
+int gemm_w4a4_num_variants(void);
+int gemm_w4a4_variant_info(int variant, gemm_w4a4_plan_t* plan);
+
+/* Static string for a return code (never NULL). */
+const char* gemm_w4a4_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_W4A4_H */

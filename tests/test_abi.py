@@ -1,0 +1,168 @@
+"""The C-ABI library: loads, exports what include/*.h declares, validates its
+arguments, and its budget solver agrees with the compiled code objects.
+
+CPU only: no call here reaches a kernel launch. Invalid-argument calls return
+before any HIP call; the metadata check reads the library's own code object.
+"""
+import ctypes
+import glob
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import bit_quantized_gemm_amd as w4
+from bit_quantized_gemm_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gemm_w4a4\w*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _native.load()
+    names = _declared_functions()
+    assert "gemm_w4a4" in names and len(names) >= 5
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", w4.library_path()],
+                        capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def _call(**over):
+    # plausible fake device addresses: validation must reject before using them
+    a = dict(act=0x10000, ascales=0x20000, wgt=0x30000, wscales=0x40000, wcscale=0x50000,
+             bias=0x60000, lora_act_in=0x70000, lora_up=0x80000, out=0x90000000,
+             M=64, N=64, K=128, R=16, stream=0)
+    a.update(over)
+    return w4.gemm_w4a4_raw(a["act"], a["ascales"], a["wgt"], a["wscales"], a["wcscale"],
+                            a["bias"], a["lora_act_in"], a["lora_up"], a["out"], a["M"], a["N"],
+                            a["K"], a["R"], a["stream"])
+
+
+@pytest.mark.parametrize("over", [
+    dict(M=0), dict(N=0), dict(K=0), dict(K=8), dict(K=24), dict(R=-1), dict(M=-5),
+    dict(R=w4.MAX_R + 1), dict(act=0), dict(ascales=0), dict(wgt=0), dict(wscales=0),
+    dict(wcscale=0), dict(bias=0), dict(out=0), dict(lora_act_in=0), dict(lora_up=0),
+    dict(M=70000, K=70000),                         # act over 2^31 bytes
+    dict(M=1 << 20, N=1 << 12),                     # out over 2^31 bytes
+])
+def test_invalid_arguments(over):
+    assert _call(**over) == w4.EINVAL
+
+
+@pytest.mark.parametrize("over", [
+    dict(act=0x10008), dict(wgt=0x30004), dict(wcscale=0x50002), dict(bias=0x60001),
+    dict(out=0x90000001), dict(lora_act_in=0x70001), dict(lora_up=0x80003),
+])
+def test_misaligned(over):
+    assert _call(**over) == w4.EALIGN
+
+
+def test_null_lora_allowed_without_rank():
+    # with R == 0 the LoRA pointers are not needed; validation passes and only the
+    # device check (no GPU here) can fail
+    rc = _call(R=0, lora_act_in=0, lora_up=0)
+    assert rc in (w4.EDEVICE, w4.ELAUNCH, w4.OK)
+    assert rc != w4.EINVAL
+
+
+@pytest.mark.parametrize("target", ["act", "ascales", "wgt", "wscales", "wcscale", "bias",
+                                    "lora_act_in", "lora_up"])
+def test_output_overlapping_an_input(target):
+    assert _call(**{target: 0x90000000 + 256}) == w4.EOVERLAP
+
+
+def test_strerror():
+    for code in (w4.OK, w4.EINVAL, w4.EALIGN, w4.ELAUNCH, w4.EOVERLAP, w4.EDEVICE, -99):
+        assert isinstance(w4.strerror(code), str) and w4.strerror(code)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 512, 32), (4096, 3072, 3072, 32),
+                                   (4096, 12288, 3072, 32), (4096, 3072, 12288, 128),
+                                   (1000, 3072, 3072, 16), (1, 1, 16, 0), (7, 33, 144, 3)])
+def test_plan(shape):
+    M, N, K, R = shape
+    p = w4.plan(M, N, K, R)
+    assert p["tiles_m"] * p["block_m"] >= M and (p["tiles_m"] - 1) * p["block_m"] < M
+    assert p["tiles_n"] * p["block_n"] >= N and (p["tiles_n"] - 1) * p["block_n"] < N
+    assert p["grid"] == p["tiles_m"] * p["tiles_n"]
+    assert p["k_stages"] == -(-K // p["block_k"])
+    assert p["lora_steps"] == -(-R // 16)
+    assert p["lds_bytes"] <= p["lds_limit"] == 163840
+    assert p["threads"] == 64 * p["waves_m"] * p["waves_n"]
+    with pytest.raises(ValueError):
+        w4.plan(M, N, K + 8, R)
+
+
+def test_plan_prefers_full_chip_at_qkv():
+    # 4096 x 3072 in 256 x 192 tiles is exactly one tile per compute unit
+    p = w4.plan(4096, 3072, 3072, 32)
+    assert (p["block_m"], p["block_n"]) == (256, 192) and p["grid"] == 256
+
+
+def _code_object_metadata():
+    lib = w4.library_path()
+    tmp = os.path.join(ROOT, "_build_meta")
+    os.makedirs(tmp, exist_ok=True)
+    fat = os.path.join(tmp, "fatbin.bin")
+    co = os.path.join(tmp, "co.o")
+    subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", lib],
+                   check=True)
+    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
+                    f"--input={fat}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                    f"--output={co}"], check=True)
+    notes = subprocess.run([f"{LLVM}/llvm-readelf", "--notes", co], capture_output=True,
+                           text=True, check=True).stdout
+    shutil.rmtree(tmp, ignore_errors=True)
+    kernels = {}
+    cur = {}
+    for line in notes.splitlines():
+        line = line.strip().lstrip("- ").strip()
+        if ":" not in line:
+            continue
+        k, _, v = line.partition(":")
+        k, v = k.strip(), v.strip()
+        if k in (".agpr_count", ".args") and cur.get(".name"):
+            kernels[cur[".name"]] = cur
+            cur = {}
+        cur[k] = v
+    if cur.get(".name"):
+        kernels[cur[".name"]] = cur
+    return kernels
+
+
+@pytest.mark.skipif(not os.path.exists(f"{LLVM}/clang-offload-bundler"), reason="no ROCm llvm")
+def test_solver_lds_matches_code_objects():
+    """The LDS bytes the solver budgets equal what the compiler reserved
+    (ratio 1.000) for every compiled instance; the register count allows the
+    occupancy each instance is budgeted for; nothing spills inside a kernel
+    that the solver may pick for a full-chip workload."""
+    meta = _code_object_metadata()
+    assert meta, "no kernels found in the code object"
+    for v in w4.variants():
+        key = "TileCfgILi%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
+                                                    v["waves_n"], v["stages"])
+        hits = [m for n, m in meta.items() if key in n]
+        assert len(hits) == 2, (key, list(meta))     # rows 16-byte multiple or not
+        for m in hits:
+            assert int(m[".group_segment_fixed_size"]) == v["lds_bytes"], (key, m)
+            regs = int(m[".vgpr_count"])
+            waves_per_simd = max(1, (v["waves_m"] * v["waves_n"] + 3) // 4)
+            occ = v["lds_limit"] // v["lds_bytes"]
+            assert regs * waves_per_simd <= 512, (key, regs)
+            assert occ >= 1

@@ -1,0 +1,286 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle. Needs a gfx950 GPU.
+
+Acceptance per element: |y_gpu - y_ref| <= 4e-3 * T + 1 bf16 ulp(y_ref), with
+T = |wcscale| sum_k |A W| + |bias| + sum_r |la lu| (oracle.check_output). Where
+the exact result is representable in bf16 the check is bit-for-value exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_gemm_amd as w4
+import oracle.w4a4_ref as ref
+import synthetic
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ARGS = ("act", "ascales", "wgt", "wscales", "wcscale", "bias", "lora_act_in", "lora_up")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(x):
+    d = {}
+    for k in ("act", "ascales", "wgt", "wscales"):
+        d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(DEV)
+    d["wcscale"] = torch.from_numpy(np.ascontiguousarray(x["wcscale"])).to(DEV)
+    d["bias"] = torch.from_numpy(np.ascontiguousarray(x["bias"])).to(DEV)
+    if x["R"] > 0:
+        for k in ("lora_act_in", "lora_up"):
+            t = torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16))
+            d[k] = t.view(torch.bfloat16).to(DEV)
+    else:
+        d["lora_act_in"] = d["lora_up"] = None
+    return d
+
+
+def run_gpu(x, out=None):
+    d = to_device(x)
+    o = w4.gemm_w4a4(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+                     d["lora_act_in"], d["lora_up"], out=out)
+    torch.cuda.synchronize()
+    return o.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_full(x):
+    a = [x[k] for k in ARGS]
+    return ref.gemm_w4a4_ref(*a), ref.term_magnitude(*a)
+
+
+def assert_parity(got, y, T, what):
+    res = ref.check_output(got, y, T)
+    _say(f"  {what}: max err/bound {res['max_ratio']:.3g}, failures {res['n_fail']}")
+    assert res["ok"], (what, res)
+
+
+def const_inputs(M, N, K, R, a_code, w_code, a_scale, w_scale, la_bits=0x3F00, lu_bits=0x3E80,
+                 seed=5):
+    rng = np.random.default_rng(seed)
+    byte = lambda c: np.uint8(c | (c << 4))
+    return dict(
+        act=np.full((M, K // 2), byte(a_code), np.uint8),
+        ascales=np.full((K // 16, M), a_scale, np.uint8),
+        wgt=np.full((N, K // 2), byte(w_code), np.uint8),
+        wscales=np.full((K // 16, N), w_scale, np.uint8),
+        wcscale=rng.uniform(0.5, 1.5, N).astype(np.float32),
+        bias=rng.standard_normal(N).astype(np.float32),
+        lora_act_in=np.full((M, R), la_bits, np.uint16),
+        lora_up=np.full((R, N), lu_bits, np.uint16), M=M, N=N, K=K, R=R)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_tiny_full():
+    _say("case: tiny workload 256x256x512 R=32, full comparison")
+    x = synthetic.make_inputs("tiny")
+    got = run_gpu(x)
+    y, T = oracle_full(x)
+    assert_parity(got, y, T, "tiny")
+
+
+def _sample_rows(M, block_m, rng):
+    rows = set(range(0, min(M, 40)))                          # first tile head
+    rows |= set(range(max(0, M - 40), M))                     # last (ragged) rows
+    for t in range(0, M, block_m):                            # tile boundaries
+        rows |= {t, min(M - 1, t + block_m - 1)}
+    rows |= set(rng.choice(M, size=min(M, 64), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "ragged"])
+def test_workload_full_size_sampled(name):
+    wl = synthetic.workload(name)
+    _say(f"case: {name} {wl.shape}, full-size launch, sampled rows vs oracle")
+    x = synthetic.make_inputs(name)
+    got = run_gpu(x)
+    plan = w4.plan(*wl.shape)
+    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(7))
+    y, T = ref.reference_rows(x, rows)
+    assert_parity(got[rows], y, T, f"{name} ({len(rows)} rows x {wl.N})")
+    # every output is finite (no NaN scale bytes in these inputs)
+    vals = (got.astype(np.uint32) << 16).view(np.float32)
+    assert np.isfinite(vals).all()
+
+
+def test_deterministic_bytes():
+    _say("case: determinism, ragged workload twice")
+    x = synthetic.make_inputs("ragged")
+    assert np.array_equal(run_gpu(x), run_gpu(x))
+
+
+# ---------------------------------------------------------------- exhaustive decode
+
+def _decode_case(side):
+    """Every (E2M1 code, E4M3 byte) pair on one operand side, exact output expected."""
+    rows = 16 * 256
+    code = np.arange(rows) % 16
+    sbyte = (np.arange(rows) // 16).astype(np.uint8)
+    packed = (code | (code << 4)).astype(np.uint8)[:, None].repeat(8, axis=1)
+    other = 64
+    x = dict(K=16, R=0, lora_act_in=None, lora_up=None)
+    one_packed = np.full((other, 8), 0x22, np.uint8)           # all 1.0
+    one_scale = np.full((1, other), 0x38, np.uint8)            # 1.0
+    if side == "act":
+        x.update(M=rows, N=other, act=packed, ascales=sbyte[None, :], wgt=one_packed,
+                 wscales=one_scale)
+    else:
+        x.update(M=other, N=rows, act=one_packed, ascales=one_scale, wgt=packed,
+                 wscales=sbyte[None, :])
+    x["wcscale"] = np.full(x["N"], 1 / 16, np.float32)          # 16 equal terms -> exact
+    x["bias"] = np.zeros(x["N"], np.float32)
+    x["lora_act_in"] = np.zeros((x["M"], 0), np.uint16)
+    x["lora_up"] = np.zeros((0, x["N"]), np.uint16)
+    return x
+
+
+@pytest.mark.parametrize("side", ["act", "wgt"])
+def test_decode_exhaustive(side):
+    _say(f"case: exhaustive decode, {side} side, 16 codes x 256 scale bytes")
+    x = _decode_case(side)
+    got = run_gpu(x)
+    y, T = oracle_full(x)
+    gv = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nan_y = np.isnan(y)
+    assert np.array_equal(np.isnan(gv), nan_y)
+    assert np.array_equal(gv[~nan_y], y[~nan_y])                # exact, value for value
+
+
+# ---------------------------------------------------------------- structured probes
+
+def test_probe_closed_form():
+    _say("case: closed form, constant codes and scales, R=4")
+    for (ac, wc_, asb, wsb) in [(2, 2, 0x38, 0x38), (5, 12, 0x40, 0x30), (7, 9, 0x3F, 0x01)]:
+        x = const_inputs(300, 200, 256, 4, ac, wc_, asb, wsb)
+        y, T = oracle_full(x)
+        assert_parity(run_gpu(x), y, T, f"closed form {ac},{wc_}")
+
+
+def test_probe_nibble_and_scale_layout():
+    _say("case: single-nibble and single-scale probes")
+    rng = np.random.default_rng(3)
+    for k0 in (0, 19, 200, 255):
+        x = const_inputs(70, 90, 256, 2, 0, 0, 0x38, 0x38)
+        x["act"][33, k0 // 2] = 13 << (4 * (k0 % 2))
+        x["wgt"][:] = np.uint8(4 | (2 << 4))
+        x["wscales"] = rng.choice([0x30, 0x38, 0x40, 0x48], size=x["wscales"].shape).astype(
+            np.uint8)
+        y, T = oracle_full(x)
+        assert_parity(run_gpu(x), y, T, f"nibble k0={k0}")
+    for (kb0, m0, kb1, n1) in [(1, 3, 4, 2), (2, 250, 2, 190), (15, 299, 0, 0)]:
+        x = const_inputs(300, 200, 256, 0, 2, 2, 0x38, 0x38)
+        x["lora_act_in"] = np.zeros((300, 0), np.uint16)
+        x["lora_up"] = np.zeros((0, 200), np.uint16)
+        x["ascales"][kb0, m0] = 0x48
+        x["wscales"][kb1, n1] = 0x30
+        y, T = oracle_full(x)
+        got = run_gpu(x)
+        assert_parity(got, y, T, f"scale probe {(kb0, m0, kb1, n1)}")
+        gv = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        # main term 16 * (integers) * wc: compare the rounded values exactly
+        assert np.array_equal(gv, ref.bf16_bits_to_f64(ref.bf16_rne_bits(y)))
+
+
+def test_probe_zero_main_term_shows_lora_and_bias():
+    """All act scales zero: y = bias + LoRA, O(1), so a dropped or mis-scaled
+    LoRA or bias term fails the tolerance."""
+    _say("case: zero main term, LoRA + bias visible")
+    for R in (1, 16, 32, 128, 3):
+        x = synthetic.custom_inputs(260, 200, 256, R, seed=100 + R)
+        x["ascales"][:] = 0
+        y, T = oracle_full(x)
+        got = run_gpu(x)
+        assert_parity(got, y, T, f"zero main R={R}")
+        # tighter than the tolerance: fp32 sum of at most R+1 terms
+        gv = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(gv - y) <= 2 * ref.ulp_bf16(y) + 1e-6)
+
+
+def test_probe_subnormal_scales():
+    _say("case: subnormal E4M3 scales, small main term")
+    x = synthetic.custom_inputs(256, 192, 3072, 32, seed=9)
+    rng = np.random.default_rng(10)
+    x["ascales"] = rng.integers(1, 8, size=x["ascales"].shape).astype(np.uint8)
+    x["wscales"] = rng.integers(1, 8, size=x["wscales"].shape).astype(np.uint8)
+    y, T = oracle_full(x)
+    assert_parity(run_gpu(x), y, T, "subnormal scales")
+
+
+def test_probe_r0_equals_zero_lora_up():
+    _say("case: R=0 (no LoRA pointers) equals R=16 with lora_up = 0")
+    x = synthetic.custom_inputs(300, 260, 384, 16, seed=21)
+    x0 = dict(x)
+    x0["R"] = 0
+    x0["lora_act_in"] = np.zeros((300, 0), np.uint16)
+    x0["lora_up"] = np.zeros((0, 260), np.uint16)
+    xz = dict(x)
+    xz["lora_up"] = np.zeros_like(x["lora_up"])
+    g0 = run_gpu(x0)
+    assert np.array_equal(g0, run_gpu(xz))
+    y, T = oracle_full(x0)
+    assert_parity(g0, y, T, "R=0")
+
+
+def test_probe_nan_scale_propagates():
+    _say("case: NaN scale byte")
+    x = synthetic.custom_inputs(64, 64, 64, 0, seed=31)
+    x["ascales"][1, 5] = 0x7F
+    x["wscales"][3, 9] = 0xFF
+    got = run_gpu(x)
+    y, T = oracle_full(x)
+    assert_parity(got, y, T, "nan scale")
+    gv = (got.astype(np.uint32) << 16).view(np.float32)
+    assert np.isnan(gv[5]).all() and np.isnan(gv[:, 9]).all()
+    assert np.isfinite(np.delete(np.delete(gv, 5, 0), 9, 1)).all()
+
+
+# ---------------------------------------------------------------- edge shapes
+
+EDGE = [(1, 1, 16, 0), (1, 5, 16, 1), (7, 33, 48, 3), (33, 200, 144, 16), (257, 193, 272, 32),
+        (300, 129, 160, 17), (64, 64, 4096, 128), (513, 385, 256, 128), (129, 1, 32, 8),
+        (2, 1000, 112, 24), (1000, 64, 208, 40)]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
+def test_edge_shapes(shape):
+    M, N, K, R = shape
+    _say(f"case: edge shape M={M} N={N} K={K} R={R}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=M * 7 + N * 13 + K + R)
+    y, T = oracle_full(x)
+    assert_parity(run_gpu(x), y, T, f"edge {shape}")
+
+
+def test_no_write_outside_output():
+    _say("case: guard band around out")
+    M, N, K, R = 257, 193, 272, 32
+    x = synthetic.custom_inputs(M, N, K, R, seed=77)
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 0x5A5A, dtype=torch.int16, device=DEV)
+    out = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    got = run_gpu(x, out=out)
+    host = buf.cpu().numpy().view(np.uint16)
+    assert np.all(host[:pad] == 0x5A5A) and np.all(host[-pad:] == 0x5A5A)
+    y, T = oracle_full(x)
+    assert_parity(got, y, T, "guarded")
+
+
+def test_rejects_bad_arguments_on_device():
+    _say("case: C-ABI validation with real device buffers")
+    x = synthetic.custom_inputs(64, 64, 128, 16, seed=1)
+    d = to_device(x)
+    out = torch.empty((64, 64), dtype=torch.bfloat16, device=DEV)
+    base = [d[k].data_ptr() for k in ARGS] + [out.data_ptr()]
+    s = torch.cuda.current_stream().cuda_stream
+    assert w4.gemm_w4a4_raw(*base, 64, 64, 128, 16, s) == w4.OK
+    bad = list(base)
+    bad[0] += 8
+    assert w4.gemm_w4a4_raw(*bad, 64, 64, 128, 16, s) == w4.EALIGN
+    assert w4.gemm_w4a4_raw(*base, 64, 64, 120, 16, s) == w4.EINVAL
+    bad = list(base)
+    bad[8] = base[0]                       # out aliases act
+    assert w4.gemm_w4a4_raw(*bad, 64, 64, 128, 16, s) == w4.EOVERLAP
+    torch.cuda.synchronize()
