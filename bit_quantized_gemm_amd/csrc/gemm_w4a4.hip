@@ -4,18 +4,20 @@
 // (operator and formats: the SVDQuant W4A4 on Blackwell page, sections 2, 3.1
 // and 6.6; E2M1 bit layout: the DeepGEMM FP4 indexer page, "Step 0").
 //
-// Design (one workgroup per BM x BN output tile, WM x WN waves):
-//  * Loader: each K stage (128 values of k = 64 packed bytes per row) of act
-//    and wgt is read from HBM with coalesced 16-byte loads into registers one
-//    stage ahead, then written into an LDS ring whose 16-byte chunks are XOR
-//    swizzled by row so that the consumer's 128-bit LDS reads do not conflict.
+// Design (one workgroup per BM x BN output tile, WM x WN waves, 1 wave/SIMD):
+//  * Loader: a 3-deep LDS ring. Each stage (128 values of k) of packed act and
+//    wgt moves HBM -> LDS by direct-to-LDS DMA (global_load_lds), 16-byte
+//    chunks XOR-swizzled by row so the consumer's LDS reads do not conflict.
+//    The stage's E4M3 scale tiles are loaded by the workgroup with coalesced
+//    8-byte loads, converted once to fp16 and stored [k-block][row] in LDS.
+//    A stage is issued two iterations before it is consumed.
 //  * Decode: NVFP4 is exact in fp16. Every E2M1 value times every E4M3 scale
 //    has at most 6 significant bits and lies in [2^-10, 2688], so each operand
-//    value is built exactly as fp16: v_cvt_scalef32_pk_f16_fp4 (scale 1.0)
-//    turns two nibbles into two fp16 values and one packed fp16 multiply by
-//    the (s, s) scale pair applies the block scale. The E4M3 -> fp16 scale
-//    conversion is a 256-entry table in LDS, built once per workgroup with
-//    integer arithmetic.
+//    value is built exactly as fp16: v_cvt_scalef32_pk_f16_fp4 (scale 1.0;
+//    the instruction applies only the exponent of its scale operand, so the
+//    E4M3 mantissa cannot ride on it) turns two nibbles into two fp16 values
+//    and one packed fp16 multiply by the broadcast block scale applies the
+//    scale.
 //  * K-loop: v_mfma_f32_32x32x16_f16, whose 16-deep k-step is exactly one
 //    NVFP4 scale block. Each lane feeds 8 values of k that share one scale.
 //    The k <-> MFMA-slot assignment is free as long as both operands use the
@@ -56,76 +58,112 @@ struct Params {
   const uint16_t* lora_up;
   uint16_t* out;
   int M, N, K, R;
-  int tiles_n;
+  int tiles_m, tiles_n;
 };
 
-// 16-byte chunk c of a row is stored at chunk position c ^ swz(row). Rows are
-// 64 bytes apart, so without it rows r and r+2 (32 banks) or r and r+4
-// (64 banks) would share banks under a 128-bit read; this XOR spreads any 8
-// (or 16) consecutive rows of one chunk over distinct 16-byte bank groups.
+// 16-byte chunk c of a 64-byte row is stored at chunk position c ^ swz(row).
+// Without it rows r and r+2 (32 banks) or r and r+4 (64 banks) share banks
+// under the consumer's reads; this XOR spreads 8 (or 16) consecutive rows of
+// one chunk over distinct bank groups.
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// E4M3FN byte -> fp16 bit pattern. Exact: every E4M3 value is zero, NaN or an
-// fp16 normal number (the smallest E4M3 subnormal, 2^-9, is above fp16's 2^-14).
-__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
-  const uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
-  uint32_t h;
-  if (e == 15u && m == 7u) {
-    h = 0x7E00u;                                     // NaN
-  } else if (e == 0u) {
-    if (m == 0u) {
-      h = 0u;
-    } else {                                         // m * 2^-9 = 2^(p-9) * (m / 2^p)
-      const uint32_t p = 31u - __builtin_clz(m);
-      h = ((p + 6u) << 10) | ((m - (1u << p)) << (10u - p));
-    }
-  } else {                                           // 2^(e-7) * (1 + m/8)
-    h = ((e + 8u) << 10) | (m << 7);
-  }
-  return (s << 15) | h;
+// s_waitcnt vmcnt(VM) lgkmcnt(0), gfx9 encoding (vmcnt split over bits 3:0 and 15:14).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
 }
 
-// Eight E2M1 nibbles of one dword, times the block scale pair (s, s), as fp16.
-// Which nibble lands in which of the eight slots is irrelevant (see the file
-// comment); both operands go through this same function.
-__device__ __forceinline__ f16x8 decode8(uint32_t w, uint32_t scale_pair) {
-  const f16x2 s = __builtin_bit_cast(f16x2, scale_pair);
-  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+// Workgroup barrier without the memory fence __syncthreads() carries: the
+// fence would wait for every outstanding DMA (vmcnt(0)) and serialize the
+// ring. Each caller waits for exactly the DMA it needs first; the asm memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Direct-to-LDS copy: lane l of the wave writes BYTES bytes at lds_wave_base + l*BYTES.
+template <int BYTES>
+__device__ __forceinline__ void dma(const void* gsrc, void* lds_wave_base) {
+  static_assert(BYTES == 16 || BYTES == 4, "gfx950 DMA piece sizes used here");
+  const auto src = (const __attribute__((address_space(1))) void*)gsrc;
+  const auto dst = (__attribute__((address_space(3))) void*)lds_wave_base;
+  if constexpr (BYTES == 16) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+  }
+}
+
+// Eight E2M1 nibbles of one dword times the block scale (fp16 bits in the low
+// half of `scale`), as fp16. Which nibble lands in which of the eight slots is
+// irrelevant (see the file comment); both operands go through this function.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, uint32_t scale) {
+  const _Float16 s = __builtin_bit_cast(f16x2, scale)[0];
+  const f16x2 ss = {s, s};
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-// One 16-byte chunk of a packed row, zero past the row end. Rows are a
-// multiple of 8 bytes (K % 16 == 0); VEC16 says they are a multiple of 16.
-template <bool VEC16>
-__device__ __forceinline__ u32x4 load_chunk(const uint8_t* rowp, int kbyte, int rowbytes) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (kbyte + 16 <= rowbytes) {
-    if constexpr (VEC16) {
-      v = *reinterpret_cast<const u32x4*>(rowp + kbyte);
-    } else {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp + kbyte);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + kbyte + 8);
-      v = u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
-  } else if (kbyte + 8 <= rowbytes) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp + kbyte);
-    v.x = lo.x;
-    v.y = lo.y;
-  }
-  return v;
+// Eight E4M3 bytes -> eight fp16 (exact: every E4M3 value is zero, NaN or an
+// fp16 normal number). The conversion applies only the exponent of its scale
+// operand, and 1.0 has exponent 0.
+__device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 b) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 1.0f, true))};
 }
 
 __device__ __forceinline__ uint32_t bf16_pair(uint16_t lo, uint16_t hi) {
   return uint32_t(lo) | (uint32_t(hi) << 16);
 }
 
-template <class C, bool VEC16>
-__global__ __launch_bounds__(C::THREADS) void gemm_w4a4_kernel(const Params p) {
+// Eight scale bytes of k-block kb (clamped to the last one) for rows
+// r0 .. r0+7 of a [KB][rows] tensor. `fast` (uniform over the workgroup) says
+// the whole tile lies inside `rows` and rows are 8-byte aligned; otherwise each
+// byte is read separately with its row clamped into range. The load itself is
+// unconditional: k-blocks past K are zeroed where the scales are stored, so no
+// register is written before the load returns.
+__device__ __forceinline__ u32x2 load_scales8(const uint8_t* sc, int kb, int KB, int r0, int rows,
+                                              bool fast) {
+  const uint32_t base = uint32_t(min(kb, KB - 1)) * uint32_t(rows);
+  if (fast) return *reinterpret_cast<const u32x2*>(sc + base + uint32_t(r0));
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = sc[base + uint32_t(min(r0 + i, rows - 1))];
+    w[i >> 2] |= b << (8 * (i & 3));
+  }
+  return u32x2{w[0], w[1]};
+}
+
+// Tile order: workgroups are dealt round-robin to the 8 XCDs (workgroup b
+// runs on XCD b % 8), each with its own L2. Renumber so that each XCD gets a
+// contiguous run of tiles, and walk that run GROUP tile-rows at a time, so
+// the A rows and B columns one XCD reads concurrently stay in its L2.
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcd = 8, kGroup = 4;
+  const int T = tiles_m * tiles_n;
+  const int per = T / kXcd, rem = T % kXcd;
+  const int x = b % kXcd, l = b / kXcd;
+  const int L = x < rem ? x * (per + 1) + l : rem * (per + 1) + (x - rem) * per + l;
+  const int span = kGroup * tiles_n;
+  const int first = (L / span) * kGroup;
+  const int gsz = min(tiles_m - first, kGroup);
+  const int in = L % span;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+// DMA_BYTES = 16 when packed rows are a multiple of 16 bytes (K % 32 == 0),
+// else 4 (rows are always a multiple of 8 bytes).
+template <class C, int DMA_BYTES>
+__global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4a4_kernel(
+    const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
-  uint32_t* lut = reinterpret_cast<uint32_t*>(smem + C::LUT_OFF);
+  constexpr int DMA_N = C::PACKED_BYTES / (C::THREADS * DMA_BYTES);   // DMA per thread per stage
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,108 +172,154 @@ __global__ __launch_bounds__(C::THREADS) void gemm_w4a4_kernel(const Params p) {
   const int wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  const int tile = blockIdx.x;
-  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int M = p.M, N = p.N, K = p.K, R = p.R;
   const int rowbytes = K >> 1;
   const int KB = K >> 4;                   // scale blocks along k
   const int nst = (K + C::BK - 1) / C::BK;
 
-  if (tid < 256) {
-    const uint32_t h = e4m3_to_f16_bits(uint32_t(tid));
-    lut[tid] = h | (h << 16);
-  }
+  // ---- DMA sources. LDS slot q (DMA_BYTES each) of a stage's packed region,
+  // q = u*THREADS + tid, holds for row = byte/64, swizzled chunk position cp
+  // and piece pc, the bytes of data chunk cp ^ swz(row). A round u moves
+  // THREADS*DMA_BYTES/64 whole rows, so the row of slot q is the row of round 0
+  // plus u*ROWS_PER_ROUND. The swizzle repeats every 32 rows; when a round is a
+  // multiple of 32 rows the offset inside the row is the same in every round,
+  // otherwise (4-byte pieces) it is recomputed per round.
+  static_assert(C::B_OFF % (C::THREADS * DMA_BYTES) == 0, "DMA rounds must not straddle A/B");
+  constexpr int ROWS_PER_ROUND = C::THREADS * DMA_BYTES / C::ROW_BYTES;
+  constexpr bool SAME_INROW = ROWS_PER_ROUND % 32 == 0;
+  constexpr int A_ROUNDS = C::B_OFF / (C::THREADS * DMA_BYTES);
+  const int dma_row0 = tid * DMA_BYTES / C::ROW_BYTES;
+  const int dma_cp = (tid * DMA_BYTES / 16) & 3;
+  const int dma_pc = (tid * DMA_BYTES % 16) / DMA_BYTES;
+  const uint32_t dma_inrow = uint32_t(((dma_cp ^ swz(dma_row0)) * 16) + dma_pc * DMA_BYTES);
+  const bool dma_a_inside = m0 + C::BM <= M, dma_b_inside = n0 + C::BN <= N;
+  const uint32_t dma_a0 = uint32_t(m0 + dma_row0) * uint32_t(rowbytes) + dma_inrow;
+  const uint32_t dma_b0 = uint32_t(n0 + dma_row0) * uint32_t(rowbytes) + dma_inrow;
+  const uint32_t dma_round = uint32_t(ROWS_PER_ROUND) * uint32_t(rowbytes);
 
-  // Byte offsets (32-bit: every tensor is below 2^31 bytes) of the rows of
-  // act and wgt this thread copies into LDS. Rows past M or N are clamped
-  // into range: they are loaded but their outputs are never stored.
-  uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+  const int full_stages = rowbytes / C::ROW_BYTES;   // stages lying entirely inside K
+  // Stage `st`'s packed bytes into ring slot `buf` % STAGES.
+  auto issue_dma = [&](int st, int buf) __attribute__((always_inline)) {
+    uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
+    const uint32_t k0 = uint32_t(st * C::ROW_BYTES);
+    // pieces past the row end (partial last stage only) re-read the row's
+    // first piece; their k-blocks get a zero scale
+    const bool tail_stage = st >= full_stages;
 #pragma unroll
-  for (int u = 0; u < C::A_LOADS; ++u) {
-    const int q = tid + u * C::THREADS;
-    const int row = q >> 2;
-    const int c = (q & 3) ^ swz(row);
-    a_off[u] = uint32_t(min(m0 + row, M - 1)) * uint32_t(rowbytes) + uint32_t(c * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < C::B_LOADS; ++u) {
-    const int q = tid + u * C::THREADS;
-    const int row = q >> 2;
-    const int c = (q & 3) ^ swz(row);
-    b_off[u] = uint32_t(min(n0 + row, N - 1)) * uint32_t(rowbytes) + uint32_t(c * 16);
-  }
-
-  // Rows / columns of this lane's MFMA tiles (for scales and the epilogue).
-  int arow[C::MI], bcol[C::NI];
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i) arow[i] = min(m0 + wm * C::TM + 32 * i + l32, M - 1);
-#pragma unroll
-  for (int j = 0; j < C::NI; ++j) bcol[j] = min(n0 + wn * C::TN + 32 * j + l32, N - 1);
-  // lane half g reads scale blocks st*8 + 4g + q (q = 0..3) of stage st
-  const uint32_t sa_lane = uint32_t(g * C::QS) * uint32_t(M);
-  const uint32_t sb_lane = uint32_t(g * C::QS) * uint32_t(N);
-
-  u32x4 pa[C::A_LOADS], pb[C::B_LOADS];
-  uint32_t sa_b[C::MI][C::QS], sb_b[C::NI][C::QS];
-
-  // FULL: the whole stage lies inside K (every stage but a partial last one),
-  // so no chunk needs a bounds check.
-  auto load_stage = [&]<bool FULL>(int st) {
-    const uint32_t kbyte0 = uint32_t(st * C::ROW_BYTES);
-    if constexpr (FULL) {
-#pragma unroll
-      for (int u = 0; u < C::A_LOADS; ++u)
-        pa[u] = *reinterpret_cast<const u32x4*>(p.act + (a_off[u] + kbyte0));
-#pragma unroll
-      for (int u = 0; u < C::B_LOADS; ++u)
-        pb[u] = *reinterpret_cast<const u32x4*>(p.wgt + (b_off[u] + kbyte0));
-    } else {
-      // chunk position inside its row = offset modulo the row length
-#pragma unroll
-      for (int u = 0; u < C::A_LOADS; ++u) {
-        const uint32_t o = a_off[u] + kbyte0;
-        const uint32_t in_row = ((tid + u * C::THREADS) & 3 ^ swz((tid + u * C::THREADS) >> 2)) * 16 + kbyte0;
-        pa[u] = load_chunk<VEC16>(p.act + (o - in_row), int(in_row), rowbytes);
+    for (int u = 0; u < DMA_N; ++u) {
+      const bool is_b = u >= A_ROUNDS;
+      const int ur = is_b ? u - A_ROUNDS : u;
+      const uint32_t inrow =
+          SAME_INROW ? dma_inrow
+                     : uint32_t(((dma_cp ^ swz(dma_row0 + ur * ROWS_PER_ROUND)) * 16) +
+                                dma_pc * DMA_BYTES);
+      const bool tail = tail_stage && inrow + k0 + DMA_BYTES > uint32_t(rowbytes);
+      const uint32_t kin = tail ? 0u : k0 + inrow;
+      uint32_t row_off;
+      if (is_b ? dma_b_inside : dma_a_inside) {
+        row_off = (is_b ? dma_b0 : dma_a0) - dma_inrow + uint32_t(ur) * dma_round;
+      } else {   // edge tile: rows past M or N are clamped into range
+        const int row = (is_b ? n0 : m0) + dma_row0 + ur * ROWS_PER_ROUND;
+        row_off = uint32_t(min(row, (is_b ? N : M) - 1)) * uint32_t(rowbytes);
       }
-#pragma unroll
-      for (int u = 0; u < C::B_LOADS; ++u) {
-        const uint32_t o = b_off[u] + kbyte0;
-        const uint32_t in_row = ((tid + u * C::THREADS) & 3 ^ swz((tid + u * C::THREADS) >> 2)) * 16 + kbyte0;
-        pb[u] = load_chunk<VEC16>(p.wgt + (o - in_row), int(in_row), rowbytes);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < C::QS; ++q) {
-      const int kb = st * C::KSTEPS + g * C::QS + q;
-      const bool ok = FULL || kb < KB;
-      const uint32_t oa = ok ? uint32_t(st * C::KSTEPS + q) * uint32_t(M) + sa_lane : 0u;
-      const uint32_t ob = ok ? uint32_t(st * C::KSTEPS + q) * uint32_t(N) + sb_lane : 0u;
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) {
-        const uint32_t v = p.ascales[oa + uint32_t(arow[i])];
-        sa_b[i][q] = ok ? v : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j) {
-        const uint32_t v = p.wscales[ob + uint32_t(bcol[j])];
-        sb_b[j][q] = ok ? v : 0u;
-      }
+      const uint8_t* src = (is_b ? p.wgt : p.act) + (row_off + kin);
+      dma<DMA_BYTES>(src, stage + (u * C::THREADS + wave * 64) * DMA_BYTES);
     }
   };
-  auto store_stage = [&](int buf) {
-    uint8_t* base = smem + C::RING_OFF + buf * C::STAGE_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::A_LOADS; ++u)
-      *reinterpret_cast<u32x4*>(base + (tid + u * C::THREADS) * 16) = pa[u];
-#pragma unroll
-    for (int u = 0; u < C::B_LOADS; ++u)
-      *reinterpret_cast<u32x4*>(base + C::A_BYTES + (tid + u * C::THREADS) * 16) = pb[u];
+
+  // ---- scale loader. Thread t < SA_THREADS owns rows r8 .. r8+7 of the act
+  // scales for k-block pair kp (k-blocks 2kp, 2kp+1 of the stage); the next
+  // SB_THREADS threads do the same for wgt; the rest load nothing.
+  const bool s_is_a = tid < C::SA_THREADS;
+  const bool s_is_b = !s_is_a && tid < C::SA_THREADS + C::SB_THREADS;
+  const int s_idx = s_is_a ? tid : tid - C::SA_THREADS;
+  const int s_rows8 = (s_is_a ? C::BM : C::BN) / 8;
+  const int s_kp = s_idx / s_rows8;
+  const int s_r8 = (s_idx % s_rows8) * 8;
+  const uint8_t* s_src = s_is_a ? p.ascales : p.wscales;
+  const int s_rows = s_is_a ? M : N;
+  const int s_r0 = (s_is_a ? m0 : n0) + s_r8;
+  const int s_off = (s_is_a ? C::SA_OFF : C::SB_OFF) +
+                    (s_kp * (s_is_a ? C::BM : C::BN) + s_r8) * 4;
+  // 8-byte scale loads need the whole tile in range and 8-aligned rows
+  const bool s_fast = s_is_a ? ((M & 7) == 0 && (reinterpret_cast<uintptr_t>(p.ascales) & 7u) == 0 &&
+                                m0 + C::BM <= M)
+                             : ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.wscales) & 7u) == 0 &&
+                                n0 + C::BN <= N);
+  // raw scale bytes of two stages in flight, indexed by stage parity
+  u32x2 s_raw[2][2] = {{{0u, 0u}, {0u, 0u}}, {{0u, 0u}, {0u, 0u}}};
+
+  auto load_scales = [&](int st, u32x2 (&raw)[2]) __attribute__((always_inline)) {
+    if (s_is_a || s_is_b) {
+      const int kb = st * C::KBLK + 2 * s_kp;
+      raw[0] = load_scales8(s_src, kb, KB, s_r0, s_rows, s_fast);
+      raw[1] = load_scales8(s_src, kb + 1, KB, s_r0, s_rows, s_fast);
+    }
   };
-  const int full_stages = rowbytes / C::ROW_BYTES;   // stages entirely inside K
-  auto load_any = [&](int st) {
-    if (st < full_stages) load_stage.template operator()<true>(st);
-    else load_stage.template operator()<false>(st);
+  // k-blocks past K get scale 0: their packed bytes (re-read from the row
+  // start) then contribute exactly zero, since E2M1 values are finite.
+  // Stored interleaved: row r of pair kp holds (scale of 2kp, scale of 2kp+1).
+  auto store_scales = [&](int st, int buf, const u32x2 (&raw)[2]) __attribute__((always_inline)) {
+    if (s_is_a || s_is_b) {
+      const int kb = st * C::KBLK + 2 * s_kp;
+      const u32x2 zero = {0u, 0u};
+      const u32x4 h0 = e4m3x8_to_f16(kb < KB ? raw[0] : zero);
+      const u32x4 h1 = e4m3x8_to_f16(kb + 1 < KB ? raw[1] : zero);
+      uint8_t* dst = smem + (buf % C::STAGES) * C::STAGE_BYTES + s_off;
+      const u32x4 lo = {__builtin_amdgcn_perm(h1.x, h0.x, 0x05040100u),
+                        __builtin_amdgcn_perm(h1.x, h0.x, 0x07060302u),
+                        __builtin_amdgcn_perm(h1.y, h0.y, 0x05040100u),
+                        __builtin_amdgcn_perm(h1.y, h0.y, 0x07060302u)};
+      const u32x4 hi = {__builtin_amdgcn_perm(h1.z, h0.z, 0x05040100u),
+                        __builtin_amdgcn_perm(h1.z, h0.z, 0x07060302u),
+                        __builtin_amdgcn_perm(h1.w, h0.w, 0x05040100u),
+                        __builtin_amdgcn_perm(h1.w, h0.w, 0x07060302u)};
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 16) = hi;
+    }
+  };
+
+  // ---- per-lane LDS read offsets (relative to a stage). Lane (row l32,
+  // half g) of MFMA tile i reads row r = wm*TM + 32i + l32, bytes 32g .. 32g+31
+  // of the stage: data chunk 2g (k-steps 0-3) and 2g+1 (k-steps 4-7); k-step s
+  // uses dword s & 3 of chunk s >> 2. Its scales are k-blocks 4g .. 4g+3,
+  // pairs 2g (chunk 0) and 2g+1 (chunk 1). Rows 32 apart have the same
+  // swizzle, so tile i's offsets are tile 0's plus the constant i*32 rows.
+  const int ra = wm * C::TM + l32, rb = wn * C::TN + l32;
+  const uint32_t a_rd0 = C::A_OFF + ra * C::ROW_BYTES + (((2 * g) ^ swz(ra)) << 4);
+  const uint32_t b_rd0 = C::B_OFF + rb * C::ROW_BYTES + (((2 * g) ^ swz(rb)) << 4);
+  const uint32_t sa_rd0 = C::SA_OFF + (2 * g * C::BM + ra) * 4;
+  const uint32_t sb_rd0 = C::SB_OFF + (2 * g * C::BN + rb) * 4;
+
+  // One 16-byte chunk (4 k-steps) of this lane's operands and its two block
+  // scales, each scale alone in the low half of a register (the packed fp16
+  // multiply broadcasts a low half for free).
+  struct Chunk {
+    u32x4 a[C::MI], b[C::NI];
+    uint32_t sa[C::MI][2], sb[C::NI][2];   // fp16 bits in the low half
+  };
+  auto read_chunk = [&](int st, int h, Chunk& R) __attribute__((always_inline)) {
+    const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
+    // chunk 2g+1 sits at chunk position ((2g) ^ swz) ^ 1: flip bit 4
+    const uint8_t* pa = stage + (h ? (a_rd0 ^ 16u) : a_rd0);
+    const uint8_t* pb = stage + (h ? (b_rd0 ^ 16u) : b_rd0);
+    const uint16_t* qa = reinterpret_cast<const uint16_t*>(stage + sa_rd0 + h * C::BM * 4);
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(stage + sb_rd0 + h * C::BN * 4);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      R.a[i] = *reinterpret_cast<const u32x4*>(pa + i * 32 * C::ROW_BYTES);
+      R.sa[i][0] = qa[i * 64];
+      R.sa[i][1] = qa[i * 64 + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+      R.b[j] = *reinterpret_cast<const u32x4*>(pb + j * 32 * C::ROW_BYTES);
+      R.sb[j][0] = qb[j * 64];
+      R.sb[j][1] = qb[j * 64 + 1];
+    }
   };
 
   f32x16 acc[C::MI][C::NI];
@@ -246,66 +330,86 @@ __global__ __launch_bounds__(C::THREADS) void gemm_w4a4_kernel(const Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_any(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st % C::STAGES;
-    // block scales of this stage -> (s, s) fp16 pairs
-    uint32_t sa[C::MI][C::QS], sb[C::NI][C::QS];
+  // Four k-steps from one chunk: k-step s uses dword s and scale s >> 1.
+  auto compute_chunk = [&](const Chunk& R) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < C::QS; ++q) {
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) sa[i][q] = lut[sa_b[i][q]];
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j) sb[j][q] = lut[sb_b[j][q]];
-    }
-    if (st + 1 < nst) load_any(st + 1);
-
-    // this lane's packed bytes: row l32 of each tile, chunks 2g and 2g+1
-    const uint8_t* base = smem + C::RING_OFF + buf * C::STAGE_BYTES;
-    uint32_t a[C::MI][8], b[C::NI][8];
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const int row = wm * C::TM + 32 * i + l32;
-      const uint8_t* rp = base + row * C::ROW_BYTES;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + (((2 * g) ^ swz(row)) << 4));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (((2 * g + 1) ^ swz(row)) << 4));
-      a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
-      a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
-    }
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j) {
-      const int row = wn * C::TN + 32 * j + l32;
-      const uint8_t* rp = base + C::A_BYTES + row * C::ROW_BYTES;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + (((2 * g) ^ swz(row)) << 4));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (((2 * g + 1) ^ swz(row)) << 4));
-      b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
-      b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
-    }
-
-    // k-step s uses dword s of the lane's 32 bytes: k = 64*g + 8*s + (0..7),
-    // all inside scale block 4*g + s/2 of this stage.
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
+    for (int s = 0; s < 4; ++s) {
       f16x8 av[C::MI], bv[C::NI];
 #pragma unroll
-      for (int i = 0; i < C::MI; ++i) av[i] = decode8(a[i][s], sa[i][s >> 1]);
+      for (int i = 0; i < C::MI; ++i) av[i] = decode8(R.a[i][s], R.sa[i][s >> 1]);
 #pragma unroll
-      for (int j = 0; j < C::NI; ++j) bv[j] = decode8(b[j][s], sb[j][s >> 1]);
+      for (int j = 0; j < C::NI; ++j) bv[j] = decode8(R.b[j][s], R.sb[j][s >> 1]);
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
 #pragma unroll
         for (int j = 0; j < C::NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
+  };
 
-    if (st + 1 < nst) store_stage((st + 1) % C::STAGES);
-    __syncthreads();
+  // ---- pipeline over a 4-deep LDS ring. Iteration st issues the scale loads
+  // of stage st+2 and the DMA of stage st+3, and prefetches chunk 0 of stage
+  // st+1 into registers while computing stage st. Prefetches past the last
+  // stage read clamped, in-range addresses into buffers nobody reads again,
+  // which keeps the loop body free of branches. At the top of iteration st
+  // the outstanding vector-memory ops are, in issue order, DMA(st+1),
+  // SCL(st+1), DMA(st+2): waiting until at most DMA_N remain completes the
+  // first two, whatever the number of scale loads.
+  const int last = nst - 1;
+  // decode VALU per k-step spread over the k-step's MFMAs, rounded up
+  constexpr int VALU_PER_MFMA = (8 * (C::MI + C::NI) + C::MI * C::NI - 1) / (C::MI * C::NI) + 1;
+  Chunk C0, C1;
+  load_scales(0, s_raw[0]);
+  issue_dma(0, 0);
+  issue_dma(min(1, last), 1);
+  load_scales(min(1, last), s_raw[1]);
+  issue_dma(min(2, last), 2);
+  wait_vm_lgkm0<2 * DMA_N>();
+  store_scales(0, 0, s_raw[0]);
+  wait_vm_lgkm0<63>();
+  wg_barrier();
+  read_chunk(0, 0, C0);
+
+  // PAR = st & 1, fixed per call site of the two-way unrolled loop.
+  auto iteration = [&]<int PAR>(int st) __attribute__((always_inline)) {
+    // DMA(st+1) and SCL(st+1) complete: publish stage st+1's scales. The
+    // barrier then makes stage st+1 visible to every wave and guarantees
+    // every wave is done with iteration st-1, whose buffer (st-1) % 4 =
+    // (st+3) % 4 takes DMA(st+3).
+    wait_vm_lgkm0<DMA_N>();
+    store_scales(min(st + 1, last), st + 1, s_raw[1 - PAR]);
+    wait_vm_lgkm0<63>();
+    wg_barrier();
+    load_scales(min(st + 2, last), s_raw[PAR]);
+    issue_dma(min(st + 3, last), st + 3);
+    read_chunk(st, 1, C1);
+    compute_chunk(C0);
+    read_chunk(st + 1, 0, C0);
+    compute_chunk(C1);
+    // Issue order for the scheduler: one MFMA (32 cycles in the matrix pipe),
+    // then up to VALU_PER_MFMA vector ALU ops that run meanwhile; an MFMA
+    // queued right behind another would stall the wave, and a long VALU run
+    // would leave the matrix pipe idle.
+#pragma unroll
+    for (int k = 0; k < 2 * C::KBLK / 2 * C::MI * C::NI; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);   // VALU
+    }
+  };
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    iteration.template operator()<0>(st);
+    iteration.template operator()<1>(st + 1);
   }
+  if (st < nst) iteration.template operator()<0>(st);
+  wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
   // ---------------- epilogue: *wcscale, + LoRA (same accumulators), + bias, bf16 store
+  int arow[C::MI], bcol[C::NI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) arow[i] = min(m0 + wm * C::TM + 32 * i + l32, M - 1);
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) bcol[j] = min(n0 + wn * C::TN + 32 * j + l32, N - 1);
   float wc[C::NI], bs[C::NI];
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
@@ -384,13 +488,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_w4a4_kernel(const Params p) {
 // ------------------------------------------------------------------ host side
 
 struct Variant {
-  void (*kernel[2])(const Params);   // [rows 16-byte multiple]
+  void (*kernel[2])(const Params);   // [0]: 4-byte DMA pieces, [1]: 16-byte (K % 32 == 0)
   int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
 };
 
 template <class C>
 constexpr Variant make_variant() {
-  return Variant{{gemm_w4a4_kernel<C, false>, gemm_w4a4_kernel<C, true>},
+  return Variant{{gemm_w4a4_kernel<C, 4>, gemm_w4a4_kernel<C, 16>},
                  C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
                  C::LDS_BYTES, C::STAGE_BYTES, C::OCC};
 }
@@ -557,6 +661,7 @@ extern "C" int gemm_w4a4(const uint8_t* act, const uint8_t* ascales, const uint8
   prm.N = N;
   prm.K = K;
   prm.R = R;
+  prm.tiles_m = pl.tiles_m;
   prm.tiles_n = pl.tiles_n;
 
   const Variant& v = kVariants[pl.variant];

@@ -16,44 +16,49 @@ namespace w4a4 {
 constexpr int kLdsLimit = 163840;   // LDS one workgroup may use on gfx950 (160 KiB)
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kWave = 64;           // CDNA wavefront width
-constexpr int kLutBytes = 256 * 4;  // E4M3 byte -> packed (s, s) fp16 pair
 
 // BM x BN output tile per workgroup, WM x WN waves, each wave owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles. Every pipeline stage covers
 // BK = 128 values of k, i.e. 8 NVFP4 scale blocks and 8 MFMA k-steps of 16.
+//
+// One LDS ring stage holds, in this order:
+//   A  packed act  [BM rows][64 bytes]  16-byte chunks XOR-swizzled by row
+//   B  packed wgt  [BN rows][64 bytes]  same swizzle
+//   SA act scales  fp16 [4 k-block pairs][BM rows][2]
+//   SB wgt scales  fp16 [4 k-block pairs][BN rows][2]
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int STAGES = STAGES_;        // LDS ring depth (operand stages)
+  static constexpr int STAGES = STAGES_;        // LDS ring depth (stages in flight)
   static constexpr int OCC = OCC_;              // workgroups per CU the variant is built for
   static constexpr int BK = 128;
   static constexpr int THREADS = WM * WN * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
   static constexpr int MI = TM / 32, NI = TN / 32;   // 32x32 MFMA tiles per wave
   static constexpr int ROW_BYTES = BK / 2;      // packed bytes of one row per stage
-  static constexpr int CHUNKS = ROW_BYTES / 16; // 16-byte chunks per row per stage
-  static constexpr int KSTEPS = BK / 16;        // MFMA k-steps per stage
-  static constexpr int QS = BK / 32;            // scale blocks one lane touches per stage
-  static constexpr int A_BYTES = BM * ROW_BYTES;
-  static constexpr int B_BYTES = BN * ROW_BYTES;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int RING_OFF = 0;
-  static constexpr int LUT_OFF = STAGES * STAGE_BYTES;
-  static constexpr int LDS_BYTES = LUT_OFF + kLutBytes;
-  static constexpr int A_LOADS = BM * CHUNKS / THREADS;  // 16-B chunks per thread per stage
-  static constexpr int B_LOADS = BN * CHUNKS / THREADS;
+  static constexpr int KBLK = BK / 16;          // scale blocks (= MFMA k-steps) per stage
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = A_OFF + BM * ROW_BYTES;
+  static constexpr int SA_OFF = B_OFF + BN * ROW_BYTES;
+  static constexpr int SB_OFF = SA_OFF + KBLK * BM * 2;
+  static constexpr int STAGE_BYTES = SB_OFF + KBLK * BN * 2;
+  static constexpr int PACKED_BYTES = SA_OFF;   // bytes moved by DMA per stage
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  // scale loader: one thread per 8 consecutive rows of one k-block pair
+  static constexpr int SA_THREADS = BM / 2;     // (KBLK / 2) * (BM / 8)
+  static constexpr int SB_THREADS = BN / 2;
 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
-  static_assert(CHUNKS == 4, "swizzle assumes four 16-byte chunks per row per stage");
-  static_assert((BM * CHUNKS) % THREADS == 0 && (BN * CHUNKS) % THREADS == 0,
-                "every thread loads the same number of chunks");
-  static_assert(THREADS >= 256, "the E4M3 table is filled by the first 256 threads");
+  static_assert(BK == 128, "the lane <-> k mapping assumes 8 k-steps per stage");
+  static_assert(PACKED_BYTES % (THREADS * 16) == 0, "whole 16-byte DMA rounds per stage");
+  static_assert(SA_THREADS + SB_THREADS <= THREADS, "one scale chunk per thread");
+  static_assert(STAGES == 4, "the pipeline below is written for a 4-deep ring");
   static_assert(LDS_BYTES <= kLdsLimit, "LDS budget exceeded");
   static_assert(LDS_BYTES * OCC <= kLdsLimit, "occupancy target exceeds the LDS budget");
 };
 
 // The compiled instances, in variant order. The solver picks among them.
-using Cfg256x192 = TileCfg<256, 192, 2, 2, 2, 1>;
-using Cfg128x128 = TileCfg<128, 128, 2, 2, 2, 2>;
+using Cfg256x192 = TileCfg<256, 192, 2, 2, 4, 1>;
+using Cfg128x128 = TileCfg<128, 128, 2, 2, 4, 2>;
 
 }  // namespace w4a4
