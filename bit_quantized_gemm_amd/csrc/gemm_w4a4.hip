@@ -46,6 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
   const uint8_t* act;
@@ -322,13 +323,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     }
   };
 
-  f32x16 acc[C::MI][C::NI];
+  // acc[j][i] is the 32x32 tile D[n][m] = sum_k W[n,k] A[m,k] (wgt as the
+  // MFMA's A operand, act as its B operand): lane (l32, g) holds column
+  // m = 32i + l32 and, in element 4q + t, row n = 32j + 8q + 4g + t, i.e. four
+  // consecutive output columns of one output row.
+  f32x16 acc[C::NI][C::MI];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+  for (int j = 0; j < C::NI; ++j)
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j)
+    for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
   // Four k-steps from one chunk: k-step s uses dword s and scale s >> 1.
   auto compute_chunk = [&](const Chunk& R) __attribute__((always_inline)) {
@@ -340,10 +345,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 #pragma unroll
       for (int j = 0; j < C::NI; ++j) bv[j] = decode8(R.b[j][s], R.sb[j][s >> 1]);
 #pragma unroll
-      for (int i = 0; i < C::MI; ++i)
+      for (int j = 0; j < C::NI; ++j)
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < C::MI; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[j][i], 0, 0, 0);
     }
   };
 
@@ -356,8 +361,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   // SCL(st+1), DMA(st+2): waiting until at most DMA_N remain completes the
   // first two, whatever the number of scale loads.
   const int last = nst - 1;
-  // decode VALU per k-step spread over the k-step's MFMAs, rounded up
-  constexpr int VALU_PER_MFMA = (8 * (C::MI + C::NI) + C::MI * C::NI - 1) / (C::MI * C::NI) + 1;
   Chunk C0, C1;
   load_scales(0, s_raw[0]);
   issue_dma(0, 0);
@@ -386,15 +389,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     compute_chunk(C0);
     read_chunk(st + 1, 0, C0);
     compute_chunk(C1);
-    // Issue order for the scheduler: one MFMA (32 cycles in the matrix pipe),
-    // then up to VALU_PER_MFMA vector ALU ops that run meanwhile; an MFMA
-    // queued right behind another would stall the wave, and a long VALU run
-    // would leave the matrix pipe idle.
-#pragma unroll
-    for (int k = 0; k < 2 * C::KBLK / 2 * C::MI * C::NI; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);   // VALU
-    }
   };
   int st = 0;
   for (; st + 1 < nst; st += 2) {
@@ -405,34 +399,45 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
   // ---------------- epilogue: *wcscale, + LoRA (same accumulators), + bias, bf16 store
-  int arow[C::MI], bcol[C::NI];
+  // This lane's output rows m (one per MFMA tile i) and the first of its four
+  // consecutive output columns in (tile j, group q).
+  int mrow[C::MI];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) arow[i] = min(m0 + wm * C::TM + 32 * i + l32, M - 1);
-#pragma unroll
-  for (int j = 0; j < C::NI; ++j) bcol[j] = min(n0 + wn * C::TN + 32 * j + l32, N - 1);
-  float wc[C::NI], bs[C::NI];
+  for (int i = 0; i < C::MI; ++i) mrow[i] = min(m0 + wm * C::TM + 32 * i + l32, M - 1);
+  const int ncol0 = n0 + wn * C::TN + 4 * g;          // + 32j + 8q
+  const bool n_inside = n0 + C::BN <= N;
+
+  // Per-column factor at columns ncol0 + 32j + 8q + (0..3), clamped at the N edge.
+  auto col4 = [&](const float* v, int j, int q) __attribute__((always_inline)) {
+    const int n = ncol0 + 32 * j + 8 * q;
+    if (n_inside) return *reinterpret_cast<const f32x4*>(v + n);
+    return f32x4{v[min(n, N - 1)], v[min(n + 1, N - 1)], v[min(n + 2, N - 1)], v[min(n + 3, N - 1)]};
+  };
+
+  // S * wcscale[n]
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
-    wc[j] = p.wcscale[bcol[j]];
-    bs[j] = p.bias[bcol[j]];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w = col4(p.wcscale, j, q);
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[j][i][4 * q + t] *= w[t];
+    }
   }
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] *= wc[j];
 
-  // LoRA-up: ceil(R/16) further k-steps into the same accumulators. Lane
-  // (row l32, half g) feeds ranks rb .. rb+7 with rb = r0 + 8g; ranks past R
-  // read a clamped address and are replaced by zero (no branches).
+  // LoRA-up: ceil(R/16) further k-steps into the same accumulators, with
+  // lora_up as the A operand (rows n) and lora_act_in as the B operand (rows
+  // m). Lane (l32, g) feeds ranks rb .. rb+7, rb = r0 + 8g; ranks past R read a
+  // clamped address and are replaced by zero (no branches).
   const bool la_vec = (R & 7) == 0 && (reinterpret_cast<uintptr_t>(p.lora_act_in) & 15u) == 0;
   for (int r0 = 0; r0 < R; r0 += 16) {
     bf16x8 la[C::MI], lu[C::NI];
     const int rb = r0 + 8 * g;
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) {
-      const uint16_t* src = p.lora_act_in + uint32_t(arow[i]) * uint32_t(R);
+      const uint16_t* src = p.lora_act_in + uint32_t(mrow[i]) * uint32_t(R);
       if (la_vec) {
         // R % 8 == 0 and rb % 8 == 0: the eight ranks are all in range or all out
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + min(rb, R - 8));
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     }
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
-      const uint16_t* src = p.lora_up + bcol[j];
+      const uint16_t* src = p.lora_up + min(n0 + wn * C::TN + 32 * j + l32, N - 1);
       uint32_t w[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -463,24 +468,58 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
       lu[j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
     }
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i)
+    for (int j = 0; j < C::NI; ++j)
 #pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lu[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < C::MI; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[j], la[i], acc[j][i], 0, 0, 0);
   }
 
-  // accumulator element r of a 32x32 tile: row 8*(r/4) + 4*g + r%4, column l32
-  __bf16* out = reinterpret_cast<__bf16*>(p.out);
+  // + bias, bf16 (round to nearest even), staged through LDS: the ring is
+  // free once every wave has drained its DMA and passed this barrier. The
+  // tile is row-major with a padded row stride (OUT_STRIDE bytes) so the
+  // 8-byte writes of 32 rows at once spread over the banks.
+  wg_barrier();
+  constexpr int OUT_STRIDE = C::BN * 2 + 16;
+  static_assert(C::BM * OUT_STRIDE <= C::LDS_BYTES, "output tile must fit in the ring");
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
+  for (int j = 0; j < C::NI; ++j) {
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) {
-      const int col = n0 + wn * C::TN + 32 * j + l32;
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 b = col4(p.bias, j, q);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * C::TM + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row < M && col < N) out[size_t(row) * N + col] = __bf16(acc[i][j][r] + bs[j]);
+      for (int i = 0; i < C::MI; ++i) {
+        const int ml = wm * C::TM + 32 * i + l32;
+        const int nl = wn * C::TN + 32 * j + 8 * q + 4 * g;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 v = {__bf16(acc[j][i][4 * q] + b[0]), __bf16(acc[j][i][4 * q + 1] + b[1]),
+                          __bf16(acc[j][i][4 * q + 2] + b[2]), __bf16(acc[j][i][4 * q + 3] + b[3])};
+        *reinterpret_cast<bf16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
       }
+    }
+  }
+  wait_vm_lgkm0<63>();
+  wg_barrier();
+
+  // LDS -> HBM in 16-byte pieces of whole output rows (8 columns each).
+  constexpr int PIECES_PER_ROW = C::BN / 8;
+  constexpr int PIECES = C::BM * PIECES_PER_ROW;
+  static_assert(PIECES % C::THREADS == 0, "whole store rounds");
+  const bool vec_out = n_inside && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0;
+#pragma unroll
+  for (int u = 0; u < PIECES / C::THREADS; ++u) {
+    const int piece = u * C::THREADS + tid;
+    const int rl = piece / PIECES_PER_ROW, cl = (piece % PIECES_PER_ROW) * 8;
+    const int row = m0 + rl;
+    if (row >= M) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
+    uint16_t* dst = p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl);
+    if (vec_out) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n0 + cl + e < N) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
