@@ -171,6 +171,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const int l32 = lane & 31;
   const int g = lane >> 5;                 // which half of the wave (k group)
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy (for M0)
   const int wm = wave / C::WN, wn = wave % C::WN;
 
   int tm, tn;
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
         row_off = uint32_t(min(row, (is_b ? N : M) - 1)) * uint32_t(rowbytes);
       }
       const uint8_t* src = (is_b ? p.wgt : p.act) + (row_off + kin);
-      dma<DMA_BYTES>(src, stage + (u * C::THREADS + wave * 64) * DMA_BYTES);
+      dma<DMA_BYTES>(src, stage + (u * C::THREADS + wave_u * 64) * DMA_BYTES);
     }
   };
 
@@ -430,48 +431,63 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   // LoRA-up: ceil(R/16) further k-steps into the same accumulators, with
   // lora_up as the A operand (rows n) and lora_act_in as the B operand (rows
   // m). Lane (l32, g) feeds ranks rb .. rb+7, rb = r0 + 8g; ranks past R read a
-  // clamped address and are replaced by zero (no branches).
+  // clamped address and are replaced by zero (no branches). The operands of
+  // up to LORA_BATCH k-steps are loaded before any of their MFMAs, so the
+  // load latency is paid once per batch rather than once per k-step.
+  constexpr int LORA_BATCH = 8;
   const bool la_vec = (R & 7) == 0 && (reinterpret_cast<uintptr_t>(p.lora_act_in) & 15u) == 0;
-  for (int r0 = 0; r0 < R; r0 += 16) {
-    bf16x8 la[C::MI], lu[C::NI];
-    const int rb = r0 + 8 * g;
+  auto lora_a = [&](int i, int rb) __attribute__((always_inline)) {
+    const uint16_t* src = p.lora_act_in + uint32_t(mrow[i]) * uint32_t(R);
+    if (la_vec) {
+      // R % 8 == 0 and rb % 8 == 0: the eight ranks are all in range or all out
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + min(rb, R - 8));
+      return __builtin_bit_cast(bf16x8, rb < R ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+    uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const uint16_t* src = p.lora_act_in + uint32_t(mrow[i]) * uint32_t(R);
-      if (la_vec) {
-        // R % 8 == 0 and rb % 8 == 0: the eight ranks are all in range or all out
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + min(rb, R - 8));
-        la[i] = __builtin_bit_cast(bf16x8, rb < R ? v : u32x4{0u, 0u, 0u, 0u});
-      } else {
-        uint32_t w[4];
+    for (int t = 0; t < 4; ++t) {
+      const int r = rb + 2 * t;
+      const uint16_t x0 = src[min(r, R - 1)];
+      const uint16_t x1 = src[min(r + 1, R - 1)];
+      w[t] = bf16_pair(r < R ? x0 : uint16_t(0), r + 1 < R ? x1 : uint16_t(0));
+    }
+    return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  };
+  auto lora_u = [&](int j, int rb) __attribute__((always_inline)) {
+    const uint16_t* src = p.lora_up + min(n0 + wn * C::TN + 32 * j + l32, N - 1);
+    uint32_t w[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = rb + 2 * t;
-          const uint16_t x0 = src[min(r, R - 1)];
-          const uint16_t x1 = src[min(r + 1, R - 1)];
-          w[t] = bf16_pair(r < R ? x0 : uint16_t(0), r + 1 < R ? x1 : uint16_t(0));
-        }
-        la[i] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+    for (int t = 0; t < 4; ++t) {
+      const int r = rb + 2 * t;
+      const uint16_t x0 = src[uint32_t(min(r, R - 1)) * uint32_t(N)];
+      const uint16_t x1 = src[uint32_t(min(r + 1, R - 1)) * uint32_t(N)];
+      w[t] = bf16_pair(r < R ? x0 : uint16_t(0), r + 1 < R ? x1 : uint16_t(0));
+    }
+    return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  };
+  for (int rs0 = 0; rs0 * 16 < R; rs0 += LORA_BATCH) {
+    const int nsteps = min(LORA_BATCH, (R + 15) / 16 - rs0);
+    bf16x8 la[LORA_BATCH][C::MI], lu[LORA_BATCH][C::NI];
+#pragma unroll
+    for (int s = 0; s < LORA_BATCH; ++s) {
+      if (s < nsteps) {
+        const int rb = (rs0 + s) * 16 + 8 * g;
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) la[s][i] = lora_a(i, rb);
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) lu[s][j] = lora_u(j, rb);
       }
     }
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) {
-      const uint16_t* src = p.lora_up + min(n0 + wn * C::TN + 32 * j + l32, N - 1);
-      uint32_t w[4];
+    for (int s = 0; s < LORA_BATCH; ++s) {
+      if (s < nsteps) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = rb + 2 * t;
-        const uint16_t x0 = src[uint32_t(min(r, R - 1)) * uint32_t(N)];
-        const uint16_t x1 = src[uint32_t(min(r + 1, R - 1)) * uint32_t(N)];
-        w[t] = bf16_pair(r < R ? x0 : uint16_t(0), r + 1 < R ? x1 : uint16_t(0));
+        for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+          for (int i = 0; i < C::MI; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[s][j], la[s][i], acc[j][i], 0, 0, 0);
       }
-      lu[j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
     }
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[j], la[i], acc[j][i], 0, 0, 0);
   }
 
   // + bias, bf16 (round to nearest even), staged through LDS: the ring is
