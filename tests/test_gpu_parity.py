@@ -242,7 +242,10 @@ def test_probe_nan_scale_propagates():
 
 EDGE = [(1, 1, 16, 0), (1, 5, 16, 1), (7, 33, 48, 3), (33, 200, 144, 16), (257, 193, 272, 32),
         (300, 129, 160, 17), (64, 64, 4096, 128), (513, 385, 256, 128), (129, 1, 32, 8),
-        (2, 1000, 112, 24), (1000, 64, 208, 40)]
+        (2, 1000, 112, 24), (1000, 64, 208, 40),
+        # fast flavour (K % 32 == 0, N % 8 == 0, R % 8 == 0): N-edge tiles,
+        # several LoRA rank chunks, a last chunk only partly inside R
+        (300, 200, 256, 40), (100, 3000, 512, 72), (129, 8, 32, 8)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
