@@ -159,11 +159,12 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 }
 
 // Two flavours per tile shape. The fast one (GENERAL = false) needs packed
-// rows that are a multiple of 16 bytes (K % 32 == 0), R % 8 == 0, N % 8 == 0
-// and 16-byte aligned LoRA operands: it moves packed data in 16-byte DMA
-// pieces and LoRA operands in 16-byte loads. The general one takes every
-// valid shape: 4-byte DMA pieces (packed rows are always a multiple of 8
-// bytes) and LoRA operands read element by element.
+// rows that are a multiple of 16 bytes (K % 32 == 0), M % 8 == 0, N % 8 == 0,
+// R % 8 == 0, 8-byte aligned scales and 16-byte aligned LoRA operands: it
+// moves packed data in 16-byte DMA pieces, scales in 8-byte loads and LoRA
+// operands in 16-byte loads, with no per-lane branches. The general one takes
+// every valid shape: 4-byte DMA pieces (packed rows are always a multiple of
+// 8 bytes), scales byte by byte at the edges, LoRA operands element by element.
 template <class C, bool GENERAL>
 __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4a4_kernel(
     const Params p) {
@@ -208,15 +209,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const uint32_t dma_round = uint32_t(ROWS_PER_ROUND) * uint32_t(rowbytes);
 
   const int full_stages = rowbytes / C::ROW_BYTES;   // stages lying entirely inside K
-  // Stage `st`'s packed bytes into ring slot `buf` % STAGES.
-  auto issue_dma = [&](int st, int buf) __attribute__((always_inline)) {
+  // Round u of stage `st`'s packed bytes into ring slot `buf` % STAGES.
+  auto dma_part = [&](int st, int buf, int u) __attribute__((always_inline)) {
     uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
     const uint32_t k0 = uint32_t(st * C::ROW_BYTES);
     // pieces past the row end (partial last stage only) re-read the row's
     // first piece; their k-blocks get a zero scale
     const bool tail_stage = st >= full_stages;
-#pragma unroll
-    for (int u = 0; u < DMA_N; ++u) {
+    {
       const bool is_b = u >= A_ROUNDS;
       const int ur = is_b ? u - A_ROUNDS : u;
       const uint32_t inrow =
@@ -235,6 +235,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
       const uint8_t* src = (is_b ? p.wgt : p.act) + (row_off + kin);
       dma<DMA_BYTES>(src, stage + (u * C::THREADS + wave_u * 64) * DMA_BYTES);
     }
+  };
+  auto issue_dma = [&](int st, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < DMA_N; ++u) dma_part(st, buf, u);
   };
 
   // ---- scale loader. Thread t < SA_THREADS owns rows r8 .. r8+7 of the act
@@ -259,12 +263,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   // raw scale bytes of two stages in flight, indexed by stage parity
   u32x2 s_raw[2][2] = {{{0u, 0u}, {0u, 0u}}, {{0u, 0u}, {0u, 0u}}};
 
-  auto load_scales = [&](int st, u32x2 (&raw)[2]) __attribute__((always_inline)) {
-    if (s_is_a || s_is_b) {
-      const int kb = st * C::KBLK + 2 * s_kp;
-      raw[0] = load_scales8(s_src, kb, KB, s_r0, s_rows, s_fast);
-      raw[1] = load_scales8(s_src, kb + 1, KB, s_r0, s_rows, s_fast);
+  auto load_scale_half = [&](int st, u32x2 (&raw)[2], int e) __attribute__((always_inline)) {
+    const int kb = st * C::KBLK + 2 * s_kp + e;
+    if constexpr (!GENERAL) {
+      // rows % 8 == 0 and 8-byte aligned scales: a group of 8 rows is wholly
+      // inside or wholly past the edge, where it re-reads the last group (its
+      // rows only reach discarded outputs). Threads without a scale role read
+      // a clamped address too and store nothing, so this load is unconditional.
+      raw[e] = *reinterpret_cast<const u32x2*>(s_src + uint32_t(min(kb, KB - 1)) * uint32_t(s_rows) +
+                                               uint32_t(min(s_r0, s_rows - 8)));
+    } else {
+      if (s_is_a || s_is_b) raw[e] = load_scales8(s_src, kb, KB, s_r0, s_rows, s_fast);
     }
+  };
+  auto load_scales = [&](int st, u32x2 (&raw)[2]) __attribute__((always_inline)) {
+    load_scale_half(st, raw, 0);
+    load_scale_half(st, raw, 1);
   };
   // k-blocks past K get scale 0: their packed bytes (re-read from the row
   // start) then contribute exactly zero, since E2M1 values are finite.
@@ -308,25 +322,28 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     u32x4 a[C::MI], b[C::NI];
     uint32_t sa[C::MI][2], sb[C::NI][2];   // fp16 bits in the low half
   };
-  auto read_chunk = [&](int st, int h, Chunk& R) __attribute__((always_inline)) {
+  // Tile t (act tiles 0 .. MI-1, then wgt tiles) of chunk h of stage st.
+  auto read_tile = [&](int st, int h, int t, Chunk& R) __attribute__((always_inline)) {
     const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
     // chunk 2g+1 sits at chunk position ((2g) ^ swz) ^ 1: flip bit 4
-    const uint8_t* pa = stage + (h ? (a_rd0 ^ 16u) : a_rd0);
-    const uint8_t* pb = stage + (h ? (b_rd0 ^ 16u) : b_rd0);
-    const uint16_t* qa = reinterpret_cast<const uint16_t*>(stage + sa_rd0 + h * C::BM * 4);
-    const uint16_t* qb = reinterpret_cast<const uint16_t*>(stage + sb_rd0 + h * C::BN * 4);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      R.a[i] = *reinterpret_cast<const u32x4*>(pa + i * 32 * C::ROW_BYTES);
-      R.sa[i][0] = qa[i * 64];
-      R.sa[i][1] = qa[i * 64 + 1];
-    }
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j) {
+    if (t < C::MI) {
+      const uint8_t* pa = stage + (h ? (a_rd0 ^ 16u) : a_rd0);
+      const uint16_t* qa = reinterpret_cast<const uint16_t*>(stage + sa_rd0 + h * C::BM * 4);
+      R.a[t] = *reinterpret_cast<const u32x4*>(pa + t * 32 * C::ROW_BYTES);
+      R.sa[t][0] = qa[t * 64];
+      R.sa[t][1] = qa[t * 64 + 1];
+    } else {
+      const int j = t - C::MI;
+      const uint8_t* pb = stage + (h ? (b_rd0 ^ 16u) : b_rd0);
+      const uint16_t* qb = reinterpret_cast<const uint16_t*>(stage + sb_rd0 + h * C::BN * 4);
       R.b[j] = *reinterpret_cast<const u32x4*>(pb + j * 32 * C::ROW_BYTES);
       R.sb[j][0] = qb[j * 64];
       R.sb[j][1] = qb[j * 64 + 1];
     }
+  };
+  auto read_chunk = [&](int st, int h, Chunk& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < C::MI + C::NI; ++t) read_tile(st, h, t, R);
   };
 
   // acc[j][i] is the 32x32 tile D[n][m] = sum_k W[n,k] A[m,k] (wgt as the
@@ -341,31 +358,52 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  // Four k-steps from one chunk: k-step s uses dword s and scale s >> 1.
-  auto compute_chunk = [&](const Chunk& R) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f16x8 av[C::MI], bv[C::NI];
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) av[i] = decode8(R.a[i][s], R.sa[i][s >> 1]);
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j) bv[j] = decode8(R.b[j][s], R.sb[j][s >> 1]);
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[j][i], 0, 0, 0);
-    }
+  // ---- decode software-pipelined one k-step ahead of the MFMAs. D[p] holds
+  // the decoded operands of the k-steps of parity p. k-step s of a chunk uses
+  // dword s and scale s >> 1 of every tile. The 12 MFMAs of one k-step are
+  // issued one per group, each followed by at most one tile decode (8 VALU)
+  // for the next k-step; a scheduling fence closes every group. The VALU work
+  // then runs in the shadow of the MFMA just issued instead of piling up
+  // between MFMAs, which a single wave per SIMD cannot hide.
+  struct Dec {
+    f16x8 a[C::MI], b[C::NI];
   };
-
-  // ---- pipeline over a 4-deep LDS ring. Iteration st issues the scale loads
-  // of stage st+2 and the DMA of stage st+3, and prefetches chunk 0 of stage
-  // st+1 into registers while computing stage st. Prefetches past the last
-  // stage read clamped, in-range addresses into buffers nobody reads again,
-  // which keeps the loop body free of branches. At the top of iteration st
-  // the outstanding vector-memory ops are, in issue order, DMA(st+1),
-  // SCL(st+1), DMA(st+2): waiting until at most DMA_N remain completes the
-  // first two, whatever the number of scale loads.
+  Dec D[2];
+  auto decode_tile = [&](int t, const Chunk& R, int s, Dec& d) __attribute__((always_inline)) {
+    if (t < C::MI)
+      d.a[t] = decode8(R.a[t][s], R.sa[t][s >> 1]);
+    else
+      d.b[t - C::MI] = decode8(R.b[t - C::MI][s], R.sb[t - C::MI][s >> 1]);
+  };
+  auto decode_all = [&](const Chunk& R, int s, Dec& d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < C::MI + C::NI; ++t) decode_tile(t, R, s, d);
+  };
+  // ---- pipeline over a 4-deep LDS ring. Iteration st computes stage st,
+  // issues the scale loads of stage st+2 and the DMA of stage st+3, and reads
+  // chunk 1 of stage st and chunk 0 of stage st+1 into registers. Prefetches
+  // past the last stage read clamped, in-range addresses into buffers nobody
+  // reads again, which keeps the loop body free of branches. At the top of
+  // iteration st the outstanding vector-memory ops are, in issue order,
+  // DMA(st+1), SCL(st+1), DMA(st+2): waiting until at most DMA_N remain
+  // completes the first two, whatever the number of scale loads.
+  //
+  // Inside an iteration every instruction has a fixed slot: k-step S (0..7)
+  // runs G MFMA groups; group q issues MFMA q, decodes tile q of k-step S+1
+  // (q < T), and issues the memory op of slot S*G + q, if any:
+  //   slots 0, 1                scale loads of stage st+2 (two k-blocks)
+  //   slots 2 .. 2+DMA_SLOTS-1  DMA rounds of stage st+3 (one per slot; the
+  //                             general flavour's many 4-byte rounds at once)
+  //   next T slots              tiles of chunk 1 of stage st (decoded from k-step 3 on)
+  //   slots 4G .. 4G+T-1        tiles of chunk 0 of stage st+1 (decoded in k-step 7)
+  // A scheduling fence closes every group, so no memory op or decode bunches
+  // up between two MFMAs: one wave per SIMD keeps its MFMA pipe fed.
+  constexpr int G = C::MI * C::NI;
+  constexpr int T = C::MI + C::NI;
+  constexpr int DMA_SLOTS = GENERAL ? 1 : DMA_N, DMA_PER_SLOT = DMA_N / DMA_SLOTS;
+  constexpr int SLOT_RD1 = 2 + DMA_SLOTS, SLOT_RD0 = 4 * G;
+  static_assert(T <= G, "one decode per MFMA group");
+  static_assert(SLOT_RD1 + T <= 3 * G, "chunk 1 must be requested before k-step 3 decodes it");
   const int last = nst - 1;
   Chunk C0, C1;
   load_scales(0, s_raw[0]);
@@ -378,6 +416,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   wait_vm_lgkm0<63>();
   wg_barrier();
   read_chunk(0, 0, C0);
+  decode_all(C0, 0, D[0]);
 
   // PAR = st & 1, fixed per call site of the two-way unrolled loop.
   auto iteration = [&]<int PAR>(int st) __attribute__((always_inline)) {
@@ -389,12 +428,31 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     store_scales(min(st + 1, last), st + 1, s_raw[1 - PAR]);
     wait_vm_lgkm0<63>();
     wg_barrier();
-    load_scales(min(st + 2, last), s_raw[PAR]);
-    issue_dma(min(st + 3, last), st + 3);
-    read_chunk(st, 1, C1);
-    compute_chunk(C0);
-    read_chunk(st + 1, 0, C0);
-    compute_chunk(C1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int st_scl = min(st + 2, last), st_dma = min(st + 3, last);
+#pragma unroll
+    for (int S = 0; S < 8; ++S) {
+      const Dec& cur = D[S & 1];
+      Dec& nxt = D[(S + 1) & 1];
+      const Chunk& Rn = (S + 1 >= 4 && S + 1 < 8) ? C1 : C0;
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        const int j = q / C::MI, i = q % C::MI;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
+        if (q < T) decode_tile(q, Rn, (S + 1) & 3, nxt);
+        const int slot = S * G + q;
+        if (slot < 2)
+          load_scale_half(st_scl, s_raw[PAR], slot);
+        else if (slot < SLOT_RD1)
+#pragma unroll
+          for (int u = 0; u < DMA_PER_SLOT; ++u) dma_part(st_dma, st + 3, (slot - 2) * DMA_PER_SLOT + u);
+        else if (slot < SLOT_RD1 + T)
+          read_tile(st, 1, slot - SLOT_RD1, C1);
+        else if (slot >= SLOT_RD0 && slot < SLOT_RD0 + T)
+          read_tile(st + 1, 0, slot - SLOT_RD0, C0);   // visible since this iteration's barrier
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
   int st = 0;
   for (; st + 1 < nst; st += 2) {
@@ -793,7 +851,8 @@ extern "C" int gemm_w4a4(const uint8_t* act, const uint8_t* ascales, const uint8
   prm.tiles_n = pl.tiles_n;
 
   const Variant& v = kVariants[pl.variant];
-  const bool fast = K % 32 == 0 && N % 8 == 0 &&
+  const bool fast = K % 32 == 0 && M % 8 == 0 && N % 8 == 0 &&
+                    ((uintptr_t(ascales) | uintptr_t(wscales)) & 7u) == 0 &&
                     (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
   void* args[] = {&prm};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[fast ? 1 : 0]),
