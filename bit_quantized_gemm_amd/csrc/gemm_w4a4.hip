@@ -375,6 +375,25 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     else
       d.b[t - C::MI] = decode8(R.b[t - C::MI][s], R.sb[t - C::MI][s >> 1]);
   };
+  // Pair p (0 .. 4T-1) of a k-step: the two fp16 values 2h, 2h+1 of tile
+  // t = p / 4, h = p % 4 (one conversion and one packed multiply).
+  auto decode_pair = [&](int pr, const Chunk& R, int s, Dec& d) __attribute__((always_inline)) {
+    const int t = pr / 4, h = pr % 4;
+    const uint32_t w = t < C::MI ? R.a[t][s] : R.b[t - C::MI][s];
+    const uint32_t sc = t < C::MI ? R.sa[t][s >> 1] : R.sb[t - C::MI][s >> 1];
+    const _Float16 sv = __builtin_bit_cast(f16x2, sc)[0];
+    f16x2 c;
+    switch (h) {   // the word select must be an immediate; folds after unrolling
+      case 0: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0); break;
+      case 1: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1); break;
+      case 2: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2); break;
+      default: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3); break;
+    }
+    const f16x2 v = c * f16x2{sv, sv};
+    f16x8& o = t < C::MI ? d.a[t] : d.b[t - C::MI];
+    o[2 * h] = v[0];
+    o[2 * h + 1] = v[1];
+  };
   auto decode_all = [&](const Chunk& R, int s, Dec& d) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < C::MI + C::NI; ++t) decode_tile(t, R, s, d);
@@ -389,8 +408,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   // completes the first two, whatever the number of scale loads.
   //
   // Inside an iteration every instruction has a fixed slot: k-step S (0..7)
-  // runs G MFMA groups; group q issues MFMA q, decodes tile q of k-step S+1
-  // (q < T), and issues the memory op of slot S*G + q, if any:
+  // runs G MFMA groups; group q issues MFMA q, decodes
+  // pairs [4Tq/G, 4T(q+1)/G) of the next k-step's decode (the conversion
+  // issues at half rate, so the decode is spread evenly over all groups),
+  // and issues the memory op of slot S*G + q, if any:
   //   slots 0, 1                scale loads of stage st+2 (two k-blocks)
   //   slots 2 .. 2+DMA_SLOTS-1  DMA rounds of stage st+3 (one per slot; the
   //                             general flavour's many 4-byte rounds at once)
@@ -439,7 +460,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
       for (int q = 0; q < G; ++q) {
         const int j = q / C::MI, i = q % C::MI;
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
-        if (q < T) decode_tile(q, Rn, (S + 1) & 3, nxt);
+#pragma unroll
+        for (int pr = 4 * T * q / G; pr < 4 * T * (q + 1) / G; ++pr) decode_pair(pr, Rn, (S + 1) & 3, nxt);
         const int slot = S * G + q;
         if (slot < 2)
           load_scale_half(st_scl, s_raw[PAR], slot);
