@@ -8,18 +8,18 @@ K-loop, wcscale, LoRA-up, bias, bf16 store) on inputs already resident in HBM.
 Prints one JSON line. TFLOP/s counts the algorithmic 2MNK + 2MRN flops.
 
 The JSON carries:
-  roofline      achieved TFLOP/s of the kernel (per-launch HIP events on the
-                launch stream) against the dense fp16 MFMA peak of MI355X
+  roofline      achieved TFLOP/s of the kernel (average launch duration from
+                HIP events around each of K further launches on the launch
+                stream) against the dense fp16 MFMA peak of MI355X
                 (2.5 PFLOP/s), plus the fraction of the dense FP4 peak; traffic
                 = HBM bytes per launch from the committed rocprofv3 counter
                 summary when it was taken on the current kernel source, else null
-  cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on a bounded row
-                sample of the same workload on this host's cores
+  cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on the same full
+                workload on this host's cores, repeated for about --cpu-seconds
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,16 +32,8 @@ if ROOT not in sys.path:
 PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_gemm_amd", "csrc", f)
-                  for f in ("gemm_w4a4.hip", "w4a4_layout.hpp")]
 
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+from bit_quantized_gemm_amd.profsum import kernel_source_hash  # noqa: E402  (no native load)
 
 
 def committed_traffic(workload: str):
@@ -64,10 +56,9 @@ def committed_traffic(workload: str):
         return None
 
 
-def cpu_baseline(inputs: dict, rows: int) -> dict:
-    """Time the CPU oracle (as it stands) on the first `rows` output rows."""
-    import numpy as np
-
+def cpu_baseline(inputs: dict, seconds: float) -> dict:
+    """Time the CPU oracle (as it stands) on the whole workload, repeated until
+    about `seconds` have passed (at least once)."""
     import oracle.w4a4_ref as ref
     try:
         from threadpoolctl import threadpool_info
@@ -75,17 +66,21 @@ def cpu_baseline(inputs: dict, rows: int) -> dict:
         threads = int(blas[0]["num_threads"]) if blas else 1
     except Exception:  # pragma: no cover
         threads = 1
-    sel = np.arange(rows)
-    args = (inputs["act"][sel], inputs["ascales"][:, sel], inputs["wgt"], inputs["wscales"],
-            inputs["wcscale"], inputs["bias"], inputs["lora_act_in"][sel], inputs["lora_up"])
+    args = (inputs["act"], inputs["ascales"], inputs["wgt"], inputs["wscales"],
+            inputs["wcscale"], inputs["bias"], inputs["lora_act_in"], inputs["lora_up"])
+    reps = 0
     t0 = time.perf_counter()
-    ref.gemm_w4a4_ref(*args)
-    dt = time.perf_counter() - t0
+    while True:
+        ref.gemm_w4a4_ref(*args)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
     M, N, K, R = inputs["M"], inputs["N"], inputs["K"], inputs["R"]
-    flops = 2 * rows * N * K + 2 * rows * R * N
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of M={M} (all N={N}, K={K}, R={R}); "
-                      f"{dt:.2f} s; decode single-threaded numpy, dgemm on {threads} BLAS threads"}
+    flops = (2 * M * N * K + 2 * M * R * N) * reps
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full workload (M={M}, N={N}, K={K}, R={R}) {reps} times, {dt:.1f} s; "
+                      f"float64 decode in numpy, dgemm on {threads} BLAS threads"}
 
 
 def main() -> int:
@@ -94,8 +89,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
-                    help="rows of the CPU-oracle baseline sample (0 skips it)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the CPU-oracle baseline (0 skips it)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter scale probe)")
     a = ap.parse_args()
@@ -151,21 +146,33 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    # Timed region: exactly K back-to-back steps, events only at its two ends.
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region0.record(stream)
+    for _ in range(a.steps):
+        step()
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = region0.elapsed_time(region1)
+
+    # Kernel duration for the roofline: K more launches, each bracketed by
+    # events on the launch stream (the event packets between launches would
+    # otherwise be charged to the timed region above).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     for i in range(a.steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     if bad:
         print(f"gemm_w4a4 returned {bad[0]} ({w4.strerror(bad[0])})", file=sys.stderr)
         return 1
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    region_ms = starts[0].elapsed_time(ends[-1])
 
     # a sampled parity check of the timed output (first rows) against the oracle
     import oracle.w4a4_ref as ref
@@ -209,8 +216,8 @@ def main() -> int:
                           "ok": chk["ok"]},
         "wall_s": round(wall, 3),
     }
-    if a.cpu_rows > 0:
-        res["cpu_baseline"] = cpu_baseline(x, min(a.cpu_rows, wl.M))
+    if a.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(x, a.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0 if chk["ok"] else 3
 

@@ -1,0 +1,158 @@
+"""Summaries of rocprofv3 runs of the W4A4 kernel, as short text files.
+
+    python -m bit_quantized_gemm_amd.profsum trace DIR --workload qkv --command "..."
+    python -m bit_quantized_gemm_amd.profsum traffic FETCH_DIR WRITE_DIR --copy-mib 256 \
+        --workload qkv --command "..."
+    python -m bit_quantized_gemm_amd.profsum counters DIR --workload qkv --command "..."
+
+`trace` reads the kernel statistics of a `--kernel-trace --stats` run.
+`traffic` reads two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a program
+that also made one device copy of COPY_MIB MiB (bench.py --copy-probe-mb): each
+counter is scaled by (true bytes of that copy) / (what the counter read for
+it), and the GEMM's HBM bytes per launch are the scaled median over its
+dispatches. `counters` tabulates the SQ/GRBM counters of one `--pmc` run.
+The file carries the hash of the kernel sources it was taken on, so a reader
+(bench.py) can tell whether it still describes the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+from collections import defaultdict
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("gemm_w4a4.hip", "w4a4_layout.hpp")]
+GEMM_TAG = "gemm_w4a4_kernel"
+COPY_TAG = "copyBuffer"
+
+
+def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 over the kernel sources."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def _per_dispatch(directory: str):
+    """{dispatch id: (kernel name, {counter: summed value})} of a --pmc run."""
+    path = _one(os.path.join(directory, "*counter_collection.csv"))
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        name, vals = out.setdefault(d, (r["Kernel_Name"], defaultdict(float)))
+        vals[r["Counter_Name"]] += float(r["Counter_Value"])
+    return dict(sorted(out.items()))
+
+
+def trace(args) -> str:
+    stats = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_stats.csv")))))
+    rows = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_trace.csv")))))
+    g = [r for r in rows if GEMM_TAG in r["Kernel_Name"]]
+    lines = [f"# gemm_w4a4 kernel trace, {args.workload} workload", "",
+             "Command (repository root, one MI355X, library built in-tree):", "",
+             f"    {args.command}", "",
+             f"Kernel source sha256[:16]: {kernel_source_hash()}", "",
+             "| Kernel | Calls | Average ns | Min ns | Max ns | StdDev ns |",
+             "|---|---|---|---|---|---|"]
+    for s in stats:
+        lines.append(f"| `{s['Name'][:110]}` | {s['Calls']} | {float(s['AverageNs']):.1f} | "
+                     f"{s['MinNs']} | {s['MaxNs']} | {float(s['StdDev']):.1f} |")
+    if g:
+        r = g[0]
+        lines += ["", f"Launch: grid {r['Grid_Size_X']} work-items / workgroup {r['Workgroup_Size_X']}, "
+                      f"LDS {r['LDS_Block_Size']} B, VGPR {r['VGPR_Count']}, AGPR {r['Accum_VGPR_Count']}, "
+                      f"SGPR {r['SGPR_Count']}, scratch {r['Scratch_Size']} B."]
+        gs = sorted(g, key=lambda r: int(r["Start_Timestamp"]))
+        gaps = [int(b["Start_Timestamp"]) - int(a["End_Timestamp"]) for a, b in zip(gs, gs[1:])]
+        if gaps:
+            lines.append(f"Median gap between consecutive launches under the tracer: "
+                         f"{statistics.median(gaps):.0f} ns.")
+    return "\n".join(lines) + "\n"
+
+
+def traffic(args) -> str:
+    fetch, write = _per_dispatch(args.fetch_dir), _per_dispatch(args.write_dir)
+    true_kib = args.copy_mib * 1024.0
+
+    def scale(runs, counter):
+        copies = [v[counter] for n, v in runs.values() if COPY_TAG in n]
+        if not copies:
+            raise SystemExit(f"no copy dispatch found for {counter}")
+        probe = max(copies)   # the probe is by far the largest copy
+        gemm = [v[counter] for n, v in runs.values() if GEMM_TAG in n]
+        if not gemm:
+            raise SystemExit(f"no gemm dispatch found for {counter}")
+        return probe, true_kib / probe, statistics.median(gemm), len(gemm)
+
+    fp, ff, fg, fn = scale(fetch, "FETCH_SIZE")
+    wp, wf, wg, wn = scale(write, "WRITE_SIZE")
+    fetch_b, write_b = fg * ff * 1024.0, wg * wf * 1024.0
+    lines = [f"# gemm_w4a4 HBM traffic per launch, {args.workload} workload",
+             "# Commands (repository root, one MI355X, library built in-tree):",
+             f"#   {args.command_fetch}", f"#   {args.command_write}",
+             f"# copy probe: one device copy of {args.copy_mib} MiB = {true_kib:.0f} KiB read and written",
+             f"# FETCH_SIZE read {fp:.1f} KiB for the probe -> scale {ff:.4f}; "
+             f"gemm median over {fn} dispatches {fg:.1f} KiB",
+             f"# WRITE_SIZE read {wp:.1f} KiB for the probe -> scale {wf:.4f}; "
+             f"gemm median over {wn} dispatches {wg:.1f} KiB",
+             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"fetch_bytes_per_launch: {fetch_b:.0f}",
+             f"write_bytes_per_launch: {write_b:.0f}",
+             f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}"]
+    return "\n".join(lines) + "\n"
+
+
+def counters(args) -> str:
+    runs = _per_dispatch(args.dir)
+    g = [v for n, v in runs.values() if GEMM_TAG in n]
+    names = sorted(g[0]) if g else []
+    lines = [f"# gemm_w4a4 SQ/GRBM counters, {args.workload} workload", "",
+             "Command (repository root, one MI355X, library built in-tree):", "",
+             f"    {args.command}", "",
+             f"Kernel source sha256[:16]: {kernel_source_hash()}", "",
+             f"Median over {len(g)} dispatches (values summed over the device):", "",
+             "| Counter | Value |", "|---|---|"]
+    for c in names:
+        lines.append(f"| {c} | {statistics.median(v[c] for v in g):.0f} |")
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(prog="profsum")
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--command", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_dir")
+    f.add_argument("write_dir")
+    f.add_argument("--copy-mib", type=float, required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--command-fetch", required=True)
+    f.add_argument("--command-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    sys.stdout.write({"trace": trace, "traffic": traffic, "counters": counters}[a.what](a))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
