@@ -75,6 +75,13 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(VM) only (expcnt and lgkmcnt at their maxima: no wait).
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+}
+
 // Workgroup barrier without the memory fence __syncthreads() carries: the
 // fence would wait for every outstanding DMA (vmcnt(0)) and serialize the
 // ring. Each caller waits for exactly the DMA it needs first; the asm memory
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
                                 m0 + C::BM <= M)
                              : ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.wscales) & 7u) == 0 &&
                                 n0 + C::BN <= N);
-  // raw scale bytes of two stages in flight, indexed by stage parity
+  // raw scale bytes (two k-blocks) of one stage: [0] in the loop, [1] too in the prologue
   u32x2 s_raw[2][2] = {{{0u, 0u}, {0u, 0u}}, {{0u, 0u}, {0u, 0u}}};
 
   auto load_scale_half = [&](int st, u32x2 (&raw)[2], int e) __attribute__((always_inline)) {
@@ -399,13 +406,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     for (int t = 0; t < C::MI + C::NI; ++t) decode_tile(t, R, s, d);
   };
   // ---- pipeline over a 4-deep LDS ring. Iteration st computes stage st,
-  // issues the scale loads of stage st+2 and the DMA of stage st+3, and reads
-  // chunk 1 of stage st and chunk 0 of stage st+1 into registers. Prefetches
-  // past the last stage read clamped, in-range addresses into buffers nobody
-  // reads again, which keeps the loop body free of branches. At the top of
-  // iteration st the outstanding vector-memory ops are, in issue order,
-  // DMA(st+1), SCL(st+1), DMA(st+2): waiting until at most DMA_N remain
-  // completes the first two, whatever the number of scale loads.
+  // loads the scales of stage st+2 and stores them (as fp16) into its buffer
+  // later in the same iteration, DMAs stage st+3, and reads chunk 1 of stage
+  // st and chunk 0 of stage st+1 into registers. Prefetches past the last
+  // stage read clamped, in-range addresses into buffers nobody reads again,
+  // which keeps the loop body free of branches. Vector-memory ops complete in
+  // issue order; at the scale-store slot of iteration st the outstanding ones
+  // are DMA(st+2), SCL(st+2), DMA(st+3), so waiting until at most DMA_N remain
+  // completes the first two, whatever the number of scale loads. Buffer
+  // (st+2) % 4 held stage st-2, which every wave finished before this
+  // iteration's barrier. The top of an iteration is then only that barrier.
   //
   // Inside an iteration every instruction has a fixed slot: k-step S (0..7)
   // runs G MFMA groups; group q issues MFMA q, decodes
@@ -417,12 +427,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   //                             general flavour's many 4-byte rounds at once)
   //   next T slots              tiles of chunk 1 of stage st (decoded from k-step 3 on)
   //   slots 4G .. 4G+T-1        tiles of chunk 0 of stage st+1 (decoded in k-step 7)
+  //   slot SLOT_SCL (k-step 6)  fp16 scales of stage st+2 into its buffer
   // A scheduling fence closes every group, so no memory op or decode bunches
   // up between two MFMAs: one wave per SIMD keeps its MFMA pipe fed.
   constexpr int G = C::MI * C::NI;
   constexpr int T = C::MI + C::NI;
   constexpr int DMA_SLOTS = GENERAL ? 1 : DMA_N, DMA_PER_SLOT = DMA_N / DMA_SLOTS;
-  constexpr int SLOT_RD1 = 2 + DMA_SLOTS, SLOT_RD0 = 4 * G;
+  constexpr int SLOT_RD1 = 2 + DMA_SLOTS, SLOT_RD0 = 4 * G, SLOT_SCL = 6 * G + G / 2;
   static_assert(T <= G, "one decode per MFMA group");
   static_assert(SLOT_RD1 + T <= 3 * G, "chunk 1 must be requested before k-step 3 decodes it");
   const int last = nst - 1;
@@ -432,22 +443,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   issue_dma(min(1, last), 1);
   load_scales(min(1, last), s_raw[1]);
   issue_dma(min(2, last), 2);
-  wait_vm_lgkm0<2 * DMA_N>();
+  wait_vm_lgkm0<2 * DMA_N>();   // SCL(0), DMA(0)
   store_scales(0, 0, s_raw[0]);
+  wait_vm<DMA_N>();              // DMA(1), SCL(1)
+  store_scales(1, 1, s_raw[1]);  // unclamped: a stage past K gets zero scales
   wait_vm_lgkm0<63>();
   wg_barrier();
   read_chunk(0, 0, C0);
   decode_all(C0, 0, D[0]);
 
-  // PAR = st & 1, fixed per call site of the two-way unrolled loop.
-  auto iteration = [&]<int PAR>(int st) __attribute__((always_inline)) {
-    // DMA(st+1) and SCL(st+1) complete: publish stage st+1's scales. The
-    // barrier then makes stage st+1 visible to every wave and guarantees
-    // every wave is done with iteration st-1, whose buffer (st-1) % 4 =
-    // (st+3) % 4 takes DMA(st+3).
+  auto iteration = [&](int st) __attribute__((always_inline)) {
+    // Stage st+1 (DMA and scales) is complete in this wave's view since the
+    // previous iteration's scale slot; the barrier makes it visible to every
+    // wave and guarantees every wave is done with iteration st-1, whose
+    // buffer (st-1) % 4 = (st+3) % 4 takes DMA(st+3).
     wait_vm_lgkm0<DMA_N>();
-    store_scales(min(st + 1, last), st + 1, s_raw[1 - PAR]);
-    wait_vm_lgkm0<63>();
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int st_scl = min(st + 2, last), st_dma = min(st + 3, last);
@@ -464,7 +474,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
         for (int pr = 4 * T * q / G; pr < 4 * T * (q + 1) / G; ++pr) decode_pair(pr, Rn, (S + 1) & 3, nxt);
         const int slot = S * G + q;
         if (slot < 2)
-          load_scale_half(st_scl, s_raw[PAR], slot);
+          load_scale_half(st_scl, s_raw[0], slot);
         else if (slot < SLOT_RD1)
 #pragma unroll
           for (int u = 0; u < DMA_PER_SLOT; ++u) dma_part(st_dma, st + 3, (slot - 2) * DMA_PER_SLOT + u);
@@ -472,16 +482,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
           read_tile(st, 1, slot - SLOT_RD1, C1);
         else if (slot >= SLOT_RD0 && slot < SLOT_RD0 + T)
           read_tile(st + 1, 0, slot - SLOT_RD0, C0);   // visible since this iteration's barrier
+        else if (slot == SLOT_SCL) {
+          wait_vm<DMA_N>();
+          store_scales(st + 2, st + 2, s_raw[0]);   // unclamped: stages past K get zero scales
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  int st = 0;
-  for (; st + 1 < nst; st += 2) {
-    iteration.template operator()<0>(st);
-    iteration.template operator()<1>(st + 1);
-  }
-  if (st < nst) iteration.template operator()<0>(st);
+  for (int st = 0; st < nst; ++st) iteration(st);
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
   // ---------------- epilogue: *wcscale + bias, + LoRA (same accumulators), bf16 store
