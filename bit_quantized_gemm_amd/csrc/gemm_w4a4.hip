@@ -406,16 +406,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     for (int t = 0; t < C::MI + C::NI; ++t) decode_tile(t, R, s, d);
   };
   // ---- pipeline over a 4-deep LDS ring. Iteration st computes stage st,
-  // loads the scales of stage st+2 and stores them (as fp16) into its buffer
-  // later in the same iteration, DMAs stage st+3, and reads chunk 1 of stage
-  // st and chunk 0 of stage st+1 into registers. Prefetches past the last
-  // stage read clamped, in-range addresses into buffers nobody reads again,
-  // which keeps the loop body free of branches. Vector-memory ops complete in
-  // issue order; at the scale-store slot of iteration st the outstanding ones
-  // are DMA(st+2), SCL(st+2), DMA(st+3), so waiting until at most DMA_N remain
-  // completes the first two, whatever the number of scale loads. Buffer
-  // (st+2) % 4 held stage st-2, which every wave finished before this
-  // iteration's barrier. The top of an iteration is then only that barrier.
+  // DMAs stage st+3, loads the raw scales of stage st+2 (register set st % 2),
+  // stores the fp16 scales of stage st+1 (loaded one iteration earlier, set
+  // (st+1) % 2) into its buffer, and reads chunk 1 of stage st and chunk 0 of
+  // stage st+1 into registers. The one barrier sits in the middle of the
+  // iteration, right before the first read of stage st+1: it publishes stage
+  // st+1 (DMA and scales), and every read of stage st-1 (its chunk 1 is read
+  // in k-steps 0-1 of iteration st-1) happened before the previous one, so
+  // DMA(st+3) may refill buffer (st+3) % 4 = (st-1) % 4 from the start of
+  // iteration st. The prologue only waits for stage 0; stage 1 has three
+  // k-steps of stage 0's compute to arrive in.
+  //
+  // Prefetches past the last stage read clamped, in-range addresses into
+  // buffers nobody reads again, and stages past K get zero scales, which keeps
+  // the loop body free of branches. Vector-memory ops complete in issue
+  // order: per iteration SCL(st+2) then DMA(st+3), so at the scale store of
+  // iteration st the ops issued after SCL(st+1) are DMA(st+2), SCL(st+2) and
+  // DMA(st+3); waiting until at most that many remain completes SCL(st+1)
+  // and everything before it, DMA(st+1) included.
   //
   // Inside an iteration every instruction has a fixed slot: k-step S (0..7)
   // runs G MFMA groups; group q issues MFMA q, decodes
@@ -426,40 +434,37 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   //   slots 2 .. 2+DMA_SLOTS-1  DMA rounds of stage st+3 (one per slot; the
   //                             general flavour's many 4-byte rounds at once)
   //   next T slots              tiles of chunk 1 of stage st (decoded from k-step 3 on)
+  //   slot SLOT_SCL (k-step 3)  fp16 scales of stage st+1 into its buffer
+  //   slot 4G (k-step 4)        the barrier, after that group's MFMA
   //   slots 4G .. 4G+T-1        tiles of chunk 0 of stage st+1 (decoded in k-step 7)
-  //   slot SLOT_SCL (k-step 6)  fp16 scales of stage st+2 into its buffer
   // A scheduling fence closes every group, so no memory op or decode bunches
   // up between two MFMAs: one wave per SIMD keeps its MFMA pipe fed.
   constexpr int G = C::MI * C::NI;
   constexpr int T = C::MI + C::NI;
   constexpr int DMA_SLOTS = GENERAL ? 1 : DMA_N, DMA_PER_SLOT = DMA_N / DMA_SLOTS;
-  constexpr int SLOT_RD1 = 2 + DMA_SLOTS, SLOT_RD0 = 4 * G, SLOT_SCL = 6 * G + G / 2;
+  constexpr int SLOT_RD1 = 2 + DMA_SLOTS, SLOT_RD0 = 4 * G, SLOT_SCL = 3 * G + G / 2;
+  // ops issued after SCL(st+1): DMA(st+2), SCL(st+2) (2 loads per thread in
+  // the fast flavour; the general one counts none, which waits longer), DMA(st+3)
+  constexpr int VM_AFTER_SCL = 2 * DMA_N + (GENERAL ? 0 : 2);
   static_assert(T <= G, "one decode per MFMA group");
   static_assert(SLOT_RD1 + T <= 3 * G, "chunk 1 must be requested before k-step 3 decodes it");
+  static_assert(SLOT_RD1 + T <= SLOT_SCL, "slots overlap");
   const int last = nst - 1;
   Chunk C0, C1;
   load_scales(0, s_raw[0]);
   issue_dma(0, 0);
-  issue_dma(min(1, last), 1);
   load_scales(min(1, last), s_raw[1]);
+  issue_dma(min(1, last), 1);
   issue_dma(min(2, last), 2);
-  wait_vm_lgkm0<2 * DMA_N>();   // SCL(0), DMA(0)
+  wait_vm_lgkm0<2 * DMA_N + (GENERAL ? 0 : 2)>();   // SCL(0), DMA(0)
   store_scales(0, 0, s_raw[0]);
-  wait_vm<DMA_N>();              // DMA(1), SCL(1)
-  store_scales(1, 1, s_raw[1]);  // unclamped: a stage past K gets zero scales
   wait_vm_lgkm0<63>();
   wg_barrier();
   read_chunk(0, 0, C0);
   decode_all(C0, 0, D[0]);
 
-  auto iteration = [&](int st) __attribute__((always_inline)) {
-    // Stage st+1 (DMA and scales) is complete in this wave's view since the
-    // previous iteration's scale slot; the barrier makes it visible to every
-    // wave and guarantees every wave is done with iteration st-1, whose
-    // buffer (st-1) % 4 = (st+3) % 4 takes DMA(st+3).
-    wait_vm_lgkm0<DMA_N>();
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+  // PAR = st & 1, fixed per call site of the two-way unrolled loop.
+  auto iteration = [&]<int PAR>(int st) __attribute__((always_inline)) {
     const int st_scl = min(st + 2, last), st_dma = min(st + 3, last);
 #pragma unroll
     for (int S = 0; S < 8; ++S) {
@@ -470,27 +475,35 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
       for (int q = 0; q < G; ++q) {
         const int j = q / C::MI, i = q % C::MI;
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
+        const int slot = S * G + q;
+        if (slot == SLOT_RD0) {
+          wait_vm_lgkm0<63>();   // this wave's scale stores
+          wg_barrier();
+        }
 #pragma unroll
         for (int pr = 4 * T * q / G; pr < 4 * T * (q + 1) / G; ++pr) decode_pair(pr, Rn, (S + 1) & 3, nxt);
-        const int slot = S * G + q;
         if (slot < 2)
-          load_scale_half(st_scl, s_raw[0], slot);
+          load_scale_half(st_scl, s_raw[PAR], slot);
         else if (slot < SLOT_RD1)
 #pragma unroll
           for (int u = 0; u < DMA_PER_SLOT; ++u) dma_part(st_dma, st + 3, (slot - 2) * DMA_PER_SLOT + u);
         else if (slot < SLOT_RD1 + T)
           read_tile(st, 1, slot - SLOT_RD1, C1);
-        else if (slot >= SLOT_RD0 && slot < SLOT_RD0 + T)
-          read_tile(st + 1, 0, slot - SLOT_RD0, C0);   // visible since this iteration's barrier
         else if (slot == SLOT_SCL) {
-          wait_vm<DMA_N>();
-          store_scales(st + 2, st + 2, s_raw[0]);   // unclamped: stages past K get zero scales
-        }
+          wait_vm<VM_AFTER_SCL>();
+          store_scales(st + 1, st + 1, s_raw[1 - PAR]);   // unclamped: stages past K get zero scales
+        } else if (slot >= SLOT_RD0 && slot < SLOT_RD0 + T)
+          read_tile(st + 1, 0, slot - SLOT_RD0, C0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  for (int st = 0; st < nst; ++st) iteration(st);
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    iteration.template operator()<0>(st);
+    iteration.template operator()<1>(st + 1);
+  }
+  if (st < nst) iteration.template operator()<0>(st);
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
   // ---------------- epilogue: *wcscale + bias, + LoRA (same accumulators), bf16 store
