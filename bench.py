@@ -88,7 +88,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qkv")
+    ap.add_argument("--workload", default="qkv", choices=sorted(__import__("synthetic").WORKLOADS))
+    ap.add_argument("--ceiling", action="store_true",
+                    help="LoRA and affine off (R=0, wcscale=1, bias=0): the plain block-scaled GEMM")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle baseline (0 skips it)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -111,6 +113,10 @@ def main() -> int:
         return 1
     wl = synthetic.workload(a.workload)
     x = synthetic.make_inputs(wl)
+    if a.ceiling:
+        import dataclasses
+        x = synthetic.no_lora_affine(x)
+        wl = dataclasses.replace(wl, R=0)
     dev = torch.device("cuda:0")
     t = {k: torch.from_numpy(x[k]).to(dev) for k in ("act", "ascales", "wgt", "wscales",
                                                      "wcscale", "bias")}
@@ -201,7 +207,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
+        "config": {"workload": wl.name, "mode": "ceiling (no LoRA, no affine)" if a.ceiling else "full",
+                   "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
                    "operands": "NVFP4 (E2M1 + E4M3 per 16 k), LoRA bf16, out bf16",
                    "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),

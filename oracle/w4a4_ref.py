@@ -107,9 +107,9 @@ def dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     scales = np.asarray(scales, dtype=np.uint8)
     if scales.shape != (K // 16, rows):
         raise ValueError(f"scales shape {scales.shape} != {(K // 16, rows)}")
-    vals = E2M1_TABLE[codes]
-    per_k = np.repeat(E4M3_TABLE[scales].T, 16, axis=1)  # [rows, K]: scale of (r, k)
-    return vals * per_k
+    vals = E2M1_TABLE[codes].reshape(rows, K // 16, 16)   # [row, k // 16, k % 16]
+    per_block = E4M3_TABLE[scales].T                      # [row, k // 16]: scale of the block
+    return (vals * per_block[:, :, None]).reshape(rows, K)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -29,8 +29,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "bf16_bits_from_f32",
-           "e4m3_scale_byte"]
+__all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "custom_inputs", "no_lora_affine",
+           "bf16_bits_from_f32", "e4m3_scale_byte"]
 
 
 @dataclass(frozen=True)
@@ -69,6 +69,18 @@ WORKLOADS = {
     "ragged": Workload("ragged", 1000, 3072, 3072, 16, seed=1004, zero_scale_frac=0.10,
                        zero_bias_frac=0.01,
                        notes="M not a tile multiple; 10% zero scale blocks, 1% zero bias"),
+    # The four production shapes the SVDQuant W4A4 on Blackwell page measures
+    # (section 9, "calibration": 9.1 the plain block-scaled GEMM ceiling, 9.2
+    # the per-shape MFU table; M = 4352, (K, N, R) below), with the same value
+    # distributions as the workloads above.
+    "prod_k3840_n3072": Workload("prod_k3840_n3072", 4352, 3072, 3840, 128, seed=1005,
+                                 notes="production shape M=4352 K=3840 N=3072, R=128"),
+    "prod_k3840_n15360": Workload("prod_k3840_n15360", 4352, 15360, 3840, 128, seed=1006,
+                                  notes="production shape M=4352 K=3840 N=15360, R=128"),
+    "prod_k15360_n3840": Workload("prod_k15360_n3840", 4352, 3840, 15360, 128, seed=1007,
+                                  notes="production shape M=4352 K=15360 N=3840, R=128"),
+    "prod_k10240_n3072": Workload("prod_k10240_n3072", 4352, 3072, 10240, 32, seed=1008,
+                                  notes="production shape M=4352 K=10240 N=3072, R=32"),
 }
 
 
@@ -139,6 +151,20 @@ def make_inputs(wl: Workload | str, seed: int | None = None) -> dict:
         (rng.standard_normal(size=(R, N)) * wl.lora_up_std).astype(np.float32))
     return dict(act=act, ascales=ascales, wgt=wgt, wscales=wscales, wcscale=wcscale,
                 bias=bias, lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R)
+
+
+def no_lora_affine(x: dict) -> dict:
+    """The same packed operands and scales with the LoRA term and the affine
+    switched off (R = 0, wcscale = 1, bias = 0): the plain block-scaled GEMM,
+    the "ceiling" configuration the SVDQuant page compares against."""
+    y = dict(x)
+    M, N = x["M"], x["N"]
+    y["R"] = 0
+    y["lora_act_in"] = np.zeros((M, 0), np.uint16)
+    y["lora_up"] = np.zeros((0, N), np.uint16)
+    y["wcscale"] = np.ones(N, np.float32)
+    y["bias"] = np.zeros(N, np.float32)
+    return y
 
 
 def custom_inputs(M: int, N: int, K: int, R: int, seed: int, **kw) -> dict:

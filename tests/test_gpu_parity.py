@@ -92,7 +92,8 @@ def _sample_rows(M, block_m, rng):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "ragged"])
+@pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "ragged", "prod_k3840_n3072",
+                                  "prod_k3840_n15360", "prod_k15360_n3840", "prod_k10240_n3072"])
 def test_workload_full_size_sampled(name):
     wl = synthetic.workload(name)
     _say(f"case: {name} {wl.shape}, full-size launch, sampled rows vs oracle")
@@ -105,6 +106,19 @@ def test_workload_full_size_sampled(name):
     # every output is finite (no NaN scale bytes in these inputs)
     vals = (got.astype(np.uint32) << 16).view(np.float32)
     assert np.isfinite(vals).all()
+
+
+@pytest.mark.parametrize("name", ["qkv", "prod_k3840_n3072"])
+def test_ceiling_mode_sampled(name):
+    """LoRA and affine off (R = 0, wcscale = 1, bias = 0) at full size."""
+    wl = synthetic.workload(name)
+    _say(f"case: {name} ceiling mode (no LoRA, no affine), sampled rows vs oracle")
+    x = synthetic.no_lora_affine(synthetic.make_inputs(name))
+    got = run_gpu(x)
+    plan = w4.plan(wl.M, wl.N, wl.K, 0)
+    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(8))
+    y, T = ref.reference_rows(x, rows)
+    assert_parity(got[rows], y, T, f"{name} ceiling ({len(rows)} rows x {wl.N})")
 
 
 def test_deterministic_bytes():
@@ -245,7 +259,8 @@ EDGE = [(1, 1, 16, 0), (1, 5, 16, 1), (7, 33, 48, 3), (33, 200, 144, 16), (257, 
         (2, 1000, 112, 24), (1000, 64, 208, 40),
         # fast flavour (K % 32 == 0, N % 8 == 0, R % 8 == 0): N-edge tiles,
         # several LoRA rank chunks, a last chunk only partly inside R
-        (300, 200, 256, 40), (100, 3000, 512, 72), (129, 8, 32, 8)]
+        (300, 200, 256, 40), (104, 3000, 512, 72), (136, 8, 32, 8), (64, 64, 384, 24),
+        (256, 200, 640, 16), (512, 384, 1024, 0)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
