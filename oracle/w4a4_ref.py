@@ -41,9 +41,15 @@ import numpy as np
 
 __all__ = [
     "e2m1_value", "e4m3_value", "E2M1_TABLE", "E4M3_TABLE", "unpack_codes", "dequantize",
-    "bf16_bits_to_f64", "main_product", "lora_product", "gemm_w4a4_ref", "term_magnitude",
-    "bf16_rne_bits", "ulp_bf16", "tolerance_bound", "check_output", "validate",
+    "bf16_bits_to_f64", "f16_bits_to_f64", "half_bits_to_f64", "main_product", "lora_product",
+    "gemm_w4a4_ref", "term_magnitude", "bf16_rne_bits", "f16_rne_bits", "ulp_bf16", "ulp_f16",
+    "tolerance_bound", "check_output", "validate", "HALF_TYPES",
 ]
+
+# The two 16-bit types the LoRA operands and the output may take. The
+# SVDQuant page runs its operator with either ("c_dtype" fp16 or bf16, its
+# sections 6.6 and 9.2); one call uses one type for lora_act_in, lora_up and out.
+HALF_TYPES = ("bf16", "f16")
 
 
 # ---------------------------------------------------------------- formats
@@ -118,6 +124,30 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> exact float64 values.
+
+    1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits; exponent field 0
+    is zero/subnormal (m * 2^-24), field 31 is infinity (m = 0) or NaN.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 31
+    m = (b & 1023).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -24, np.ldexp(1.0 + m / 1024.0, e - 15))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def half_bits_to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Bits of one of HALF_TYPES -> exact float64 values."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if dtype == "f16":
+        return f16_bits_to_f64(bits)
+    raise ValueError(f"unknown 16-bit type {dtype!r}")
+
+
 # ---------------------------------------------------------------- the operator
 
 def validate(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up):
@@ -154,33 +184,36 @@ def main_product(act, ascales, wgt, wscales) -> np.ndarray:
     return A @ W.T
 
 
-def lora_product(lora_act_in, lora_up) -> np.ndarray:
+def lora_product(lora_act_in, lora_up, dtype: str = "bf16") -> np.ndarray:
     """L[m, n] = sum_r lora_act_in[m, r] * lora_up[r, n] in float64."""
-    la = bf16_bits_to_f64(lora_act_in)
-    lu = bf16_bits_to_f64(lora_up)
+    la = half_bits_to_f64(lora_act_in, dtype)
+    lu = half_bits_to_f64(lora_up, dtype)
     if la.shape[1] == 0:
         return np.zeros((la.shape[0], lu.shape[1]), dtype=np.float64)
     return la @ lu
 
 
-def gemm_w4a4_ref(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up) -> np.ndarray:
-    """Reference result y (float64, [M, N]) of the fused operator."""
+def gemm_w4a4_ref(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                  dtype: str = "bf16") -> np.ndarray:
+    """Reference result y (float64, [M, N]) of the fused operator; `dtype` is
+    the 16-bit type (HALF_TYPES) of the LoRA operands."""
     validate(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up)
     S = main_product(act, ascales, wgt, wscales)
     wc = np.asarray(wcscale, dtype=np.float32).astype(np.float64)
     b = np.asarray(bias, dtype=np.float32).astype(np.float64)
-    L = lora_product(lora_act_in, lora_up)
+    L = lora_product(lora_act_in, lora_up, dtype)
     return wc[None, :] * S + b[None, :] + L
 
 
-def term_magnitude(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up) -> np.ndarray:
+def term_magnitude(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                   dtype: str = "bf16") -> np.ndarray:
     """T[m, n] = |wc[n]| sum_k |A W| + |bias[n]| + sum_r |la lu|: the scale of the tolerance."""
     A = np.abs(dequantize(act, ascales))
     W = np.abs(dequantize(wgt, wscales))
     wc = np.abs(np.asarray(wcscale, dtype=np.float32).astype(np.float64))
     b = np.abs(np.asarray(bias, dtype=np.float32).astype(np.float64))
-    la = np.abs(bf16_bits_to_f64(lora_act_in))
-    lu = np.abs(bf16_bits_to_f64(lora_up))
+    la = np.abs(half_bits_to_f64(lora_act_in, dtype))
+    lu = np.abs(half_bits_to_f64(lora_up, dtype))
     L = la @ lu if la.shape[1] else np.zeros((la.shape[0], lu.shape[1]))
     return wc[None, :] * (A @ W.T) + b[None, :] + L
 
@@ -191,7 +224,8 @@ def reference_rows(inputs: dict, rows) -> tuple:
     la = inputs["lora_act_in"][rows]
     args = (inputs["act"][rows], inputs["ascales"][:, rows], inputs["wgt"], inputs["wscales"],
             inputs["wcscale"], inputs["bias"], la, inputs["lora_up"])
-    return gemm_w4a4_ref(*args), term_magnitude(*args)
+    dtype = inputs.get("dtype", "bf16")
+    return gemm_w4a4_ref(*args, dtype=dtype), term_magnitude(*args, dtype=dtype)
 
 
 # ---------------------------------------------------------------- output rounding + tolerance
@@ -222,6 +256,46 @@ def bf16_rne_bits(y: np.ndarray) -> np.ndarray:
     return out
 
 
+def f16_rne_bits(y: np.ndarray) -> np.ndarray:
+    """Round float64 values straight to IEEE binary16 (nearest, ties to even); uint16 bits.
+
+    binary16 keeps 11 significant bits: normal numbers from 2^-14, subnormals
+    with spacing 2^-24, largest finite 65504. A value at or above 65520 (the
+    midpoint between 65504 and 2^16, a tie that goes to the even 2^16) becomes
+    infinity. Rounding happens once, from float64.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    out = np.zeros(y.shape, dtype=np.uint16)
+    finite = np.isfinite(y)
+    a = np.abs(np.where(finite, y, 0.0))
+    _, e = np.frexp(a)                        # a = f * 2^e, f in [0.5, 1)
+    q = np.ldexp(1.0, np.maximum(e - 11, -24))   # spacing of binary16 numbers around a
+    r = np.rint(a / q) * q                    # exact: division by a power of two; rint ties to even
+    overflow = r >= 2.0 ** 16
+    # encode the (exactly representable) magnitude from its fields
+    rs = np.where(overflow, 1.0, r)
+    _, er = np.frexp(np.where(rs > 0, rs, 1.0))
+    normal = rs >= 2.0 ** -14
+    exp_field = np.where(normal, er - 1 + 15, 0)
+    man = np.where(normal, rs / np.ldexp(1.0, er - 1) - 1.0, rs / 2.0 ** -24 / 1024.0) * 1024.0
+    bits = (exp_field.astype(np.int64) << 10) | np.rint(man).astype(np.int64)
+    bits = np.where(overflow, 0x7C00, np.where(rs > 0, bits, 0)).astype(np.uint16)
+    bits = np.where(np.signbit(y) & finite, bits | np.uint16(0x8000), bits)
+    out[finite] = bits[finite]
+    out[np.isnan(y)] = 0x7E00
+    out[np.isposinf(y)] = 0x7C00
+    out[np.isneginf(y)] = 0xFC00
+    return out
+
+
+def ulp_f16(x: np.ndarray) -> np.ndarray:
+    """Spacing of binary16 numbers at |x|: 2^(max(floor(log2|x|), -14) - 10); 2^-24 at 0."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.where(a > 0, a, 1.0))   # floor(log2 a) = e - 1
+    u = np.ldexp(1.0, np.maximum(e - 1, -14) - 10)
+    return np.where(a > 0, u, 2.0 ** -24)
+
+
 def ulp_bf16(x: np.ndarray) -> np.ndarray:
     """Spacing of bf16 numbers at |x|: 2^(max(floor(log2|x|), -126) - 7); 2^-133 at 0."""
     a = np.abs(np.asarray(x, dtype=np.float64))
@@ -230,23 +304,34 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     return np.where(a > 0, u, 2.0 ** -133)
 
 
-def tolerance_bound(y_ref: np.ndarray, T: np.ndarray) -> np.ndarray:
-    """Per-element bound 4e-3 * T + one bf16 ulp of y_ref."""
-    return 4e-3 * np.asarray(T, dtype=np.float64) + ulp_bf16(y_ref)
+# Smallest magnitude that rounds to infinity under round-to-nearest-even.
+OVERFLOW_AT = {"bf16": (2 - 2.0 ** -8) * 2.0 ** 127, "f16": 65520.0}
 
 
-def check_output(out_bits: np.ndarray, y_ref: np.ndarray, T: np.ndarray) -> dict:
-    """Compare bf16 output bits with the reference; NaN must match NaN exactly.
+def tolerance_bound(y_ref: np.ndarray, T: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Per-element bound 4e-3 * T + one ulp of y_ref in the output type."""
+    ulp = ulp_bf16 if dtype == "bf16" else ulp_f16
+    return 4e-3 * np.asarray(T, dtype=np.float64) + ulp(y_ref)
 
+
+def check_output(out_bits: np.ndarray, y_ref: np.ndarray, T: np.ndarray, dtype: str = "bf16") -> dict:
+    """Compare output bits (type `dtype`) with the reference; NaN must match NaN.
+
+    An infinite output is accepted only with the reference's sign and when the
+    tolerance interval around the reference reaches the magnitude that rounds
+    to infinity in that type (the output type cannot hold the value).
     Returns dict(ok, n_fail, max_ratio, worst) where ratio = |err| / bound.
     """
-    got = bf16_bits_to_f64(out_bits)
+    got = half_bits_to_f64(out_bits, dtype)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     nan_ref = np.isnan(y_ref)
     nan_got = np.isnan(got)
-    bound = tolerance_bound(np.where(nan_ref, 0.0, y_ref), np.where(nan_ref, 0.0, T))
-    err = np.abs(np.where(nan_ref | nan_got, 0.0, got - y_ref))
-    ratio = err / bound
+    bound = tolerance_bound(np.where(nan_ref, 0.0, y_ref), np.where(nan_ref, 0.0, T), dtype)
+    inf_got = np.isinf(got)
+    inf_ok = inf_got & (np.sign(got) == np.sign(y_ref)) & \
+        (np.abs(np.where(nan_ref, 0.0, y_ref)) + bound >= OVERFLOW_AT[dtype])
+    err = np.abs(np.where(nan_ref | nan_got | inf_got, 0.0, got - y_ref))
+    ratio = np.where(inf_got & ~inf_ok, np.inf, err / bound)
     fail = (ratio > 1.0) | (nan_ref != nan_got)
     worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else None
     return dict(ok=not bool(fail.any()), n_fail=int(fail.sum()),

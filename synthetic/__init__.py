@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "custom_inputs", "no_lora_affine",
-           "bf16_bits_from_f32", "e4m3_scale_byte"]
+           "bf16_bits_from_f32", "f16_bits_from_f32", "e4m3_scale_byte"]
 
 
 @dataclass(frozen=True)
@@ -129,8 +129,16 @@ def _scales(rng: np.random.Generator, kblocks: int, rows: int, zero_frac: float)
     return s
 
 
-def make_inputs(wl: Workload | str, seed: int | None = None) -> dict:
-    """Draw one seeded input set for a workload; returns a dict of numpy arrays."""
+def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (numpy's nearest-even cast; input recipe only)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def make_inputs(wl: Workload | str, seed: int | None = None, dtype: str = "bf16") -> dict:
+    """Draw one seeded input set for a workload; returns a dict of numpy arrays.
+
+    dtype ("bf16" or "f16") is the 16-bit type of the LoRA operands (and of
+    the output the caller asks for); the draws are the same for both."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     M, N, K, R = wl.shape
@@ -145,12 +153,14 @@ def make_inputs(wl: Workload | str, seed: int | None = None) -> dict:
     bias = rng.standard_normal(size=N).astype(np.float32)
     if wl.zero_bias_frac > 0.0:
         bias[rng.random(size=N) < wl.zero_bias_frac] = 0.0
-    lora_act_in = bf16_bits_from_f32(
-        (rng.standard_normal(size=(M, R)) * wl.lora_act_std).astype(np.float32))
-    lora_up = bf16_bits_from_f32(
-        (rng.standard_normal(size=(R, N)) * wl.lora_up_std).astype(np.float32))
+    if dtype not in ("bf16", "f16"):
+        raise ValueError("dtype must be bf16 or f16")
+    to_bits = bf16_bits_from_f32 if dtype == "bf16" else f16_bits_from_f32
+    lora_act_in = to_bits((rng.standard_normal(size=(M, R)) * wl.lora_act_std).astype(np.float32))
+    lora_up = to_bits((rng.standard_normal(size=(R, N)) * wl.lora_up_std).astype(np.float32))
     return dict(act=act, ascales=ascales, wgt=wgt, wscales=wscales, wcscale=wcscale,
-                bias=bias, lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R)
+                bias=bias, lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R,
+                dtype=dtype)
 
 
 def no_lora_affine(x: dict) -> dict:
@@ -167,7 +177,7 @@ def no_lora_affine(x: dict) -> dict:
     return y
 
 
-def custom_inputs(M: int, N: int, K: int, R: int, seed: int, **kw) -> dict:
+def custom_inputs(M: int, N: int, K: int, R: int, seed: int, dtype: str = "bf16", **kw) -> dict:
     """Inputs for an arbitrary shape with the standard distributions."""
     wl = Workload("custom", M, N, K, R, seed=seed, **kw)
-    return make_inputs(wl)
+    return make_inputs(wl, dtype=dtype)

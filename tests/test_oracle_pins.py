@@ -385,6 +385,86 @@ def pin_checker():
     assert not ref.check_output(ref.bf16_rne_bits(no_lora), y, T)["ok"]
 
 
+# ------------------------------------------------------------ fp16 variant (LoRA and output in binary16)
+
+def _golden_rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                yield [p.strip() for p in line.split(";")]
+
+
+def pin_f16_decode():
+    for bits, expr, _ in _golden_rows("f16_values.txt"):
+        want = eval(expr, {"__builtins__": {}, "float": float})
+        got = float(ref.f16_bits_to_f64(np.array([int(bits, 16)], np.uint16))[0])
+        if math.isnan(want):
+            assert math.isnan(got), bits
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (bits, got, want)
+    # every one of the 65536 patterns against numpy's own binary16 type
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = ref.f16_bits_to_f64(allbits)
+    npv = allbits.view(np.float16).astype(np.float64)
+    nan = np.isnan(npv)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], npv[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(npv[~nan]))
+
+
+def pin_f16_rounding():
+    for expr, bits, _ in _golden_rows("f16_rounding.txt"):
+        v = eval(expr, {"__builtins__": {}})
+        got = int(ref.f16_rne_bits(np.array([v]))[0])
+        assert got == int(bits, 16), (expr, hex(got), bits)
+    # finite values from subnormal to overflow against numpy's float64 -> float16 cast
+    rng = np.random.default_rng(92)
+    v = rng.standard_normal(50000) * np.exp(rng.uniform(-20, 12, 50000))
+    v = np.concatenate([v, rng.integers(-70000, 70000, 2000).astype(np.float64) + 0.5])
+    with np.errstate(over="ignore"):
+        npb = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ref.f16_rne_bits(v), npb)
+    special = np.array([np.nan, np.inf, -np.inf])
+    assert list(ref.f16_rne_bits(special)) == [0x7E00, 0x7C00, 0xFC00]
+
+
+def pin_ulp_f16():
+    u = ref.ulp_f16(np.array([1.0, 1.5, 2.0, -3.0, 2.0 ** -14, 2.0 ** -20, 0.0, 65504.0, 1000.0]))
+    want = [2.0 ** -10, 2.0 ** -10, 2.0 ** -9, 2.0 ** -9, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24,
+            32.0, 0.5]
+    assert list(u) == want
+
+
+def pin_f16_lora_closed_form():
+    """fp16 LoRA operands: la = 0.5 (0x3800), lu = 0.25 (0x3400) -> the LoRA term is R/8."""
+    M, N, K, R = 6, 10, 48, 5
+    x = _const_inputs(M, N, K, R, 2, 2, 0x38, 0x38, 0x3800, 0x3400)
+    y = ref.gemm_w4a4_ref(*_args(x), dtype="f16")
+    want = K * 1.0 * x["wcscale"].astype(np.float64)[None, :] + x["bias"].astype(np.float64)[None, :] \
+        + R * 0.125
+    assert np.array_equal(y, np.broadcast_to(want, (M, N)))
+
+
+def pin_checker_f16():
+    """The fp16 check passes the rounded reference, catches a dropped LoRA or bias on a
+    zero-main case, and accepts infinity only where the value overflows binary16."""
+    x = synthetic.custom_inputs(8, 8, 32, 4, seed=103, dtype="f16")
+    x["ascales"][:] = 0
+    y = ref.gemm_w4a4_ref(*_args(x), dtype="f16")
+    T = ref.term_magnitude(*_args(x), dtype="f16")
+    assert ref.check_output(ref.f16_rne_bits(y), y, T, "f16")["ok"]
+    no_bias = y - x["bias"].astype(np.float64)[None, :]
+    assert not ref.check_output(ref.f16_rne_bits(no_bias), y, T, "f16")["ok"]
+    no_lora = y - ref.lora_product(x["lora_act_in"], x["lora_up"], "f16")
+    assert not ref.check_output(ref.f16_rne_bits(no_lora), y, T, "f16")["ok"]
+    big = np.array([[70000.0, -70000.0, 60000.0]])
+    Tb = np.abs(big)
+    inf_bits = np.array([[0x7C00, 0xFC00, 0x7C00]], np.uint16)
+    r = ref.check_output(inf_bits, big, Tb, "f16")
+    assert r["n_fail"] == 1 and r["worst"] == (0, 2)   # 60000 + 240 < 65520: inf is wrong
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -428,17 +508,17 @@ def _mut_block32(mp):
 
 
 def _mut_lora_scaled(mp):
-    def bad(*a):
+    def bad(*a, dtype="bf16"):
         S = ref.main_product(*a[:4])
         wc = np.asarray(a[4], np.float64)
-        return wc * (S + ref.lora_product(a[6], a[7])) + np.asarray(a[5], np.float64)
+        return wc * (S + ref.lora_product(a[6], a[7], dtype)) + np.asarray(a[5], np.float64)
     mp.setattr(ref, "gemm_w4a4_ref", bad)
 
 
 def _mut_drop_bias(mp):
-    def bad(*a):
+    def bad(*a, dtype="bf16"):
         S = ref.main_product(*a[:4])
-        return np.asarray(a[4], np.float64) * S + ref.lora_product(a[6], a[7])
+        return np.asarray(a[4], np.float64) * S + ref.lora_product(a[6], a[7], dtype)
     mp.setattr(ref, "gemm_w4a4_ref", bad)
 
 
@@ -464,9 +544,9 @@ def _mut_e4m3_subnormal_as_normal(mp):
 
 
 def _mut_lora_up_transposed(mp):
-    def bad(la, lu):
-        a = ref.bf16_bits_to_f64(la)
-        u = ref.bf16_bits_to_f64(lu)
+    def bad(la, lu, dtype="bf16"):
+        a = ref.half_bits_to_f64(la, dtype)
+        u = ref.half_bits_to_f64(lu, dtype)
         if a.shape[1] == 0:
             return np.zeros((a.shape[0], u.shape[1]))
         # reads lora_up as if it were stored [N, R]
@@ -490,6 +570,23 @@ def _mut_bf16_truncate(mp):
         y32 = np.asarray(y, np.float64).astype(np.float32)
         return (y32.view(np.uint32) >> 16).astype(np.uint16)
     mp.setattr(ref, "bf16_rne_bits", bad)
+
+
+def _mut_f16_exponent_bias16(mp):
+    orig = ref.f16_bits_to_f64
+    mp.setattr(ref, "f16_bits_to_f64", lambda b: orig(b) / 2)
+
+
+def _mut_f16_round_toward_zero(mp):
+    orig = ref.f16_rne_bits
+    def bad(y):
+        y = np.asarray(y, np.float64)
+        return orig(np.sign(y) * np.maximum(np.abs(y) - 0.49 * ref.ulp_f16(y), 0.0))
+    mp.setattr(ref, "f16_rne_bits", bad)
+
+
+def _mut_lora_type_ignored(mp):
+    mp.setattr(ref, "half_bits_to_f64", lambda b, dtype="bf16": ref.bf16_bits_to_f64(b))
 
 
 MUTANTS = [v for k, v in sorted(globals().items()) if k.startswith("_mut_")]
