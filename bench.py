@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv", choices=sorted(__import__("synthetic").WORKLOADS))
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="16-bit type of the LoRA operands and the output (gemm_w4a4 / gemm_w4a4_f16)")
     ap.add_argument("--ceiling", action="store_true",
                     help="LoRA and affine off (R=0, wcscale=1, bias=0): the plain block-scaled GEMM")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -112,7 +114,7 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     wl = synthetic.workload(a.workload)
-    x = synthetic.make_inputs(wl)
+    x = synthetic.make_inputs(wl, dtype=a.dtype)
     if a.ceiling:
         import dataclasses
         x = synthetic.no_lora_affine(x)
@@ -120,9 +122,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     t = {k: torch.from_numpy(x[k]).to(dev) for k in ("act", "ascales", "wgt", "wscales",
                                                      "wcscale", "bias")}
-    la = torch.from_numpy(x["lora_act_in"].view(np.int16)).view(torch.bfloat16).to(dev)
-    lu = torch.from_numpy(x["lora_up"].view(np.int16)).view(torch.bfloat16).to(dev)
-    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev)
+    half = torch.float16 if a.dtype == "f16" else torch.bfloat16
+    la = torch.from_numpy(x["lora_act_in"].view(np.int16)).view(half).to(dev)
+    lu = torch.from_numpy(x["lora_up"].view(np.int16)).view(half).to(dev)
+    out = torch.empty((wl.M, wl.N), dtype=half, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     # First call through the checked binding; the timed loop then calls the C
@@ -134,7 +137,7 @@ def main() -> int:
             t["wscales"].data_ptr(), t["wcscale"].data_ptr(), t["bias"].data_ptr(),
             la.data_ptr(), lu.data_ptr(), out.data_ptr(), wl.M, wl.N, wl.K, wl.R,
             stream.cuda_stream)
-    raw = w4.gemm_w4a4_raw
+    raw = w4.gemm_w4a4_f16_raw if a.dtype == "f16" else w4.gemm_w4a4_raw
     bad = []
 
     def step():
@@ -185,7 +188,7 @@ def main() -> int:
     rows = np.arange(min(16, wl.M))
     y, T = ref.reference_rows(x, rows)
     got = out[:len(rows)].view(torch.int16).cpu().numpy().view(np.uint16)
-    chk = ref.check_output(got, y, T)
+    chk = ref.check_output(got, y, T, a.dtype)
 
     flops = wl.flops()
     ms_per_step = region_ms / a.steps
@@ -205,11 +208,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16",   # the MFMA's operand type; LoRA/output type in config
         "data": "synthetic",
         "config": {"workload": wl.name, "mode": "ceiling (no LoRA, no affine)" if a.ceiling else "full",
                    "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
-                   "operands": "NVFP4 (E2M1 + E4M3 per 16 k), LoRA bf16, out bf16",
+                   "operands": f"NVFP4 (E2M1 + E4M3 per 16 k), LoRA {a.dtype}, out {a.dtype}",
                    "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",

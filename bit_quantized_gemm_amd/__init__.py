@@ -9,10 +9,10 @@ in the library's HIP kernels. If the library is missing the calls raise.
 from __future__ import annotations
 
 from . import _native
-from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, MAX_R, OK, gemm_w4a4_raw,
-                      library_path, plan, strerror, variants)
+from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, MAX_R, OK, gemm_w4a4_f16_raw,
+                      gemm_w4a4_raw, library_path, plan, strerror, variants)
 
-__all__ = ["gemm_w4a4", "gemm_w4a4_raw", "plan", "variants", "strerror", "library_path",
+__all__ = ["gemm_w4a4", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "plan", "variants", "strerror", "library_path",
            "GemmError", "OK", "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R"]
 
 
@@ -37,13 +37,15 @@ def _check(t, name, dtype, shape, device):
 
 
 def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_up=None,
-              out=None, stream=None):
+              out=None, stream=None, dtype=None):
     """Enqueue the fused operator on `stream` (default: torch's current stream).
 
     act uint8 [M, K/2]; ascales uint8 (or float8_e4m3fn) [K/16, M];
     wgt uint8 [N, K/2]; wscales uint8 (or float8_e4m3fn) [K/16, N];
-    wcscale, bias float32 [N]; lora_act_in bfloat16 [M, R]; lora_up bfloat16 [R, N]
-    (both None for R = 0). Returns out, bfloat16 [M, N] (allocated if None).
+    wcscale, bias float32 [N]; lora_act_in [M, R] and lora_up [R, N] (both None
+    for R = 0). Returns out [M, N] (allocated if None). The LoRA operands and
+    out share one 16-bit type, torch.bfloat16 (gemm_w4a4) or torch.float16
+    (gemm_w4a4_f16): `dtype`, else that of out, else of lora_act_in, else bf16.
     """
     import torch
     if act.dim() != 2 or wgt.dim() != 2:
@@ -66,22 +68,28 @@ def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_
     _check(bias, "bias", torch.float32, (N,), device)
     if (lora_act_in is None) != (lora_up is None):
         raise ValueError("lora_act_in and lora_up go together")
+    if dtype is None:
+        dtype = out.dtype if out is not None else (
+            lora_act_in.dtype if lora_act_in is not None else torch.bfloat16)
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"the LoRA/output type must be bfloat16 or float16, got {dtype}")
     if lora_act_in is None:
         R = 0
         la_ptr = lu_ptr = 0
     else:
         R = lora_act_in.shape[1]
-        _check(lora_act_in, "lora_act_in", torch.bfloat16, (M, R), device)
-        _check(lora_up, "lora_up", torch.bfloat16, (R, N), device)
+        _check(lora_act_in, "lora_act_in", dtype, (M, R), device)
+        _check(lora_up, "lora_up", dtype, (R, N), device)
         la_ptr, lu_ptr = lora_act_in.data_ptr(), lora_up.data_ptr()
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
-    _check(out, "out", torch.bfloat16, (M, N), device)
+        out = torch.empty((M, N), dtype=dtype, device=device)
+    _check(out, "out", dtype, (M, N), device)
     if stream is None:
         stream = torch.cuda.current_stream(device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(device):
-        rc = gemm_w4a4_raw(act.data_ptr(), ascales.data_ptr(), wgt.data_ptr(),
+        call = gemm_w4a4_f16_raw if dtype == torch.float16 else gemm_w4a4_raw
+        rc = call(act.data_ptr(), ascales.data_ptr(), wgt.data_ptr(),
                            wscales.data_ptr(), wcscale.data_ptr(), bias.data_ptr(), la_ptr,
                            lu_ptr, out.data_ptr(), M, N, K, R, handle)
     if rc != OK:

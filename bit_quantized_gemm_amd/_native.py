@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
         vp, i = ctypes.c_void_p, ctypes.c_int
         lib.gemm_w4a4.argtypes = [vp] * 9 + [i, i, i, i, vp]
         lib.gemm_w4a4.restype = i
+        lib.gemm_w4a4_f16.argtypes = [vp] * 9 + [i, i, i, i, vp]
+        lib.gemm_w4a4_f16.restype = i
         lib.gemm_w4a4_plan.argtypes = [i, i, i, i, ctypes.POINTER(Plan)]
         lib.gemm_w4a4_plan.restype = i
         lib.gemm_w4a4_num_variants.argtypes = []
@@ -75,6 +77,13 @@ def gemm_w4a4_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_u
     """Direct call of the C entry point with integer addresses; returns its code."""
     return load().gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
                             out, M, N, K, R, stream)
+
+
+def gemm_w4a4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                      M, N, K, R, stream) -> int:
+    """Direct call of the fp16 C entry point (LoRA and out in binary16); returns its code."""
+    return load().gemm_w4a4_f16(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                                out, M, N, K, R, stream)
 
 
 def plan(M: int, N: int, K: int, R: int) -> dict:

@@ -124,6 +124,19 @@ __device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 b) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 1.0f, true))};
 }
 
+// One LoRA k-step: 8 ranks per lane of lora_up (rows n) and lora_act_in
+// (rows m) as raw 16-bit patterns, fp16 or bf16; both MFMAs have the K-loop's
+// 32x32 accumulator layout.
+template <bool F16>
+__device__ __forceinline__ f32x16 lora_mfma(u32x4 up, u32x4 act, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, up), __builtin_bit_cast(f16x8, act),
+                                                  c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, up), __builtin_bit_cast(bf16x8, act),
+                                                   c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t bf16_pair(uint16_t lo, uint16_t hi) {
   return uint32_t(lo) | (uint32_t(hi) << 16);
 }
@@ -172,7 +185,9 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 // operands in 16-byte loads, with no per-lane branches. The general one takes
 // every valid shape: 4-byte DMA pieces (packed rows are always a multiple of
 // 8 bytes), scales byte by byte at the edges, LoRA operands element by element.
-template <class C, bool GENERAL>
+// F16 selects the 16-bit type of the LoRA operands and of the output:
+// IEEE binary16 (true) or bfloat16 (false); both round to nearest even.
+template <class C, bool GENERAL, bool F16>
 __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4a4_kernel(
     const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
@@ -650,18 +665,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 #pragma unroll
     for (int s = 0; s < RC / 16; ++s) {
       if (s > 0 && c * RC + 16 * s >= R) break;   // an all-zero k-step
-      bf16x8 la[C::MI], lu[C::NI];
+      u32x4 la[C::MI], lu[C::NI];
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
-        la[i] = *reinterpret_cast<const bf16x8*>(smem + la_rd + i * 32 * LR_STRIDE + s * 32);
+        la[i] = *reinterpret_cast<const u32x4*>(smem + la_rd + i * 32 * LR_STRIDE + s * 32);
 #pragma unroll
       for (int j = 0; j < C::NI; ++j)
-        lu[j] = *reinterpret_cast<const bf16x8*>(smem + lu_rd + j * 32 * LR_STRIDE + s * 32);
+        lu[j] = *reinterpret_cast<const u32x4*>(smem + lu_rd + j * 32 * LR_STRIDE + s * 32);
 #pragma unroll
       for (int j = 0; j < C::NI; ++j)
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[j], la[i], acc[j][i], 0, 0, 0);
+        for (int i = 0; i < C::MI; ++i) acc[j][i] = lora_mfma<F16>(lu[j], la[i], acc[j][i]);
     }
   }
 
@@ -682,9 +696,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
         const int ml = wm * C::TM + 32 * i + l32;
         const int nl = wn * C::TN + 32 * j + 8 * q + 4 * g;
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 v = {__bf16(acc[j][i][4 * q]), __bf16(acc[j][i][4 * q + 1]),
-                          __bf16(acc[j][i][4 * q + 2]), __bf16(acc[j][i][4 * q + 3])};
-        *reinterpret_cast<bf16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        if constexpr (F16) {
+          const f16x4 v = {_Float16(acc[j][i][4 * q]), _Float16(acc[j][i][4 * q + 1]),
+                           _Float16(acc[j][i][4 * q + 2]), _Float16(acc[j][i][4 * q + 3])};
+          *reinterpret_cast<f16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
+        } else {
+          const bf16x4 v = {__bf16(acc[j][i][4 * q]), __bf16(acc[j][i][4 * q + 1]),
+                            __bf16(acc[j][i][4 * q + 2]), __bf16(acc[j][i][4 * q + 3])};
+          *reinterpret_cast<bf16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
+        }
       }
     }
   }
@@ -718,13 +739,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 // ------------------------------------------------------------------ host side
 
 struct Variant {
-  void (*kernel[2])(const Params);   // [0]: general, [1]: fast (see gemm_w4a4_kernel)
+  void (*kernel[2][2])(const Params);   // [F16][fast] (see gemm_w4a4_kernel)
   int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
 };
 
 template <class C>
 constexpr Variant make_variant() {
-  return Variant{{gemm_w4a4_kernel<C, true>, gemm_w4a4_kernel<C, false>},
+  return Variant{{{gemm_w4a4_kernel<C, true, false>, gemm_w4a4_kernel<C, false, false>},
+                  {gemm_w4a4_kernel<C, true, true>, gemm_w4a4_kernel<C, false, true>}},
                  C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
                  C::LDS_BYTES, C::STAGE_BYTES, C::OCC};
 }
@@ -851,10 +873,11 @@ extern "C" const char* gemm_w4a4_strerror(int code) {
   }
 }
 
-extern "C" int gemm_w4a4(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
-                         const uint8_t* wscales, const float* wcscale, const float* bias,
-                         const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
-                         int M, int N, int K, int R, void* stream) {
+// Validation and launch shared by the bf16 and the fp16 entry points.
+static int launch(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                  const uint8_t* wscales, const float* wcscale, const float* bias,
+                  const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
+                  int M, int N, int K, int R, void* stream, bool f16) {
   if (!sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
   if (!act || !ascales || !wgt || !wscales || !wcscale || !bias || !out) return GEMM_W4A4_EINVAL;
   if (R > 0 && (!lora_act_in || !lora_up)) return GEMM_W4A4_EINVAL;
@@ -899,8 +922,24 @@ extern "C" int gemm_w4a4(const uint8_t* act, const uint8_t* ascales, const uint8
                     ((uintptr_t(ascales) | uintptr_t(wscales)) & 7u) == 0 &&
                     (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[fast ? 1 : 0]),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][fast ? 1 : 0]),
                                        dim3(pl.grid), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}
+
+extern "C" int gemm_w4a4(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                         const uint8_t* wscales, const float* wcscale, const float* bias,
+                         const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
+                         int M, int N, int K, int R, void* stream) {
+  return launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
+                stream, false);
+}
+
+extern "C" int gemm_w4a4_f16(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                             const uint8_t* wscales, const float* wcscale, const float* bias,
+                             const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
+                             int M, int N, int K, int R, void* stream) {
+  return launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
+                stream, true);
 }

@@ -77,6 +77,23 @@ int gemm_w4a4(const uint8_t* act, const uint8_t* ascales,
               uint16_t* out, int M, int N, int K, int R, void* stream);
 
 /*
+ * gemm_w4a4_f16 — the same operation with the LoRA operands and the output in
+ * IEEE binary16 instead of bfloat16 (the SVDQuant page runs its operator with
+ * either 16-bit type, "c_dtype", sections 6.6 and 9.2):
+ *   lora_act_in  uint16  [M, R]     binary16 bit patterns
+ *   lora_up      uint16  [R, N]     binary16 bit patterns
+ *   out          uint16  [M, N]     binary16 bit patterns (written), rounded to
+ *                                   nearest even; magnitudes of 65520 and above
+ *                                   become infinity
+ * Every other argument, rule, alignment and return code is gemm_w4a4's.
+ */
+int gemm_w4a4_f16(const uint8_t* act, const uint8_t* ascales,
+                  const uint8_t* wgt, const uint8_t* wscales,
+                  const float* wcscale, const float* bias,
+                  const uint16_t* lora_act_in, const uint16_t* lora_up,
+                  uint16_t* out, int M, int N, int K, int R, void* stream);
+
+/*
  * Launch plan chosen by the LDS/register budget solver for one problem size.
  * Filled by gemm_w4a4_plan; pure host arithmetic (no HIP call), so it also
  * runs on a machine without a GPU.

@@ -43,13 +43,16 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
-def _call(**over):
+ENTRIES = {"bf16": w4.gemm_w4a4_raw, "f16": w4.gemm_w4a4_f16_raw}
+
+
+def _call(entry="bf16", **over):
     # plausible fake device addresses: validation must reject before using them
     a = dict(act=0x10000, ascales=0x20000, wgt=0x30000, wscales=0x40000, wcscale=0x50000,
              bias=0x60000, lora_act_in=0x70000, lora_up=0x80000, out=0x90000000,
              M=64, N=64, K=128, R=16, stream=0)
     a.update(over)
-    return w4.gemm_w4a4_raw(a["act"], a["ascales"], a["wgt"], a["wscales"], a["wcscale"],
+    return ENTRIES[entry](a["act"], a["ascales"], a["wgt"], a["wscales"], a["wcscale"],
                             a["bias"], a["lora_act_in"], a["lora_up"], a["out"], a["M"], a["N"],
                             a["K"], a["R"], a["stream"])
 
@@ -61,16 +64,18 @@ def _call(**over):
     dict(M=70000, K=70000),                         # act over 2^31 bytes
     dict(M=1 << 20, N=1 << 12),                     # out over 2^31 bytes
 ])
-def test_invalid_arguments(over):
-    assert _call(**over) == w4.EINVAL
+@pytest.mark.parametrize("entry", sorted(ENTRIES))
+def test_invalid_arguments(over, entry):
+    assert _call(entry, **over) == w4.EINVAL
 
 
 @pytest.mark.parametrize("over", [
     dict(act=0x10008), dict(wgt=0x30004), dict(wcscale=0x50002), dict(bias=0x60001),
     dict(out=0x90000001), dict(lora_act_in=0x70001), dict(lora_up=0x80003),
 ])
-def test_misaligned(over):
-    assert _call(**over) == w4.EALIGN
+@pytest.mark.parametrize("entry", sorted(ENTRIES))
+def test_misaligned(over, entry):
+    assert _call(entry, **over) == w4.EALIGN
 
 
 def test_null_lora_allowed_without_rank():
@@ -83,8 +88,9 @@ def test_null_lora_allowed_without_rank():
 
 @pytest.mark.parametrize("target", ["act", "ascales", "wgt", "wscales", "wcscale", "bias",
                                     "lora_act_in", "lora_up"])
-def test_output_overlapping_an_input(target):
-    assert _call(**{target: 0x90000000 + 256}) == w4.EOVERLAP
+@pytest.mark.parametrize("entry", sorted(ENTRIES))
+def test_output_overlapping_an_input(target, entry):
+    assert _call(entry, **{target: 0x90000000 + 256}) == w4.EOVERLAP
 
 
 def test_strerror():
@@ -158,7 +164,7 @@ def test_solver_lds_matches_code_objects():
         key = "TileCfgILi%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
                                                     v["waves_n"], v["stages"])
         hits = [m for n, m in meta.items() if key in n]
-        assert len(hits) == 2, (key, list(meta))     # rows 16-byte multiple or not
+        assert len(hits) == 4, (key, list(meta))     # {fast, general} x {bf16, fp16}
         for m in hits:
             assert int(m[".group_segment_fixed_size"]) == v["lds_bytes"], (key, m)
             regs = int(m[".vgpr_count"])

@@ -30,10 +30,11 @@ def to_device(x):
         d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(DEV)
     d["wcscale"] = torch.from_numpy(np.ascontiguousarray(x["wcscale"])).to(DEV)
     d["bias"] = torch.from_numpy(np.ascontiguousarray(x["bias"])).to(DEV)
+    half = torch.float16 if x.get("dtype", "bf16") == "f16" else torch.bfloat16
     if x["R"] > 0:
         for k in ("lora_act_in", "lora_up"):
             t = torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16))
-            d[k] = t.view(torch.bfloat16).to(DEV)
+            d[k] = t.view(half).to(DEV)
     else:
         d["lora_act_in"] = d["lora_up"] = None
     return d
@@ -41,19 +42,21 @@ def to_device(x):
 
 def run_gpu(x, out=None):
     d = to_device(x)
+    half = torch.float16 if x.get("dtype", "bf16") == "f16" else torch.bfloat16
     o = w4.gemm_w4a4(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
-                     d["lora_act_in"], d["lora_up"], out=out)
+                     d["lora_act_in"], d["lora_up"], out=out, dtype=half)
     torch.cuda.synchronize()
     return o.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def oracle_full(x):
     a = [x[k] for k in ARGS]
-    return ref.gemm_w4a4_ref(*a), ref.term_magnitude(*a)
+    dt = x.get("dtype", "bf16")
+    return ref.gemm_w4a4_ref(*a, dtype=dt), ref.term_magnitude(*a, dtype=dt)
 
 
-def assert_parity(got, y, T, what):
-    res = ref.check_output(got, y, T)
+def assert_parity(got, y, T, what, dtype="bf16"):
+    res = ref.check_output(got, y, T, dtype)
     _say(f"  {what}: max err/bound {res['max_ratio']:.3g}, failures {res['n_fail']}")
     assert res["ok"], (what, res)
 
@@ -302,3 +305,78 @@ def test_rejects_bad_arguments_on_device():
     bad[8] = base[0]                       # out aliases act
     assert w4.gemm_w4a4_raw(*bad, 64, 64, 128, 16, s) == w4.EOVERLAP
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- fp16 variant (gemm_w4a4_f16)
+
+def test_f16_tiny_full():
+    _say("case: fp16 variant, tiny workload, every element")
+    x = synthetic.make_inputs("tiny", dtype="f16")
+    y, T = oracle_full(x)
+    assert_parity(run_gpu(x), y, T, "f16 tiny", "f16")
+
+
+@pytest.mark.parametrize("name", ["qkv", "mlp_down", "prod_k3840_n3072"])
+def test_f16_workload_sampled(name):
+    wl = synthetic.workload(name)
+    _say(f"case: fp16 variant, {name} {wl.shape}, sampled rows vs oracle")
+    x = synthetic.make_inputs(name, dtype="f16")
+    got = run_gpu(x)
+    plan = w4.plan(*wl.shape)
+    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(9))
+    y, T = ref.reference_rows(x, rows)
+    assert_parity(got[rows], y, T, f"f16 {name} ({len(rows)} rows)", "f16")
+
+
+def test_f16_zero_main_term_shows_lora_and_bias():
+    _say("case: fp16 variant, zero main term, LoRA + bias visible")
+    for R in (1, 16, 32, 128):
+        x = synthetic.custom_inputs(260, 200, 256, R, seed=200 + R, dtype="f16")
+        x["ascales"][:] = 0
+        y, T = oracle_full(x)
+        got = run_gpu(x)
+        assert_parity(got, y, T, f"f16 zero main R={R}", "f16")
+        gv = ref.f16_bits_to_f64(got)
+        assert np.all(np.abs(gv - y) <= 2 * ref.ulp_f16(y) + 1e-6)
+
+
+F16_EDGE = [(1, 5, 16, 1), (7, 33, 48, 3), (257, 193, 272, 32), (300, 200, 256, 40),
+            (136, 8, 32, 8), (512, 384, 1024, 0)]
+
+
+@pytest.mark.parametrize("shape", F16_EDGE, ids=["x".join(map(str, s)) for s in F16_EDGE])
+def test_f16_edge_shapes(shape):
+    M, N, K, R = shape
+    _say(f"case: fp16 variant, edge shape M={M} N={N} K={K} R={R}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=M * 5 + N * 11 + K + R, dtype="f16")
+    y, T = oracle_full(x)
+    assert_parity(run_gpu(x), y, T, f"f16 edge {shape}", "f16")
+
+
+def test_f16_overflow_becomes_infinity():
+    """Columns whose value exceeds binary16's range come out as infinity, the
+    others finite: every code 6 (E2M1 0x7), every scale 7.5 (0x4F), K = 64 gives
+    a main term of 64 * 45 * 45 = 129600 before wcscale in [0.1, 1]."""
+    _say("case: fp16 variant, outputs beyond 65504")
+    M, N, K = 64, 96, 64
+    x = const_inputs(M, N, K, 0, 7, 7, 0x4F, 0x4F)
+    x["dtype"] = "f16"
+    x["wcscale"] = np.linspace(0.1, 1.0, N).astype(np.float32)
+    x["bias"] = np.zeros(N, np.float32)
+    y, T = oracle_full(x)
+    got = run_gpu(x)
+    assert_parity(got, y, T, "f16 overflow", "f16")
+    gv = ref.f16_bits_to_f64(got)
+    want = ref.f16_bits_to_f64(ref.f16_rne_bits(y))
+    assert np.array_equal(np.isinf(gv), np.isinf(want))
+    assert np.isinf(gv).any() and np.isfinite(gv).any()
+
+
+def test_f16_nan_scale_propagates():
+    _say("case: fp16 variant, NaN scale byte")
+    x = synthetic.custom_inputs(64, 64, 64, 8, seed=33, dtype="f16")
+    x["ascales"][1, 5] = 0x7F
+    got = run_gpu(x)
+    y, T = oracle_full(x)
+    assert_parity(got, y, T, "f16 nan scale", "f16")
+    assert np.isnan(ref.f16_bits_to_f64(got)[5]).all()
