@@ -28,6 +28,15 @@ Readings where the pages are silent (each also listed in the design notes):
   NaN at S.1111.111, no infinities); wcscale and bias are fp32; R == 0 means no
   LoRA term.
 
+The MXFP4 variant (second operator of this module, the *_mx functions):
+  the same operator with OCP MX-scaled FP4 operands instead of NVFP4: E2M1
+  codes as above, one UE8M0 scale per 32 consecutive k (an unsigned 8-bit
+  power of two, 2^(b - 127), 0xFF = NaN, no zero). The DeepGEMM FP4 indexer
+  page ("Step 0") describes this pairing, E2M1 data with a UE8M0 block scale
+  that the matrix unit applies itself; its kernel shares one scale per 128
+  elements, the MX block and gfx950's scaled MFMA use 32 (reading). Scales
+  are laid out as for NVFP4: scales[k // 32, row].
+
 Everything is evaluated in float64 after an exact decode. Every decoded value
 has at most 6 significant bits and every product at most 12, so for the
 synthetic workloads the main sum is exact in float64 whatever the summation
@@ -44,6 +53,8 @@ __all__ = [
     "bf16_bits_to_f64", "f16_bits_to_f64", "half_bits_to_f64", "main_product", "lora_product",
     "gemm_w4a4_ref", "term_magnitude", "bf16_rne_bits", "f16_rne_bits", "ulp_bf16", "ulp_f16",
     "tolerance_bound", "check_output", "validate", "HALF_TYPES",
+    "e8m0_value", "E8M0_TABLE", "dequantize_mx", "gemm_mxfp4_ref", "term_magnitude_mx",
+    "reference_rows_mx", "MX_BLOCK",
 ]
 
 # The two 16-bit types the LoRA operands and the output may take. The
@@ -336,3 +347,65 @@ def check_output(out_bits: np.ndarray, y_ref: np.ndarray, T: np.ndarray, dtype: 
     worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else None
     return dict(ok=not bool(fail.any()), n_fail=int(fail.sum()),
                 max_ratio=float(ratio.max()) if ratio.size else 0.0, worst=worst)
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+
+MX_BLOCK = 32   # k values per UE8M0 scale
+
+
+def e8m0_value(b: int) -> float:
+    """Value of a UE8M0 byte: 2^(b - 127); 0xFF is NaN (there is no zero or sign)."""
+    if not 0 <= b <= 255:
+        raise ValueError("E8M0 byte must be in 0..255")
+    return math.nan if b == 255 else math.ldexp(1.0, b - 127)
+
+
+E8M0_TABLE = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64)
+
+
+def dequantize_mx(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact float64 values of one MXFP4 operand.
+
+    packed: [rows, K/2] uint8; scales: [K/32, rows] UE8M0 bytes.
+    Element (r, k) = E2M1(code[r, k]) * E8M0(scales[k // 32, r]).
+    """
+    codes = unpack_codes(packed)
+    rows, K = codes.shape
+    scales = np.asarray(scales, dtype=np.uint8)
+    if K % MX_BLOCK or scales.shape != (K // MX_BLOCK, rows):
+        raise ValueError(f"scales shape {scales.shape} != {(K // MX_BLOCK, rows)}")
+    vals = E2M1_TABLE[codes].reshape(rows, K // MX_BLOCK, MX_BLOCK)
+    per_block = E8M0_TABLE[scales].T
+    return (vals * per_block[:, :, None]).reshape(rows, K)
+
+
+def gemm_mxfp4_ref(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                   dtype: str = "bf16") -> np.ndarray:
+    """Reference y (float64, [M, N]) of the MXFP4 variant of the fused operator."""
+    S = dequantize_mx(act, ascales) @ dequantize_mx(wgt, wscales).T
+    wc = np.asarray(wcscale, dtype=np.float32).astype(np.float64)
+    b = np.asarray(bias, dtype=np.float32).astype(np.float64)
+    return wc[None, :] * S + b[None, :] + lora_product(lora_act_in, lora_up, dtype)
+
+
+def term_magnitude_mx(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                      dtype: str = "bf16") -> np.ndarray:
+    """T for the MXFP4 variant: |wc| sum_k |A W| + |bias| + sum_r |la lu|."""
+    A = np.abs(dequantize_mx(act, ascales))
+    W = np.abs(dequantize_mx(wgt, wscales))
+    wc = np.abs(np.asarray(wcscale, dtype=np.float32).astype(np.float64))
+    b = np.abs(np.asarray(bias, dtype=np.float32).astype(np.float64))
+    la = np.abs(half_bits_to_f64(lora_act_in, dtype))
+    lu = np.abs(half_bits_to_f64(lora_up, dtype))
+    L = la @ lu if la.shape[1] else np.zeros((la.shape[0], lu.shape[1]))
+    return wc[None, :] * (A @ W.T) + b[None, :] + L
+
+
+def reference_rows_mx(inputs: dict, rows) -> tuple:
+    """(y, T) of the MXFP4 variant for a subset of output rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    args = (inputs["act"][rows], inputs["ascales"][:, rows], inputs["wgt"], inputs["wscales"],
+            inputs["wcscale"], inputs["bias"], inputs["lora_act_in"][rows], inputs["lora_up"])
+    dtype = inputs.get("dtype", "bf16")
+    return gemm_mxfp4_ref(*args, dtype=dtype), term_magnitude_mx(*args, dtype=dtype)

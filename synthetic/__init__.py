@@ -134,21 +134,43 @@ def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
-def make_inputs(wl: Workload | str, seed: int | None = None, dtype: str = "bf16") -> dict:
+def _e8m0_scales(rng: np.random.Generator, kblocks: int, rows: int, zero_frac: float) -> np.ndarray:
+    # UE8M0 byte 127 + e: a power of two 2^e, e uniform in -4..2 (the NVFP4
+    # recipe's exponent range; MX scales carry no mantissa). "Zero" blocks get
+    # the smallest scale 2^-127 (byte 0x00): E8M0 has no zero.
+    s = (127 + rng.integers(-4, 3, size=(kblocks, rows))).astype(np.uint8)
+    if zero_frac > 0.0:
+        s[rng.random(size=s.shape) < zero_frac] = 0x00
+    return s
+
+
+def make_inputs(wl: Workload | str, seed: int | None = None, dtype: str = "bf16",
+                fmt: str = "nvfp4") -> dict:
     """Draw one seeded input set for a workload; returns a dict of numpy arrays.
 
     dtype ("bf16" or "f16") is the 16-bit type of the LoRA operands (and of
-    the output the caller asks for); the draws are the same for both."""
+    the output the caller asks for); the draws are the same for both.
+    fmt "nvfp4": E4M3 scales [K/16, rows]; "mxfp4": UE8M0 scales [K/32, rows]."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     M, N, K, R = wl.shape
     if K % 16 != 0:
         raise ValueError("K must be a multiple of 16")
     rng = np.random.default_rng(wl.seed if seed is None else seed)
+    if fmt not in ("nvfp4", "mxfp4"):
+        raise ValueError("fmt must be nvfp4 or mxfp4")
+    if fmt == "mxfp4" and K % 32:
+        raise ValueError("MXFP4 needs K % 32 == 0")
     act = _packed_codes(rng, M, K)
-    ascales = _scales(rng, K // 16, M, wl.zero_scale_frac)
+    if fmt == "nvfp4":
+        ascales = _scales(rng, K // 16, M, wl.zero_scale_frac)
+    else:
+        ascales = _e8m0_scales(rng, K // 32, M, wl.zero_scale_frac)
     wgt = _packed_codes(rng, N, K)
-    wscales = _scales(rng, K // 16, N, wl.zero_scale_frac)
+    if fmt == "nvfp4":
+        wscales = _scales(rng, K // 16, N, wl.zero_scale_frac)
+    else:
+        wscales = _e8m0_scales(rng, K // 32, N, wl.zero_scale_frac)
     wcscale = rng.uniform(0.5, 1.5, size=N).astype(np.float32)
     bias = rng.standard_normal(size=N).astype(np.float32)
     if wl.zero_bias_frac > 0.0:
@@ -160,7 +182,7 @@ def make_inputs(wl: Workload | str, seed: int | None = None, dtype: str = "bf16"
     lora_up = to_bits((rng.standard_normal(size=(R, N)) * wl.lora_up_std).astype(np.float32))
     return dict(act=act, ascales=ascales, wgt=wgt, wscales=wscales, wcscale=wcscale,
                 bias=bias, lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R,
-                dtype=dtype)
+                dtype=dtype, fmt=fmt)
 
 
 def no_lora_affine(x: dict) -> dict:
@@ -177,7 +199,8 @@ def no_lora_affine(x: dict) -> dict:
     return y
 
 
-def custom_inputs(M: int, N: int, K: int, R: int, seed: int, dtype: str = "bf16", **kw) -> dict:
+def custom_inputs(M: int, N: int, K: int, R: int, seed: int, dtype: str = "bf16",
+                  fmt: str = "nvfp4", **kw) -> dict:
     """Inputs for an arbitrary shape with the standard distributions."""
     wl = Workload("custom", M, N, K, R, seed=seed, **kw)
-    return make_inputs(wl, dtype=dtype)
+    return make_inputs(wl, dtype=dtype, fmt=fmt)

@@ -465,6 +465,135 @@ def pin_checker_f16():
     assert r["n_fail"] == 1 and r["worst"] == (0, 2)   # 60000 + 240 < 65520: inf is wrong
 
 
+# ------------------------------------------------------------ MXFP4 variant (UE8M0 per 32 k)
+
+def _mx(M, N, K, R, seed, **kw):
+    return synthetic.custom_inputs(M, N, K, R, seed=seed, fmt="mxfp4", **kw)
+
+
+def _y_mx(x):
+    return ref.gemm_mxfp4_ref(*_args(x))
+
+
+def pin_e8m0_golden():
+    for byte, expr, _ in _golden_rows("e8m0_values.txt"):
+        want = eval(expr, {"__builtins__": {}, "float": float})
+        got = ref.e8m0_value(int(byte, 16))
+        assert (math.isnan(got) and math.isnan(want)) or got == want, (byte, got, want)
+
+
+def pin_e8m0_torch():
+    t = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu)
+    tv = t.to(torch.float64).numpy()
+    nan = np.isnan(tv)
+    assert np.array_equal(np.isnan(ref.E8M0_TABLE), nan)
+    assert np.array_equal(ref.E8M0_TABLE[~nan], tv[~nan])
+
+
+def brute_force_mx(x):
+    """Exact rational evaluation with element loops and the golden E2M1 table;
+    returns (y, T) as floats of the exact values."""
+    e2m1 = _golden_e2m1()
+    e8 = {b: Fraction(2) ** (b - 127) for b in range(255)}
+    M, N, K, R = x["M"], x["N"], x["K"], x["R"]
+    codes = lambda packed, r, k: (int(packed[r, k // 2]) >> (4 * (k % 2))) & 15
+    la = ref.bf16_bits_to_f64(x["lora_act_in"])
+    lu = ref.bf16_bits_to_f64(x["lora_up"])
+    y = np.zeros((M, N))
+    T = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = tot = Fraction(0)
+            for k in range(K):
+                a = _frac(e2m1[codes(x["act"], m, k)]) * e8[int(x["ascales"][k // 32, m])]
+                w = _frac(e2m1[codes(x["wgt"], n, k)]) * e8[int(x["wscales"][k // 32, n])]
+                acc += a * w
+                tot += abs(a * w)
+            lora = sum((_frac(la[m, r]) * _frac(lu[r, n]) for r in range(R)), Fraction(0))
+            wc = _frac(float(x["wcscale"][n]))
+            y[m, n] = float(wc * acc + _frac(float(x["bias"][n])) + lora)
+            T[m, n] = float(abs(wc) * tot + abs(_frac(float(x["bias"][n]))))
+    return y, T
+
+
+def pin_mx_bruteforce_tiny():
+    rng = np.random.default_rng(61)
+    for (M, N, K, R) in [(3, 4, 32, 0), (5, 3, 64, 1), (4, 6, 96, 3)]:
+        x = _mx(M, N, K, R, seed=int(rng.integers(1 << 30)))
+        # exponents -7..7: every product is a multiple of 2^-16 below 2^20, so
+        # the float64 sums are exact and must equal the rational values
+        x["ascales"] = rng.integers(120, 135, size=x["ascales"].shape).astype(np.uint8)
+        x["wscales"] = rng.integers(120, 135, size=x["wscales"].shape).astype(np.uint8)
+        y, _ = brute_force_mx(x)
+        assert np.array_equal(_y_mx(x), y), (M, N, K, R)
+        # exponents over -31..32 and the smallest scale 2^-127: float64 sums
+        # round; the oracle stays within K ulps of the exact value
+        x["ascales"] = rng.integers(96, 160, size=x["ascales"].shape).astype(np.uint8)
+        x["wscales"] = rng.integers(96, 160, size=x["wscales"].shape).astype(np.uint8)
+        x["ascales"][0, 0] = 0
+        y, T = brute_force_mx(x)
+        assert np.all(np.abs(_y_mx(x) - y) <= 2.0 ** -45 * T), (M, N, K, R)
+
+
+def pin_mx_block_boundary():
+    """k = 31 is scaled by block 0 and k = 32 by block 1, for act and for wgt."""
+    M, N, K = 2, 3, 64
+    for side, k in (("act", 31), ("act", 32), ("wgt", 31), ("wgt", 32)):
+        x = _mx(M, N, K, 0, seed=62)
+        x["act"][:] = 0x22 if side == "wgt" else 0
+        x["wgt"][:] = 0x22 if side == "act" else 0
+        x["ascales"][:] = 127
+        x["wscales"][:] = 127
+        x["wcscale"][:] = 1.0
+        x["bias"][:] = 0.0
+        pk = x[side]
+        pk[0, k // 2] = (0x4 << (4 * (k % 2)))           # code 4 = 2.0 at (row 0, k)
+        sc = "ascales" if side == "act" else "wscales"
+        x[sc][1, 0] = 130                                 # block 1 of row 0 scaled by 8
+        y = _y_mx(x)
+        want = 2.0 * (8.0 if k >= 32 else 1.0)            # the other operand is all 1.0
+        if side == "act":
+            assert np.all(y[0] == want) and np.all(y[1] == 0), (side, k, y)
+        else:
+            assert np.all(y[:, 0] == want) and np.all(y[:, 1:] == 0), (side, k, y)
+
+
+def pin_mx_closed_form():
+    M, N, K, R = 3, 5, 96, 2
+    x = _mx(M, N, K, R, seed=63)
+    x["act"][:] = 0x77     # 6.0 everywhere
+    x["wgt"][:] = 0x33     # 1.5 everywhere
+    x["ascales"][:] = 125  # 2^-2
+    x["wscales"][:] = 130  # 2^3
+    x["lora_act_in"][:] = 0x3F00   # bf16 0.5
+    x["lora_up"][:] = 0x3E80       # bf16 0.25
+    y = _y_mx(x)
+    want = K * 6.0 * 0.25 * 1.5 * 8.0 * x["wcscale"].astype(np.float64)[None, :] \
+        + x["bias"].astype(np.float64)[None, :] + R * 0.125
+    assert np.array_equal(y, np.broadcast_to(want, (M, N)))
+
+
+def pin_mx_matches_nvfp4_where_both_apply():
+    """An MXFP4 input whose scales are powers of two inside E4M3's range is also an
+    NVFP4 input (each scale repeated for the two 16-k blocks of its 32): both
+    oracles must agree exactly (the NVFP4 one is pinned independently above)."""
+    x = _mx(17, 13, 192, 3, seed=64)
+    nv = dict(x)
+    e = x["ascales"].astype(np.int64) - 127
+    nv["ascales"] = np.repeat(synthetic.e4m3_scale_byte(e, np.zeros_like(e)), 2, axis=0)
+    e = x["wscales"].astype(np.int64) - 127
+    nv["wscales"] = np.repeat(synthetic.e4m3_scale_byte(e, np.zeros_like(e)), 2, axis=0)
+    assert np.array_equal(_y_mx(x), ref.gemm_w4a4_ref(*_args(nv)))
+    assert np.array_equal(ref.term_magnitude_mx(*_args(x)), ref.term_magnitude(*_args(nv)))
+
+
+def pin_mx_nan_scale():
+    x = _mx(4, 4, 64, 0, seed=65)
+    x["ascales"][1, 2] = 0xFF
+    y = _y_mx(x)
+    assert np.isnan(y[2]).all() and np.isfinite(np.delete(y, 2, 0)).all()
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -587,6 +716,34 @@ def _mut_f16_round_toward_zero(mp):
 
 def _mut_lora_type_ignored(mp):
     mp.setattr(ref, "half_bits_to_f64", lambda b, dtype="bf16": ref.bf16_bits_to_f64(b))
+
+
+def _mut_mx_block16(mp):
+    def bad(packed, scales):
+        codes = ref.unpack_codes(packed)
+        rows, K = codes.shape
+        idx = np.minimum(np.arange(K) // 16, K // 32 - 1)
+        return ref.E2M1_TABLE[codes] * ref.E8M0_TABLE[np.asarray(scales)[idx, :].T]
+    mp.setattr(ref, "dequantize_mx", bad)
+
+
+def _mut_e8m0_bias128(mp):
+    mp.setattr(ref, "E8M0_TABLE", ref.E8M0_TABLE / 2)
+
+
+def _mut_e8m0_nan_as_number(mp):
+    t = ref.E8M0_TABLE.copy()
+    t[255] = 2.0 ** 128
+    mp.setattr(ref, "E8M0_TABLE", t)
+
+
+def _mut_mx_scales_row_major(mp):
+    def bad(packed, scales):
+        codes = ref.unpack_codes(packed)
+        rows, K = codes.shape
+        s = np.asarray(scales).reshape(-1)[: rows * (K // 32)].reshape(rows, K // 32)
+        return ref.E2M1_TABLE[codes] * np.repeat(ref.E8M0_TABLE[s], 32, axis=1)
+    mp.setattr(ref, "dequantize_mx", bad)
 
 
 MUTANTS = [v for k, v in sorted(globals().items()) if k.startswith("_mut_")]
