@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
-"""Throughput of the fused NVFP4 W4A4 GEMM on one MI355X.
+"""Throughput of the fused W4A4 GEMM on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload qkv] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload qkv] [--fmt nvfp4] [--gpus 1]
 
-One step is one call of gemm_w4a4 (the whole operator: loader, decode, MFMA
-K-loop, wcscale, LoRA-up, bias, bf16 store) on inputs already resident in HBM.
-Prints one JSON line. TFLOP/s counts the algorithmic 2MNK + 2MRN flops.
+One step is one call of gemm_w4a4 (NVFP4; or gemm_mxfp4 with --fmt mxfp4): the
+whole operator (loader, decode, MFMA K-loop, wcscale, LoRA-up, bias, 16-bit
+store) on inputs already resident in HBM. Prints one JSON line. TFLOP/s counts
+the algorithmic 2MNK + 2MRN flops.
 
 The JSON carries:
   roofline      achieved TFLOP/s of the kernel (average launch duration from
                 HIP events around each of K further launches on the launch
-                stream) against the dense fp16 MFMA peak of MI355X
-                (2.5 PFLOP/s), plus the fraction of the dense FP4 peak; traffic
-                = HBM bytes per launch from the committed rocprofv3 counter
-                summary when it was taken on the current kernel source, else null
+                stream) against the dense peak of the MFMA it runs on: fp16
+                (2.5 PFLOP/s) for NVFP4, whose operands are decoded to fp16;
+                FP4 (10.1 PFLOP/s) for MXFP4, which feeds the scaled FP4 MFMA
+                directly. traffic = HBM bytes per launch from the committed
+                rocprofv3 counter summary when it was taken on the current
+                kernel source, else null
   cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on the same full
                 workload on this host's cores, repeated for about --cpu-seconds
 """
@@ -33,13 +36,13 @@ PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 
-from bit_quantized_gemm_amd.profsum import kernel_source_hash  # noqa: E402  (no native load)
+from bit_quantized_gemm_amd.profsum import KERNELS, kernel_source_hash  # noqa: E402  (no native load)
 
 
-def committed_traffic(workload: str):
+def committed_traffic(workload: str, fmt: str = "nvfp4"):
     """HBM bytes per launch from profiles/<kernel>_<workload>_traffic.txt, if that
     summary was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"gemm_w4a4_{workload}_traffic.txt")
+    path = os.path.join(PROFILES, f"{KERNELS[fmt][1]}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -48,7 +51,7 @@ def committed_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_source_sha256") != kernel_source_hash(fmt):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -56,10 +59,11 @@ def committed_traffic(workload: str):
         return None
 
 
-def cpu_baseline(inputs: dict, seconds: float) -> dict:
+def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4") -> dict:
     """Time the CPU oracle (as it stands) on the whole workload, repeated until
     about `seconds` have passed (at least once)."""
     import oracle.w4a4_ref as ref
+    oracle_fn = ref.gemm_mxfp4_ref if fmt == "mxfp4" else ref.gemm_w4a4_ref
     try:
         from threadpoolctl import threadpool_info
         blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
@@ -71,7 +75,7 @@ def cpu_baseline(inputs: dict, seconds: float) -> dict:
     reps = 0
     t0 = time.perf_counter()
     while True:
-        ref.gemm_w4a4_ref(*args)
+        oracle_fn(*args, dtype=inputs.get("dtype", "bf16"))
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
@@ -89,6 +93,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv", choices=sorted(__import__("synthetic").WORKLOADS))
+    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"],
+                    help="operand format: NVFP4 (E4M3 scale per 16 k) or MXFP4 (UE8M0 per 32 k)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="16-bit type of the LoRA operands and the output (gemm_w4a4 / gemm_w4a4_f16)")
     ap.add_argument("--ceiling", action="store_true",
@@ -114,7 +120,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     wl = synthetic.workload(a.workload)
-    x = synthetic.make_inputs(wl, dtype=a.dtype)
+    mx = a.fmt == "mxfp4"
+    x = synthetic.make_inputs(wl, dtype=a.dtype, fmt=a.fmt)
     if a.ceiling:
         import dataclasses
         x = synthetic.no_lora_affine(x)
@@ -131,13 +138,17 @@ def main() -> int:
     # First call through the checked binding; the timed loop then calls the C
     # entry point directly with the same (validated) addresses, so per-call
     # Python work cannot leave the GPU idle between launches.
-    w4.gemm_w4a4(t["act"], t["ascales"], t["wgt"], t["wscales"], t["wcscale"], t["bias"],
-                 la, lu, out=out, stream=stream)
+    (w4.gemm_mxfp4 if mx else w4.gemm_w4a4)(t["act"], t["ascales"], t["wgt"], t["wscales"],
+                                             t["wcscale"], t["bias"], la, lu, out=out,
+                                             stream=stream)
     args = (t["act"].data_ptr(), t["ascales"].data_ptr(), t["wgt"].data_ptr(),
             t["wscales"].data_ptr(), t["wcscale"].data_ptr(), t["bias"].data_ptr(),
             la.data_ptr(), lu.data_ptr(), out.data_ptr(), wl.M, wl.N, wl.K, wl.R,
             stream.cuda_stream)
-    raw = w4.gemm_w4a4_f16_raw if a.dtype == "f16" else w4.gemm_w4a4_raw
+    if mx:
+        raw = w4.gemm_mxfp4_f16_raw if a.dtype == "f16" else w4.gemm_mxfp4_raw
+    else:
+        raw = w4.gemm_w4a4_f16_raw if a.dtype == "f16" else w4.gemm_w4a4_raw
     bad = []
 
     def step():
@@ -179,14 +190,14 @@ def main() -> int:
         ends[i].record(stream)
     torch.cuda.synchronize()
     if bad:
-        print(f"gemm_w4a4 returned {bad[0]} ({w4.strerror(bad[0])})", file=sys.stderr)
+        print(f"{KERNELS[a.fmt][1]} returned {bad[0]} ({w4.strerror(bad[0])})", file=sys.stderr)
         return 1
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
     # a sampled parity check of the timed output (first rows) against the oracle
     import oracle.w4a4_ref as ref
     rows = np.arange(min(16, wl.M))
-    y, T = ref.reference_rows(x, rows)
+    y, T = (ref.reference_rows_mx if mx else ref.reference_rows)(x, rows)
     got = out[:len(rows)].view(torch.int16).cpu().numpy().view(np.uint16)
     chk = ref.check_output(got, y, T, a.dtype)
 
@@ -195,8 +206,9 @@ def main() -> int:
     avg_launch_ms = float(np.mean(per_launch_ms))
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     value = flops * a.steps / (region_ms * 1e-3) / 1e12
-    traffic = committed_traffic(a.workload)
-    plan = w4.plan(*wl.shape)
+    traffic = committed_traffic(a.workload, a.fmt)
+    plan = w4.plan(*wl.shape, fmt=a.fmt)
+    peak = PEAK_FP4_TFLOPS if mx else PEAK_F16_MFMA_TFLOPS
     res = {
         "metric": "W4A4 GEMM TFLOP/s + % of used-MFMA/FP4 peak, M=4096 N=K=3072 R=32",
         "value": round(value, 2),
@@ -208,26 +220,27 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",   # the MFMA's operand type; LoRA/output type in config
+        "dtype": "fp4" if mx else "f16",   # the MFMA's operand type; LoRA/output type in config
         "data": "synthetic",
         "config": {"workload": wl.name, "mode": "ceiling (no LoRA, no affine)" if a.ceiling else "full",
                    "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
-                   "operands": f"NVFP4 (E2M1 + E4M3 per 16 k), LoRA {a.dtype}, out {a.dtype}",
+                   "operands": (("MXFP4 (E2M1 + UE8M0 per 32 k)" if mx else "NVFP4 (E2M1 + E4M3 per 16 k)")
+                                + f", LoRA {a.dtype}, out {a.dtype}"),
                    "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_F16_MFMA_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "frac_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(per_launch_ms) * 1e3, 2),
-                     "kernel_source_sha256": kernel_source_hash()},
+                     "kernel_source_sha256": kernel_source_hash(a.fmt)},
         "parity_sample": {"rows": int(len(rows)), "max_err_over_bound": round(chk["max_ratio"], 4),
                           "ok": chk["ok"]},
         "wall_s": round(wall, 3),
     }
     if a.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(x, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(x, a.cpu_seconds, a.fmt)
     print(json.dumps(res), flush=True)
     return 0 if chk["ok"] else 3
 

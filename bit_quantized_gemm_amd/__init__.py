@@ -1,6 +1,9 @@
-"""Fused NVFP4 W4A4 GEMM for AMD Instinct MI355X (gfx950).
+"""Fused 4-bit W4A4 GEMM for AMD Instinct MI355X (gfx950).
 
     y = scaled_mma(act4, wgt4) * wcscale + bias + lora_act_in @ lora_up
+
+with E2M1 operands and either NVFP4 block scales (FP8-E4M3, one per 16 k:
+gemm_w4a4) or MXFP4 block scales (UE8M0, one per 32 k: gemm_mxfp4).
 
 Python binding over the C ABI of libgemm_w4a4.so (include/gemm_w4a4.h).
 PyTorch supplies device memory and the stream; every step of the operator runs
@@ -9,16 +12,18 @@ in the library's HIP kernels. If the library is missing the calls raise.
 from __future__ import annotations
 
 from . import _native
-from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, MAX_R, OK, gemm_w4a4_f16_raw,
-                      gemm_w4a4_raw, library_path, plan, strerror, variants)
+from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK,
+                      gemm_mxfp4_f16_raw, gemm_mxfp4_raw, gemm_w4a4_f16_raw, gemm_w4a4_raw,
+                      library_path, plan, strerror, variants)
 
-__all__ = ["gemm_w4a4", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "plan", "variants", "strerror", "library_path",
-           "GemmError", "OK", "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R"]
+__all__ = ["gemm_w4a4", "gemm_mxfp4", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
+           "gemm_mxfp4_f16_raw", "plan", "variants", "strerror", "library_path", "GemmError", "OK",
+           "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R", "FORMATS"]
 
 
 class GemmError(RuntimeError):
     def __init__(self, code: int):
-        super().__init__(f"gemm_w4a4 failed: {strerror(code)} ({code})")
+        super().__init__(f"fused W4A4 GEMM failed: {strerror(code)} ({code})")
         self.code = code
 
 
@@ -38,7 +43,7 @@ def _check(t, name, dtype, shape, device):
 
 def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_up=None,
               out=None, stream=None, dtype=None):
-    """Enqueue the fused operator on `stream` (default: torch's current stream).
+    """Enqueue the fused NVFP4 operator on `stream` (default: torch's current stream).
 
     act uint8 [M, K/2]; ascales uint8 (or float8_e4m3fn) [K/16, M];
     wgt uint8 [N, K/2]; wscales uint8 (or float8_e4m3fn) [K/16, N];
@@ -47,7 +52,27 @@ def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_
     out share one 16-bit type, torch.bfloat16 (gemm_w4a4) or torch.float16
     (gemm_w4a4_f16): `dtype`, else that of out, else of lora_act_in, else bf16.
     """
+    return _launch("nvfp4", act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                   out, stream, dtype)
+
+
+def gemm_mxfp4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_up=None,
+               out=None, stream=None, dtype=None):
+    """Enqueue the fused MXFP4 operator on `stream`: as gemm_w4a4, but the
+    block scales are UE8M0 bytes (2^(b-127); 255 = NaN), one per 32 k:
+    ascales uint8 (or float8_e8m0fnu) [K/32, M], wscales [K/32, N]; K % 32 == 0.
+    """
+    return _launch("mxfp4", act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                   out, stream, dtype)
+
+
+_BLOCK = {"nvfp4": 16, "mxfp4": 32}
+
+
+def _launch(fmt, act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, stream,
+            dtype):
     import torch
+    block = _BLOCK[fmt]
     if act.dim() != 2 or wgt.dim() != 2:
         raise ValueError("act and wgt must be 2-D")
     device = act.device
@@ -56,14 +81,15 @@ def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_
     M, half = act.shape
     N = wgt.shape[0]
     K = 2 * half
-    if ascales.dtype == torch.float8_e4m3fn:
+    scale_dtype = torch.float8_e4m3fn if fmt == "nvfp4" else getattr(torch, "float8_e8m0fnu", None)
+    if ascales.dtype == scale_dtype:
         ascales = ascales.view(torch.uint8)
-    if wscales.dtype == torch.float8_e4m3fn:
+    if wscales.dtype == scale_dtype:
         wscales = wscales.view(torch.uint8)
     _check(act, "act", torch.uint8, (M, half), device)
     _check(wgt, "wgt", torch.uint8, (N, half), device)
-    _check(ascales, "ascales", torch.uint8, (K // 16, M), device)
-    _check(wscales, "wscales", torch.uint8, (K // 16, N), device)
+    _check(ascales, "ascales", torch.uint8, (K // block, M), device)
+    _check(wscales, "wscales", torch.uint8, (K // block, N), device)
     _check(wcscale, "wcscale", torch.float32, (N,), device)
     _check(bias, "bias", torch.float32, (N,), device)
     if (lora_act_in is None) != (lora_up is None):
@@ -88,10 +114,14 @@ def gemm_w4a4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in=None, lora_
         stream = torch.cuda.current_stream(device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(device):
-        call = gemm_w4a4_f16_raw if dtype == torch.float16 else gemm_w4a4_raw
-        rc = call(act.data_ptr(), ascales.data_ptr(), wgt.data_ptr(),
-                           wscales.data_ptr(), wcscale.data_ptr(), bias.data_ptr(), la_ptr,
-                           lu_ptr, out.data_ptr(), M, N, K, R, handle)
+        f16 = dtype == torch.float16
+        if fmt == "nvfp4":
+            call = gemm_w4a4_f16_raw if f16 else gemm_w4a4_raw
+        else:
+            call = gemm_mxfp4_f16_raw if f16 else gemm_mxfp4_raw
+        rc = call(act.data_ptr(), ascales.data_ptr(), wgt.data_ptr(), wscales.data_ptr(),
+                  wcscale.data_ptr(), bias.data_ptr(), la_ptr, lu_ptr, out.data_ptr(), M, N, K, R,
+                  handle)
     if rc != OK:
         raise GemmError(rc)
     return out

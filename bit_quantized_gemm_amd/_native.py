@@ -62,6 +62,15 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a4_num_variants.restype = i
         lib.gemm_w4a4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
         lib.gemm_w4a4_variant_info.restype = i
+        for name in ("gemm_mxfp4", "gemm_mxfp4_f16"):
+            getattr(lib, name).argtypes = [vp] * 9 + [i, i, i, i, vp]
+            getattr(lib, name).restype = i
+        lib.gemm_mxfp4_plan.argtypes = [i, i, i, i, ctypes.POINTER(Plan)]
+        lib.gemm_mxfp4_plan.restype = i
+        lib.gemm_mxfp4_num_variants.argtypes = []
+        lib.gemm_mxfp4_num_variants.restype = i
+        lib.gemm_mxfp4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
+        lib.gemm_mxfp4_variant_info.restype = i
         lib.gemm_w4a4_strerror.argtypes = [i]
         lib.gemm_w4a4_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -86,20 +95,44 @@ def gemm_w4a4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lo
                                 out, M, N, K, R, stream)
 
 
-def plan(M: int, N: int, K: int, R: int) -> dict:
+def gemm_mxfp4_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                   M, N, K, R, stream) -> int:
+    """Direct call of the MXFP4 C entry point (UE8M0 scales per 32 k); returns its code."""
+    return load().gemm_mxfp4(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                             out, M, N, K, R, stream)
+
+
+def gemm_mxfp4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                       M, N, K, R, stream) -> int:
+    """Direct call of the MXFP4 fp16 C entry point; returns its code."""
+    return load().gemm_mxfp4_f16(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
+                                 out, M, N, K, R, stream)
+
+
+FORMATS = ("nvfp4", "mxfp4")
+_PREFIX = {"nvfp4": "gemm_w4a4", "mxfp4": "gemm_mxfp4"}
+
+
+def _fn(fmt: str, suffix: str):
+    if fmt not in _PREFIX:
+        raise ValueError(f"fmt must be one of {FORMATS}, got {fmt!r}")
+    return getattr(load(), _PREFIX[fmt] + suffix)
+
+
+def plan(M: int, N: int, K: int, R: int, fmt: str = "nvfp4") -> dict:
     p = Plan()
-    rc = load().gemm_w4a4_plan(M, N, K, R, ctypes.byref(p))
+    rc = _fn(fmt, "_plan")(M, N, K, R, ctypes.byref(p))
     if rc != OK:
-        raise ValueError(f"gemm_w4a4_plan: {strerror(rc)} ({rc})")
+        raise ValueError(f"{_PREFIX[fmt]}_plan: {strerror(rc)} ({rc})")
     return p.as_dict()
 
 
-def variants() -> list:
-    lib = load()
+def variants(fmt: str = "nvfp4") -> list:
     out = []
-    for v in range(lib.gemm_w4a4_num_variants()):
+    info = _fn(fmt, "_variant_info")
+    for v in range(_fn(fmt, "_num_variants")()):
         p = Plan()
-        if lib.gemm_w4a4_variant_info(v, ctypes.byref(p)) != OK:
+        if info(v, ctypes.byref(p)) != OK:
             raise RuntimeError("variant_info failed")
         out.append(p.as_dict())
     return out

@@ -1,0 +1,390 @@
+// gemm_mxfp4.hip — the fused operator with MXFP4 operands, on gfx950's scaled FP4 MFMA.
+//
+// y[m,n] = wcscale[n] * sum_k A[m,k] W[n,k] + bias[n] + sum_r la[m,r] lu[r,n]
+//
+// A and W are E2M1 codes (two per byte, low nibble = even k) times one UE8M0
+// scale 2^(b-127) per 32 consecutive k. The DeepGEMM FP4 indexer page ("Step
+// 0") describes this pairing: E2M1 data whose UE8M0 block scale the matrix
+// unit applies itself, the dequantized value never existing in a register;
+// the 32-wide block is the OCP MX one gfx950's instruction takes. The affine
+// and the LoRA residual are the SVDQuant W4A4 on Blackwell page's (sections 2,
+// 6.3, 6.6), shared with the NVFP4 kernel (w4a4_epilogue.hpp).
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 A and B (cbsz = blgp = 4) computes
+// a 32x32 tile over 64 values of k and applies the scales itself. Lane l holds
+// row (A) or column (B) l % 32 and k = 32*(l/32) .. +31 as the 32 nibbles of
+// 16 bytes, and supplies the scale of exactly that 32-block as one byte of a
+// VGPR chosen by op_sel (measured on gfx950 with a one-wave probe against a
+// host reference, every op_sel). So nothing is decoded: operand bytes and
+// scale bytes go HBM -> LDS by direct-to-LDS DMA and LDS -> MFMA unchanged,
+// and the kernel is a DMA ring feeding MFMAs.
+//
+// Pipeline (4-deep LDS ring, one stage = 128 k = two MFMA k-steps): iteration
+// st runs k-step 0 of stage st while it DMAs stage st+3 and reads k-step 1's
+// operands, waits for its own DMA of stage st+1 and meets the workgroup
+// barrier, then runs k-step 1 while it reads stage st+1's k-step 0 operands
+// and scales. Every read of stage st-1 happened before the previous barrier,
+// so DMA(st+3) may refill buffer (st-1) % 4 from the start of iteration st.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gemm_w4a4.h"
+#include "w4a4_common.hpp"
+#include "w4a4_epilogue.hpp"
+#include "w4a4_host.hpp"
+#include "w4a4_layout.hpp"
+
+namespace w4a4 {
+
+// D += (A * 2^(sa_byte - 127)) (B * 2^(sb_byte - 127)) over 64 k, FP4 operands;
+// byte SEL of sa / sb is the scale (one per lane, for its 32 k).
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t sa, uint32_t sb) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i av = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};   // FP4 uses the low 4 dwords
+  const v8i bv = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, SEL, int(sa), SEL, int(sb));
+}
+
+// GENERAL = false (fast): K % 128 == 0, M % 4 == 0, N % 8 == 0, 4-byte aligned scales and
+// the LoRA conditions of the shared epilogue's fast path (R % 8 == 0, 16-byte
+// aligned LoRA operands); scales move by DMA into LDS. GENERAL = true: any
+// valid shape; each lane loads its own scale bytes one stage ahead.
+// F16: LoRA operands and output in binary16 (else bfloat16).
+template <class C, bool GENERAL, bool F16>
+__global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mxfp4_kernel(
+    const Params p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+  constexpr int P_ROUNDS = C::PACKED_BYTES / (C::THREADS * 16);   // packed DMA rounds per stage
+  constexpr int A_ROUNDS = C::B_OFF / (C::THREADS * 16);
+  constexpr int S_ROUNDS = GENERAL ? 0 : C::SCALE_ROUNDS;        // scale DMA rounds per stage
+  constexpr int DMA_N = P_ROUNDS + S_ROUNDS;                     // DMA per thread per stage
+  constexpr int T = C::MI + C::NI;                               // operand tiles per wave
+  constexpr int G = C::MI * C::NI;                               // MFMAs per k-step
+  constexpr int ROWS_PER_ROUND = C::THREADS * 16 / C::ROW_BYTES;
+  static_assert(ROWS_PER_ROUND % 32 == 0, "the chunk swizzle repeats every 32 rows");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int rowbytes = K >> 1;
+  const int KB = K >> 5;                     // scale blocks along k
+  const int nst = (K + C::BK - 1) / C::BK;
+  const int last = nst - 1;
+
+  // ---- packed DMA (as the NVFP4 kernel's, 16-byte pieces only: K % 32 == 0
+  // makes rows a multiple of 16 bytes). Slot q = u*THREADS + tid of a stage's
+  // packed region holds the bytes of data chunk cp ^ swz(row) of its row.
+  const int dma_row0 = tid * 16 / C::ROW_BYTES;
+  const uint32_t dma_inrow = uint32_t(((tid & 3) ^ swz(dma_row0)) * 16);
+  const int full_stages = rowbytes / C::ROW_BYTES;
+  auto dma_packed = [&](int st, int buf, int u) __attribute__((always_inline)) {
+    uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
+    const bool is_b = u >= A_ROUNDS;
+    const int ur = is_b ? u - A_ROUNDS : u;
+    const uint32_t k0 = uint32_t(st * C::ROW_BYTES);
+    // pieces past the row end (partial last stage only) re-read the row start;
+    // their 32-blocks are masked to zero where the operands are used
+    const uint32_t kin = (st >= full_stages && dma_inrow + k0 + 16 > uint32_t(rowbytes)) ? 0u : k0 + dma_inrow;
+    const int row = min((is_b ? n0 : m0) + dma_row0 + ur * ROWS_PER_ROUND, (is_b ? N : M) - 1);
+    const uint8_t* src = (is_b ? p.wgt : p.act) + (uint32_t(row) * uint32_t(rowbytes) + kin);
+    dma<16>(src, stage + (u * C::THREADS + wave_u * 64) * 16);
+  };
+  // ---- scale DMA (fast flavour): 4-byte pieces = 4 consecutive rows of one
+  // k-block, the global [K/32][rows] order kept: [4][BM] act then [4][BN]
+  // wgt. Blocks past K read the last block (their data is masked); rows past
+  // the edge read the last 4 rows (only discarded outputs); padding lanes
+  // re-read a valid piece.
+  auto dma_scales = [&](int st, int buf, int v) __attribute__((always_inline)) {
+    uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
+    const int o = (v * C::THREADS + tid) * 4;
+    const uint8_t* src;
+    if (o < C::KBLK * C::BM) {
+      const int kb = min(st * C::KBLK + o / C::BM, KB - 1);
+      src = p.ascales + uint32_t(kb) * uint32_t(M) + uint32_t(min(m0 + o % C::BM, M - 4));
+    } else {
+      const int ob = min(o - C::KBLK * C::BM, C::KBLK * C::BN - 4);
+      const int kb = min(st * C::KBLK + ob / C::BN, KB - 1);
+      src = p.wscales + uint32_t(kb) * uint32_t(N) + uint32_t(min(n0 + ob % C::BN, N - 4));
+    }
+    dma<4>(src, stage + C::SA_OFF + (v * C::THREADS + wave_u * 64) * 4);
+  };
+  auto dma_round = [&](int st, int buf, int u) __attribute__((always_inline)) {
+    if (u < P_ROUNDS)
+      dma_packed(st, buf, u);
+    else
+      dma_scales(st, buf, u - P_ROUNDS);
+  };
+
+  // ---- operand reads. Lane (l32, g) of tile t reads row r = (wave's first
+  // row) + 32t' + l32 of the stage, data chunk 2s + g for k-step s (k =
+  // 32(2s+g) .. +31 of the stage, scale block 2s + g). Tiles 0 .. MI-1 are
+  // act rows (the MFMA's B operand), MI .. T-1 wgt rows (its A operand).
+  const int ra = wm * C::TM + l32, rb = wn * C::TN + l32;
+  auto read_tile = [&](int st, int s, int t) __attribute__((always_inline)) {
+    const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
+    const int r = t < C::MI ? ra + 32 * t : rb + 32 * (t - C::MI);
+    const int off = t < C::MI ? C::A_OFF : C::B_OFF;
+    return *reinterpret_cast<const u32x4*>(stage + off + r * C::ROW_BYTES + (((2 * s + g) ^ swz(r)) << 4));
+  };
+  // The lane's two scale bytes of a stage (blocks g and 2+g) as bytes 0 and 1.
+  auto read_scales = [&](int st, int t) __attribute__((always_inline)) {
+    if constexpr (!GENERAL) {
+      const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
+      const uint8_t* q = t < C::MI ? stage + C::SA_OFF + ra + 32 * t
+                                   : stage + C::SB_OFF + rb + 32 * (t - C::MI);
+      const int rows = t < C::MI ? C::BM : C::BN;
+      return uint32_t(q[g * rows]) | (uint32_t(q[(2 + g) * rows]) << 8);
+    } else {
+      const bool is_a = t < C::MI;
+      const uint8_t* src = is_a ? p.ascales : p.wscales;
+      const int nrows = is_a ? M : N;
+      const int row = min((is_a ? m0 + ra + 32 * t : n0 + rb + 32 * (t - C::MI)), nrows - 1);
+      const int kb0 = min(st * C::KBLK + g, KB - 1), kb1 = min(st * C::KBLK + 2 + g, KB - 1);
+      return uint32_t(src[uint32_t(kb0) * uint32_t(nrows) + uint32_t(row)]) |
+             (uint32_t(src[uint32_t(kb1) * uint32_t(nrows) + uint32_t(row)]) << 8);
+    }
+  };
+
+  f32x16 acc[C::NI][C::MI];
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+  // One k-step: MFMA group q (tile pair j, i) followed by `op(q)`, fenced.
+  // 32-blocks past K (k-step s of stage st, lane half g) get zero act bytes.
+  auto kstep = [&]<int S>(int st, const u32x4 (&o)[T], const uint32_t (&sc)[T], auto op)
+      __attribute__((always_inline)) {
+    const bool live = GENERAL ? st * C::KBLK + 2 * S + g < KB : true;   // fast: K % 128 == 0
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const int j = q / C::MI, i = q % C::MI;
+      const u32x4 a = (GENERAL && !live) ? u32x4{0u, 0u, 0u, 0u} : o[i];
+      acc[j][i] = mfma_fp4<S>(o[C::MI + j], a, acc[j][i], sc[C::MI + j], sc[i]);
+      op(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: DMA stages 0..2, wait for stage 0, publish it, read its
+  // k-step 0 operands and its scales.
+  u32x4 O0[T], O1[T];
+  uint32_t SC[T], SCn[T];
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int u = 0; u < DMA_N; ++u) dma_round(min(s, last), s, u);
+  wait_vm_lgkm0<2 * DMA_N>();
+  wg_barrier();
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    O0[t] = read_tile(0, 0, t);
+    SC[t] = read_scales(0, t);
+  }
+
+  for (int st = 0; st < nst; ++st) {
+    // k-step 0 of stage st; alongside: DMA(st+3) and k-step 1's operands
+    kstep.template operator()<0>(st, O0, SC, [&](int q) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = q; u < DMA_N; u += G) dma_round(min(st + 3, last), st + 3, u);
+      const int t = q - (G - T);
+      if (t >= 0 && t < T) O1[t] = read_tile(st, 1, t);
+    });
+    // stage st+1 complete in this wave's view (the ops after it are DMA(st+2)
+    // and DMA(st+3), plus, in the general flavour, scale loads, which only
+    // makes the wait longer); publish it
+    wait_vm_lgkm0<2 * DMA_N>();
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1 of stage st; alongside: stage st+1's k-step 0 operands and scales
+    kstep.template operator()<1>(st, O1, SC, [&](int q) __attribute__((always_inline)) {
+      if (q < T) O0[q] = read_tile(st + 1, 0, q);
+      const int t = q - (G - T);
+      if (t >= 0 && t < T) SCn[t] = read_scales(st + 1, t);
+    });
+#pragma unroll
+    for (int t = 0; t < T; ++t) SC[t] = SCn[t];
+  }
+  wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
+
+  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0);
+}
+
+// ------------------------------------------------------------------ host side
+
+struct MxVariant {
+  void (*kernel[2][2])(const Params);   // [F16][fast]
+  int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
+};
+
+template <class C>
+constexpr MxVariant make_mx_variant() {
+  return MxVariant{{{gemm_mxfp4_kernel<C, true, false>, gemm_mxfp4_kernel<C, false, false>},
+                    {gemm_mxfp4_kernel<C, true, true>, gemm_mxfp4_kernel<C, false, true>}},
+                   C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
+                   C::LDS_BYTES, C::STAGE_BYTES, C::OCC};
+}
+
+static const MxVariant kMxVariants[] = {make_mx_variant<MxCfg256x192>(), make_mx_variant<MxCfg128x128>()};
+static constexpr int kNumMxVariants = int(sizeof(kMxVariants) / sizeof(kMxVariants[0]));
+
+static void mx_fill_static(const MxVariant& v, int idx, gemm_w4a4_plan_t* pl) {
+  memset(pl, 0, sizeof(*pl));
+  pl->variant = idx;
+  pl->block_m = v.block_m;
+  pl->block_n = v.block_n;
+  pl->block_k = v.block_k;
+  pl->stages = v.stages;
+  pl->waves_m = v.waves_m;
+  pl->waves_n = v.waves_n;
+  pl->threads = v.threads;
+  pl->lds_bytes = v.lds_bytes;
+  pl->lds_stage_bytes = v.stage_bytes;
+  pl->lds_limit = kLdsLimit;
+}
+
+// K a multiple of the 32-wide scale block; every tensor below 2^31 bytes.
+static bool mx_sizes_ok(int M, int N, int K, int R) {
+  if (!(M >= 1 && N >= 1 && K >= 32 && K % 32 == 0 && R >= 0 && R <= GEMM_W4A4_MAX_R)) return false;
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t m = M, n = N, k = K, r = R;
+  return m * k / 2 < lim && n * k / 2 < lim && m * n * 2 < lim && m * r * 2 < lim && r * n * 2 < lim;
+}
+
+// Rounds of the chip x the work of one round, as for NVFP4; nothing is
+// decoded, so the per-tile factor is the LDS operand traffic per MFMA, which
+// grows as (TM + TN) / (TM * TN) for a wave tile TM x TN.
+static int mx_choose_variant(int M, int N) {
+  int best = 0;
+  double best_cost = 0.0;
+  for (int v = 0; v < kNumMxVariants; ++v) {
+    const MxVariant& x = kMxVariants[v];
+    const long tiles = long((M + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
+    const long slots = long(kNumCUs) * x.occ;
+    const long rounds = (tiles + slots - 1) / slots;
+    const double tm = double(x.block_m / x.waves_m), tn = double(x.block_n / x.waves_n);
+    const double per_round = double(x.occ) * x.block_m * x.block_n * (1.0 + 16.0 * (tm + tn) / (tm * tn));
+    const double cost = double(rounds) * per_round;
+    if (v == 0 || cost < best_cost) {
+      best = v;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+static int mx_plan_impl(int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
+  const int v = mx_choose_variant(M, N);
+  const MxVariant& x = kMxVariants[v];
+  mx_fill_static(x, v, pl);
+  pl->tiles_m = (M + x.block_m - 1) / x.block_m;
+  pl->tiles_n = (N + x.block_n - 1) / x.block_n;
+  const long grid = long(pl->tiles_m) * pl->tiles_n;
+  if (grid > 0x7fffffffL) return GEMM_W4A4_EINVAL;
+  pl->grid = int(grid);
+  pl->k_stages = (K + x.block_k - 1) / x.block_k;
+  pl->lora_steps = (R + 15) / 16;
+  return GEMM_W4A4_OK;
+}
+
+static int mx_launch(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                     const uint8_t* wscales, const float* wcscale, const float* bias,
+                     const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
+                     int M, int N, int K, int R, void* stream, bool f16) {
+  if (!mx_sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
+  if (!act || !ascales || !wgt || !wscales || !wcscale || !bias || !out) return GEMM_W4A4_EINVAL;
+  if (R > 0 && (!lora_act_in || !lora_up)) return GEMM_W4A4_EINVAL;
+  if ((uintptr_t(act) | uintptr_t(wgt)) & 15u) return GEMM_W4A4_EALIGN;
+  if ((uintptr_t(wcscale) | uintptr_t(bias)) & 3u) return GEMM_W4A4_EALIGN;
+  if ((uintptr_t(out) | (R > 0 ? (uintptr_t(lora_act_in) | uintptr_t(lora_up)) : 0u)) & 1u)
+    return GEMM_W4A4_EALIGN;
+
+  const size_t Ms = size_t(M), Ns = size_t(N), Ks = size_t(K), Rs = size_t(R);
+  const size_t out_bytes = Ms * Ns * 2;
+  const struct { const void* p; size_t n; } ins[] = {
+      {act, Ms * Ks / 2},      {ascales, Ks / 32 * Ms}, {wgt, Ns * Ks / 2},
+      {wscales, Ks / 32 * Ns}, {wcscale, Ns * 4},       {bias, Ns * 4},
+      {lora_act_in, Ms * Rs * 2}, {lora_up, Rs * Ns * 2}};
+  for (const auto& in : ins)
+    if (overlaps(out, out_bytes, in.p, in.n)) return GEMM_W4A4_EOVERLAP;
+
+  gemm_w4a4_plan_t pl;
+  if (mx_plan_impl(M, N, K, R, &pl) != GEMM_W4A4_OK) return GEMM_W4A4_EINVAL;
+  const int dev_rc = check_device();
+  if (dev_rc != GEMM_W4A4_OK) return dev_rc;
+
+  Params prm;
+  prm.act = act;
+  prm.ascales = ascales;
+  prm.wgt = wgt;
+  prm.wscales = wscales;
+  prm.wcscale = wcscale;
+  prm.bias = bias;
+  prm.lora_act_in = lora_act_in;
+  prm.lora_up = lora_up;
+  prm.out = out;
+  prm.M = M;
+  prm.N = N;
+  prm.K = K;
+  prm.R = R;
+  prm.tiles_m = pl.tiles_m;
+  prm.tiles_n = pl.tiles_n;
+
+  const MxVariant& v = kMxVariants[pl.variant];
+  const bool fast = K % 128 == 0 && M % 4 == 0 && N % 8 == 0 &&
+                    ((uintptr_t(ascales) | uintptr_t(wscales)) & 3u) == 0 &&
+                    (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
+  void* args[] = {&prm};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][fast ? 1 : 0]),
+                                       dim3(pl.grid), dim3(v.threads), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}
+
+}  // namespace w4a4
+
+using namespace w4a4;
+
+extern "C" int gemm_mxfp4(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                          const uint8_t* wscales, const float* wcscale, const float* bias,
+                          const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
+                          int M, int N, int K, int R, void* stream) {
+  return mx_launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
+                   stream, false);
+}
+
+extern "C" int gemm_mxfp4_f16(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                              const uint8_t* wscales, const float* wcscale, const float* bias,
+                              const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
+                              int M, int N, int K, int R, void* stream) {
+  return mx_launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
+                   stream, true);
+}
+
+extern "C" int gemm_mxfp4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan) {
+  if (!plan || !mx_sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
+  return mx_plan_impl(M, N, K, R, plan);
+}
+
+extern "C" int gemm_mxfp4_num_variants(void) { return kNumMxVariants; }
+
+extern "C" int gemm_mxfp4_variant_info(int variant, gemm_w4a4_plan_t* plan) {
+  if (!plan || variant < 0 || variant >= kNumMxVariants) return GEMM_W4A4_EINVAL;
+  mx_fill_static(kMxVariants[variant], variant, plan);
+  return GEMM_W4A4_OK;
+}

@@ -34,72 +34,15 @@
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "gemm_w4a4.h"
+#include "w4a4_common.hpp"
+#include "w4a4_epilogue.hpp"
+#include "w4a4_host.hpp"
 #include "w4a4_layout.hpp"
 
 namespace w4a4 {
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-struct Params {
-  const uint8_t* act;
-  const uint8_t* ascales;
-  const uint8_t* wgt;
-  const uint8_t* wscales;
-  const float* wcscale;
-  const float* bias;
-  const uint16_t* lora_act_in;
-  const uint16_t* lora_up;
-  uint16_t* out;
-  int M, N, K, R;
-  int tiles_m, tiles_n;
-};
-
-// 16-byte chunk c of a 64-byte row is stored at chunk position c ^ swz(row).
-// Without it rows r and r+2 (32 banks) or r and r+4 (64 banks) share banks
-// under the consumer's reads; this XOR spreads 8 (or 16) consecutive rows of
-// one chunk over distinct bank groups.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-
-// s_waitcnt vmcnt(VM) lgkmcnt(0), gfx9 encoding (vmcnt split over bits 3:0 and 15:14).
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-}
-
-// s_waitcnt vmcnt(VM) only (expcnt and lgkmcnt at their maxima: no wait).
-template <int VM>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
-}
-
-// Workgroup barrier without the memory fence __syncthreads() carries: the
-// fence would wait for every outstanding DMA (vmcnt(0)) and serialize the
-// ring. Each caller waits for exactly the DMA it needs first; the asm memory
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Direct-to-LDS copy: lane l of the wave writes BYTES bytes at lds_wave_base + l*BYTES.
-template <int BYTES>
-__device__ __forceinline__ void dma(const void* gsrc, void* lds_wave_base) {
-  static_assert(BYTES == 16 || BYTES == 4, "gfx950 DMA piece sizes used here");
-  const auto src = (const __attribute__((address_space(1))) void*)gsrc;
-  const auto dst = (__attribute__((address_space(3))) void*)lds_wave_base;
-  if constexpr (BYTES == 16) {
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-  } else {
-    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
-  }
-}
 
 // Eight E2M1 nibbles of one dword times the block scale (fp16 bits in the low
 // half of `scale`), as fp16. Which nibble lands in which of the eight slots is
@@ -124,23 +67,6 @@ __device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 b) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 1.0f, true))};
 }
 
-// One LoRA k-step: 8 ranks per lane of lora_up (rows n) and lora_act_in
-// (rows m) as raw 16-bit patterns, fp16 or bf16; both MFMAs have the K-loop's
-// 32x32 accumulator layout.
-template <bool F16>
-__device__ __forceinline__ f32x16 lora_mfma(u32x4 up, u32x4 act, f32x16 c) {
-  if constexpr (F16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, up), __builtin_bit_cast(f16x8, act),
-                                                  c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, up), __builtin_bit_cast(bf16x8, act),
-                                                   c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t bf16_pair(uint16_t lo, uint16_t hi) {
-  return uint32_t(lo) | (uint32_t(hi) << 16);
-}
-
 // Eight scale bytes of k-block kb (clamped to the last one) for rows
 // r0 .. r0+7 of a [KB][rows] tensor. `fast` (uniform over the workgroup) says
 // the whole tile lies inside `rows` and rows are 8-byte aligned; otherwise each
@@ -158,24 +84,6 @@ __device__ __forceinline__ u32x2 load_scales8(const uint8_t* sc, int kb, int KB,
     w[i >> 2] |= b << (8 * (i & 3));
   }
   return u32x2{w[0], w[1]};
-}
-
-// Tile order: workgroups are dealt round-robin to the 8 XCDs (workgroup b
-// runs on XCD b % 8), each with its own L2. Renumber so that each XCD gets a
-// contiguous run of tiles, and walk that run GROUP tile-rows at a time, so
-// the A rows and B columns one XCD reads concurrently stay in its L2.
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int kXcd = 8, kGroup = 4;
-  const int T = tiles_m * tiles_n;
-  const int per = T / kXcd, rem = T % kXcd;
-  const int x = b % kXcd, l = b / kXcd;
-  const int L = x < rem ? x * (per + 1) + l : rem * (per + 1) + (x - rem) * per + l;
-  const int span = kGroup * tiles_n;
-  const int first = (L / span) * kGroup;
-  const int gsz = min(tiles_m - first, kGroup);
-  const int in = L % span;
-  tm = first + in % gsz;
-  tn = in / gsz;
 }
 
 // Two flavours per tile shape. The fast one (GENERAL = false) needs packed
@@ -205,7 +113,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int M = p.M, N = p.N, K = p.K, R = p.R;
+  const int M = p.M, N = p.N, K = p.K;
   const int rowbytes = K >> 1;
   const int KB = K >> 4;                   // scale blocks along k
   const int nst = (K + C::BK - 1) / C::BK;
@@ -481,8 +389,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   // PAR = st & 1, fixed per call site of the two-way unrolled loop.
   auto iteration = [&]<int PAR>(int st) __attribute__((always_inline)) {
     const int st_scl = min(st + 2, last), st_dma = min(st + 3, last);
-#pragma unroll
-    for (int S = 0; S < 8; ++S) {
+    // k-step S: Sv is an int, or (general flavour) a std::integral_constant
+    auto kstep = [&](auto Sv) __attribute__((always_inline)) {
+      const int S = Sv;
       const Dec& cur = D[S & 1];
       Dec& nxt = D[(S + 1) & 1];
       const Chunk& Rn = (S + 1 >= 4 && S + 1 < 8) ? C1 : C0;
@@ -511,6 +420,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
           read_tile(st + 1, 0, slot - SLOT_RD0, C0);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    // The general flavour's branches keep the compiler from resolving the
+    // chunk and decode-buffer choices of a runtime k-step index, which then
+    // leaves those arrays in scratch memory; a compile-time index avoids it.
+    // The fast flavour schedules slightly better from the plain loop.
+    if constexpr (GENERAL) {
+      static_for<0, 8>([&]<int S>() __attribute__((always_inline)) { kstep(std::integral_constant<int, S>{}); });
+    } else {
+#pragma unroll
+      for (int S = 0; S < 8; ++S) kstep(S);
     }
   };
   int st = 0;
@@ -521,219 +440,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   if (st < nst) iteration.template operator()<0>(st);
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
-  // ---------------- epilogue: *wcscale + bias, + LoRA (same accumulators), bf16 store
-  // The first of this lane's four consecutive output columns in (tile j, group q).
-  const int ncol0 = n0 + wn * C::TN + 4 * g;          // + 32j + 8q
-  const bool n_inside = n0 + C::BN <= N;
-
-  // ---- LoRA-up operands are staged through LDS (the ring is free once the
-  // K-loop is done) in chunks of RC ranks = two MFMA k-steps:
-  //   LA  lora_act_in rows m0.., [BM][RC] bf16, row-major
-  //   LU  lora_up columns n0.., transposed to [BN][RC] bf16
-  // so each MFMA operand (8 consecutive ranks of one row) is one 16-byte LDS
-  // read. Rows are LR_STRIDE bytes apart (16 bytes of padding), which puts the
-  // 16-byte reads of 16 consecutive rows on distinct banks. Ranks past R (and
-  // rows past M, columns past N, read clamped) are stored as zero / clamped
-  // copies: zero ranks add nothing, clamped rows only reach discarded outputs.
-  constexpr int RC = 32;
-  constexpr int LR_STRIDE = RC * 2 + 16;
-  constexpr int LA_OFF = 0, LU_OFF = C::BM * LR_STRIDE;
-  static_assert(LU_OFF + C::BN * LR_STRIDE <= C::LDS_BYTES, "LoRA chunk must fit in the ring");
-  // LA: one 16-byte piece = 8 ranks of one row; pieces q = u*THREADS + tid
-  constexpr int LA_PIECES = C::BM * RC / 8;
-  constexpr int LA_PER = (LA_PIECES + C::THREADS - 1) / C::THREADS;
-  // LU: one task = 4 ranks x 8 columns (four 16-byte row pieces), written back
-  // as eight 8-byte column pieces; ranks vary fastest across lanes so that 8
-  // neighbouring lanes fill one 64-byte LDS row
-  constexpr int LU_TASKS = (RC / 4) * (C::BN / 8);
-  static_assert(LU_TASKS <= C::THREADS, "one LoRA-up task per thread");
-  const bool lu_task = tid < LU_TASKS;
-  const int lu_r4 = (tid % (RC / 4)) * 4;
-  const int lu_n8 = (tid / (RC / 4)) * 8;
-  u32x4 la_reg[LA_PER], lu_reg[4];
-
-  auto lora_load = [&](int rc0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < LA_PER; ++u) {
-      const int q = min(u * C::THREADS + tid, LA_PIECES - 1);
-      const int row = min(m0 + q / (RC / 8), M - 1);
-      const int r = rc0 + (q % (RC / 8)) * 8;
-      const uint16_t* src = p.lora_act_in + uint32_t(row) * uint32_t(R);
-      if constexpr (!GENERAL) {
-        // R % 8 == 0 and r % 8 == 0: the eight ranks are all in range or all
-        // out; out-of-range pieces are zeroed when stored
-        la_reg[u] = *reinterpret_cast<const u32x4*>(src + min(r, R - 8));
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint16_t x0 = src[min(r + 2 * t, R - 1)], x1 = src[min(r + 2 * t + 1, R - 1)];
-          w[t] = bf16_pair(r + 2 * t < R ? x0 : uint16_t(0), r + 2 * t + 1 < R ? x1 : uint16_t(0));
-        }
-        la_reg[u] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = rc0 + lu_r4 + e;
-      const uint16_t* src = p.lora_up + uint32_t(min(r, R - 1)) * uint32_t(N);
-      if constexpr (!GENERAL) {
-        // N % 8 == 0: the eight columns are all inside N or all past it; a
-        // piece past N re-reads the last one and feeds only discarded outputs
-        lu_reg[e] = *reinterpret_cast<const u32x4*>(src + min(n0 + lu_n8, N - 8));
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint16_t x0 = src[min(n0 + lu_n8 + 2 * t, N - 1)];
-          const uint16_t x1 = src[min(n0 + lu_n8 + 2 * t + 1, N - 1)];
-          w[t] = r < R ? bf16_pair(x0, x1) : 0u;
-        }
-        lu_reg[e] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-  };
-  // The fast flavour zeroes ranks past R here rather than at the load, so a
-  // prefetch stays in flight until its chunk is stored.
-  auto lora_store = [&](int rc0) __attribute__((always_inline)) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < LA_PER; ++u) {
-      const int q = u * C::THREADS + tid;
-      const bool keep = GENERAL || rc0 + (q % (RC / 8)) * 8 < R;
-      if (LA_PIECES % C::THREADS == 0 || q < LA_PIECES)
-        *reinterpret_cast<u32x4*>(smem + LA_OFF + (q / (RC / 8)) * LR_STRIDE + (q % (RC / 8)) * 16) =
-            keep ? la_reg[u] : zero;
-    }
-    if constexpr (!GENERAL) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (rc0 + lu_r4 + e >= R) lu_reg[e] = zero;
-    }
-    if (lu_task) {
-      // column c of the four row pieces -> LU[n8 + c][r4 .. r4+3]
-      uint8_t* dst = smem + LU_OFF + lu_n8 * LR_STRIDE + lu_r4 * 2;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const u32x2 lo = {__builtin_amdgcn_perm(lu_reg[1][h], lu_reg[0][h], 0x05040100u),
-                          __builtin_amdgcn_perm(lu_reg[3][h], lu_reg[2][h], 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(lu_reg[1][h], lu_reg[0][h], 0x07060302u),
-                          __builtin_amdgcn_perm(lu_reg[3][h], lu_reg[2][h], 0x07060302u)};
-        *reinterpret_cast<u32x2*>(dst + (2 * h) * LR_STRIDE) = lo;
-        *reinterpret_cast<u32x2*>(dst + (2 * h + 1) * LR_STRIDE) = hi;
-      }
-    }
-  };
-
-  const int nchunks = (R + RC - 1) / RC;
-  if (nchunks > 0) lora_load(0);
-
-  // Per-column factor at columns ncol0 + 32j + 8q + (0..3), clamped at the N edge.
-  auto col4 = [&](const float* v, int j, int q) __attribute__((always_inline)) {
-    const int n = ncol0 + 32 * j + 8 * q;
-    if (n_inside) return *reinterpret_cast<const f32x4*>(v + n);
-    return f32x4{v[min(n, N - 1)], v[min(n + 1, N - 1)], v[min(n + 2, N - 1)], v[min(n + 3, N - 1)]};
-  };
-
-  // S * wcscale[n] + bias[n] (the LoRA terms are added on top by the MFMAs below)
-#pragma unroll
-  for (int j = 0; j < C::NI; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 w = col4(p.wcscale, j, q);
-      const f32x4 b = col4(p.bias, j, q);
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[j][i][4 * q + t] = __builtin_fmaf(acc[j][i][4 * q + t], w[t], b[t]);
-    }
-  }
-
-  // LoRA-up: per chunk, store the staged operands, prefetch the next chunk,
-  // then two k-steps of v_mfma_f32_32x32x16_bf16 (same accumulator layout as
-  // the K-loop: lora_up as the A operand, rows n; lora_act_in as B, rows m).
-  // Lane (l32, g) feeds ranks 8g .. 8g+7 of each 16-rank k-step.
-  const uint32_t la_rd = LA_OFF + (wm * C::TM + l32) * LR_STRIDE + g * 16;
-  const uint32_t lu_rd = LU_OFF + (wn * C::TN + l32) * LR_STRIDE + g * 16;
-  for (int c = 0; c < nchunks; ++c) {
-    wait_vm_lgkm0<0>();
-    wg_barrier();   // every wave is done with the ring / the previous chunk
-    lora_store(c * RC);
-    if (c + 1 < nchunks) lora_load((c + 1) * RC);
-    wait_vm_lgkm0<63>();
-    wg_barrier();
-#pragma unroll
-    for (int s = 0; s < RC / 16; ++s) {
-      if (s > 0 && c * RC + 16 * s >= R) break;   // an all-zero k-step
-      u32x4 la[C::MI], lu[C::NI];
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-        la[i] = *reinterpret_cast<const u32x4*>(smem + la_rd + i * 32 * LR_STRIDE + s * 32);
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-        lu[j] = *reinterpret_cast<const u32x4*>(smem + lu_rd + j * 32 * LR_STRIDE + s * 32);
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i) acc[j][i] = lora_mfma<F16>(lu[j], la[i], acc[j][i]);
-    }
-  }
-
-  // bf16 (round to nearest even), staged through LDS: the tile is row-major
-  // with a padded row stride (OUT_STRIDE bytes) so the 8-byte writes of 32
-  // rows at once spread over the banks. The barrier makes sure every wave is
-  // done with the ring (K-loop) and with the LoRA operands.
-  wait_vm_lgkm0<0>();
-  wg_barrier();
-  constexpr int OUT_STRIDE = C::BN * 2 + 16;
-  static_assert(C::BM * OUT_STRIDE <= C::LDS_BYTES, "output tile must fit in the ring");
-#pragma unroll
-  for (int j = 0; j < C::NI; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) {
-        const int ml = wm * C::TM + 32 * i + l32;
-        const int nl = wn * C::TN + 32 * j + 8 * q + 4 * g;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-        if constexpr (F16) {
-          const f16x4 v = {_Float16(acc[j][i][4 * q]), _Float16(acc[j][i][4 * q + 1]),
-                           _Float16(acc[j][i][4 * q + 2]), _Float16(acc[j][i][4 * q + 3])};
-          *reinterpret_cast<f16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
-        } else {
-          const bf16x4 v = {__bf16(acc[j][i][4 * q]), __bf16(acc[j][i][4 * q + 1]),
-                            __bf16(acc[j][i][4 * q + 2]), __bf16(acc[j][i][4 * q + 3])};
-          *reinterpret_cast<bf16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
-        }
-      }
-    }
-  }
-  wait_vm_lgkm0<63>();
-  wg_barrier();
-
-  // LDS -> HBM in 16-byte pieces of whole output rows (8 columns each).
-  constexpr int PIECES_PER_ROW = C::BN / 8;
-  constexpr int PIECES = C::BM * PIECES_PER_ROW;
-  static_assert(PIECES % C::THREADS == 0, "whole store rounds");
-  const bool vec_out = n_inside && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0;
-#pragma unroll
-  for (int u = 0; u < PIECES / C::THREADS; ++u) {
-    const int piece = u * C::THREADS + tid;
-    const int rl = piece / PIECES_PER_ROW, cl = (piece % PIECES_PER_ROW) * 8;
-    const int row = m0 + rl;
-    if (row >= M) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
-    uint16_t* dst = p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl);
-    if (vec_out) {
-      *reinterpret_cast<u32x4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n0 + cl + e < N) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
-    }
-  }
+  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0);
 }
 
 // ------------------------------------------------------------------ host side
@@ -820,28 +527,6 @@ static int plan_impl(int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
   pl->k_stages = (K + x.block_k - 1) / x.block_k;
   pl->lora_steps = (R + 15) / 16;
   return GEMM_W4A4_OK;
-}
-
-static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || na == 0 || nb == 0) return false;
-  const uintptr_t x = uintptr_t(a), y = uintptr_t(b);
-  return x < y + nb && y < x + na;
-}
-
-static std::atomic<int> g_arch_ok[64];   // 0 unknown, 1 gfx950, 2 other
-
-static int check_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return GEMM_W4A4_EDEVICE;
-  if (dev < 0 || dev >= 64) return GEMM_W4A4_EDEVICE;
-  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_W4A4_EDEVICE;
-    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    g_arch_ok[dev].store(st, std::memory_order_relaxed);
-  }
-  return st == 1 ? GEMM_W4A4_OK : GEMM_W4A4_EDEVICE;
 }
 
 }  // namespace w4a4

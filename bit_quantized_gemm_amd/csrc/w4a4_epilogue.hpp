@@ -1,0 +1,243 @@
+// w4a4_epilogue.hpp — the fused epilogue shared by the NVFP4 and MXFP4 kernels:
+// acc * wcscale[n] + bias[n] (the SVDQuant W4A4 on Blackwell page, section
+// 6.6), then the rank-R LoRA-up product (section 2's formula adds it after the
+// wcscale product; section 6.3 runs it on the same accumulators) as further
+// 32x32 MFMA k-steps, then the 16-bit store. Both kernels hold their
+// accumulators in the same layout: acc[j][i] is the 32x32 tile of output
+// rows m = 32i + l32 (one per lane) and columns n = 32j + 8q + 4g + t in
+// element 4q + t, for wave (wm, wn) of the workgroup's BM x BN tile.
+#pragma once
+
+#include "w4a4_common.hpp"
+
+namespace w4a4 {
+
+// GENERAL: LoRA operands element by element (any R, N, alignment) rather than
+// in 16-byte pieces; F16: LoRA operands and output in binary16, else bfloat16.
+// The LDS ring of C::LDS_BYTES is dead when this runs and is reused.
+template <class C, bool GENERAL, bool F16>
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Params& p, uint8_t* smem,
+                                         const int tid, const int m0, const int n0) {
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int M = p.M, N = p.N, R = p.R;
+
+  // ---------------- epilogue: *wcscale + bias, + LoRA (same accumulators), bf16 store
+  // The first of this lane's four consecutive output columns in (tile j, group q).
+  const int ncol0 = n0 + wn * C::TN + 4 * g;          // + 32j + 8q
+  const bool n_inside = n0 + C::BN <= N;
+
+  // ---- LoRA-up operands are staged through LDS (the ring is free once the
+  // K-loop is done) in chunks of RC ranks = two MFMA k-steps:
+  //   LA  lora_act_in rows m0.., [BM][RC] bf16, row-major
+  //   LU  lora_up columns n0.., transposed to [BN][RC] bf16
+  // so each MFMA operand (8 consecutive ranks of one row) is one 16-byte LDS
+  // read. Rows are LR_STRIDE bytes apart (16 bytes of padding), which puts the
+  // 16-byte reads of 16 consecutive rows on distinct banks. Ranks past R (and
+  // rows past M, columns past N, read clamped) are stored as zero / clamped
+  // copies: zero ranks add nothing, clamped rows only reach discarded outputs.
+  constexpr int RC = 32;
+  constexpr int LR_STRIDE = RC * 2 + 16;
+  constexpr int LA_OFF = 0, LU_OFF = C::BM * LR_STRIDE;
+  static_assert(LU_OFF + C::BN * LR_STRIDE <= C::LDS_BYTES, "LoRA chunk must fit in the ring");
+  // LA: one 16-byte piece = 8 ranks of one row; pieces q = u*THREADS + tid
+  constexpr int LA_PIECES = C::BM * RC / 8;
+  constexpr int LA_PER = (LA_PIECES + C::THREADS - 1) / C::THREADS;
+  // LU: one task = 4 ranks x 8 columns (four 16-byte row pieces), written back
+  // as eight 8-byte column pieces; ranks vary fastest across lanes so that 8
+  // neighbouring lanes fill one 64-byte LDS row
+  constexpr int LU_TASKS = (RC / 4) * (C::BN / 8);
+  static_assert(LU_TASKS <= C::THREADS, "one LoRA-up task per thread");
+  const bool lu_task = tid < LU_TASKS;
+  const int lu_r4 = (tid % (RC / 4)) * 4;
+  const int lu_n8 = (tid / (RC / 4)) * 8;
+  u32x4 la_reg[LA_PER], lu_reg[4];
+
+  auto lora_load = [&](int rc0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LA_PER; ++u) {
+      const int q = min(u * C::THREADS + tid, LA_PIECES - 1);
+      const int row = min(m0 + q / (RC / 8), M - 1);
+      const int r = rc0 + (q % (RC / 8)) * 8;
+      const uint16_t* src = p.lora_act_in + uint32_t(row) * uint32_t(R);
+      if constexpr (!GENERAL) {
+        // R % 8 == 0 and r % 8 == 0: the eight ranks are all in range or all
+        // out; out-of-range pieces are zeroed when stored
+        la_reg[u] = *reinterpret_cast<const u32x4*>(src + min(r, R - 8));
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint16_t x0 = src[min(r + 2 * t, R - 1)], x1 = src[min(r + 2 * t + 1, R - 1)];
+          w[t] = bf16_pair(r + 2 * t < R ? x0 : uint16_t(0), r + 2 * t + 1 < R ? x1 : uint16_t(0));
+        }
+        la_reg[u] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rc0 + lu_r4 + e;
+      const uint16_t* src = p.lora_up + uint32_t(min(r, R - 1)) * uint32_t(N);
+      if constexpr (!GENERAL) {
+        // N % 8 == 0: the eight columns are all inside N or all past it; a
+        // piece past N re-reads the last one and feeds only discarded outputs
+        lu_reg[e] = *reinterpret_cast<const u32x4*>(src + min(n0 + lu_n8, N - 8));
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint16_t x0 = src[min(n0 + lu_n8 + 2 * t, N - 1)];
+          const uint16_t x1 = src[min(n0 + lu_n8 + 2 * t + 1, N - 1)];
+          w[t] = r < R ? bf16_pair(x0, x1) : 0u;
+        }
+        lu_reg[e] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+  };
+  // The fast flavour zeroes ranks past R here rather than at the load, so a
+  // prefetch stays in flight until its chunk is stored.
+  auto lora_store = [&](int rc0) __attribute__((always_inline)) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < LA_PER; ++u) {
+      const int q = u * C::THREADS + tid;
+      const bool keep = GENERAL || rc0 + (q % (RC / 8)) * 8 < R;
+      if (LA_PIECES % C::THREADS == 0 || q < LA_PIECES)
+        *reinterpret_cast<u32x4*>(smem + LA_OFF + (q / (RC / 8)) * LR_STRIDE + (q % (RC / 8)) * 16) =
+            keep ? la_reg[u] : zero;
+    }
+    if constexpr (!GENERAL) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (rc0 + lu_r4 + e >= R) lu_reg[e] = zero;
+    }
+    if (lu_task) {
+      // column c of the four row pieces -> LU[n8 + c][r4 .. r4+3]
+      uint8_t* dst = smem + LU_OFF + lu_n8 * LR_STRIDE + lu_r4 * 2;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const u32x2 lo = {__builtin_amdgcn_perm(lu_reg[1][h], lu_reg[0][h], 0x05040100u),
+                          __builtin_amdgcn_perm(lu_reg[3][h], lu_reg[2][h], 0x05040100u)};
+        const u32x2 hi = {__builtin_amdgcn_perm(lu_reg[1][h], lu_reg[0][h], 0x07060302u),
+                          __builtin_amdgcn_perm(lu_reg[3][h], lu_reg[2][h], 0x07060302u)};
+        *reinterpret_cast<u32x2*>(dst + (2 * h) * LR_STRIDE) = lo;
+        *reinterpret_cast<u32x2*>(dst + (2 * h + 1) * LR_STRIDE) = hi;
+      }
+    }
+  };
+
+  const int nchunks = (R + RC - 1) / RC;
+  if (nchunks > 0) lora_load(0);
+
+  // Per-column factor at columns ncol0 + 32j + 8q + (0..3), clamped at the N edge.
+  auto col4 = [&](const float* v, int j, int q) __attribute__((always_inline)) {
+    const int n = ncol0 + 32 * j + 8 * q;
+    if (n_inside) return *reinterpret_cast<const f32x4*>(v + n);
+    return f32x4{v[min(n, N - 1)], v[min(n + 1, N - 1)], v[min(n + 2, N - 1)], v[min(n + 3, N - 1)]};
+  };
+
+  // S * wcscale[n] + bias[n] (the LoRA terms are added on top by the MFMAs below)
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w = col4(p.wcscale, j, q);
+      const f32x4 b = col4(p.bias, j, q);
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[j][i][4 * q + t] = __builtin_fmaf(acc[j][i][4 * q + t], w[t], b[t]);
+    }
+  }
+
+  // LoRA-up: per chunk, store the staged operands, prefetch the next chunk,
+  // then two k-steps of v_mfma_f32_32x32x16_bf16 (same accumulator layout as
+  // the K-loop: lora_up as the A operand, rows n; lora_act_in as B, rows m).
+  // Lane (l32, g) feeds ranks 8g .. 8g+7 of each 16-rank k-step.
+  const uint32_t la_rd = LA_OFF + (wm * C::TM + l32) * LR_STRIDE + g * 16;
+  const uint32_t lu_rd = LU_OFF + (wn * C::TN + l32) * LR_STRIDE + g * 16;
+  for (int c = 0; c < nchunks; ++c) {
+    wait_vm_lgkm0<0>();
+    wg_barrier();   // every wave is done with the ring / the previous chunk
+    lora_store(c * RC);
+    if (c + 1 < nchunks) lora_load((c + 1) * RC);
+    wait_vm_lgkm0<63>();
+    wg_barrier();
+#pragma unroll
+    for (int s = 0; s < RC / 16; ++s) {
+      if (s > 0 && c * RC + 16 * s >= R) break;   // an all-zero k-step
+      u32x4 la[C::MI], lu[C::NI];
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+        la[i] = *reinterpret_cast<const u32x4*>(smem + la_rd + i * 32 * LR_STRIDE + s * 32);
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+        lu[j] = *reinterpret_cast<const u32x4*>(smem + lu_rd + j * 32 * LR_STRIDE + s * 32);
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) acc[j][i] = lora_mfma<F16>(lu[j], la[i], acc[j][i]);
+    }
+  }
+
+  // bf16 (round to nearest even), staged through LDS: the tile is row-major
+  // with a padded row stride (OUT_STRIDE bytes) so the 8-byte writes of 32
+  // rows at once spread over the banks. The barrier makes sure every wave is
+  // done with the ring (K-loop) and with the LoRA operands.
+  wait_vm_lgkm0<0>();
+  wg_barrier();
+  constexpr int OUT_STRIDE = C::BN * 2 + 16;
+  static_assert(C::BM * OUT_STRIDE <= C::LDS_BYTES, "output tile must fit in the ring");
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int ml = wm * C::TM + 32 * i + l32;
+        const int nl = wn * C::TN + 32 * j + 8 * q + 4 * g;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        if constexpr (F16) {
+          const f16x4 v = {_Float16(acc[j][i][4 * q]), _Float16(acc[j][i][4 * q + 1]),
+                           _Float16(acc[j][i][4 * q + 2]), _Float16(acc[j][i][4 * q + 3])};
+          *reinterpret_cast<f16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
+        } else {
+          const bf16x4 v = {__bf16(acc[j][i][4 * q]), __bf16(acc[j][i][4 * q + 1]),
+                            __bf16(acc[j][i][4 * q + 2]), __bf16(acc[j][i][4 * q + 3])};
+          *reinterpret_cast<bf16x4*>(smem + ml * OUT_STRIDE + nl * 2) = v;
+        }
+      }
+    }
+  }
+  wait_vm_lgkm0<63>();
+  wg_barrier();
+
+  // LDS -> HBM in 16-byte pieces of whole output rows (8 columns each).
+  constexpr int PIECES_PER_ROW = C::BN / 8;
+  constexpr int PIECES = C::BM * PIECES_PER_ROW;
+  static_assert(PIECES % C::THREADS == 0, "whole store rounds");
+  const bool vec_out = n_inside && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0;
+#pragma unroll
+  for (int u = 0; u < PIECES / C::THREADS; ++u) {
+    const int piece = u * C::THREADS + tid;
+    const int rl = piece / PIECES_PER_ROW, cl = (piece % PIECES_PER_ROW) * 8;
+    const int row = m0 + rl;
+    if (row >= M) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
+    uint16_t* dst = p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl);
+    if (vec_out) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n0 + cl + e < N) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+}  // namespace w4a4

@@ -61,4 +61,44 @@ struct TileCfg {
 using Cfg256x192 = TileCfg<256, 192, 2, 2, 4, 1>;
 using Cfg128x128 = TileCfg<128, 128, 2, 2, 4, 2>;
 
+// MXFP4 kernel: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN), 32x32x64
+// scaled FP4 MFMAs. A stage covers BK = 128 values of k = 2 MFMA k-steps = 4
+// UE8M0 scale blocks of 32. One ring stage holds, in this order:
+//   A  packed act  [BM rows][64 bytes]  16-byte chunks XOR-swizzled by row
+//   B  packed wgt  [BN rows][64 bytes]  same swizzle
+//   S  raw UE8M0 scale bytes: act [4][BM] then wgt [4][BN] ([k-block][row],
+//      the global layout's order), padded to whole 4-byte DMA rounds
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_>
+struct MxTileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int STAGES = STAGES_, OCC = OCC_;
+  static constexpr int BK = 128;
+  static constexpr int THREADS = WM * WN * kWave;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int MI = TM / 32, NI = TN / 32;
+  static constexpr int ROW_BYTES = BK / 2;
+  static constexpr int KBLK = BK / 32;            // scale blocks per stage
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = A_OFF + BM * ROW_BYTES;
+  static constexpr int SA_OFF = B_OFF + BN * ROW_BYTES;
+  static constexpr int SB_OFF = SA_OFF + KBLK * BM;
+  static constexpr int SCALE_BYTES = KBLK * (BM + BN);
+  static constexpr int SCALE_ROUNDS = (SCALE_BYTES + THREADS * 4 - 1) / (THREADS * 4);
+  static constexpr int PACKED_BYTES = SA_OFF;
+  static constexpr int STAGE_BYTES = SA_OFF + SCALE_ROUNDS * THREADS * 4;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+  static_assert(BM % 4 == 0 && BN % 4 == 0, "4-row scale DMA pieces");
+  static_assert(PACKED_BYTES % (THREADS * 16) == 0 && B_OFF % (THREADS * 16) == 0,
+                "whole 16-byte DMA rounds per operand");
+  static_assert(STAGES == 4, "the pipeline is written for a 4-deep ring");
+  static_assert(LDS_BYTES * OCC <= kLdsLimit, "LDS budget exceeded");
+};
+
+// 256 x 192, not 256 x 256: 256 accumulators fill the accumulator file and
+// the epilogue then spills; 192 leave it room (as in the NVFP4 kernel).
+using MxCfg256x192 = MxTileCfg<256, 192, 2, 2, 4, 1>;
+using MxCfg128x128 = MxTileCfg<128, 128, 2, 2, 4, 2>;
+
 }  // namespace w4a4

@@ -1,4 +1,4 @@
-"""Summaries of rocprofv3 runs of the W4A4 kernel, as short text files.
+"""Summaries of rocprofv3 runs of the W4A4 kernels, as short text files.
 
     python -m bit_quantized_gemm_amd.profsum trace DIR --workload qkv --command "..."
     python -m bit_quantized_gemm_amd.profsum traffic FETCH_DIR WRITE_DIR --copy-mib 256 \
@@ -10,7 +10,8 @@
 that also made one device copy of COPY_MIB MiB (bench.py --copy-probe-mb): each
 counter is scaled by (true bytes of that copy) / (what the counter read for
 it), and the GEMM's HBM bytes per launch are the scaled median over its
-dispatches. `counters` tabulates the SQ/GRBM counters of one `--pmc` run.
+dispatches. `counters` tabulates the SQ/GRBM counters of one `--pmc` run. `--fmt mxfp4`
+selects the MXFP4 kernel (default: the NVFP4 one).
 The file carries the hash of the kernel sources it was taken on, so a reader
 (bench.py) can tell whether it still describes the current kernel.
 """
@@ -26,15 +27,20 @@ import sys
 from collections import defaultdict
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(_HERE, "csrc", f) for f in ("gemm_w4a4.hip", "w4a4_layout.hpp")]
-GEMM_TAG = "gemm_w4a4_kernel"
+_SHARED = ("w4a4_common.hpp", "w4a4_epilogue.hpp", "w4a4_layout.hpp")
+# per format: (kernel name tag, summary file prefix, the sources the kernel is built from)
+KERNELS = {
+    "nvfp4": ("gemm_w4a4_kernel", "gemm_w4a4", ("gemm_w4a4.hip",) + _SHARED),
+    "mxfp4": ("gemm_mxfp4_kernel", "gemm_mxfp4", ("gemm_mxfp4.hip",) + _SHARED),
+}
 COPY_TAG = "copyBuffer"
 
 
-def kernel_source_hash() -> str:
-    """First 16 hex digits of the sha256 over the kernel sources."""
+def kernel_source_hash(fmt: str = "nvfp4") -> str:
+    """First 16 hex digits of the sha256 over one kernel's sources."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for f in KERNELS[fmt][2]:
+        p = os.path.join(_HERE, "csrc", f)
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -59,13 +65,14 @@ def _per_dispatch(directory: str):
 
 
 def trace(args) -> str:
+    tag, name, _ = KERNELS[args.fmt]
     stats = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_stats.csv")))))
     rows = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_trace.csv")))))
-    g = [r for r in rows if GEMM_TAG in r["Kernel_Name"]]
-    lines = [f"# gemm_w4a4 kernel trace, {args.workload} workload", "",
+    g = [r for r in rows if tag in r["Kernel_Name"]]
+    lines = [f"# {name} kernel trace, {args.workload} workload", "",
              "Command (repository root, one MI355X, library built in-tree):", "",
              f"    {args.command}", "",
-             f"Kernel source sha256[:16]: {kernel_source_hash()}", "",
+             f"Kernel source sha256[:16]: {kernel_source_hash(args.fmt)}", "",
              "| Kernel | Calls | Average ns | Min ns | Max ns | StdDev ns |",
              "|---|---|---|---|---|---|"]
     for s in stats:
@@ -85,6 +92,7 @@ def trace(args) -> str:
 
 
 def traffic(args) -> str:
+    tag, name, _ = KERNELS[args.fmt]
     fetch, write = _per_dispatch(args.fetch_dir), _per_dispatch(args.write_dir)
     true_kib = args.copy_mib * 1024.0
 
@@ -93,7 +101,7 @@ def traffic(args) -> str:
         if not copies:
             raise SystemExit(f"no copy dispatch found for {counter}")
         probe = max(copies)   # the probe is by far the largest copy
-        gemm = [v[counter] for n, v in runs.values() if GEMM_TAG in n]
+        gemm = [v[counter] for n, v in runs.values() if tag in n]
         if not gemm:
             raise SystemExit(f"no gemm dispatch found for {counter}")
         return probe, true_kib / probe, statistics.median(gemm), len(gemm)
@@ -101,7 +109,7 @@ def traffic(args) -> str:
     fp, ff, fg, fn = scale(fetch, "FETCH_SIZE")
     wp, wf, wg, wn = scale(write, "WRITE_SIZE")
     fetch_b, write_b = fg * ff * 1024.0, wg * wf * 1024.0
-    lines = [f"# gemm_w4a4 HBM traffic per launch, {args.workload} workload",
+    lines = [f"# {name} HBM traffic per launch, {args.workload} workload",
              "# Commands (repository root, one MI355X, library built in-tree):",
              f"#   {args.command_fetch}", f"#   {args.command_write}",
              f"# copy probe: one device copy of {args.copy_mib} MiB = {true_kib:.0f} KiB read and written",
@@ -109,7 +117,7 @@ def traffic(args) -> str:
              f"gemm median over {fn} dispatches {fg:.1f} KiB",
              f"# WRITE_SIZE read {wp:.1f} KiB for the probe -> scale {wf:.4f}; "
              f"gemm median over {wn} dispatches {wg:.1f} KiB",
-             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"kernel_source_sha256: {kernel_source_hash(args.fmt)}",
              f"fetch_bytes_per_launch: {fetch_b:.0f}",
              f"write_bytes_per_launch: {write_b:.0f}",
              f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}"]
@@ -117,13 +125,14 @@ def traffic(args) -> str:
 
 
 def counters(args) -> str:
+    tag, name, _ = KERNELS[args.fmt]
     runs = _per_dispatch(args.dir)
-    g = [v for n, v in runs.values() if GEMM_TAG in n]
+    g = [v for n, v in runs.values() if tag in n]
     names = sorted(g[0]) if g else []
-    lines = [f"# gemm_w4a4 SQ/GRBM counters, {args.workload} workload", "",
+    lines = [f"# {name} SQ/GRBM counters, {args.workload} workload", "",
              "Command (repository root, one MI355X, library built in-tree):", "",
              f"    {args.command}", "",
-             f"Kernel source sha256[:16]: {kernel_source_hash()}", "",
+             f"Kernel source sha256[:16]: {kernel_source_hash(args.fmt)}", "",
              f"Median over {len(g)} dispatches (values summed over the device):", "",
              "| Counter | Value |", "|---|---|"]
     for c in names:
@@ -149,6 +158,8 @@ def main(argv=None) -> int:
     c.add_argument("dir")
     c.add_argument("--workload", required=True)
     c.add_argument("--command", required=True)
+    for p in (t, f, c):
+        p.add_argument("--fmt", default="nvfp4", choices=sorted(KERNELS))
     a = ap.parse_args(argv)
     sys.stdout.write({"trace": trace, "traffic": traffic, "counters": counters}[a.what](a))
     return 0

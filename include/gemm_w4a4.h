@@ -94,6 +94,29 @@ int gemm_w4a4_f16(const uint8_t* act, const uint8_t* ascales,
                   uint16_t* out, int M, int N, int K, int R, void* stream);
 
 /*
+ * gemm_mxfp4 / gemm_mxfp4_f16 — the same operator with MXFP4 operands: E2M1
+ * codes as above, but one UE8M0 scale per 32 consecutive k (value
+ * 2^(b - 127), 0xFF = NaN; the DeepGEMM FP4 indexer page, "Step 0", pairs
+ * E2M1 data with this block scale, applied by the matrix unit itself):
+ *   ascales      uint8   [K/32, M]  UE8M0 bytes; scale of (m,k) is ascales[k/32][m]
+ *   wscales      uint8   [K/32, N]
+ * K >= 32 with K % 32 == 0; everything else (layouts, LoRA, affine, output
+ * type bf16 or binary16, alignments, return codes) is gemm_w4a4's /
+ * gemm_w4a4_f16's. No decode happens on the GPU: gfx950's scaled FP4 MFMA
+ * consumes the packed bytes and the scale bytes as they are.
+ */
+int gemm_mxfp4(const uint8_t* act, const uint8_t* ascales,
+               const uint8_t* wgt, const uint8_t* wscales,
+               const float* wcscale, const float* bias,
+               const uint16_t* lora_act_in, const uint16_t* lora_up,
+               uint16_t* out, int M, int N, int K, int R, void* stream);
+int gemm_mxfp4_f16(const uint8_t* act, const uint8_t* ascales,
+                   const uint8_t* wgt, const uint8_t* wscales,
+                   const float* wcscale, const float* bias,
+                   const uint16_t* lora_act_in, const uint16_t* lora_up,
+                   uint16_t* out, int M, int N, int K, int R, void* stream);
+
+/*
  * Launch plan chosen by the LDS/register budget solver for one problem size.
  * Filled by gemm_w4a4_plan; pure host arithmetic (no HIP call), so it also
  * runs on a machine without a GPU.
@@ -126,6 +149,11 @@ int gemm_w4a4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan);
  * unknown index. Used to check the solver against the compiled code objects. */
 int gemm_w4a4_num_variants(void);
 int gemm_w4a4_variant_info(int variant, gemm_w4a4_plan_t* plan);
+
+/* The same three for the MXFP4 kernels (K % 32 == 0). */
+int gemm_mxfp4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan);
+int gemm_mxfp4_num_variants(void);
+int gemm_mxfp4_variant_info(int variant, gemm_w4a4_plan_t* plan);
 
 /* Static string for a return code (never NULL). */
 const char* gemm_w4a4_strerror(int code);

@@ -25,7 +25,7 @@ def _declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gemm_w4a4\w*)\s*\(",
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gemm_(?:w4a4|mxfp4)\w*)\s*\(",
                              text, flags=re.M):
             names.add(m.group(1))
     return sorted(names)
@@ -34,7 +34,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _native.load()
     names = _declared_functions()
-    assert "gemm_w4a4" in names and len(names) >= 5
+    assert {"gemm_w4a4", "gemm_w4a4_f16", "gemm_mxfp4", "gemm_mxfp4_f16"} <= set(names)
+    assert len(names) >= 11
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", w4.library_path()],
@@ -43,7 +44,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
-ENTRIES = {"bf16": w4.gemm_w4a4_raw, "f16": w4.gemm_w4a4_f16_raw}
+ENTRIES = {"bf16": w4.gemm_w4a4_raw, "f16": w4.gemm_w4a4_f16_raw,
+           "mx_bf16": w4.gemm_mxfp4_raw, "mx_f16": w4.gemm_mxfp4_f16_raw}
 
 
 def _call(entry="bf16", **over):
@@ -76,6 +78,19 @@ def test_invalid_arguments(over, entry):
 @pytest.mark.parametrize("entry", sorted(ENTRIES))
 def test_misaligned(over, entry):
     assert _call(entry, **over) == w4.EALIGN
+
+
+@pytest.mark.parametrize("K", [48, 80, 16])
+@pytest.mark.parametrize("entry", ["mx_bf16", "mx_f16"])
+def test_mxfp4_needs_whole_scale_blocks(K, entry):
+    # the MXFP4 block is 32 values of k: a K that is a multiple of 16 only is refused
+    assert _call(entry, K=K) == w4.EINVAL
+
+
+@pytest.mark.parametrize("entry", sorted(ENTRIES))
+def test_null_lora_allowed_without_rank_all_entries(entry):
+    rc = _call(entry, R=0, lora_act_in=0, lora_up=0)
+    assert rc in (w4.EDEVICE, w4.ELAUNCH, w4.OK)
 
 
 def test_null_lora_allowed_without_rank():
@@ -115,6 +130,24 @@ def test_plan(shape):
         w4.plan(M, N, K + 8, R)
 
 
+@pytest.mark.parametrize("shape", [(256, 256, 512, 32), (4096, 3072, 3072, 32),
+                                   (4096, 12288, 3072, 32), (4352, 3840, 15360, 128),
+                                   (1000, 3072, 3072, 16), (1, 1, 32, 0), (7, 33, 160, 3)])
+def test_plan_mxfp4(shape):
+    M, N, K, R = shape
+    p = w4.plan(M, N, K, R, fmt="mxfp4")
+    assert p["block_k"] == 128
+    assert p["tiles_m"] * p["block_m"] >= M and (p["tiles_m"] - 1) * p["block_m"] < M
+    assert p["tiles_n"] * p["block_n"] >= N and (p["tiles_n"] - 1) * p["block_n"] < N
+    assert p["grid"] == p["tiles_m"] * p["tiles_n"]
+    assert p["k_stages"] == -(-K // 128)
+    assert p["lds_bytes"] <= p["lds_limit"] == 163840
+    with pytest.raises(ValueError):
+        w4.plan(M, N, K + 16, R, fmt="mxfp4")
+    with pytest.raises(ValueError):
+        w4.plan(M, N, K, R, fmt="int4")
+
+
 def test_plan_prefers_full_chip_at_qkv():
     # 4096 x 3072 in 256 x 192 tiles is exactly one tile per compute unit
     p = w4.plan(4096, 3072, 3072, 32)
@@ -129,11 +162,21 @@ def _code_object_metadata():
     co = os.path.join(tmp, "co.o")
     subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", lib],
                    check=True)
-    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
-                    f"--input={fat}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
-                    f"--output={co}"], check=True)
-    notes = subprocess.run([f"{LLVM}/llvm-readelf", "--notes", co], capture_output=True,
-                           text=True, check=True).stdout
+    # one offload bundle per translation unit, concatenated in the section
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    blob = open(fat, "rb").read()
+    starts = [i for i in range(len(blob)) if blob.startswith(magic, i)]
+    assert starts, "no offload bundle in the library"
+    notes = ""
+    for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(blob)])):
+        part = os.path.join(tmp, f"bundle{n}.bin")
+        with open(part, "wb") as f:
+            f.write(blob[a:b])
+        subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
+                        f"--input={part}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                        f"--output={co}"], check=True)
+        notes += subprocess.run([f"{LLVM}/llvm-readelf", "--notes", co], capture_output=True,
+                                text=True, check=True).stdout
     shutil.rmtree(tmp, ignore_errors=True)
     kernels = {}
     cur = {}
@@ -160,13 +203,18 @@ def test_solver_lds_matches_code_objects():
     that the solver may pick for a full-chip workload."""
     meta = _code_object_metadata()
     assert meta, "no kernels found in the code object"
-    for v in w4.variants():
-        key = "TileCfgILi%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
-                                                    v["waves_n"], v["stages"])
+    # mangled tile configurations: w4a4::TileCfg (NVFP4) and w4a4::MxTileCfg (MXFP4)
+    cases = [(v, "7TileCfgI") for v in w4.variants("nvfp4")] + \
+            [(v, "9MxTileCfgI") for v in w4.variants("mxfp4")]
+    for v, tag in cases:
+        key = tag + "Li%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
+                                                  v["waves_n"], v["stages"])
         hits = [m for n, m in meta.items() if key in n]
         assert len(hits) == 4, (key, list(meta))     # {fast, general} x {bf16, fp16}
         for m in hits:
             assert int(m[".group_segment_fixed_size"]) == v["lds_bytes"], (key, m)
+            assert int(m[".vgpr_spill_count"]) == 0, (key, m)
+            assert int(m.get(".private_segment_fixed_size", 0)) == 0, (key, m)
             regs = int(m[".vgpr_count"])
             waves_per_simd = max(1, (v["waves_m"] * v["waves_n"] + 3) // 4)
             occ = v["lds_limit"] // v["lds_bytes"]

@@ -4,8 +4,6 @@ Acceptance per element: |y_gpu - y_ref| <= 4e-3 * T + 1 bf16 ulp(y_ref), with
 T = |wcscale| sum_k |A W| + |bias| + sum_r |la lu| (oracle.check_output). Where
 the exact result is representable in bf16 the check is bit-for-value exact.
 """
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -14,30 +12,9 @@ import bit_quantized_gemm_amd as w4
 import oracle.w4a4_ref as ref
 import synthetic
 
+from gpu_helpers import ARGS, DEV, _say, _sample_rows, assert_parity, to_device
+
 pytestmark = pytest.mark.gpu
-DEV = "cuda:0"
-ARGS = ("act", "ascales", "wgt", "wscales", "wcscale", "bias", "lora_act_in", "lora_up")
-
-
-def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def to_device(x):
-    d = {}
-    for k in ("act", "ascales", "wgt", "wscales"):
-        d[k] = torch.from_numpy(np.ascontiguousarray(x[k])).to(DEV)
-    d["wcscale"] = torch.from_numpy(np.ascontiguousarray(x["wcscale"])).to(DEV)
-    d["bias"] = torch.from_numpy(np.ascontiguousarray(x["bias"])).to(DEV)
-    half = torch.float16 if x.get("dtype", "bf16") == "f16" else torch.bfloat16
-    if x["R"] > 0:
-        for k in ("lora_act_in", "lora_up"):
-            t = torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16))
-            d[k] = t.view(half).to(DEV)
-    else:
-        d["lora_act_in"] = d["lora_up"] = None
-    return d
 
 
 def run_gpu(x, out=None):
@@ -53,12 +30,6 @@ def oracle_full(x):
     a = [x[k] for k in ARGS]
     dt = x.get("dtype", "bf16")
     return ref.gemm_w4a4_ref(*a, dtype=dt), ref.term_magnitude(*a, dtype=dt)
-
-
-def assert_parity(got, y, T, what, dtype="bf16"):
-    res = ref.check_output(got, y, T, dtype)
-    _say(f"  {what}: max err/bound {res['max_ratio']:.3g}, failures {res['n_fail']}")
-    assert res["ok"], (what, res)
 
 
 def const_inputs(M, N, K, R, a_code, w_code, a_scale, w_scale, la_bits=0x3F00, lu_bits=0x3E80,
@@ -84,15 +55,6 @@ def test_tiny_full():
     got = run_gpu(x)
     y, T = oracle_full(x)
     assert_parity(got, y, T, "tiny")
-
-
-def _sample_rows(M, block_m, rng):
-    rows = set(range(0, min(M, 40)))                          # first tile head
-    rows |= set(range(max(0, M - 40), M))                     # last (ragged) rows
-    for t in range(0, M, block_m):                            # tile boundaries
-        rows |= {t, min(M - 1, t + block_m - 1)}
-    rows |= set(rng.choice(M, size=min(M, 64), replace=False).tolist())
-    return np.array(sorted(rows))
 
 
 @pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "ragged", "prod_k3840_n3072",
