@@ -19,12 +19,13 @@
 // scale bytes go HBM -> LDS by direct-to-LDS DMA and LDS -> MFMA unchanged,
 // and the kernel is a DMA ring feeding MFMAs.
 //
-// Pipeline (4-deep LDS ring, one stage = 128 k = two MFMA k-steps): iteration
-// st runs k-step 0 of stage st while it DMAs stage st+3 and reads k-step 1's
-// operands, waits for its own DMA of stage st+1 and meets the workgroup
-// barrier, then runs k-step 1 while it reads stage st+1's k-step 0 operands
-// and scales. Every read of stage st-1 happened before the previous barrier,
-// so DMA(st+3) may refill buffer (st-1) % 4 from the start of iteration st.
+// Pipeline (LDS ring of S stages, one stage = 128 k = two MFMA k-steps,
+// prefetch distance PF = S - 1): iteration st runs k-step 0 of stage st while
+// it DMAs stage st+PF and reads k-step 1's operands, waits for its own DMA of
+// stage st+1 and meets the workgroup barrier, then runs k-step 1 while it
+// reads stage st+1's k-step 0 operands and scales. Every read of stage st-1
+// happened before the previous barrier, so DMA(st+PF) may refill buffer
+// (st-1) % S from the start of iteration st.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -65,6 +66,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   constexpr int T = C::MI + C::NI;                               // operand tiles per wave
   constexpr int G = C::MI * C::NI;                               // MFMAs per k-step
   constexpr int ROWS_PER_ROUND = C::THREADS * 16 / C::ROW_BYTES;
+  constexpr int PF = C::STAGES - 1;                              // prefetch distance in stages
+  static_assert((PF - 1) * DMA_N < 64, "vmcnt range");
   static_assert(ROWS_PER_ROUND % 32 == 0, "the chunk swizzle repeats every 32 rows");
 
   const int tid = threadIdx.x;
@@ -181,15 +184,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     }
   };
 
-  // ---- prologue: DMA stages 0..2, wait for stage 0, publish it, read its
-  // k-step 0 operands and its scales.
+  // ---- prologue: the epilogue's side DMA, then DMA stages 0 .. PF-1, wait
+  // for stage 0, publish it, read its k-step 0 operands and its scales.
+  EpiRegs epi_regs;
+  epilogue_prefetch<C, GENERAL>(p, smem, tid, m0, n0, epi_regs);
   u32x4 O0[T], O1[T];
   uint32_t SC[T], SCn[T];
 #pragma unroll
-  for (int s = 0; s < 3; ++s)
+  for (int s = 0; s < PF; ++s)
 #pragma unroll
     for (int u = 0; u < DMA_N; ++u) dma_round(min(s, last), s, u);
-  wait_vm_lgkm0<2 * DMA_N>();
+  wait_vm_lgkm0<(PF - 1) * DMA_N>();
   wg_barrier();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -198,17 +203,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   }
 
   for (int st = 0; st < nst; ++st) {
-    // k-step 0 of stage st; alongside: DMA(st+3) and k-step 1's operands
+    // k-step 0 of stage st; alongside: DMA(st+PF) and k-step 1's operands
     kstep.template operator()<0>(st, O0, SC, [&](int q) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = q; u < DMA_N; u += G) dma_round(min(st + 3, last), st + 3, u);
+      for (int u = q; u < DMA_N; u += G) dma_round(min(st + PF, last), st + PF, u);
       const int t = q - (G - T);
       if (t >= 0 && t < T) O1[t] = read_tile(st, 1, t);
     });
     // stage st+1 complete in this wave's view (the ops after it are DMA(st+2)
-    // and DMA(st+3), plus, in the general flavour, scale loads, which only
+    // .. DMA(st+PF), plus, in the general flavour, scale loads, which only
     // makes the wait longer); publish it
-    wait_vm_lgkm0<2 * DMA_N>();
+    wait_vm_lgkm0<(PF - 1) * DMA_N>();
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // k-step 1 of stage st; alongside: stage st+1's k-step 0 operands and scales
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   }
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
-  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0);
+  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0, epi_regs);
 }
 
 // ------------------------------------------------------------------ host side

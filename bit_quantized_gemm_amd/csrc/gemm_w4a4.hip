@@ -374,6 +374,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   static_assert(SLOT_RD1 + T <= SLOT_SCL, "slots overlap");
   const int last = nst - 1;
   Chunk C0, C1;
+  EpiRegs epi_regs;
+  epilogue_prefetch<C, GENERAL>(p, smem, tid, m0, n0, epi_regs);   // older than every ring op below
   load_scales(0, s_raw[0]);
   issue_dma(0, 0);
   load_scales(min(1, last), s_raw[1]);
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   if (st < nst) iteration.template operator()<0>(st);
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
-  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0);
+  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0, epi_regs);
 }
 
 // ------------------------------------------------------------------ host side

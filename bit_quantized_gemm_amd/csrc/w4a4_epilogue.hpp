@@ -12,12 +12,84 @@
 
 namespace w4a4 {
 
+// LoRA chunk size (ranks) and the lora_up transpose task of a thread: 4 ranks
+// x 8 columns, ranks fastest across threads.
+constexpr int kLoraChunk = 32;
+__device__ __forceinline__ int lu_task_r4(int tid) { return (tid % (kLoraChunk / 4)) * 4; }
+__device__ __forceinline__ int lu_task_n8(int tid) { return (tid / (kLoraChunk / 4)) * 8; }
+
+// Registers the kernel holds through its K-loop for the epilogue: the first
+// LoRA chunk's lora_up pieces, where the side region has no room for them.
+struct EpiRegs {
+  u32x4 lu[4];
+};
+
+// The fast flavour with a side region (C::Side::ON): at the start of the
+// kernel, before its first ring DMA, bring wcscale / bias of the tile's
+// columns and the first 32 LoRA ranks (act rows; lora_up rows where
+// C::Side::LU_ON) into the side region by DMA. These ops are older than every
+// ring DMA, so the K-loop's waits for its first stage cover them and the
+// epilogue finds them in LDS. Reads past an edge are clamped to valid
+// addresses: columns past N and rows past M only reach discarded outputs;
+// ranks past R are zeroed by the epilogue.
+template <class C, bool GENERAL>
+__device__ __forceinline__ void epilogue_prefetch(const Params& p, uint8_t* smem, const int tid,
+                                                  const int m0, const int n0, EpiRegs& regs) {
+  using S = typename C::Side;
+  if constexpr (!GENERAL && S::ON) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = p.N, R = p.R;
+#pragma unroll
+    for (int u = 0; u < S::WB_SLOTS / C::THREADS; ++u) {
+      const int q = u * C::THREADS + tid;          // [2][BN] fp32; slots past 2*BN pad
+      const int arr = q < 2 * C::BN ? q / C::BN : 0;
+      const int col = q < 2 * C::BN ? q % C::BN : 0;
+      const float* src = (arr ? p.bias : p.wcscale) + min(n0 + col, N - 1);
+      dma<4>(src, smem + S::WB_OFF + (u * C::THREADS + wave_u * 64) * 4);
+    }
+    if (R > 0) {
+      // LA: slot q = (row, chunk position c) holds data piece c ^ swz(row),
+      // ranks 8 (c ^ swz(row)) .. +7 (R % 8 == 0: all in range or all past R)
+#pragma unroll
+      for (int u = 0; u < C::BM * 4 / C::THREADS; ++u) {
+        const int q = u * C::THREADS + tid;
+        const int row = q >> 2, dp = (q & 3) ^ swz(row);
+        const uint16_t* src = p.lora_act_in + uint32_t(min(m0 + row, p.M - 1)) * uint32_t(R) +
+                              uint32_t(min(8 * dp, R - 8));
+        dma<16>(src, smem + S::LA_OFF + (u * C::THREADS + wave_u * 64) * 16);
+      }
+      if constexpr (S::LU_ON) {
+        // LU: [32][BN] as stored; rows past R re-read row R-1 (zeroed later)
+        constexpr int PER_ROW = C::BN / 8;
+#pragma unroll
+        for (int u = 0; u < 32 * PER_ROW / C::THREADS; ++u) {
+          const int q = u * C::THREADS + tid;
+          const int r = q / PER_ROW, c8 = q % PER_ROW;
+          const uint16_t* src = p.lora_up + uint32_t(min(r, R - 1)) * uint32_t(N) +
+                                uint32_t(min(n0 + 8 * c8, N - 8));
+          dma<16>(src, smem + S::LU_OFF + (u * C::THREADS + wave_u * 64) * 16);
+        }
+      } else if (tid < (kLoraChunk / 4) * (C::BN / 8)) {
+        // LU into registers (this thread's transpose task), as the epilogue
+        // would load it
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t* src = p.lora_up + uint32_t(min(lu_task_r4(tid) + e, R - 1)) * uint32_t(N);
+          regs.lu[e] = *reinterpret_cast<const u32x4*>(src + min(n0 + lu_task_n8(tid), N - 8));
+        }
+      }
+    }
+  }
+}
+
 // GENERAL: LoRA operands element by element (any R, N, alignment) rather than
 // in 16-byte pieces; F16: LoRA operands and output in binary16, else bfloat16.
-// The LDS ring of C::LDS_BYTES is dead when this runs and is reused.
+// The LDS ring (C::RING_BYTES) is dead when this runs and is reused; the side
+// region, if any, holds what epilogue_prefetch brought in.
 template <class C, bool GENERAL, bool F16>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Params& p, uint8_t* smem,
-                                         const int tid, const int m0, const int n0) {
+                                         const int tid, const int m0, const int n0,
+                                         const EpiRegs& regs) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -39,10 +111,15 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   // 16-byte reads of 16 consecutive rows on distinct banks. Ranks past R (and
   // rows past M, columns past N, read clamped) are stored as zero / clamped
   // copies: zero ranks add nothing, clamped rows only reach discarded outputs.
-  constexpr int RC = 32;
+  // With a side region (PRE) LA lives there instead, 64-byte rows with the
+  // operand tiles' chunk swizzle (the layout its DMA writes), and LU moves to
+  // the start of the ring.
+  using S = typename C::Side;
+  constexpr bool PRE = !GENERAL && S::ON;
+  constexpr int RC = kLoraChunk;
   constexpr int LR_STRIDE = RC * 2 + 16;
-  constexpr int LA_OFF = 0, LU_OFF = C::BM * LR_STRIDE;
-  static_assert(LU_OFF + C::BN * LR_STRIDE <= C::LDS_BYTES, "LoRA chunk must fit in the ring");
+  constexpr int LA_OFF = PRE ? S::LA_OFF : 0, LU_OFF = PRE ? 0 : C::BM * LR_STRIDE;
+  static_assert(LU_OFF + C::BN * LR_STRIDE <= C::RING_BYTES, "LoRA chunk must fit in the ring");
   // LA: one 16-byte piece = 8 ranks of one row; pieces q = u*THREADS + tid
   constexpr int LA_PIECES = C::BM * RC / 8;
   constexpr int LA_PER = (LA_PIECES + C::THREADS - 1) / C::THREADS;
@@ -52,11 +129,11 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   constexpr int LU_TASKS = (RC / 4) * (C::BN / 8);
   static_assert(LU_TASKS <= C::THREADS, "one LoRA-up task per thread");
   const bool lu_task = tid < LU_TASKS;
-  const int lu_r4 = (tid % (RC / 4)) * 4;
-  const int lu_n8 = (tid / (RC / 4)) * 8;
+  const int lu_r4 = lu_task_r4(tid);
+  const int lu_n8 = lu_task_n8(tid);
   u32x4 la_reg[LA_PER], lu_reg[4];
 
-  auto lora_load = [&](int rc0) __attribute__((always_inline)) {
+  auto la_load = [&](int rc0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < LA_PER; ++u) {
       const int q = min(u * C::THREADS + tid, LA_PIECES - 1);
@@ -77,6 +154,8 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
         la_reg[u] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
+  };
+  auto lu_load = [&](int rc0) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = rc0 + lu_r4 + e;
@@ -98,16 +177,42 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
     }
   };
   // The fast flavour zeroes ranks past R here rather than at the load, so a
-  // prefetch stays in flight until its chunk is stored.
+  // prefetch stays in flight until its chunk is stored. With PRE, chunk 0's
+  // LA is already in place (only its pieces past R get zeroed), and its LU
+  // comes from the side region when it is there.
   auto lora_store = [&](int rc0) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < LA_PER; ++u) {
       const int q = u * C::THREADS + tid;
-      const bool keep = GENERAL || rc0 + (q % (RC / 8)) * 8 < R;
-      if (LA_PIECES % C::THREADS == 0 || q < LA_PIECES)
-        *reinterpret_cast<u32x4*>(smem + LA_OFF + (q / (RC / 8)) * LR_STRIDE + (q % (RC / 8)) * 16) =
-            keep ? la_reg[u] : zero;
+      const int row = q / (RC / 8), dp = q % (RC / 8);
+      const bool keep = GENERAL || rc0 + dp * 8 < R;
+      if constexpr (PRE) {
+        // The swizzle pairs chunk position x of a row with data piece
+        // x ^ swz(row). Chunk 0: this thread's DMA filled position dp with
+        // piece dp ^ swz(row); zero it if those ranks are past R. Later
+        // chunks: la_reg[u] holds piece dp, which goes to position dp ^ swz(row).
+        const int dx = dp ^ swz(row);
+        if (rc0 == 0) {
+          if (dx * 8 >= R) *reinterpret_cast<u32x4*>(smem + LA_OFF + row * 64 + dp * 16) = zero;
+        } else {
+          *reinterpret_cast<u32x4*>(smem + LA_OFF + row * 64 + dx * 16) = keep ? la_reg[u] : zero;
+        }
+      } else if (LA_PIECES % C::THREADS == 0 || q < LA_PIECES) {
+        *reinterpret_cast<u32x4*>(smem + LA_OFF + row * LR_STRIDE + dp * 16) = keep ? la_reg[u] : zero;
+      }
+    }
+    if constexpr (PRE && S::LU_ON) {
+      if (rc0 == 0 && lu_task) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lu_reg[e] = *reinterpret_cast<const u32x4*>(smem + S::LU_OFF + ((lu_r4 + e) * C::BN + lu_n8) * 2);
+      }
+    } else if constexpr (PRE) {
+      if (rc0 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lu_reg[e] = regs.lu[e];
+      }
     }
     if constexpr (!GENERAL) {
 #pragma unroll
@@ -130,7 +235,12 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   };
 
   const int nchunks = (R + RC - 1) / RC;
-  if (nchunks > 0) lora_load(0);
+  if (nchunks > 0) {
+    if constexpr (!PRE) {
+      la_load(0);
+      lu_load(0);
+    }
+  }
 
   // Per-column factor at columns ncol0 + 32j + 8q + (0..3), clamped at the N edge.
   auto col4 = [&](const float* v, int j, int q) __attribute__((always_inline)) {
@@ -139,13 +249,21 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
     return f32x4{v[min(n, N - 1)], v[min(n + 1, N - 1)], v[min(n + 2, N - 1)], v[min(n + 3, N - 1)]};
   };
 
-  // S * wcscale[n] + bias[n] (the LoRA terms are added on top by the MFMAs below)
+  // S * wcscale[n] + bias[n] (the LoRA terms are added on top by the MFMAs
+  // below); with PRE the factors come from the side region
+  const uint32_t wb_rd = S::WB_OFF + (wn * C::TN + 4 * g) * 4;
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4 w = col4(p.wcscale, j, q);
-      const f32x4 b = col4(p.bias, j, q);
+      f32x4 w, b;
+      if constexpr (PRE) {
+        w = *reinterpret_cast<const f32x4*>(smem + wb_rd + (32 * j + 8 * q) * 4);
+        b = *reinterpret_cast<const f32x4*>(smem + wb_rd + (C::BN + 32 * j + 8 * q) * 4);
+      } else {
+        w = col4(p.wcscale, j, q);
+        b = col4(p.bias, j, q);
+      }
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -157,13 +275,17 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   // then two k-steps of v_mfma_f32_32x32x16_bf16 (same accumulator layout as
   // the K-loop: lora_up as the A operand, rows n; lora_act_in as B, rows m).
   // Lane (l32, g) feeds ranks 8g .. 8g+7 of each 16-rank k-step.
-  const uint32_t la_rd = LA_OFF + (wm * C::TM + l32) * LR_STRIDE + g * 16;
+  const int la_row = wm * C::TM + l32;   // + 32i: the same swizzle
+  const uint32_t la_rd = PRE ? LA_OFF + la_row * 64 : LA_OFF + la_row * LR_STRIDE + g * 16;
   const uint32_t lu_rd = LU_OFF + (wn * C::TN + l32) * LR_STRIDE + g * 16;
   for (int c = 0; c < nchunks; ++c) {
     wait_vm_lgkm0<0>();
     wg_barrier();   // every wave is done with the ring / the previous chunk
     lora_store(c * RC);
-    if (c + 1 < nchunks) lora_load((c + 1) * RC);
+    if (c + 1 < nchunks) {
+      la_load((c + 1) * RC);
+      lu_load((c + 1) * RC);
+    }
     wait_vm_lgkm0<63>();
     wg_barrier();
 #pragma unroll
@@ -171,8 +293,12 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
       if (s > 0 && c * RC + 16 * s >= R) break;   // an all-zero k-step
       u32x4 la[C::MI], lu[C::NI];
 #pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-        la[i] = *reinterpret_cast<const u32x4*>(smem + la_rd + i * 32 * LR_STRIDE + s * 32);
+      for (int i = 0; i < C::MI; ++i) {
+        if constexpr (PRE)
+          la[i] = *reinterpret_cast<const u32x4*>(smem + la_rd + i * 32 * 64 + (((2 * s + g) ^ swz(la_row)) << 4));
+        else
+          la[i] = *reinterpret_cast<const u32x4*>(smem + la_rd + i * 32 * LR_STRIDE + s * 32);
+      }
 #pragma unroll
       for (int j = 0; j < C::NI; ++j)
         lu[j] = *reinterpret_cast<const u32x4*>(smem + lu_rd + j * 32 * LR_STRIDE + s * 32);
@@ -190,7 +316,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   wait_vm_lgkm0<0>();
   wg_barrier();
   constexpr int OUT_STRIDE = C::BN * 2 + 16;
-  static_assert(C::BM * OUT_STRIDE <= C::LDS_BYTES, "output tile must fit in the ring");
+  static_assert(C::BM * OUT_STRIDE <= C::RING_BYTES, "output tile must fit in the ring");
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
 #pragma unroll

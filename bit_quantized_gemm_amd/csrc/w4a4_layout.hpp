@@ -17,6 +17,33 @@ constexpr int kLdsLimit = 163840;   // LDS one workgroup may use on gfx950 (160 
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kWave = 64;           // CDNA wavefront width
 
+// The epilogue's side region, after the ring, where the LDS budget of one
+// workgroup (kLdsLimit / OCC) allows it: what the epilogue needs first,
+// brought in by DMA at the start of the kernel so that its latency hides
+// behind the K-loop.
+//   WB  wcscale then bias of the tile's BN columns, fp32 [2][BN], padded to
+//       whole rounds of 4-byte DMA pieces
+//   LA  LoRA ranks 0..31 of the tile's BM act rows, 16-bit [BM][64 bytes],
+//       16-byte chunks XOR-swizzled by row as the operand tiles
+//   LU  lora_up rows 0..31 at the tile's BN columns as stored, 16-bit
+//       [32][BN] (only where it still fits; the epilogue transposes it)
+template <int BM, int BN, int THREADS, int OCC, int RING>
+struct EpiSide {
+  static constexpr int WB_SLOTS = (2 * BN + THREADS - 1) / THREADS * THREADS;
+  static constexpr int WB_BYTES = WB_SLOTS * 4;
+  static constexpr int LA_BYTES = BM * 64;
+  static constexpr int LU_BYTES = 32 * BN * 2;
+  static constexpr int BUDGET = kLdsLimit / OCC;
+  static constexpr bool ON = RING + WB_BYTES + LA_BYTES <= BUDGET;
+  static constexpr bool LU_ON = ON && RING + WB_BYTES + LA_BYTES + LU_BYTES <= BUDGET;
+  static constexpr int WB_OFF = RING;
+  static constexpr int LA_OFF = WB_OFF + WB_BYTES;
+  static constexpr int LU_OFF = LA_OFF + LA_BYTES;
+  static constexpr int BYTES = ON ? WB_BYTES + LA_BYTES + (LU_ON ? LU_BYTES : 0) : 0;
+  static_assert(RING % 16 == 0 && WB_BYTES % 16 == 0, "16-byte aligned regions");
+  static_assert((BM * 4) % THREADS == 0 && (32 * BN / 8) % THREADS == 0, "whole DMA rounds");
+};
+
 // BM x BN output tile per workgroup, WM x WN waves, each wave owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles. Every pipeline stage covers
 // BK = 128 values of k, i.e. 8 NVFP4 scale blocks and 8 MFMA k-steps of 16.
@@ -43,7 +70,9 @@ struct TileCfg {
   static constexpr int SB_OFF = SA_OFF + KBLK * BM * 2;
   static constexpr int STAGE_BYTES = SB_OFF + KBLK * BN * 2;
   static constexpr int PACKED_BYTES = SA_OFF;   // bytes moved by DMA per stage
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  using Side = EpiSide<BM, BN, THREADS, OCC, RING_BYTES>;
+  static constexpr int LDS_BYTES = RING_BYTES + Side::BYTES;
   // scale loader: one thread per 8 consecutive rows of one k-block pair
   static constexpr int SA_THREADS = BM / 2;     // (KBLK / 2) * (BM / 8)
   static constexpr int SB_THREADS = BN / 2;
@@ -86,13 +115,15 @@ struct MxTileCfg {
   static constexpr int SCALE_ROUNDS = (SCALE_BYTES + THREADS * 4 - 1) / (THREADS * 4);
   static constexpr int PACKED_BYTES = SA_OFF;
   static constexpr int STAGE_BYTES = SA_OFF + SCALE_ROUNDS * THREADS * 4;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  using Side = EpiSide<BM, BN, THREADS, OCC, RING_BYTES>;
+  static constexpr int LDS_BYTES = RING_BYTES + Side::BYTES;
 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
   static_assert(BM % 4 == 0 && BN % 4 == 0, "4-row scale DMA pieces");
   static_assert(PACKED_BYTES % (THREADS * 16) == 0 && B_OFF % (THREADS * 16) == 0,
                 "whole 16-byte DMA rounds per operand");
-  static_assert(STAGES == 4, "the pipeline is written for a 4-deep ring");
+  static_assert(STAGES >= 3, "at least two stages in flight");
   static_assert(LDS_BYTES * OCC <= kLdsLimit, "LDS budget exceeded");
 };
 
