@@ -17,8 +17,14 @@ The JSON carries:
                 directly. traffic = HBM bytes per launch from the committed
                 rocprofv3 counter summary when it was taken on the current
                 kernel source, else null
+                The "attainable" entry is the rate of the same MFMA instruction
+                alone under full-chip load (gemm_w4a4_mfma_peak) with the shader
+                clock it ran at, and the kernel's fraction of that rate.
   cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on the same full
                 workload on this host's cores, repeated for about --cpu-seconds
+
+--cold rotates enough copies of the inputs (at least 4, at least 512 MiB in
+all) that a launch cannot find its operands in the 256 MB Infinity Cache.
 """
 from __future__ import annotations
 
@@ -59,6 +65,40 @@ def committed_traffic(workload: str, fmt: str = "nvfp4"):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def attainable_peak(w4, kind: int, dev, stream, iters: int = 2048, reps: int = 10) -> dict:
+    """Rate of one MFMA kind alone on every SIMD (gemm_w4a4_mfma_peak) and the
+    shader clock it ran at (median over workgroups)."""
+    import numpy as np
+    import torch
+    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=dev)
+    call = lambda: w4.mfma_peak_raw(kind, iters, clocks.data_ptr(), stream.cuda_stream)
+    for _ in range(3):
+        if call() != 0:
+            raise RuntimeError("gemm_w4a4_mfma_peak failed")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+    mhz = float(np.median(c[:, 0] / (c[:, 1] / 100.0)))
+    flops = w4.PEAK_GROUPS * 4 * iters * 8 * w4.PEAK_FLOP[kind]
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_mhz": round(mhz, 1)}
+
+
 def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4") -> dict:
     """Time the CPU oracle (as it stands) on the whole workload, repeated until
     about `seconds` have passed (at least once)."""
@@ -84,7 +124,8 @@ def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4") -> dict:
     flops = (2 * M * N * K + 2 * M * R * N) * reps
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"the full workload (M={M}, N={N}, K={K}, R={R}) {reps} times, {dt:.1f} s; "
-                      f"float64 decode in numpy, dgemm on {threads} BLAS threads"}
+                      f"float64 decode in numpy, dgemm on {threads} BLAS threads; "
+                      f"{len(os.sched_getaffinity(0))} cores in the affinity mask, {cpu_model()}"}
 
 
 def main() -> int:
@@ -101,6 +142,8 @@ def main() -> int:
                     help="LoRA and affine off (R=0, wcscale=1, bias=0): the plain block-scaled GEMM")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle baseline (0 skips it)")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate input copies so that no launch finds its operands in the Infinity Cache")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter scale probe)")
     a = ap.parse_args()
@@ -141,10 +184,16 @@ def main() -> int:
     (w4.gemm_mxfp4 if mx else w4.gemm_w4a4)(t["act"], t["ascales"], t["wgt"], t["wscales"],
                                              t["wcscale"], t["bias"], la, lu, out=out,
                                              stream=stream)
-    args = (t["act"].data_ptr(), t["ascales"].data_ptr(), t["wgt"].data_ptr(),
-            t["wscales"].data_ptr(), t["wcscale"].data_ptr(), t["bias"].data_ptr(),
-            la.data_ptr(), lu.data_ptr(), out.data_ptr(), wl.M, wl.N, wl.K, wl.R,
-            stream.cuda_stream)
+    sets = [(t, la, lu)]
+    if a.cold:
+        set_bytes = sum(v.numel() * v.element_size() for v in t.values()) + 2 * (la.numel() + lu.numel())
+        n_sets = max(4, -(-(512 << 20) // set_bytes))
+        sets += [({k: v.clone() for k, v in t.items()}, la.clone(), lu.clone()) for _ in range(n_sets - 1)]
+    arg_sets = [(s["act"].data_ptr(), s["ascales"].data_ptr(), s["wgt"].data_ptr(),
+                 s["wscales"].data_ptr(), s["wcscale"].data_ptr(), s["bias"].data_ptr(),
+                 sla.data_ptr(), slu.data_ptr(), out.data_ptr(), wl.M, wl.N, wl.K, wl.R,
+                 stream.cuda_stream) for s, sla, slu in sets]
+    counter = [0]
     if mx:
         raw = w4.gemm_mxfp4_f16_raw if a.dtype == "f16" else w4.gemm_mxfp4_raw
     else:
@@ -152,7 +201,8 @@ def main() -> int:
     bad = []
 
     def step():
-        rc = raw(*args)
+        rc = raw(*arg_sets[counter[0] % len(arg_sets)])
+        counter[0] += 1
         if rc != 0:
             bad.append(rc)
 
@@ -194,6 +244,11 @@ def main() -> int:
         return 1
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
+    # the output of the timed loop's last call with the first input set
+    counter[0] = 0
+    step()
+    torch.cuda.synchronize()
+
     # a sampled parity check of the timed output (first rows) against the oracle
     import oracle.w4a4_ref as ref
     rows = np.arange(min(16, wl.M))
@@ -209,6 +264,8 @@ def main() -> int:
     traffic = committed_traffic(a.workload, a.fmt)
     plan = w4.plan(*wl.shape, fmt=a.fmt)
     peak = PEAK_FP4_TFLOPS if mx else PEAK_F16_MFMA_TFLOPS
+    attain = attainable_peak(w4, 1 if mx else 0, dev, stream)
+    attain["frac"] = round(achieved / attain["tflops"], 4)
     res = {
         "metric": "W4A4 GEMM TFLOP/s + % of used-MFMA/FP4 peak, M=4096 N=K=3072 R=32",
         "value": round(value, 2),
@@ -223,6 +280,7 @@ def main() -> int:
         "dtype": "fp4" if mx else "f16",   # the MFMA's operand type; LoRA/output type in config
         "data": "synthetic",
         "config": {"workload": wl.name, "mode": "ceiling (no LoRA, no affine)" if a.ceiling else "full",
+                   "inputs": f"cold ({len(arg_sets)} rotating copies)" if a.cold else "warm (one copy)",
                    "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
                    "operands": (("MXFP4 (E2M1 + UE8M0 per 32 k)" if mx else "NVFP4 (E2M1 + E4M3 per 16 k)")
                                 + f", LoRA {a.dtype}, out {a.dtype}"),
@@ -233,7 +291,9 @@ def main() -> int:
                      "traffic": traffic,
                      "frac_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "median_launch_us": round(float(np.median(per_launch_ms)) * 1e3, 2),
                      "min_launch_us": round(min(per_launch_ms) * 1e3, 2),
+                     "attainable": attain,
                      "kernel_source_sha256": kernel_source_hash(a.fmt)},
         "parity_sample": {"rows": int(len(rows)), "max_err_over_bound": round(chk["max_ratio"], 4),
                           "ok": chk["ok"]},

@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_mxfp4_num_variants.restype = i
         lib.gemm_mxfp4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
         lib.gemm_mxfp4_variant_info.restype = i
+        lib.gemm_w4a4_mfma_peak.argtypes = [i, i, vp, vp]
+        lib.gemm_w4a4_mfma_peak.restype = i
         lib.gemm_w4a4_strerror.argtypes = [i]
         lib.gemm_w4a4_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -107,6 +109,15 @@ def gemm_mxfp4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, l
     """Direct call of the MXFP4 fp16 C entry point; returns its code."""
     return load().gemm_mxfp4_f16(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
                                  out, M, N, K, R, stream)
+
+
+PEAK_GROUPS = 256
+PEAK_FLOP = {0: 32768, 1: 131072, 2: 32768}   # per MFMA of each gemm_w4a4_mfma_peak kind
+
+
+def mfma_peak_raw(kind: int, iters: int, clocks, stream) -> int:
+    """Launch the attainable-MFMA-peak microbenchmark (measurement aid)."""
+    return load().gemm_w4a4_mfma_peak(kind, iters, clocks, stream)
 
 
 FORMATS = ("nvfp4", "mxfp4")

@@ -155,6 +155,26 @@ int gemm_mxfp4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan);
 int gemm_mxfp4_num_variants(void);
 int gemm_mxfp4_variant_info(int variant, gemm_w4a4_plan_t* plan);
 
+/*
+ * gemm_w4a4_mfma_peak — measurement aid, not part of the operator: the
+ * attainable rate of one MFMA kind under full-chip load (the third peak the
+ * measurement plan asks for beside the published ones). Launches
+ * GEMM_W4A4_PEAK_GROUPS workgroups of four waves; every wave issues iters x 8
+ * back-to-back MFMAs into independent accumulators:
+ *   kind 0  v_mfma_f32_32x32x16_f16     (the NVFP4 K-loop's; 32768 flop each)
+ *   kind 1  v_mfma_scale_f32_32x32x64_f8f6f4, FP4 operands (the MXFP4
+ *           K-loop's; 131072 flop each)
+ *   kind 2  v_mfma_f32_32x32x16_bf16    (the LoRA k-steps'; 32768 flop each)
+ * clocks: caller-owned device buffer of 2 * GEMM_W4A4_PEAK_GROUPS uint64, 8-byte
+ * aligned; workgroup g writes its shader-clock cycles (s_memtime) at [2g] and
+ * its 100 MHz wall-clock ticks (s_memrealtime) at [2g+1] over the MFMA loop.
+ * Flops per launch = GEMM_W4A4_PEAK_GROUPS * 4 * iters * 8 * (flop each).
+ * Returns GEMM_W4A4_EINVAL (kind not 0..2, iters < 1, clocks NULL),
+ * GEMM_W4A4_EALIGN, GEMM_W4A4_EDEVICE, GEMM_W4A4_ELAUNCH or GEMM_W4A4_OK.
+ */
+#define GEMM_W4A4_PEAK_GROUPS 256
+int gemm_w4a4_mfma_peak(int kind, int iters, uint64_t* clocks, void* stream);
+
 /* Static string for a return code (never NULL). */
 const char* gemm_w4a4_strerror(int code);
 

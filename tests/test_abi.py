@@ -220,3 +220,10 @@ def test_solver_lds_matches_code_objects():
             occ = v["lds_limit"] // v["lds_bytes"]
             assert regs * waves_per_simd <= 512, (key, regs)
             assert occ >= 1
+
+
+@pytest.mark.parametrize("kind,iters,clocks,want", [
+    (3, 16, 0x1000, w4.EINVAL), (-1, 16, 0x1000, w4.EINVAL), (0, 0, 0x1000, w4.EINVAL),
+    (1, 16, 0, w4.EINVAL), (2, 16, 0x1004, w4.EALIGN)])
+def test_mfma_peak_validation(kind, iters, clocks, want):
+    assert w4.mfma_peak_raw(kind, iters, clocks, 0) == want

@@ -342,3 +342,25 @@ def test_f16_nan_scale_propagates():
     y, T = oracle_full(x)
     assert_parity(got, y, T, "f16 nan scale", "f16")
     assert np.isnan(ref.f16_bits_to_f64(got)[5]).all()
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_mfma_peak_microbenchmark(kind):
+    """The attainable-peak aid runs, every workgroup records its clocks, and
+    its rate is positive and below the published dense peak at 2.4 GHz."""
+    _say(f"case: MFMA peak microbenchmark, kind {kind}")
+    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=DEV)
+    s = torch.cuda.current_stream()
+    assert w4.mfma_peak_raw(kind, 64, clocks.data_ptr(), s.cuda_stream) == w4.OK
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    assert w4.mfma_peak_raw(kind, 512, clocks.data_ptr(), s.cuda_stream) == w4.OK
+    b.record()
+    torch.cuda.synchronize()
+    c = clocks.view(-1, 2).cpu().numpy()
+    assert (c[:, 0] > 0).all() and (c[:, 1] > 0).all()
+    mhz = np.median(c[:, 0] / (c[:, 1] / 100.0))
+    assert 500 < mhz < 2600
+    tf = w4.PEAK_GROUPS * 4 * 512 * 8 * w4.PEAK_FLOP[kind] / (a.elapsed_time(b) * 1e-3) / 1e12
+    published = {0: 2500.0, 1: 10100.0, 2: 2500.0}[kind]
+    assert 0 < tf < 1.05 * published
