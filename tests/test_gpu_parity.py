@@ -364,3 +364,63 @@ def test_mfma_peak_microbenchmark(kind):
     tf = w4.PEAK_GROUPS * 4 * 512 * 8 * w4.PEAK_FLOP[kind] / (a.elapsed_time(b) * 1e-3) / 1e12
     published = {0: 2500.0, 1: 10100.0, 2: 2500.0}[kind]
     assert 0 < tf < 1.05 * published
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_hip_graph_capture_and_replay(fmt):
+    """One call captured into a HIP graph (torch.cuda.graph) replays to the
+    eager result, replay after replay, with eager work and synchronisations
+    in between; the launch records no memset or allocation."""
+    _say(f"case: HIP graph capture and replay, {fmt}, 300x200x256 R=40")
+    x = synthetic.custom_inputs(300, 200, 256, 40, seed=91, fmt=fmt)
+    d = to_device(x)
+    call = w4.gemm_mxfp4 if fmt == "mxfp4" else w4.gemm_w4a4
+    out = torch.empty((300, 200), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+             d["lora_act_in"], d["lora_up"], out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.view(torch.int16).cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+             d["lora_act_in"], d["lora_up"], out=out)
+    for rep in range(4):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), eager), rep
+    a = [x[k] for k in ARGS]
+    refn = ref.gemm_mxfp4_ref if fmt == "mxfp4" else ref.gemm_w4a4_ref
+    tmag = ref.term_magnitude_mx if fmt == "mxfp4" else ref.term_magnitude
+    assert_parity(eager.view(np.uint16), refn(*a), tmag(*a), f"graph {fmt}")
+
+
+def test_concurrent_streams():
+    """Two calls on two streams at once (different shapes, both formats)
+    give the same bytes as the same calls made one after the other."""
+    _say("case: concurrent calls on two streams")
+    xa = synthetic.custom_inputs(1024, 768, 512, 32, seed=92)
+    xb = synthetic.custom_inputs(512, 1536, 1024, 16, seed=93, fmt="mxfp4")
+    da, db = to_device(xa), to_device(xb)
+    oa = torch.empty((1024, 768), dtype=torch.bfloat16, device=DEV)
+    ob = torch.empty((512, 1536), dtype=torch.bfloat16, device=DEV)
+    args_a = [da[k] for k in ARGS]
+    args_b = [db[k] for k in ARGS]
+    w4.gemm_w4a4(*args_a, out=oa)
+    w4.gemm_mxfp4(*args_b, out=ob)
+    torch.cuda.synchronize()
+    ra, rb = oa.clone(), ob.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        oa.zero_()
+        ob.zero_()
+        torch.cuda.synchronize()
+        w4.gemm_w4a4(*args_a, out=oa, stream=s1)
+        w4.gemm_mxfp4(*args_b, out=ob, stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ra) and torch.equal(ob, rb)
