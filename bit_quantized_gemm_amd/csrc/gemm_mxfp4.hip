@@ -32,6 +32,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "gemm_w4a4.h"
 #include "w4a4_common.hpp"
 #include "w4a4_epilogue.hpp"
@@ -282,8 +284,9 @@ static int mx_choose_variant(int M, int N) {
     const long tiles = long((M + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
     const long slots = long(kNumCUs) * x.occ;
     const long rounds = (tiles + slots - 1) / slots;
+    const long per_cu = std::min<long>(x.occ, (tiles + kNumCUs - 1) / kNumCUs);
     const double tm = double(x.block_m / x.waves_m), tn = double(x.block_n / x.waves_n);
-    const double per_round = double(x.occ) * x.block_m * x.block_n * (1.0 + 16.0 * (tm + tn) / (tm * tn));
+    const double per_round = double(per_cu) * x.block_m * x.block_n * (1.0 + 16.0 * (tm + tn) / (tm * tn));
     const double cost = double(rounds) * per_round;
     if (v == 0 || cost < best_cost) {
       best = v;

@@ -33,6 +33,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -450,17 +451,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 struct Variant {
   void (*kernel[2][2])(const Params);   // [F16][fast] (see gemm_w4a4_kernel)
   int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
+  double cost;   // time per output element of a full round, relative to 256x192
 };
 
 template <class C>
-constexpr Variant make_variant() {
+constexpr Variant make_variant(double cost) {
   return Variant{{{gemm_w4a4_kernel<C, true, false>, gemm_w4a4_kernel<C, false, false>},
                   {gemm_w4a4_kernel<C, true, true>, gemm_w4a4_kernel<C, false, true>}},
                  C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
-                 C::LDS_BYTES, C::STAGE_BYTES, C::OCC};
+                 C::LDS_BYTES, C::STAGE_BYTES, C::OCC, cost};
 }
 
-static const Variant kVariants[] = {make_variant<Cfg256x192>(), make_variant<Cfg128x128>()};
+// Relative costs measured on MI355X at the M = 4352 shapes (K = 3840..15360),
+// where each instance needs whole rounds: a 256x192 tile-round per output
+// element 1.00, 256x128 1.16, two 128x128 tiles sharing a CU 1.22. Smaller
+// wave tiles decode more operand tiles per MFMA (0.58, 0.75 and 1.0 per MFMA).
+static const Variant kVariants[] = {make_variant<Cfg256x192>(1.00), make_variant<Cfg128x128>(1.22),
+                                    make_variant<Cfg256x128>(1.16)};
 static constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 static void fill_static(const Variant& v, int idx, gemm_w4a4_plan_t* pl) {
@@ -492,9 +499,9 @@ static bool sizes_ok(int M, int N, int K, int R) {
 
 // Budget solver: for each compiled instance, the number of rounds the chip
 // needs (tiles / (CUs * workgroups resident per CU)) times the time of one
-// round (the resident workgroups share the CU, so occ tiles of work); picks
-// the instance with the smallest estimate. Ties go to the earlier, larger
-// tile, whose decode cost per flop is lower.
+// round (the workgroups resident on the busiest CU, times the tile's elements,
+// times the instance's measured relative cost); picks the instance with the
+// smallest estimate. Ties go to the earlier instance.
 static int choose_variant(int M, int N) {
   int best = 0;
   double best_cost = 0.0;
@@ -503,11 +510,10 @@ static int choose_variant(int M, int N) {
     const long tiles = long((M + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
     const long slots = long(kNumCUs) * x.occ;
     const long rounds = (tiles + slots - 1) / slots;
-    // relative throughput of one resident workgroup: decode VALU per MFMA grows
-    // as (TM + TN) / (TM * TN) for a wave tile TM x TN
-    const double tm = double(x.block_m / x.waves_m), tn = double(x.block_n / x.waves_n);
-    const double decode = 8.0 * 4.0 * (tm + tn) / (tm * tn);   // VALU cycles per MFMA cycle
-    const double per_round = double(x.occ) * x.block_m * x.block_n * (1.0 + 0.5 * decode);
+    // workgroups sharing the busiest compute unit in a round (fewer than occ
+    // when the tiles do not fill the chip)
+    const long per_cu = std::min<long>(x.occ, (tiles + kNumCUs - 1) / kNumCUs);
+    const double per_round = double(per_cu) * x.block_m * x.block_n * x.cost;
     const double cost = double(rounds) * per_round;
     if (v == 0 || cost < best_cost) {
       best = v;

@@ -89,6 +89,7 @@ struct TileCfg {
 // The compiled instances, in variant order. The solver picks among them.
 using Cfg256x192 = TileCfg<256, 192, 2, 2, 4, 1>;
 using Cfg128x128 = TileCfg<128, 128, 2, 2, 4, 2>;
+using Cfg256x128 = TileCfg<256, 128, 2, 2, 4, 1>;
 
 // MXFP4 kernel: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN), 32x32x64
 // scaled FP4 MFMAs. A stage covers BK = 128 values of k = 2 MFMA k-steps = 4

@@ -424,3 +424,21 @@ def test_concurrent_streams():
         w4.gemm_mxfp4(*args_b, out=ob, stream=s2)
         torch.cuda.synchronize()
         assert torch.equal(oa, ra) and torch.equal(ob, rb)
+
+
+# shapes whose plan is the 256x128 instance (more than one round of 128x128
+# tiles), with edges in m and n: fast flavour and (K % 32 != 0) general flavour
+TILE_256x128 = [(4316, 3064, 384, 40), (4300, 3000, 272, 24)]
+
+
+@pytest.mark.parametrize("shape", TILE_256x128, ids=["x".join(map(str, s)) for s in TILE_256x128])
+def test_256x128_instance_sampled(shape):
+    M, N, K, R = shape
+    plan = w4.plan(*shape)
+    assert (plan["block_m"], plan["block_n"]) == (256, 128)
+    _say(f"case: 256x128 instance, M={M} N={N} K={K} R={R}, sampled rows")
+    x = synthetic.custom_inputs(M, N, K, R, seed=M + N + K + R)
+    got = run_gpu(x)
+    rows = _sample_rows(M, 256, np.random.default_rng(11))
+    y, T = ref.reference_rows(x, rows)
+    assert_parity(got[rows], y, T, f"256x128 {shape}")

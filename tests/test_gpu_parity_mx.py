@@ -263,3 +263,4 @@ def test_mx_rejects_bad_arguments_on_device():
     bad[8] = base[0]
     assert w4.gemm_mxfp4_raw(*bad, 64, 64, 128, 16, s) == w4.EOVERLAP
     torch.cuda.synchronize()
+
