@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "custom_inputs", "no_lora_affine",
-           "bf16_bits_from_f32", "f16_bits_from_f32", "e4m3_scale_byte"]
+           "bf16_bits_from_f32", "f16_bits_from_f32", "e4m3_scale_byte", "large_inputs"]
 
 
 @dataclass(frozen=True)
@@ -204,3 +204,31 @@ def custom_inputs(M: int, N: int, K: int, R: int, seed: int, dtype: str = "bf16"
     """Inputs for an arbitrary shape with the standard distributions."""
     wl = Workload("custom", M, N, K, R, seed=seed, **kw)
     return make_inputs(wl, dtype=dtype, fmt=fmt)
+
+
+def large_inputs(M: int, N: int, K: int, R: int, seed: int, fmt: str = "nvfp4") -> dict:
+    """Inputs for shapes whose tensors approach 2^31 bytes, drawn byte-wise to
+    keep host time and memory low: packed bytes uniform over 0..255 (so each
+    nibble uniform over the 16 codes, independently), scale bytes as in
+    make_inputs (E4M3 2^[-4,2] (1 + m/8), or UE8M0 2^[-4,2]), wcscale,
+    bias and bf16 LoRA operands as in make_inputs."""
+    rng = np.random.default_rng(seed)
+    kb = K // (16 if fmt == "nvfp4" else 32)
+
+    def scales(rows):
+        if fmt == "nvfp4":
+            e = rng.integers(3, 10, size=(kb, rows), dtype=np.uint8)   # biased exponent 7 + (-4..2)
+            m = rng.integers(0, 8, size=(kb, rows), dtype=np.uint8)
+            return (e << 3) | m
+        return rng.integers(123, 130, size=(kb, rows), dtype=np.uint8)  # 127 + (-4..2)
+
+    act = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    ascales = scales(M)
+    wgt = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    wscales = scales(N)
+    wcscale = rng.uniform(0.5, 1.5, size=N).astype(np.float32)
+    bias = rng.standard_normal(size=N).astype(np.float32)
+    lora_act_in = bf16_bits_from_f32((rng.standard_normal(size=(M, R)) * 0.1).astype(np.float32))
+    lora_up = bf16_bits_from_f32((rng.standard_normal(size=(R, N)) * 0.1).astype(np.float32))
+    return dict(act=act, ascales=ascales, wgt=wgt, wscales=wscales, wcscale=wcscale, bias=bias,
+                lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R, dtype="bf16", fmt=fmt)

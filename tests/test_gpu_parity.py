@@ -442,3 +442,31 @@ def test_256x128_instance_sampled(shape):
     rows = _sample_rows(M, 256, np.random.default_rng(11))
     y, T = ref.reference_rows(x, rows)
     assert_parity(got[rows], y, T, f"256x128 {shape}")
+
+
+# Tensors just under the 2^31-byte limit the entry points accept (the kernels
+# index with 32-bit offsets): the act operand (M * K/2) and the output (M * N * 2).
+MAX_SHAPES = [("act", (65536, 64, 65504, 16)), ("out", (32768, 32760, 64, 8))]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("which,shape", MAX_SHAPES, ids=[w for w, _ in MAX_SHAPES])
+def test_largest_tensors_sampled(which, shape, fmt):
+    M, N, K, R = shape
+    big = M * K // 2 if which == "act" else M * N * 2
+    assert (1 << 31) - (1 << 22) < big < (1 << 31)
+    _say(f"case: {which} tensor of {big} bytes, {fmt}, M={M} N={N} K={K} R={R}, sampled rows")
+    x = synthetic.large_inputs(M, N, K, R, seed=95, fmt=fmt)
+    d = to_device(x)
+    call = w4.gemm_mxfp4 if fmt == "mxfp4" else w4.gemm_w4a4
+    out = call(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+               d["lora_act_in"], d["lora_up"])
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set([0, 1, 255, 256, M // 2, M - 257, M - 2, M - 1]) |
+                           set(np.random.default_rng(13).choice(M, 24, replace=False).tolist())))
+    got = out[torch.from_numpy(rows).to(DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
+    del out, d
+    torch.cuda.empty_cache()
+    refrows = ref.reference_rows_mx if fmt == "mxfp4" else ref.reference_rows
+    y, T = refrows(x, rows)
+    assert_parity(got, y, T, f"{which} max {fmt}")
