@@ -470,3 +470,25 @@ def test_largest_tensors_sampled(which, shape, fmt):
     refrows = ref.reference_rows_mx if fmt == "mxfp4" else ref.reference_rows
     y, T = refrows(x, rows)
     assert_parity(got, y, T, f"{which} max {fmt}")
+
+
+# The epilogue's prefetched first LoRA chunk (side region) with R < 32: the
+# ranks past R inside that chunk must be zeroed; 256x192 and 256x128 tiles,
+# bf16 and fp16.
+SIDE_PARTIAL = [((4096, 3072, 512, 16), "bf16"), ((4096, 3072, 512, 8), "f16"),
+                ((4316, 3064, 384, 24), "f16")]
+
+
+@pytest.mark.parametrize("shape,dtype", SIDE_PARTIAL,
+                         ids=["x".join(map(str, s)) + "-" + d for s, d in SIDE_PARTIAL])
+def test_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
+    M, N, K, R = shape
+    plan = w4.plan(*shape)
+    assert plan["block_m"] == 256
+    _say(f"case: prefetched LoRA chunk, R={R} < 32, {plan['block_m']}x{plan['block_n']}, {dtype}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=R + K, dtype=dtype)
+    x["ascales"][:] = 0          # main term zero: the output is bias + LoRA
+    got = run_gpu(x)
+    rows = _sample_rows(M, 256, np.random.default_rng(14))
+    y, T = ref.reference_rows(x, rows)
+    assert_parity(got[rows], y, T, f"side chunk R={R} {dtype}", dtype)

@@ -264,3 +264,19 @@ def test_mx_rejects_bad_arguments_on_device():
     assert w4.gemm_mxfp4_raw(*bad, 64, 64, 128, 16, s) == w4.EOVERLAP
     torch.cuda.synchronize()
 
+
+
+@pytest.mark.parametrize("shape,dtype", [((4096, 3072, 512, 16), "bf16"), ((4096, 3072, 512, 8), "f16")])
+def test_mx_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
+    """The first LoRA chunk prefetched into LDS (act rows and lora_up rows)
+    with R < 32: ranks past R must contribute nothing."""
+    M, N, K, R = shape
+    plan = w4.plan(*shape, fmt="mxfp4")
+    assert (plan["block_m"], plan["block_n"]) == (256, 192)
+    _say(f"case: MXFP4 prefetched LoRA chunk, R={R} < 32, {dtype}")
+    x = mx_inputs(M, N, K, R, seed=R + K + 1, dtype=dtype)
+    x["act"][:] = 0              # main term zero: the output is bias + LoRA
+    got = run_mx(x)
+    rows = _sample_rows(M, 256, np.random.default_rng(15))
+    y, T = ref.reference_rows_mx(x, rows)
+    assert_parity(got[rows], y, T, f"mx side chunk R={R} {dtype}", dtype)
