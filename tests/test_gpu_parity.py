@@ -222,9 +222,9 @@ def test_probe_nan_scale_propagates():
 EDGE = [(1, 1, 16, 0), (1, 5, 16, 1), (7, 33, 48, 3), (33, 200, 144, 16), (257, 193, 272, 32),
         (300, 129, 160, 17), (64, 64, 4096, 128), (513, 385, 256, 128), (129, 1, 32, 8),
         (2, 1000, 112, 24), (1000, 64, 208, 40),
-        # fast flavour (K % 32 == 0, N % 8 == 0, R % 8 == 0): N-edge tiles,
-        # several LoRA rank chunks, a last chunk only partly inside R
-        (300, 200, 256, 40), (104, 3000, 512, 72), (136, 8, 32, 8), (64, 64, 384, 24),
+        # fast flavour (K % 32 == 0, M % 8 == 0, N % 8 == 0, R % 8 == 0):
+        # edge tiles, several LoRA rank chunks, a last chunk only partly inside R
+        (304, 200, 256, 40), (104, 3000, 512, 72), (136, 8, 32, 8), (64, 64, 384, 24),
         (256, 200, 640, 16), (512, 384, 1024, 0)]
 
 
@@ -427,8 +427,9 @@ def test_concurrent_streams():
 
 
 # shapes whose plan is the 256x128 instance (more than one round of 128x128
-# tiles), with edges in m and n: fast flavour and (K % 32 != 0) general flavour
-TILE_256x128 = [(4316, 3064, 384, 40), (4300, 3000, 272, 24)]
+# tiles), with edges in m and n: the fast flavour (M % 8 == 0), the general
+# one through M % 8 != 0, and through K % 32 != 0
+TILE_256x128 = [(4320, 3064, 384, 40), (4316, 3064, 384, 40), (4300, 3000, 272, 24)]
 
 
 @pytest.mark.parametrize("shape", TILE_256x128, ids=["x".join(map(str, s)) for s in TILE_256x128])
@@ -476,7 +477,7 @@ def test_largest_tensors_sampled(which, shape, fmt):
 # ranks past R inside that chunk must be zeroed; 256x192 and 256x128 tiles,
 # bf16 and fp16.
 SIDE_PARTIAL = [((4096, 3072, 512, 16), "bf16"), ((4096, 3072, 512, 8), "f16"),
-                ((4316, 3064, 384, 24), "f16")]
+                ((4320, 3064, 384, 24), "f16")]
 
 
 @pytest.mark.parametrize("shape,dtype", SIDE_PARTIAL,
