@@ -45,11 +45,11 @@
 
 namespace w4a4 {
 
-// Eight E2M1 nibbles of one dword times the block scale (fp16 bits in the low
-// half of `scale`), as fp16. Which nibble lands in which of the eight slots is
+// Eight E2M1 nibbles of one dword times the block scale (fp16 bits in half
+// `half` of `scales`), as fp16. Which nibble lands in which of the eight slots is
 // irrelevant (see the file comment); both operands go through this function.
-__device__ __forceinline__ f16x8 decode8(uint32_t w, uint32_t scale) {
-  const _Float16 s = __builtin_bit_cast(f16x2, scale)[0];
+__device__ __forceinline__ f16x8 decode8(uint32_t w, uint32_t scales, int half) {
+  const _Float16 s = __builtin_bit_cast(f16x2, scales)[half];
   const f16x2 ss = {s, s};
   const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
   const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
@@ -247,11 +247,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const uint32_t sb_rd0 = C::SB_OFF + (2 * g * C::BN + rb) * 4;
 
   // One 16-byte chunk (4 k-steps) of this lane's operands and its two block
-  // scales, each scale alone in the low half of a register (the packed fp16
-  // multiply broadcasts a low half for free).
+  // scales, both in one register (one 4-byte LDS read; the packed fp16
+  // multiply broadcasts either half for free).
   struct Chunk {
     u32x4 a[C::MI], b[C::NI];
-    uint32_t sa[C::MI][2], sb[C::NI][2];   // fp16 bits in the low half
+    uint32_t sa[C::MI], sb[C::NI];   // fp16 scales of the chunk's two k-block pairs
   };
   // Tile t (act tiles 0 .. MI-1, then wgt tiles) of chunk h of stage st.
   auto read_tile = [&](int st, int h, int t, Chunk& R) __attribute__((always_inline)) {
@@ -259,17 +259,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     // chunk 2g+1 sits at chunk position ((2g) ^ swz) ^ 1: flip bit 4
     if (t < C::MI) {
       const uint8_t* pa = stage + (h ? (a_rd0 ^ 16u) : a_rd0);
-      const uint16_t* qa = reinterpret_cast<const uint16_t*>(stage + sa_rd0 + h * C::BM * 4);
+      const uint32_t* qa = reinterpret_cast<const uint32_t*>(stage + sa_rd0 + h * C::BM * 4);
       R.a[t] = *reinterpret_cast<const u32x4*>(pa + t * 32 * C::ROW_BYTES);
-      R.sa[t][0] = qa[t * 64];
-      R.sa[t][1] = qa[t * 64 + 1];
+      R.sa[t] = qa[t * 32];
     } else {
       const int j = t - C::MI;
       const uint8_t* pb = stage + (h ? (b_rd0 ^ 16u) : b_rd0);
-      const uint16_t* qb = reinterpret_cast<const uint16_t*>(stage + sb_rd0 + h * C::BN * 4);
+      const uint32_t* qb = reinterpret_cast<const uint32_t*>(stage + sb_rd0 + h * C::BN * 4);
       R.b[j] = *reinterpret_cast<const u32x4*>(pb + j * 32 * C::ROW_BYTES);
-      R.sb[j][0] = qb[j * 64];
-      R.sb[j][1] = qb[j * 64 + 1];
+      R.sb[j] = qb[j * 32];
     }
   };
   auto read_chunk = [&](int st, int h, Chunk& R) __attribute__((always_inline)) {
@@ -302,17 +300,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   Dec D[2];
   auto decode_tile = [&](int t, const Chunk& R, int s, Dec& d) __attribute__((always_inline)) {
     if (t < C::MI)
-      d.a[t] = decode8(R.a[t][s], R.sa[t][s >> 1]);
+      d.a[t] = decode8(R.a[t][s], R.sa[t], s >> 1);
     else
-      d.b[t - C::MI] = decode8(R.b[t - C::MI][s], R.sb[t - C::MI][s >> 1]);
+      d.b[t - C::MI] = decode8(R.b[t - C::MI][s], R.sb[t - C::MI], s >> 1);
   };
   // Pair p (0 .. 4T-1) of a k-step: the two fp16 values 2h, 2h+1 of tile
   // t = p / 4, h = p % 4 (one conversion and one packed multiply).
   auto decode_pair = [&](int pr, const Chunk& R, int s, Dec& d) __attribute__((always_inline)) {
     const int t = pr / 4, h = pr % 4;
     const uint32_t w = t < C::MI ? R.a[t][s] : R.b[t - C::MI][s];
-    const uint32_t sc = t < C::MI ? R.sa[t][s >> 1] : R.sb[t - C::MI][s >> 1];
-    const _Float16 sv = __builtin_bit_cast(f16x2, sc)[0];
+    const uint32_t sc = t < C::MI ? R.sa[t] : R.sb[t - C::MI];
+    const _Float16 sv = __builtin_bit_cast(f16x2, sc)[s >> 1];
     f16x2 c;
     switch (h) {   // the word select must be an immediate; folds after unrolling
       case 0: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0); break;
