@@ -346,22 +346,39 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   constexpr int PIECES_PER_ROW = C::BN / 8;
   constexpr int PIECES = C::BM * PIECES_PER_ROW;
   static_assert(PIECES % C::THREADS == 0, "whole store rounds");
-  const bool vec_out = n_inside && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0;
+  // A piece wholly inside N is one 16-byte store whenever output rows are
+  // 16-byte aligned (N % 8 == 0, aligned out), also in a tile at the N edge;
+  // element stores only otherwise, and never past N.
+  const bool vec_ok = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0;
+  if (vec_ok && n_inside) {
+    // the common case, kept free of per-piece column checks
+#pragma unroll
+    for (int u = 0; u < PIECES / C::THREADS; ++u) {
+      const int piece = u * C::THREADS + tid;
+      const int rl = piece / PIECES_PER_ROW, cl = (piece % PIECES_PER_ROW) * 8;
+      const int row = m0 + rl;
+      if (row >= M) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
+      *reinterpret_cast<u32x4*>(p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl)) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < PIECES / C::THREADS; ++u) {
     const int piece = u * C::THREADS + tid;
     const int rl = piece / PIECES_PER_ROW, cl = (piece % PIECES_PER_ROW) * 8;
     const int row = m0 + rl;
-    if (row >= M) continue;
+    const int left = N - (n0 + cl);   // columns of this piece inside N
+    if (row >= M || left <= 0) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
     uint16_t* dst = p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl);
-    if (vec_out) {
+    if (vec_ok && left >= 8) {
       *reinterpret_cast<u32x4*>(dst) = v;
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (n0 + cl + e < N) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+        if (e < left) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
