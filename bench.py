@@ -134,6 +134,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv", choices=sorted(__import__("synthetic").WORKLOADS))
+    ap.add_argument("--shape", default=None, metavar="M,N,K,R",
+                    help="any other shape, with the standard input distributions (overrides --workload)")
     ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"],
                     help="operand format: NVFP4 (E4M3 scale per 16 k) or MXFP4 (UE8M0 per 32 k)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
@@ -162,7 +164,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    wl = synthetic.workload(a.workload)
+    if a.shape:
+        M, N, K, R = (int(v) for v in a.shape.split(","))
+        wl = synthetic.Workload(f"custom_{M}x{N}x{K}_r{R}", M, N, K, R, seed=2000)
+    else:
+        wl = synthetic.workload(a.workload)
     mx = a.fmt == "mxfp4"
     x = synthetic.make_inputs(wl, dtype=a.dtype, fmt=a.fmt)
     if a.ceiling:
@@ -261,13 +267,14 @@ def main() -> int:
     avg_launch_ms = float(np.mean(per_launch_ms))
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     value = flops * a.steps / (region_ms * 1e-3) / 1e12
-    traffic = committed_traffic(a.workload, a.fmt)
+    traffic = None if a.shape else committed_traffic(a.workload, a.fmt)
     plan = w4.plan(*wl.shape, fmt=a.fmt)
     peak = PEAK_FP4_TFLOPS if mx else PEAK_F16_MFMA_TFLOPS
     attain = attainable_peak(w4, 1 if mx else 0, dev, stream)
     attain["frac"] = round(achieved / attain["tflops"], 4)
     res = {
-        "metric": "W4A4 GEMM TFLOP/s + % of used-MFMA/FP4 peak, M=4096 N=K=3072 R=32",
+        "metric": "W4A4 GEMM TFLOP/s + % of used-MFMA/FP4 peak, " + (
+            f"M={wl.M} N=K={wl.N} R={wl.R}" if wl.N == wl.K else f"M={wl.M} N={wl.N} K={wl.K} R={wl.R}"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
