@@ -8,10 +8,17 @@ whole operator (loader, decode, MFMA K-loop, wcscale, LoRA-up, bias, 16-bit
 store) on inputs already resident in HBM. Prints one JSON line. TFLOP/s counts
 the algorithmic 2MNK + 2MRN flops.
 
+Warm-up: W untimed steps, continued until the GPU has run the step for at
+least --settle-ms (default 500 ms): the shader clock needs tens of
+milliseconds of continuous load to leave its idle state, and a timed region
+that starts earlier measures the ramp, not the kernel. "warmup" in the JSON is
+the number of untimed steps actually run.
+
 The JSON carries:
   roofline      achieved TFLOP/s of the kernel (average launch duration from
-                HIP events around each of K further launches on the launch
-                stream) against the dense peak of the MFMA it runs on: fp16
+                the HIP events at the two ends of the timed region, on the
+                launch stream; one step is one launch and consecutive launches
+                leave no gap) against the dense peak of the MFMA it runs on: fp16
                 (2.5 PFLOP/s) for NVFP4, whose operands are decoded to fp16;
                 FP4 (10.1 PFLOP/s) for MXFP4, which feeds the scaled FP4 MFMA
                 directly. traffic = HBM bytes per launch from the committed
@@ -133,6 +140,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="keep warming up until the step has run this long (clock settling)")
     ap.add_argument("--workload", default="qkv", choices=sorted(__import__("synthetic").WORKLOADS))
     ap.add_argument("--shape", default=None, metavar="M,N,K,R",
                     help="any other shape, with the standard input distributions (overrides --workload)")
@@ -218,9 +227,18 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    # Untimed warm-up: W steps, then more until the GPU has been busy with
+    # this step for settle_ms (checked every few steps, so the GPU never idles
+    # for long enough to drop its clock again).
+    warm_steps = 0
+    t_warm = time.perf_counter()
+    while True:
+        for _ in range(max(1, a.warmup) if warm_steps == 0 else 16):
+            step()
+            warm_steps += 1
+        torch.cuda.synchronize()
+        if warm_steps >= a.warmup and (time.perf_counter() - t_warm) * 1e3 >= a.settle_ms:
+            break
 
     # Timed region: exactly K back-to-back steps, events only at its two ends.
     region0 = torch.cuda.Event(enable_timing=True)
@@ -235,20 +253,9 @@ def main() -> int:
     wall = time.perf_counter() - t0
     region_ms = region0.elapsed_time(region1)
 
-    # Kernel duration for the roofline: K more launches, each bracketed by
-    # events on the launch stream (the event packets between launches would
-    # otherwise be charged to the timed region above).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    for i in range(a.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
     if bad:
         print(f"{KERNELS[a.fmt][1]} returned {bad[0]} ({w4.strerror(bad[0])})", file=sys.stderr)
         return 1
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
     # the output of the timed loop's last call with the first input set
     counter[0] = 0
@@ -264,7 +271,7 @@ def main() -> int:
 
     flops = wl.flops()
     ms_per_step = region_ms / a.steps
-    avg_launch_ms = float(np.mean(per_launch_ms))
+    avg_launch_ms = ms_per_step   # one launch per step, back to back
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     value = flops * a.steps / (region_ms * 1e-3) / 1e12
     traffic = None if a.shape else committed_traffic(a.workload, a.fmt)
@@ -279,7 +286,7 @@ def main() -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
-        "warmup": a.warmup,
+        "warmup": warm_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -298,8 +305,6 @@ def main() -> int:
                      "traffic": traffic,
                      "frac_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-                     "median_launch_us": round(float(np.median(per_launch_ms)) * 1e3, 2),
-                     "min_launch_us": round(min(per_launch_ms) * 1e3, 2),
                      "attainable": attain,
                      "kernel_source_sha256": kernel_source_hash(a.fmt)},
         "parity_sample": {"rows": int(len(rows)), "max_err_over_bound": round(chk["max_ratio"], 4),

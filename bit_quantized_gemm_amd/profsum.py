@@ -5,7 +5,10 @@
         --workload qkv --command "..."
     python -m bit_quantized_gemm_amd.profsum counters DIR --workload qkv --command "..."
 
-`trace` reads the kernel statistics of a `--kernel-trace --stats` run.
+`trace` reads the kernel statistics of a `--kernel-trace --stats` run; given
+the JSON line bench.py printed in that run (`--bench-json`), it also gives the
+statistics of the timed region's dispatches alone (rocprofv3's own averages
+include the warm-up, whose first launches run before the clock has settled).
 `traffic` reads two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a program
 that also made one device copy of COPY_MIB MiB (bench.py --copy-probe-mb): each
 counter is scaled by (true bytes of that copy) / (what the counter read for
@@ -21,6 +24,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import json
 import os
 import statistics
 import sys
@@ -88,7 +92,35 @@ def trace(args) -> str:
         if gaps:
             lines.append(f"Median gap between consecutive launches under the tracer: "
                          f"{statistics.median(gaps):.0f} ns.")
+        if args.bench_json:
+            lines += timed_region(gs, args.bench_json)
     return "\n".join(lines) + "\n"
+
+
+def timed_region(gs, bench_json: str) -> list:
+    """Statistics of the timed region's dispatches. bench.py launches the
+    kernel once through the checked binding, then `warmup` untimed steps, then
+    the `steps` timed ones (then one more for its parity sample)."""
+    b = None
+    with open(bench_json) as f:
+        for line in f:
+            if line.lstrip().startswith("{"):
+                b = json.loads(line)
+    if b is None:
+        raise SystemExit(f"no JSON line in {bench_json}")
+    first, k = 1 + int(b["warmup"]), int(b["steps"])
+    sel = gs[first:first + k]
+    if len(sel) != k:
+        raise SystemExit(f"expected {k} timed dispatches after {first}, found {len(sel)}")
+    d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
+    span = int(sel[-1]["End_Timestamp"]) - int(sel[0]["Start_Timestamp"])
+    return ["", f"Timed region of that bench run: dispatches {first} .. {first + k - 1} of the kernel "
+                f"({k} launches after {b['warmup']} warm-up steps):", "",
+            "| Average ns | Median ns | Min ns | Max ns | Span / launches ns |", "|---|---|---|---|---|",
+            f"| {statistics.mean(d):.1f} | {statistics.median(d):.0f} | {min(d)} | {max(d)} | {span / k:.1f} |",
+            "", f"bench.py's own figure in that run (HIP events at the ends of the timed region): "
+                f"{b['roofline']['avg_launch_us'] * 1e3:.0f} ns per launch, "
+                f"{b['roofline']['achieved']:.1f} TFLOP/s."]
 
 
 def traffic(args) -> str:
@@ -147,6 +179,7 @@ def main(argv=None) -> int:
     t.add_argument("dir")
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True)
+    t.add_argument("--bench-json", default=None, help="bench.py's output of the traced run")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_dir")
     f.add_argument("write_dir")
