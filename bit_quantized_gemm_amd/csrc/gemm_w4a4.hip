@@ -5,12 +5,12 @@
 // and 6.6; E2M1 bit layout: the DeepGEMM FP4 indexer page, "Step 0").
 //
 // Design (one workgroup per BM x BN output tile, WM x WN waves, 1 wave/SIMD):
-//  * Loader: a 3-deep LDS ring. Each stage (128 values of k) of packed act and
+//  * Loader: a 4-deep LDS ring. Each stage (128 values of k) of packed act and
 //    wgt moves HBM -> LDS by direct-to-LDS DMA (global_load_lds), 16-byte
 //    chunks XOR-swizzled by row so the consumer's LDS reads do not conflict.
 //    The stage's E4M3 scale tiles are loaded by the workgroup with coalesced
 //    8-byte loads, converted once to fp16 and stored [k-block][row] in LDS.
-//    A stage is issued two iterations before it is consumed.
+//    A stage's DMA is issued three iterations before it is consumed.
 //  * Decode: NVFP4 is exact in fp16. Every E2M1 value times every E4M3 scale
 //    has at most 6 significant bits and lies in [2^-10, 2688], so each operand
 //    value is built exactly as fp16: v_cvt_scalef32_pk_f16_fp4 (scale 1.0;
