@@ -179,6 +179,29 @@ def test_probe_zero_main_term_shows_lora_and_bias():
         assert np.all(np.abs(gv - y) <= 2 * ref.ulp_bf16(y) + 1e-6)
 
 
+# ranks past the pages' production bound (R <= 128) up to the library's
+# limit: many 32-rank chunks, fast flavour (M, N, R multiples of 8, both
+# 256-row and 128x128 tiles) and general (R % 8 != 0, M % 8 != 0)
+LARGE_R = [(256, 200, 256, 160), (256, 192, 128, 1024), (64, 64, 64, 520), (260, 200, 256, 1000),
+           # 256x192 tiles (their first chunk comes from the side region) and 256x128
+           (4096, 3072, 128, 160), (4096, 3072, 128, 1024), (4352, 3072, 128, 256)]
+
+
+@pytest.mark.parametrize("shape", LARGE_R, ids=["x".join(map(str, s)) for s in LARGE_R])
+def test_probe_large_rank_lora_visible(shape):
+    """Zero main term at large R: y = bias + a sum of R LoRA products, so a
+    chunk dropped, repeated or read at the wrong ranks fails the check."""
+    M, N, K, R = shape
+    _say(f"case: zero main term at R={R}, M={M} N={N} K={K}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=500 + R)
+    x["ascales"][:] = 0
+    y, T = oracle_full(x)
+    got = run_gpu(x)
+    assert_parity(got, y, T, f"zero main R={R}")
+    gv = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(gv - y) <= 2 * ref.ulp_bf16(y) + 1e-5)
+
+
 def test_probe_subnormal_scales():
     _say("case: subnormal E4M3 scales, small main term")
     x = synthetic.custom_inputs(256, 192, 3072, 32, seed=9)

@@ -189,6 +189,23 @@ def test_mx_zero_main_term_shows_lora_and_bias(dtype):
         assert np.all(np.abs(gv - y) <= 2 * ulp(y) + 1e-6)
 
 
+@pytest.mark.parametrize("shape", [(256, 200, 256, 160), (256, 192, 128, 1024), (260, 200, 256, 1000),
+                                   (4096, 3072, 128, 160), (4096, 3072, 128, 1024)],
+                         ids=["fast_R160", "fast_R1024", "general_R1000", "256x192_R160", "256x192_R1024"])
+def test_mx_probe_large_rank_lora_visible(shape):
+    """As the NVFP4 probe: act codes zero, y = bias + a sum of R LoRA
+    products, ranks far past the pages' 128."""
+    M, N, K, R = shape
+    _say(f"case: MXFP4 zero main term at R={R}, M={M} N={N} K={K}")
+    x = mx_inputs(M, N, K, R, seed=600 + R)
+    x["act"][:] = 0
+    y, T = oracle_mx(x)
+    got = run_mx(x)
+    assert_parity(got, y, T, f"mx zero main R={R}")
+    gv = ref.half_bits_to_f64(got, "bf16")
+    assert np.all(np.abs(gv - y) <= 2 * ref.ulp_bf16(y) + 1e-5)
+
+
 def test_mx_nan_scale_propagates():
     _say("case: MXFP4 NaN scale byte (0xFF)")
     x = mx_inputs(64, 64, 128, 0, seed=51)
