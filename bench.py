@@ -29,6 +29,8 @@ The JSON carries:
                 clock it ran at, and the kernel's fraction of that rate.
   cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on the same full
                 workload on this host's cores, repeated for about --cpu-seconds
+  parity_sample the first output rows of the timed kernel checked against the
+                oracle's rows, within the same leg (--cpu-seconds 0 skips both)
 
 --cold rotates enough copies of the inputs (at least 4, at least 512 MiB in
 all) that a launch cannot find its operands in the 256 MB Infinity Cache.
@@ -106,9 +108,12 @@ def attainable_peak(w4, kind: int, dev, stream, iters: int = 2048, reps: int = 1
     return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_mhz": round(mhz, 1)}
 
 
-def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4") -> dict:
-    """Time the CPU oracle (as it stands) on the whole workload, repeated until
-    about `seconds` have passed (at least once)."""
+def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4", got_rows=None, dtype="bf16"):
+    """The one place bench.py uses the CPU oracle. Time it (as it stands) on the
+    whole workload, repeated until about `seconds` have passed (at least once);
+    and check the GPU's output rows `got_rows` (16-bit patterns of the first
+    rows) against the oracle's. Returns (baseline, parity sample)."""
+    import numpy as np
     import oracle.w4a4_ref as ref
     oracle_fn = ref.gemm_mxfp4_ref if fmt == "mxfp4" else ref.gemm_w4a4_ref
     try:
@@ -129,10 +134,18 @@ def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4") -> dict:
             break
     M, N, K, R = inputs["M"], inputs["N"], inputs["K"], inputs["R"]
     flops = (2 * M * N * K + 2 * M * R * N) * reps
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    base = {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"the full workload (M={M}, N={N}, K={K}, R={R}) {reps} times, {dt:.1f} s; "
                       f"float64 decode in numpy, dgemm on {threads} BLAS threads; "
                       f"{len(os.sched_getaffinity(0))} cores in the affinity mask, {cpu_model()}"}
+    parity = None
+    if got_rows is not None:
+        rows = np.arange(len(got_rows))
+        y, T = (ref.reference_rows_mx if fmt == "mxfp4" else ref.reference_rows)(inputs, rows)
+        chk = ref.check_output(got_rows, y, T, dtype)
+        parity = {"rows": int(len(rows)), "max_err_over_bound": round(chk["max_ratio"], 4),
+                  "ok": bool(chk["ok"])}
+    return base, parity
 
 
 def main() -> int:
@@ -262,12 +275,8 @@ def main() -> int:
     step()
     torch.cuda.synchronize()
 
-    # a sampled parity check of the timed output (first rows) against the oracle
-    import oracle.w4a4_ref as ref
-    rows = np.arange(min(16, wl.M))
-    y, T = (ref.reference_rows_mx if mx else ref.reference_rows)(x, rows)
-    got = out[:len(rows)].view(torch.int16).cpu().numpy().view(np.uint16)
-    chk = ref.check_output(got, y, T, a.dtype)
+    # its first rows, checked against the oracle in the CPU-baseline leg below
+    got_rows = out[:min(16, wl.M)].view(torch.int16).cpu().numpy().view(np.uint16)
 
     flops = wl.flops()
     ms_per_step = region_ms / a.steps
@@ -307,14 +316,13 @@ def main() -> int:
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "attainable": attain,
                      "kernel_source_sha256": kernel_source_hash(a.fmt)},
-        "parity_sample": {"rows": int(len(rows)), "max_err_over_bound": round(chk["max_ratio"], 4),
-                          "ok": chk["ok"]},
+        "parity_sample": None,
         "wall_s": round(wall, 3),
     }
     if a.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(x, a.cpu_seconds, a.fmt)
+        res["cpu_baseline"], res["parity_sample"] = cpu_baseline(x, a.cpu_seconds, a.fmt, got_rows, a.dtype)
     print(json.dumps(res), flush=True)
-    return 0 if chk["ok"] else 3
+    return 0 if res["parity_sample"] is None or res["parity_sample"]["ok"] else 3
 
 
 if __name__ == "__main__":
