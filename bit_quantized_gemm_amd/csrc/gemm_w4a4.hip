@@ -87,16 +87,46 @@ __device__ __forceinline__ u32x2 load_scales8(const uint8_t* sc, int kb, int KB,
   return u32x2{w[0], w[1]};
 }
 
+// Scale bytes where rows of the scale tensor are not 8-byte aligned
+// (M % 8 != 0): a 12-byte window of three dwords, loaded as it stands and
+// reduced to the eight bytes only when the scales are stored, an iteration
+// later, so no load result is waited for inside the K-loop. The tensor's base
+// and its size must be multiples of 4 bytes (the host checks this), and the
+// window start is clamped so that it never leaves the tensor: near the end the
+// eight bytes then begin further into the window, and bytes the window does
+// not hold belong to rows past `rows` (discarded outputs) only. Rows past
+// `rows` read clamped addresses.
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+struct ScaleWindow {
+  uint32_t start;   // byte offset of the window in the tensor (a multiple of 4)
+  uint32_t pos;     // offset of the first of the eight bytes in the window, 0 .. 11
+};
+__device__ __forceinline__ ScaleWindow scale_window(int kb, int KB, int r0, int rows) {
+  const uint32_t at = uint32_t(min(kb, KB - 1)) * uint32_t(rows) + uint32_t(min(r0, rows - 1));
+  const uint32_t start = min(at & ~3u, uint32_t(KB) * uint32_t(rows) - 12u);
+  return ScaleWindow{start, at - start};
+}
+__device__ __forceinline__ u32x2 window_bytes(u32x3_a4 v, uint32_t pos) {
+  const uint32_t q = pos >> 2, sh = (pos & 3u) * 8u;
+  const uint32_t a = q == 0 ? v.x : (q == 1 ? v.y : v.z);
+  const uint32_t b = q == 0 ? v.y : v.z;
+  return u32x2{__builtin_amdgcn_alignbit(b, a, sh), __builtin_amdgcn_alignbit(v.z, b, sh)};
+}
+
 // Two flavours per tile shape. The fast one (GENERAL = false) needs packed
-// rows that are a multiple of 16 bytes (K % 32 == 0), M % 8 == 0, N % 8 == 0,
-// R % 8 == 0, 8-byte aligned scales and 16-byte aligned LoRA operands: it
-// moves packed data in 16-byte DMA pieces, scales in 8-byte loads and LoRA
-// operands in 16-byte loads, with no per-lane branches. The general one takes
+// rows that are a multiple of 16 bytes (K % 32 == 0), N % 8 == 0, R % 8 == 0,
+// 8-byte aligned wgt scales and 16-byte aligned LoRA operands: it moves packed
+// data in 16-byte DMA pieces, scales in 8-byte loads (12-byte windows when
+// M % 8 != 0) and LoRA operands in
+// 16-byte loads, with no per-lane branches; ABYTE instantiates it with every
+// scale read through a 12-byte window (scale_window), for act scales whose rows
+// are not 8-byte aligned, so that aligned shapes run code without that path.
+// The general one takes
 // every valid shape: 4-byte DMA pieces (packed rows are always a multiple of
 // 8 bytes), scales byte by byte at the edges, LoRA operands element by element.
 // F16 selects the 16-bit type of the LoRA operands and of the output:
 // IEEE binary16 (true) or bfloat16 (false); both round to nearest even.
-template <class C, bool GENERAL, bool F16>
+template <class C, bool GENERAL, bool F16, bool ABYTE>
 __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4a4_kernel(
     const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
@@ -192,34 +222,49 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
                              : ((N & 7) == 0 && (reinterpret_cast<uintptr_t>(p.wscales) & 7u) == 0 &&
                                 n0 + C::BN <= N);
   // raw scale bytes (two k-blocks) of one stage: [0] in the loop, [1] too in the prologue
-  u32x2 s_raw[2][2] = {{{0u, 0u}, {0u, 0u}}, {{0u, 0u}, {0u, 0u}}};
+  // (ABYTE: 12-byte windows, see scale_window; both scale tensors, so that no
+  // thread branches on its role)
+  using RawT = std::conditional_t<ABYTE, u32x3_a4, u32x2>;
+  RawT s_raw[2][2] = {};
 
-  auto load_scale_half = [&](int st, u32x2 (&raw)[2], int e) __attribute__((always_inline)) {
+  auto load_scale_half = [&](int st, RawT (&raw)[2], int e) __attribute__((always_inline)) {
     const int kb = st * C::KBLK + 2 * s_kp + e;
     if constexpr (!GENERAL) {
       // rows % 8 == 0 and 8-byte aligned scales: a group of 8 rows is wholly
       // inside or wholly past the edge, where it re-reads the last group (its
       // rows only reach discarded outputs). Threads without a scale role read
       // a clamped address too and store nothing, so this load is unconditional.
-      raw[e] = *reinterpret_cast<const u32x2*>(s_src + uint32_t(min(kb, KB - 1)) * uint32_t(s_rows) +
-                                               uint32_t(min(s_r0, s_rows - 8)));
+      if constexpr (ABYTE) {
+        raw[e] = *reinterpret_cast<const u32x3_a4*>(s_src + scale_window(kb, KB, s_r0, s_rows).start);
+      } else {
+        raw[e] = *reinterpret_cast<const u32x2*>(s_src + uint32_t(min(kb, KB - 1)) * uint32_t(s_rows) +
+                                                 uint32_t(min(s_r0, s_rows - 8)));
+      }
     } else {
       if (s_is_a || s_is_b) raw[e] = load_scales8(s_src, kb, KB, s_r0, s_rows, s_fast);
     }
   };
-  auto load_scales = [&](int st, u32x2 (&raw)[2]) __attribute__((always_inline)) {
+  auto load_scales = [&](int st, RawT (&raw)[2]) __attribute__((always_inline)) {
     load_scale_half(st, raw, 0);
     load_scale_half(st, raw, 1);
   };
   // k-blocks past K get scale 0: their packed bytes (re-read from the row
   // start) then contribute exactly zero, since E2M1 values are finite.
   // Stored interleaved: row r of pair kp holds (scale of 2kp, scale of 2kp+1).
-  auto store_scales = [&](int st, int buf, const u32x2 (&raw)[2]) __attribute__((always_inline)) {
+  auto store_scales = [&](int st, int buf, const RawT (&raw)[2]) __attribute__((always_inline)) {
     if (s_is_a || s_is_b) {
       const int kb = st * C::KBLK + 2 * s_kp;
       const u32x2 zero = {0u, 0u};
-      const u32x4 h0 = e4m3x8_to_f16(kb < KB ? raw[0] : zero);
-      const u32x4 h1 = e4m3x8_to_f16(kb + 1 < KB ? raw[1] : zero);
+      u32x2 b0, b1;
+      if constexpr (ABYTE) {
+        b0 = window_bytes(raw[0], scale_window(kb, KB, s_r0, s_rows).pos);
+        b1 = window_bytes(raw[1], scale_window(kb + 1, KB, s_r0, s_rows).pos);
+      } else {
+        b0 = raw[0];
+        b1 = raw[1];
+      }
+      const u32x4 h0 = e4m3x8_to_f16(kb < KB ? b0 : zero);
+      const u32x4 h1 = e4m3x8_to_f16(kb + 1 < KB ? b1 : zero);
       uint8_t* dst = smem + (buf % C::STAGES) * C::STAGE_BYTES + s_off;
       const u32x4 lo = {__builtin_amdgcn_perm(h1.x, h0.x, 0x05040100u),
                         __builtin_amdgcn_perm(h1.x, h0.x, 0x07060302u),
@@ -447,15 +492,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 // ------------------------------------------------------------------ host side
 
 struct Variant {
-  void (*kernel[2][2])(const Params);   // [F16][fast] (see gemm_w4a4_kernel)
+  void (*kernel[2][3])(const Params);   // [F16][flavour: general, fast, fast with act scales byte by byte]
   int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
   double cost;   // time per output element of a full round, relative to 256x192
 };
 
 template <class C>
 constexpr Variant make_variant(double cost) {
-  return Variant{{{gemm_w4a4_kernel<C, true, false>, gemm_w4a4_kernel<C, false, false>},
-                  {gemm_w4a4_kernel<C, true, true>, gemm_w4a4_kernel<C, false, true>}},
+  return Variant{{{gemm_w4a4_kernel<C, true, false, false>, gemm_w4a4_kernel<C, false, false, false>,
+                   gemm_w4a4_kernel<C, false, false, true>},
+                  {gemm_w4a4_kernel<C, true, true, false>, gemm_w4a4_kernel<C, false, true, false>,
+                   gemm_w4a4_kernel<C, false, true, true>}},
                  C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
                  C::LDS_BYTES, C::STAGE_BYTES, C::OCC, cost};
 }
@@ -609,11 +656,18 @@ static int launch(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt
   prm.tiles_n = pl.tiles_n;
 
   const Variant& v = kVariants[pl.variant];
-  const bool fast = K % 32 == 0 && M % 8 == 0 && N % 8 == 0 &&
-                    ((uintptr_t(ascales) | uintptr_t(wscales)) & 7u) == 0 &&
+  // Flavour: fast where packed rows, wgt scales and LoRA operands allow wide
+  // accesses; within it, act scales in 8-byte loads when their rows are
+  // 8-byte aligned, else in 12-byte windows (needs a 4-byte aligned act-scale
+  // tensor of a multiple of 4 bytes, at least 12); general otherwise.
+  const bool fast = K % 32 == 0 && N % 8 == 0 && (uintptr_t(wscales) & 7u) == 0 &&
                     (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
+  const size_t a_bytes = Ks / 16 * Ms;
+  const bool a_rows8 = M % 8 == 0 && (uintptr_t(ascales) & 7u) == 0;
+  const bool a_window = (uintptr_t(ascales) & 3u) == 0 && a_bytes % 4 == 0 && a_bytes >= 12;
+  const int flavour = !fast ? 0 : a_rows8 ? 1 : a_window ? 2 : 0;
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][fast ? 1 : 0]),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][flavour]),
                                        dim3(pl.grid), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;

@@ -204,13 +204,15 @@ def test_solver_lds_matches_code_objects():
     meta = _code_object_metadata()
     assert meta, "no kernels found in the code object"
     # mangled tile configurations: w4a4::TileCfg (NVFP4) and w4a4::MxTileCfg (MXFP4)
-    cases = [(v, "7TileCfgI") for v in w4.variants("nvfp4")] + \
-            [(v, "9MxTileCfgI") for v in w4.variants("mxfp4")]
-    for v, tag in cases:
+    # instances per tile: NVFP4 {general, fast, fast with byte-wise act
+    # scales} x {bf16, fp16}; MXFP4 {general, fast} x {bf16, fp16}
+    cases = [(v, "7TileCfgI", 6) for v in w4.variants("nvfp4")] + \
+            [(v, "9MxTileCfgI", 4) for v in w4.variants("mxfp4")]
+    for v, tag, count in cases:
         key = tag + "Li%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
                                                   v["waves_n"], v["stages"])
         hits = [m for n, m in meta.items() if key in n]
-        assert len(hits) == 4, (key, list(meta))     # {fast, general} x {bf16, fp16}
+        assert len(hits) == count, (key, list(meta))
         for m in hits:
             assert int(m[".group_segment_fixed_size"]) == v["lds_bytes"], (key, m)
             assert int(m[".vgpr_spill_count"]) == 0, (key, m)

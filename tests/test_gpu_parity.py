@@ -248,7 +248,12 @@ EDGE = [(1, 1, 16, 0), (1, 5, 16, 1), (7, 33, 48, 3), (33, 200, 144, 16), (257, 
         # fast flavour (K % 32 == 0, M % 8 == 0, N % 8 == 0, R % 8 == 0):
         # edge tiles, several LoRA rank chunks, a last chunk only partly inside R
         (304, 200, 256, 40), (104, 3000, 512, 72), (136, 8, 32, 8), (64, 64, 384, 24),
-        (256, 200, 640, 16), (512, 384, 1024, 0)]
+        (256, 200, 640, 16), (512, 384, 1024, 0),
+        # fast flavour with M % 8 != 0 (act scales in 12-byte windows), the
+        # window clamped at the end of a tiny act-scale tensor; and M % 8 != 0
+        # where the act-scale tensor size is not a multiple of 4 (general)
+        (257, 200, 256, 32), (1001, 64, 128, 16), (259, 384, 512, 0), (3, 8, 64, 8), (5, 16, 64, 0),
+        (7, 8, 32, 8), (1001, 64, 96, 16), (1, 8, 64, 0)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
@@ -466,6 +471,47 @@ def test_256x128_instance_sampled(shape):
     rows = _sample_rows(M, 256, np.random.default_rng(11))
     y, T = ref.reference_rows(x, rows)
     assert_parity(got[rows], y, T, f"256x128 {shape}")
+
+
+# token counts that are not a multiple of 8 on the large tiles: the fast
+# flavour, with the act scales read byte by byte
+ODD_M = [(4095, 3072, 3072, 32), (4353, 3840, 3840, 128), (1001, 3072, 3072, 16)]
+
+
+@pytest.mark.parametrize("shape", ODD_M, ids=["x".join(map(str, s)) for s in ODD_M])
+def test_odd_m_sampled(shape):
+    M, N, K, R = shape
+    _say(f"case: M % 8 != 0 on the fast flavour, M={M} N={N} K={K} R={R}, sampled rows")
+    x = synthetic.custom_inputs(M, N, K, R, seed=M + 2 * N + K + R)
+    got = run_gpu(x)
+    plan = w4.plan(*shape)
+    rows = _sample_rows(M, plan["block_m"], np.random.default_rng(12))
+    y, T = ref.reference_rows(x, rows)
+    assert_parity(got[rows], y, T, f"odd M {shape}")
+
+
+@pytest.mark.parametrize("shift", [4, 1])
+def test_misaligned_act_scales(shift):
+    """Act scales at an address 4 bytes off 8-byte alignment (the fast flavour
+    reads them in 12-byte windows) or at an odd address (general flavour): the
+    same bytes as an aligned copy."""
+    M, N, K, R = 264, 200, 256, 32
+    _say(f"case: act scales at address offset {shift}, M={M} N={N} K={K} R={R}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=77)
+    d = to_device(x)
+    n = d["ascales"].numel()
+    buf = torch.zeros(n + shift, dtype=torch.uint8, device=DEV)
+    buf[shift:].copy_(d["ascales"].reshape(-1))
+    asc = buf[shift:].view(K // 16, M)
+    assert asc.data_ptr() % 8 == shift
+    out_a = w4.gemm_w4a4(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+                         d["lora_act_in"], d["lora_up"])
+    out_b = w4.gemm_w4a4(d["act"], asc, d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+                         d["lora_act_in"], d["lora_up"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    y, T = oracle_full(x)
+    assert_parity(out_b.view(torch.int16).cpu().numpy().view(np.uint16), y, T, f"act scales at offset {shift}")
 
 
 # Tensors just under the 2^31-byte limit the entry points accept (the kernels
