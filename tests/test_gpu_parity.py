@@ -331,7 +331,9 @@ def test_f16_zero_main_term_shows_lora_and_bias():
 
 
 F16_EDGE = [(1, 5, 16, 1), (7, 33, 48, 3), (257, 193, 272, 32), (300, 200, 256, 40),
-            (136, 8, 32, 8), (512, 384, 1024, 0)]
+            (136, 8, 32, 8), (512, 384, 1024, 0),
+            # M % 8 != 0 on the fast path (act scales in 12-byte windows)
+            (257, 200, 256, 32), (3, 8, 64, 8), (4095, 64, 128, 16)]
 
 
 @pytest.mark.parametrize("shape", F16_EDGE, ids=["x".join(map(str, s)) for s in F16_EDGE])
