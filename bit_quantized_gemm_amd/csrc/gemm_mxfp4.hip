@@ -144,6 +144,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     const int off = t < C::MI ? C::A_OFF : C::B_OFF;
     return *reinterpret_cast<const u32x4*>(stage + off + r * C::ROW_BYTES + (((2 * s + g) ^ swz(r)) << 4));
   };
+  // The fast flavour's two scale bytes of a stage for tile t (blocks g and
+  // 2+g), read into two registers; combined (scales_join) only where they are
+  // next used, so that no LDS read is waited for in the slot that issues it.
+  auto read_scale_bytes = [&](int st, int t, uint32_t& b0, uint32_t& b1) __attribute__((always_inline)) {
+    const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
+    const uint8_t* q = t < C::MI ? stage + C::SA_OFF + ra + 32 * t
+                                 : stage + C::SB_OFF + rb + 32 * (t - C::MI);
+    const int rows = t < C::MI ? C::BM : C::BN;
+    b0 = q[g * rows];
+    b1 = q[(2 + g) * rows];
+  };
   // The lane's two scale bytes of a stage (blocks g and 2+g) as bytes 0 and 1.
   auto read_scales = [&](int st, int t) __attribute__((always_inline)) {
     if constexpr (!GENERAL) {
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   EpiRegs epi_regs;
   epilogue_prefetch<C, GENERAL>(p, smem, tid, m0, n0, epi_regs);
   u32x4 O0[T], O1[T];
-  uint32_t SC[T], SCn[T];
+  uint32_t SC[T], SCn[T], SCh[T];   // SCh: the fast flavour's second scale bytes
 #pragma unroll
   for (int s = 0; s < PF; ++s)
 #pragma unroll
@@ -218,14 +229,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     wait_vm_lgkm0<(PF - 1) * DMA_N>();
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // k-step 1 of stage st; alongside: stage st+1's k-step 0 operands and scales
+    // k-step 1 of stage st; alongside: stage st+1's k-step 0 operands and
+    // scales (fast flavour: the scale bytes first, combined after the k-step)
     kstep.template operator()<1>(st, O1, SC, [&](int q) __attribute__((always_inline)) {
-      if (q < T) O0[q] = read_tile(st + 1, 0, q);
-      const int t = q - (G - T);
-      if (t >= 0 && t < T) SCn[t] = read_scales(st + 1, t);
+      if constexpr (GENERAL) {
+        if (q < T) O0[q] = read_tile(st + 1, 0, q);
+        const int t = q - (G - T);
+        if (t >= 0 && t < T) SCn[t] = read_scales(st + 1, t);
+      } else {
+        if (q < T) read_scale_bytes(st + 1, q, SCn[q], SCh[q]);
+        const int t = q - (G - T);
+        if (t >= 0 && t < T) O0[t] = read_tile(st + 1, 0, t);
+      }
     });
 #pragma unroll
-    for (int t = 0; t < T; ++t) SC[t] = SCn[t];
+    for (int t = 0; t < T; ++t) SC[t] = GENERAL ? SCn[t] : (SCn[t] | (SCh[t] << 8));
   }
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
