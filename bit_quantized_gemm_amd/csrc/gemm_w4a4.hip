@@ -9,7 +9,8 @@
 //    wgt moves HBM -> LDS by direct-to-LDS DMA (global_load_lds), 16-byte
 //    chunks XOR-swizzled by row so the consumer's LDS reads do not conflict.
 //    The stage's E4M3 scale tiles are loaded by the workgroup with coalesced
-//    8-byte loads, converted once to fp16 and stored [k-block][row] in LDS.
+//    8-byte loads (12-byte windows when M % 8 != 0), converted once to fp16
+//    and stored [k-block][row] in LDS.
 //    A stage's DMA is issued three iterations before it is consumed.
 //  * Decode: NVFP4 is exact in fp16. Every E2M1 value times every E4M3 scale
 //    has at most 6 significant bits and lies in [2^-10, 2688], so each operand
@@ -23,10 +24,11 @@
 //    The k <-> MFMA-slot assignment is free as long as both operands use the
 //    same one (the sum over k does not depend on its order), so a lane takes
 //    the 8 nibbles of one packed dword.
-//  * Epilogue: acc *= wcscale[n]; then the LoRA-up product runs as further
-//    k-steps of the same-shape MFMA (v_mfma_f32_32x32x16_bf16, identical
-//    accumulator layout) into the same accumulators; then + bias[n], bf16
-//    round-to-nearest-even, masked store of rows < M and columns < N.
+//  * Epilogue: acc = acc * wcscale[n] + bias[n] (one fp32 FMA); then the
+//    LoRA-up product runs as further k-steps of the same-shape MFMA
+//    (v_mfma_f32_32x32x16_bf16, identical accumulator layout) into the same
+//    accumulators; then bf16 round-to-nearest-even, masked store of rows < M
+//    and columns < N.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
