@@ -32,10 +32,11 @@ struct Params {
 };
 
 // 16-byte chunk c of a 64-byte row is stored at chunk position c ^ swz(row).
-// Without it rows r and r+2 (32 banks) or r and r+4 (64 banks) share banks
-// under the consumer's reads; this XOR spreads 8 (or 16) consecutive rows of
-// one chunk over distinct bank groups.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// The consumers read one 16-byte chunk of each of 32 consecutive rows per
+// half-wave (ds_read_b128). Measured with the LDS bank-conflict counter on
+// gfx950: unswizzled rows cost 12 extra cycles per such read, an XOR by row
+// bits 1-2 or 1^3,2^4 still 4, and an XOR by row bits 2-3 none.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // s_waitcnt vmcnt(VM) lgkmcnt(0), gfx9 encoding (vmcnt split over bits 3:0 and 15:14).
 template <int VM>

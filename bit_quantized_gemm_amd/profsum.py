@@ -156,19 +156,39 @@ def traffic(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+# rocprofv3's derived metrics used here, as its counter listing defines them
+# (sums over the device, GRBM_GUI_ACTIVE the maximum over its instances).
+DERIVED = {
+    "MfmaUtil": "100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMD count): % of SIMD time the matrix core is busy",
+    "VALUBusy": "100 * SQ_ACTIVE_INST_VALU / (CU count * GRBM_GUI_ACTIVE): % of time vector ALU instructions are processed",
+    "LDSBankConflict": "100 * SQ_LDS_BANK_CONFLICT / (GRBM_GUI_ACTIVE * CU count): % of time the LDS stalls on bank conflicts",
+    "LdsUtil": "100 * SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * CU count): % of time the LDS is busy",
+    "LdsBankConflict": "SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT): conflict cycles per LDS access cycle",
+}
+
+
 def counters(args) -> str:
     tag, name, _ = KERNELS[args.fmt]
     runs = _per_dispatch(args.dir)
     g = [v for n, v in runs.values() if tag in n]
     names = sorted(g[0]) if g else []
-    lines = [f"# {name} SQ/GRBM counters, {args.workload} workload", "",
+    derived = bool(names) and all(c in DERIVED for c in names)
+    title = "rocprofv3 derived metrics" if derived else "SQ/GRBM counters"
+    what = ("values as rocprofv3 computes them per dispatch" if derived
+            else "values summed over the device")
+    lines = [f"# {name} {title}, {args.workload} workload", "",
              "Command (repository root, one MI355X, library built in-tree):", "",
              f"    {args.command}", "",
              f"Kernel source sha256[:16]: {kernel_source_hash(args.fmt)}", "",
-             f"Median over {len(g)} dispatches (values summed over the device):", "",
-             "| Counter | Value |", "|---|---|"]
-    for c in names:
-        lines.append(f"| {c} | {statistics.median(v[c] for v in g):.0f} |")
+             f"Median over {len(g)} dispatches ({what}):", ""]
+    if derived:
+        lines += ["| Metric | Value | Definition |", "|---|---|---|"]
+        for c in names:
+            lines.append(f"| {c} | {statistics.median(v[c] for v in g):.3f} | {DERIVED[c]} |")
+    else:
+        lines += ["| Counter | Value |", "|---|---|"]
+        for c in names:
+            lines.append(f"| {c} | {statistics.median(v[c] for v in g):.0f} |")
     return "\n".join(lines) + "\n"
 
 

@@ -134,3 +134,19 @@ def test_bench_refuses_more_than_one_gpu(gpus):
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_counters_labels_rocprof_derived_metrics(tmp_path):
+    d = tmp_path / "D"
+    d.mkdir()
+    rows = []
+    for i, (mu, vb) in enumerate([(47.0, 40.0), (48.0, 42.0), (49.0, 44.0)]):
+        rows += [{"Dispatch_Id": 2 + i, "Kernel_Name": KNAME, "Counter_Name": "MfmaUtil", "Counter_Value": mu},
+                 {"Dispatch_Id": 2 + i, "Kernel_Name": KNAME, "Counter_Name": "VALUBusy", "Counter_Value": vb}]
+    _write_csv(d / "pmc_counter_collection.csv", rows)
+    out = subprocess.run([sys.executable, "-m", "bit_quantized_gemm_amd.profsum", "counters", str(d),
+                          "--workload", "qkv", "--command", "cmd"], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout
+    assert "derived metrics" in out and "Median over 3 dispatches" in out
+    assert "| MfmaUtil | 48.000 | 100 * SQ_VALU_MFMA_BUSY_CYCLES" in out
+    assert "| VALUBusy | 42.000 |" in out
