@@ -108,6 +108,39 @@ def attainable_peak(w4, kind: int, dev, stream, iters: int = 2048, reps: int = 1
     return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_mhz": round(mhz, 1)}
 
 
+def route_rates(w4, dev, stream, blocks: int, reps: int = 10) -> dict:
+    """The per-block arithmetic of both ways to run NVFP4 on the matrix cores
+    (gemm_w4a4_route_core): route 0 decodes to fp16 for the fp16 MFMA (what
+    gemm_w4a4 does), route 1 feeds the scaled FP4 MFMA one 16-k block at a
+    time and applies the scale product to each partial on the vector ALU.
+    Register-resident operands, every SIMD busy; `blocks` 16-k blocks per wave."""
+    import numpy as np
+    import torch
+    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=dev)
+    out = {}
+    for route in (0, 1):
+        call = lambda: w4.route_core_raw(route, blocks, clocks.data_ptr(), stream.cuda_stream)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:   # settle the clock under this load
+            if call() != 0:
+                raise RuntimeError("gemm_w4a4_route_core failed")
+            torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        flops = w4.PEAK_GROUPS * 4 * blocks * w4.ROUTE_FLOP_PER_BLOCK
+        out[f"route_{route}"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                                 "cycles_per_block": round(float(np.median(c[:, 0])) / blocks, 1),
+                                 "clock_mhz": round(float(np.median(c[:, 0] / (c[:, 1] / 100.0))), 1)}
+    out["route_1_over_route_0_time"] = round(out["route_1"]["ms"] / out["route_0"]["ms"], 3)
+    return out
+
+
 def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4", got_rows=None, dtype="bf16"):
     """The one place bench.py uses the CPU oracle. Time it (as it stands) on the
     whole workload, repeated until about `seconds` have passed (at least once);
@@ -170,6 +203,9 @@ def main() -> int:
                     help="rotate input copies so that no launch finds its operands in the Infinity Cache")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter scale probe)")
+    ap.add_argument("--routes", action="store_true",
+                    help="instead of the GEMM: the per-block arithmetic of the decode + fp16 MFMA route "
+                         "and of the scaled-FP4-MFMA route, for the workload's K/16 blocks per wave")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -191,6 +227,14 @@ def main() -> int:
         wl = synthetic.Workload(f"custom_{M}x{N}x{K}_r{R}", M, N, K, R, seed=2000)
     else:
         wl = synthetic.workload(a.workload)
+    if a.routes:
+        blocks = wl.K // 16
+        rates = route_rates(w4, torch.device("cuda:0"), torch.cuda.current_stream(), blocks)
+        print(json.dumps({"metric": "NVFP4 block arithmetic per route (no memory traffic), TFLOP/s",
+                          "config": {"workload": wl.name, "blocks_per_wave": blocks,
+                                     "waves": w4.PEAK_GROUPS * 4, "wave_tile": "128x96"},
+                          **rates}))
+        return 0
     mx = a.fmt == "mxfp4"
     x = synthetic.make_inputs(wl, dtype=a.dtype, fmt=a.fmt)
     if a.ceiling:

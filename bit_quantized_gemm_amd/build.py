@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgemm_w4a4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, f) for f in ("gemm_w4a4.hip", "gemm_mxfp4.hip", "mfma_peak.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gemm_w4a4.hip", "gemm_mxfp4.hip", "mfma_peak.hip", "route_probe.hip")]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,230 @@
+// route_probe.hip — measurement aid, not part of the operator: the two ways of
+// running NVFP4's block-scaled product on gfx950's matrix cores, side by side.
+//
+// The SVDQuant W4A4 on Blackwell page (section 3.1) fixes NVFP4 as E2M1 values
+// with one E4M3 scale per 16 values of k, and the product as the sum over the
+// scale blocks of (scale_a * scale_w) * (the block's dot product). gfx950 has
+// two candidate instructions:
+//   route A  decode each E2M1 value times its block scale to fp16 (exact: at
+//            most 6 significant bits) and run v_mfma_f32_32x32x16_f16, one
+//            16-k block per MFMA; the scale is inside the operands. This is
+//            what gemm_w4a4 does.
+//   route B  feed the raw E2M1 nibbles to the scaled FP4 MFMA
+//            (v_mfma_scale_f32_32x32x64_f8f6f4). Its scales are E8M0 per 32 k,
+//            which cannot express an E4M3 scale per 16 k, so an exact route B
+//            puts one 16-k block into 16 of the 64 k slots (the rest zero,
+//            E8M0 scale 1.0), gets a fresh partial sum per block and adds it
+//            with the product of the two block scales on the vector ALU: one
+//            multiply and one FMA per accumulator element per block.
+//
+// route_core_kernel runs either route's per-block work for a wave's 4 x 3
+// tiles of 32x32 (the gemm_w4a4 wave tile) on register-resident operands,
+// on every SIMD of the chip, so the two rates compare the arithmetic alone.
+// route_b_tile_kernel computes one real 32x32 tile by route B, so that its
+// exactness can be checked against the float64 reference.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "gemm_w4a4.h"
+#include "w4a4_common.hpp"
+#include "w4a4_host.hpp"
+
+namespace w4a4 {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteMI = 4, kRouteNI = 3;   // act and wgt 32-row tiles per wave
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+// The scaled FP4 MFMA with both E8M0 scales 1.0 (byte 127): D = C + A B over
+// 64 k, A the wgt rows (n), B the act rows (m), as in the GEMM kernels.
+__device__ __forceinline__ f32x16 mfma_fp4_unscaled(u32x4 a, u32x4 b, f32x16 c) {
+  const v8i_t av = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
+  const v8i_t bv = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, 127, 0, 127);
+}
+
+// One E4M3 byte (bits 0..7 of b) as float; exact (the conversion applies only
+// the exponent of its scale operand, and 1.0 has exponent 0).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return float(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false)[0]);
+}
+
+template <int ROUTE>
+__global__ __launch_bounds__(kRouteThreads, 1) void route_core_kernel(int blocks, uint64_t* clocks) {
+  constexpr int T = kRouteMI + kRouteNI;
+  const int tid = threadIdx.x;
+  const int g = (tid >> 5) & 1;
+  const uint32_t seed = 0x9e3779b9u * uint32_t(tid + 1);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x16 acc[kRouteNI][kRouteMI];
+#pragma unroll
+  for (int j = 0; j < kRouteNI; ++j)
+#pragma unroll
+    for (int i = 0; i < kRouteMI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+  // Per-tile operand words and scales, register-resident. Every block XORs a
+  // block-dependent (scalar) pattern into the words it uses, so nothing can
+  // be hoisted out of the loop; the real kernels read these from LDS instead.
+  uint32_t w[T][2];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    w[t][0] = (seed * uint32_t(2 * t + 3)) & 0x77777777u;   // E2M1 codes, no sign
+    w[t][1] = (seed * uint32_t(2 * t + 5)) & 0x77777777u;
+  }
+  // route A: fp16 block-scale pairs (as the kernel keeps them in LDS)
+  uint32_t sh[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) sh[t] = 0x3c003c00u ^ ((seed >> t) & 0x00ff00ffu);
+  // route B: E4M3 scales; act: one per lane and act tile (4 in one dword);
+  // wgt: one per accumulator row, 16 per wgt tile (four dwords)
+  const uint32_t sba = 0x38383838u ^ (seed & 0x07070707u);
+  uint32_t sbw[kRouteNI][4];
+#pragma unroll
+  for (int j = 0; j < kRouteNI; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sbw[j][q] = 0x38383838u ^ ((seed >> (j + q)) & 0x07070707u);
+  const uint32_t keep = g == 0 ? ~0u : 0u;   // route B: k slots of lane half 0 only
+
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int b = 0; b < blocks; ++b) {
+    const uint32_t x = uint32_t(b & 7) * 0x01010101u;
+    if constexpr (ROUTE == 0) {
+      // decode: 8 values of one 16-k block per lane and tile (4 conversions,
+      // 4 packed multiplies by the fp16 block scale), then 12 MFMAs
+      f16x8 d[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t v = w[t][0] ^ x;
+        const _Float16 s = __builtin_bit_cast(f16x2, sh[t] ^ (x & 0x00070007u))[0];
+        const f16x2 ss = {s, s};
+        const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0) * ss;
+        const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1) * ss;
+        const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2) * ss;
+        const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3) * ss;
+        d[t] = f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+      }
+#pragma unroll
+      for (int j = 0; j < kRouteNI; ++j)
+#pragma unroll
+        for (int i = 0; i < kRouteMI; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d[kRouteMI + j], d[i], acc[j][i], 0, 0, 0);
+    } else {
+      // raw nibbles in k slots 0..15, a fresh partial per tile, then
+      // acc += P * (sa[m] * sw[n]): sa one value per lane (its column m), sw
+      // one per accumulator row n
+      u32x4 o[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) o[t] = u32x4{(w[t][0] ^ x) & keep, (w[t][1] ^ x) & keep, 0u, 0u};
+      float sa[kRouteMI], sw[kRouteNI][16];
+      {
+        const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sba ^ x, 1.0f, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sba ^ x, 1.0f, true);
+        sa[0] = lo[0];
+        sa[1] = lo[1];
+        sa[2] = hi[0];
+        sa[3] = hi[1];
+      }
+#pragma unroll
+      for (int j = 0; j < kRouteNI; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbw[j][q] ^ x, 1.0f, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbw[j][q] ^ x, 1.0f, true);
+          sw[j][4 * q] = lo[0];
+          sw[j][4 * q + 1] = lo[1];
+          sw[j][4 * q + 2] = hi[0];
+          sw[j][4 * q + 3] = hi[1];
+        }
+      f32x16 zero;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kRouteNI; ++j)
+#pragma unroll
+        for (int i = 0; i < kRouteMI; ++i) {
+          const f32x16 P = mfma_fp4_unscaled(o[kRouteMI + j], o[i], zero);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(P[r], sa[i] * sw[j][r], acc[j][i][r]);
+        }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kRouteNI; ++j)
+#pragma unroll
+    for (int i = 0; i < kRouteMI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[j][i][r];
+  if (tid == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    // keeps the work alive: a sum equal to this value does not occur
+    clocks[2 * blockIdx.x + 1] = (sum == 1.2345e-30f) ? 0 : r1 - r0;
+  }
+}
+
+// One 32x32 tile by route B: out[m][n] = sum over blocks b of
+// sa[b][m] * sw[b][n] * (sum over the block's 16 k of a[m][k] * w[n][k]).
+// act, wgt [32][K/2] packed (two E2M1 codes a byte, low nibble first);
+// ascales, wscales [K/16][32] E4M3; one wave.
+__global__ __launch_bounds__(64) void route_b_tile_kernel(const uint8_t* act, const uint8_t* ascales,
+                                                          const uint8_t* wgt, const uint8_t* wscales,
+                                                          float* out, int K) {
+  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+  const int KB = K / 16, rowbytes = K / 2;
+  f32x16 acc, zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = zero[r] = 0.0f;
+  const uint32_t* arow = reinterpret_cast<const uint32_t*>(act + l32 * rowbytes);
+  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(wgt + l32 * rowbytes);
+  for (int b = 0; b < KB; ++b) {
+    // block b's 16 codes (8 bytes) in k slots 0..15: lane half 0, first two dwords
+    const u32x4 a = g == 0 ? u32x4{arow[2 * b], arow[2 * b + 1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 w = g == 0 ? u32x4{wrow[2 * b], wrow[2 * b + 1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+    const f32x16 P = mfma_fp4_unscaled(w, a, zero);
+    const float sa = e4m3_to_f32(ascales[b * 32 + l32]);   // column m = l32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = 8 * (r >> 2) + 4 * g + (r & 3);   // the accumulator's row of element r
+      acc[r] = __builtin_fmaf(P[r], sa * e4m3_to_f32(wscales[b * 32 + n]), acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) out[l32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3)] = acc[r];
+}
+
+}  // namespace w4a4
+
+using namespace w4a4;
+
+extern "C" int gemm_w4a4_route_core(int route, int blocks, uint64_t* clocks, void* stream) {
+  if (route < 0 || route > 1 || blocks < 1 || !clocks) return GEMM_W4A4_EINVAL;
+  if (reinterpret_cast<uintptr_t>(clocks) & 7u) return GEMM_W4A4_EALIGN;
+  const int dev_rc = check_device();
+  if (dev_rc != GEMM_W4A4_OK) return dev_rc;
+  void (*k)(int, uint64_t*) = route == 0 ? route_core_kernel<0> : route_core_kernel<1>;
+  void* args[] = {&blocks, &clocks};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(GEMM_W4A4_PEAK_GROUPS),
+                                       dim3(kRouteThreads), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}
+
+extern "C" int gemm_w4a4_route_b_tile(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+                                      const uint8_t* wscales, float* out, int K, void* stream) {
+  if (!act || !ascales || !wgt || !wscales || !out || K < 16 || K % 16 != 0 || K > GEMM_W4A4_ROUTE_B_MAX_K)
+    return GEMM_W4A4_EINVAL;
+  if (((reinterpret_cast<uintptr_t>(act) | reinterpret_cast<uintptr_t>(wgt) |
+        reinterpret_cast<uintptr_t>(out)) & 3u) != 0)
+    return GEMM_W4A4_EALIGN;
+  const int dev_rc = check_device();
+  if (dev_rc != GEMM_W4A4_OK) return dev_rc;
+  void* args[] = {&act, &ascales, &wgt, &wscales, &out, &K};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(route_b_tile_kernel), dim3(1), dim3(64),
+                                       args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}

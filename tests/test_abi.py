@@ -229,3 +229,24 @@ def test_solver_lds_matches_code_objects():
     (1, 16, 0, w4.EINVAL), (2, 16, 0x1004, w4.EALIGN)])
 def test_mfma_peak_validation(kind, iters, clocks, want):
     assert w4.mfma_peak_raw(kind, iters, clocks, 0) == want
+
+
+@pytest.mark.parametrize("route,blocks,clocks,want", [
+    (2, 16, 0x1000, w4.EINVAL), (-1, 16, 0x1000, w4.EINVAL), (0, 0, 0x1000, w4.EINVAL),
+    (1, 16, 0, w4.EINVAL), (0, 16, 0x1004, w4.EALIGN)])
+def test_route_core_validation(route, blocks, clocks, want):
+    assert w4.route_core_raw(route, blocks, clocks, 0) == want
+
+
+_TILE = (0x1000, 0x2000, 0x3000, 0x4000, 0x5000)   # act, ascales, wgt, wscales, out
+
+
+@pytest.mark.parametrize("ptrs,K,want", [
+    (_TILE, 8, w4.EINVAL), (_TILE, 24, w4.EINVAL), (_TILE, 0, w4.EINVAL),
+    (_TILE, 65536 + 16, w4.EINVAL),
+    ((0,) + _TILE[1:], 64, w4.EINVAL), (_TILE[:4] + (0,), 64, w4.EINVAL),
+    (_TILE[:1] + (0,) + _TILE[2:], 64, w4.EINVAL),
+    ((0x1002,) + _TILE[1:], 64, w4.EALIGN), (_TILE[:2] + (0x3001,) + _TILE[3:], 64, w4.EALIGN),
+    (_TILE[:4] + (0x5002,), 64, w4.EALIGN)])
+def test_route_b_tile_validation(ptrs, K, want):
+    assert w4.route_b_tile_raw(*ptrs, K, 0) == want
