@@ -52,12 +52,21 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, SEL, int(sa), SEL, int(sb));
 }
 
+// The act-scale windows of the AWIN flavour (k-block rows of BM + 4 bytes)
+// fit in the stage's scale DMA rounds.
+template <class C>
+constexpr bool kAwinRoom = C::KBLK * (C::BM + 4 + C::BN) <= C::SCALE_ROUNDS * C::THREADS * 4;
+
 // GENERAL = false (fast): K % 128 == 0, M % 4 == 0, N % 8 == 0, 4-byte aligned scales and
 // the LoRA conditions of the shared epilogue's fast path (R % 8 == 0, 16-byte
 // aligned LoRA operands); scales move by DMA into LDS. GENERAL = true: any
 // valid shape; each lane loads its own scale bytes one stage ahead.
 // F16: LoRA operands and output in binary16 (else bfloat16).
-template <class C, bool GENERAL, bool F16>
+// AWIN (fast flavour, any M): each k-block row of act scales moves as a window
+// of BM + 4 bytes from the 4-byte boundary at or below its first byte, so
+// that its 4-byte DMA pieces stay aligned when M % 4 != 0; the reader adds the
+// row's offset into its window (see act_window).
+template <class C, bool GENERAL, bool F16, bool AWIN = false>
 __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mxfp4_kernel(
     const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
@@ -107,6 +116,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     const uint8_t* src = (is_b ? p.wgt : p.act) + (uint32_t(row) * uint32_t(rowbytes) + kin);
     dma<16>(src, stage + (u * C::THREADS + wave_u * 64) * 16);
   };
+  // ---- act-scale windows (AWIN). Row stride of the act scales in LDS: BM,
+  // or BM + 4 with windows; the wgt scales follow the act ones.
+  constexpr int SW = AWIN ? C::BM + 4 : C::BM;
+  constexpr int SB_OFF = C::SA_OFF + C::KBLK * SW;
+  static_assert(!AWIN || kAwinRoom<C>, "act-scale windows need room in the stage's scale area");
+  // Start of k-block kb's window: the 4-byte boundary at or below its first
+  // byte (kb*M + m0), clamped so that the window ends inside the tensor (the
+  // host requires KB*M >= SW; KB*M % 4 == 0 as K % 128 == 0). The tile's
+  // valid rows then always lie inside the window.
+  auto act_window = [&](int kb) __attribute__((always_inline)) {
+    const uint32_t first = uint32_t(kb) * uint32_t(M) + uint32_t(m0);
+    return min(first & ~3u, uint32_t(KB) * uint32_t(M) - uint32_t(SW));
+  };
+  // Offset of the tile's row 0 in the window of k-block kb (clamped as the DMA).
+  auto act_shift = [&](int kb) __attribute__((always_inline)) {
+    const int k = min(kb, KB - 1);
+    return int(uint32_t(k) * uint32_t(M) + uint32_t(m0) - act_window(k));
+  };
   // ---- scale DMA (fast flavour): 4-byte pieces = 4 consecutive rows of one
   // k-block, the global [K/32][rows] order kept: [4][BM] act then [4][BN]
   // wgt. Blocks past K read the last block (their data is masked); rows past
@@ -116,11 +143,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
     const int o = (v * C::THREADS + tid) * 4;
     const uint8_t* src;
-    if (o < C::KBLK * C::BM) {
-      const int kb = min(st * C::KBLK + o / C::BM, KB - 1);
-      src = p.ascales + uint32_t(kb) * uint32_t(M) + uint32_t(min(m0 + o % C::BM, M - 4));
+    if (o < C::KBLK * SW) {
+      const int kb = min(st * C::KBLK + o / SW, KB - 1);
+      if constexpr (AWIN)
+        src = p.ascales + act_window(kb) + uint32_t(o % SW);
+      else
+        src = p.ascales + uint32_t(kb) * uint32_t(M) + uint32_t(min(m0 + o % C::BM, M - 4));
     } else {
-      const int ob = min(o - C::KBLK * C::BM, C::KBLK * C::BN - 4);
+      const int ob = min(o - C::KBLK * SW, C::KBLK * C::BN - 4);
       const int kb = min(st * C::KBLK + ob / C::BN, KB - 1);
       src = p.wscales + uint32_t(kb) * uint32_t(N) + uint32_t(min(n0 + ob % C::BN, N - 4));
     }
@@ -149,8 +179,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   // next used, so that no LDS read is waited for in the slot that issues it.
   auto read_scale_bytes = [&](int st, int t, uint32_t& b0, uint32_t& b1) __attribute__((always_inline)) {
     const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
+    if (AWIN && t < C::MI) {
+      const uint8_t* q = stage + C::SA_OFF + ra + 32 * t;
+      b0 = q[g * SW + act_shift(st * C::KBLK + g)];
+      b1 = q[(2 + g) * SW + act_shift(st * C::KBLK + 2 + g)];
+      return;
+    }
     const uint8_t* q = t < C::MI ? stage + C::SA_OFF + ra + 32 * t
-                                 : stage + C::SB_OFF + rb + 32 * (t - C::MI);
+                                 : stage + SB_OFF + rb + 32 * (t - C::MI);
     const int rows = t < C::MI ? C::BM : C::BN;
     b0 = q[g * rows];
     b1 = q[(2 + g) * rows];
@@ -158,11 +194,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   // The lane's two scale bytes of a stage (blocks g and 2+g) as bytes 0 and 1.
   auto read_scales = [&](int st, int t) __attribute__((always_inline)) {
     if constexpr (!GENERAL) {
-      const uint8_t* stage = smem + (st % C::STAGES) * C::STAGE_BYTES;
-      const uint8_t* q = t < C::MI ? stage + C::SA_OFF + ra + 32 * t
-                                   : stage + C::SB_OFF + rb + 32 * (t - C::MI);
-      const int rows = t < C::MI ? C::BM : C::BN;
-      return uint32_t(q[g * rows]) | (uint32_t(q[(2 + g) * rows]) << 8);
+      uint32_t b0, b1;
+      read_scale_bytes(st, t, b0, b1);
+      return b0 | (b1 << 8);
     } else {
       const bool is_a = t < C::MI;
       const uint8_t* src = is_a ? p.ascales : p.wscales;
@@ -253,15 +287,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
 // ------------------------------------------------------------------ host side
 
 struct MxVariant {
-  void (*kernel[2][2])(const Params);   // [F16][fast]
+  void (*kernel[2][3])(const Params);   // [F16][flavour: general, fast, fast with act-scale windows]
+  bool awin;                            // the third flavour exists (room for the windows)
   int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
 };
 
 template <class C>
 constexpr MxVariant make_mx_variant() {
-  return MxVariant{{{gemm_mxfp4_kernel<C, true, false>, gemm_mxfp4_kernel<C, false, false>},
-                    {gemm_mxfp4_kernel<C, true, true>, gemm_mxfp4_kernel<C, false, true>}},
-                   C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
+  return MxVariant{{{gemm_mxfp4_kernel<C, true, false>, gemm_mxfp4_kernel<C, false, false>,
+                     gemm_mxfp4_kernel<C, false, false, kAwinRoom<C>>},
+                    {gemm_mxfp4_kernel<C, true, true>, gemm_mxfp4_kernel<C, false, true>,
+                     gemm_mxfp4_kernel<C, false, true, kAwinRoom<C>>}},
+                   kAwinRoom<C>, C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
                    C::LDS_BYTES, C::STAGE_BYTES, C::OCC};
 }
 
@@ -372,11 +409,15 @@ static int mx_launch(const uint8_t* act, const uint8_t* ascales, const uint8_t* 
   prm.tiles_n = pl.tiles_n;
 
   const MxVariant& v = kMxVariants[pl.variant];
-  const bool fast = K % 128 == 0 && M % 4 == 0 && N % 8 == 0 &&
+  const bool fast = K % 128 == 0 && N % 8 == 0 &&
                     ((uintptr_t(ascales) | uintptr_t(wscales)) & 3u) == 0 &&
                     (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
+  // M % 4 != 0: act-scale windows where the tile has room for them and the
+  // tensor holds at least one window (K/32 * M >= BM + 4)
+  const bool awin = v.awin && int64_t(K / 32) * M >= v.block_m + 4;
+  const int flavour = !fast ? 0 : M % 4 == 0 ? 1 : awin ? 2 : 0;
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][fast ? 1 : 0]),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][flavour]),
                                        dim3(pl.grid), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;

@@ -297,3 +297,24 @@ def test_mx_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
     rows = _sample_rows(M, 256, np.random.default_rng(15))
     y, T = ref.reference_rows_mx(x, rows)
     assert_parity(got[rows], y, T, f"mx side chunk R={R} {dtype}", dtype)
+
+
+MX_ODD_M = [((4095, 3072, 3072, 32), "bf16"), ((4093, 3072, 512, 16), "bf16"),
+            ((4353, 3840, 3840, 128), "bf16"), ((4095, 3072, 512, 8), "f16")]
+
+
+@pytest.mark.parametrize("shape,dtype", MX_ODD_M, ids=["x".join(map(str, s)) + "-" + d for s, d in MX_ODD_M])
+def test_mx_odd_m_act_scale_windows_sampled(shape, dtype):
+    """M % 4 != 0 on the 256x192 tile: the fast flavour reads each k-block row
+    of act scales through a 4-byte aligned window (the last one clamped to
+    the tensor's end), every row offset into it different."""
+    M, N, K, R = shape
+    plan = w4.plan(*shape, fmt="mxfp4")
+    assert (plan["block_m"], plan["block_n"]) == (256, 192)
+    _say(f"case: MXFP4 odd M with act-scale windows {shape} {dtype}")
+    x = mx_inputs(M, N, K, R, seed=M + K + R, dtype=dtype)
+    got = run_mx(x)
+    rows = np.unique(np.concatenate([_sample_rows(M, 256, np.random.default_rng(M)),
+                                     np.arange(M - 5, M), np.arange(0, 3)]))
+    y, T = ref.reference_rows_mx(x, rows)
+    assert_parity(got[rows], y, T, f"mx odd M {shape} {dtype}", dtype)
