@@ -385,6 +385,99 @@ def pin_checker():
     assert not ref.check_output(ref.bf16_rne_bits(no_lora), y, T)["ok"]
 
 
+# ------------------------------------------------------------ the tolerance side: T, the bound, sampled rows
+
+def brute_force_T(x, dtype="bf16"):
+    """Exact T = |wc| * sum_k |a w| + |bias| + sum_r |la lu| from element loops over
+    rational numbers (golden E2M1 table, torch's E4M3 / binary16 decoders), one
+    (m, n, k) and (m, n, r) at a time; NVFP4 operands."""
+    M, N, K, R = x["M"], x["N"], x["K"], x["R"]
+    half = torch.float16 if dtype == "f16" else torch.bfloat16
+    la = torch.from_numpy(x["lora_act_in"].view(np.int16)).view(half).to(torch.float64).numpy()
+    lu = torch.from_numpy(x["lora_up"].view(np.int16)).view(half).to(torch.float64).numpy()
+    T = np.empty((M, N), dtype=object)
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                ca = (int(x["act"][m, k // 2]) >> (4 * (k % 2))) & 15
+                cw = (int(x["wgt"][n, k // 2]) >> (4 * (k % 2))) & 15
+                a = _frac(_E2M1_GOLD[ca]) * _frac(_E4M3_TORCH[x["ascales"][k // 16, m]])
+                w = _frac(_E2M1_GOLD[cw]) * _frac(_E4M3_TORCH[x["wscales"][k // 16, n]])
+                s += abs(a * w)
+            lora = Fraction(0)
+            for r in range(R):
+                lora += abs(_frac(float(la[m, r])) * _frac(float(lu[r, n])))
+            T[m, n] = abs(_frac(float(x["wcscale"][n]))) * s + abs(_frac(float(x["bias"][n]))) + lora
+    return T
+
+
+def _assert_T_close(got, exact, what):
+    # every term is >= 0, so the float64 sums only round (relative 2^-52 per addition)
+    for idx in np.ndindex(*got.shape):
+        assert abs(Fraction(float(got[idx])) - exact[idx]) <= Fraction(2) ** -40 * exact[idx], \
+            (what, idx, float(got[idx]), float(exact[idx]))
+
+
+def pin_term_magnitude_bruteforce():
+    """term_magnitude == exact rational sum of |terms| on tiny shapes, with negative
+    wcscale and bias, LoRA ranks 1 and 3, both 16-bit LoRA types."""
+    for (M, N, K, R, seed, dtype) in [(3, 2, 32, 3, 21, "bf16"), (2, 4, 48, 1, 22, "bf16"),
+                                      (4, 3, 32, 3, 23, "f16")]:
+        x = synthetic.custom_inputs(M, N, K, R, seed=seed, dtype=dtype)
+        x["wcscale"][0] = -x["wcscale"][0]          # |wcscale|, not wcscale
+        x["bias"][:] = -np.abs(x["bias"])           # |bias|, not bias
+        T = ref.term_magnitude(*_args(x), dtype=dtype)
+        _assert_T_close(T, brute_force_T(x, dtype), (M, N, K, R, dtype))
+
+
+def pin_term_magnitude_structured():
+    """T for constant inputs in closed form: every main term is a*sa*w*sw (signs
+    alternating over k, so the signed sum is 0 and T is not), plus |bias| and R|la lu|."""
+    M, N, K, R = 3, 4, 32, 2
+    x = _const_inputs(M, N, K, R, 2, 2, 0x38, 0x40, 0x3F00, 0xBE80)   # a=1, sa=1, w=1, sw=2
+    x["act"][:] = 0xA2          # even k: +1.0, odd k: -1.0 (code 10 = -1.0)
+    x["wcscale"][:] = -0.5
+    T = ref.term_magnitude(*_args(x))
+    y = _y(x)
+    want_T = 0.5 * K * 2.0 + np.abs(x["bias"].astype(np.float64))[None, :] + R * 0.5 * 0.25
+    assert np.array_equal(T, np.broadcast_to(want_T, (M, N))), (T, want_T)
+    want_y = x["bias"].astype(np.float64)[None, :] + R * 0.5 * -0.25
+    assert np.array_equal(y, np.broadcast_to(want_y, (M, N)))
+
+
+def pin_tolerance_golden():
+    """check_output's verdict on hand-derived cases at the edge of 4e-3*T + 1 ulp."""
+    for row in _golden_rows("tolerance_cases.txt"):
+        typ, y_e, T_e, got_e, verdict = row[:5]
+        y_ref = float(eval(y_e, {"__builtins__": {}}))
+        T = float(eval(T_e, {"__builtins__": {}}))
+        got = float(eval(got_e, {"__builtins__": {}}))
+        half = torch.float16 if typ == "f16" else torch.bfloat16
+        g = torch.tensor([got], dtype=torch.float64).to(half)
+        assert float(g.to(torch.float64)) == got, (got_e, "not exact in", typ)
+        bits = g.view(torch.int16).numpy().view(np.uint16).reshape(1, 1)
+        res = ref.check_output(bits, np.array([[y_ref]]), np.array([[T]]), typ)
+        assert res["ok"] == (verdict == "pass"), (typ, y_e, T_e, got_e, verdict, res)
+
+
+def pin_reference_rows():
+    """The row-subset reference (used by full-size tests that sample rows) equals
+    the full oracle's rows, both formats and both 16-bit types."""
+    rows = np.array([0, 3, 4, 17, 30])
+    for dtype in ("bf16", "f16"):
+        x = synthetic.custom_inputs(31, 9, 64, 5, seed=24, dtype=dtype)
+        x["dtype"] = dtype
+        y, T = ref.reference_rows(x, rows)
+        assert np.array_equal(y, ref.gemm_w4a4_ref(*_args(x), dtype=dtype)[rows])
+        assert np.array_equal(T, ref.term_magnitude(*_args(x), dtype=dtype)[rows])
+        xm = synthetic.custom_inputs(31, 9, 64, 5, seed=25, dtype=dtype, fmt="mxfp4")
+        xm["dtype"] = dtype
+        y, T = ref.reference_rows_mx(xm, rows)
+        assert np.array_equal(y, ref.gemm_mxfp4_ref(*_args(xm), dtype=dtype)[rows])
+        assert np.array_equal(T, ref.term_magnitude_mx(*_args(xm), dtype=dtype)[rows])
+
+
 # ------------------------------------------------------------ fp16 variant (LoRA and output in binary16)
 
 def _golden_rows(name):
@@ -510,9 +603,10 @@ def brute_force_mx(x):
                 acc += a * w
                 tot += abs(a * w)
             lora = sum((_frac(la[m, r]) * _frac(lu[r, n]) for r in range(R)), Fraction(0))
+            lora_abs = sum((abs(_frac(la[m, r]) * _frac(lu[r, n])) for r in range(R)), Fraction(0))
             wc = _frac(float(x["wcscale"][n]))
             y[m, n] = float(wc * acc + _frac(float(x["bias"][n])) + lora)
-            T[m, n] = float(abs(wc) * tot + abs(_frac(float(x["bias"][n]))))
+            T[m, n] = float(abs(wc) * tot + abs(_frac(float(x["bias"][n]))) + lora_abs)
     return y, T
 
 
@@ -533,6 +627,21 @@ def pin_mx_bruteforce_tiny():
         x["ascales"][0, 0] = 0
         y, T = brute_force_mx(x)
         assert np.all(np.abs(_y_mx(x) - y) <= 2.0 ** -45 * T), (M, N, K, R)
+
+
+def pin_mx_term_magnitude_bruteforce():
+    """term_magnitude_mx == the rational brute force's T (|wc| sum|a w| + |bias| +
+    sum|la lu|), with negative wcscale and bias entries and R in {1, 3}."""
+    rng = np.random.default_rng(66)
+    for (M, N, K, R) in [(3, 4, 64, 3), (2, 3, 32, 1)]:
+        x = _mx(M, N, K, R, seed=int(rng.integers(1 << 30)))
+        x["ascales"] = rng.integers(120, 135, size=x["ascales"].shape).astype(np.uint8)
+        x["wscales"] = rng.integers(120, 135, size=x["wscales"].shape).astype(np.uint8)
+        x["wcscale"][0] = -x["wcscale"][0]
+        x["bias"][:] = -np.abs(x["bias"])
+        _, T = brute_force_mx(x)
+        got = ref.term_magnitude_mx(*_args(x))
+        assert np.all(np.abs(got - T) <= 2.0 ** -40 * T), (M, N, K, R, got, T)
 
 
 def pin_mx_block_boundary():
@@ -744,6 +853,79 @@ def _mut_mx_scales_row_major(mp):
         s = np.asarray(scales).reshape(-1)[: rows * (K // 32)].reshape(rows, K // 32)
         return ref.E2M1_TABLE[codes] * np.repeat(ref.E8M0_TABLE[s], 32, axis=1)
     mp.setattr(ref, "dequantize_mx", bad)
+
+
+# The tolerance side. A shared misreading would touch both formats at once, so
+# each of these plants its mistake in the NVFP4 and the MXFP4 function together.
+
+def _both_T(mp, wrap):
+    for name in ("term_magnitude", "term_magnitude_mx"):
+        orig = getattr(ref, name)
+        mp.setattr(ref, name, wrap(orig))
+
+
+def _mut_T_times8(mp):
+    _both_T(mp, lambda f: (lambda *a, dtype="bf16": 8.0 * f(*a, dtype=dtype)))
+
+
+def _mut_T_bias_twice(mp):
+    _both_T(mp, lambda f: (lambda *a, dtype="bf16": f(*a, dtype=dtype)
+                           + np.abs(np.asarray(a[5], np.float64))[None, :]))
+
+
+def _mut_T_main_signed(mp):
+    # |sum_k a w| instead of sum_k |a w|
+    def wrap(f):
+        def bad(act, asc, wgt, wsc, wc, b, la, lu, dtype="bf16"):
+            deq = ref.dequantize if f is ref.term_magnitude else ref.dequantize_mx
+            S = np.abs(deq(act, asc) @ deq(wgt, wsc).T)
+            L = np.abs(ref.half_bits_to_f64(la, dtype)) @ np.abs(ref.half_bits_to_f64(lu, dtype)) \
+                if np.asarray(la).shape[1] else 0.0
+            return np.abs(np.asarray(wc, np.float64))[None, :] * S \
+                + np.abs(np.asarray(b, np.float64))[None, :] + L
+        return bad
+    _both_T(mp, wrap)
+
+
+def _mut_T_no_lora(mp):
+    def wrap(f):
+        def bad(act, asc, wgt, wsc, wc, b, la, lu, dtype="bf16"):
+            z = np.zeros_like(np.asarray(la))[:, :0], np.zeros_like(np.asarray(lu))[:0, :]
+            return f(act, asc, wgt, wsc, wc, b, *z, dtype=dtype)
+        return bad
+    _both_T(mp, wrap)
+
+
+def _mut_tol_coefficient_4e2(mp):
+    orig = ref.tolerance_bound
+    mp.setattr(ref, "tolerance_bound", lambda y, T, dtype="bf16": orig(y, 10.0 * np.asarray(T), dtype))
+
+
+def _mut_tol_no_ulp(mp):
+    mp.setattr(ref, "tolerance_bound", lambda y, T, dtype="bf16": 4e-3 * np.asarray(T, np.float64))
+
+
+def _mut_tol_two_ulps(mp):
+    orig = ref.tolerance_bound
+    ulp = {"bf16": ref.ulp_bf16, "f16": ref.ulp_f16}
+    mp.setattr(ref, "tolerance_bound", lambda y, T, dtype="bf16": orig(y, T, dtype) + ulp[dtype](y))
+
+
+def _mut_tol_bf16_ulp_always(mp):
+    mp.setattr(ref, "tolerance_bound", lambda y, T, dtype="bf16": 4e-3 * np.asarray(T, np.float64)
+               + ref.ulp_bf16(y))
+
+
+def _mut_reference_rows_first_scales(mp):
+    # takes the first len(rows) act-scale columns instead of the sampled rows' own
+    def bad(inputs, rows):
+        rows = np.asarray(rows, dtype=np.int64)
+        args = (inputs["act"][rows], inputs["ascales"][:, :len(rows)], inputs["wgt"],
+                inputs["wscales"], inputs["wcscale"], inputs["bias"], inputs["lora_act_in"][rows],
+                inputs["lora_up"])
+        dt = inputs.get("dtype", "bf16")
+        return ref.gemm_w4a4_ref(*args, dtype=dt), ref.term_magnitude(*args, dtype=dt)
+    mp.setattr(ref, "reference_rows", bad)
 
 
 MUTANTS = [v for k, v in sorted(globals().items()) if k.startswith("_mut_")]
