@@ -25,7 +25,7 @@ The JSON carries:
                 rocprofv3 counter summary when it was taken on the current
                 kernel source, else null
                 The "attainable" entry is the rate of the same MFMA instruction
-                alone under full-chip load (gemm_w4a4_mfma_peak) with the shader
+                alone under full-chip load (w4a4_probe_mfma_peak) with the shader
                 clock it ran at, and the kernel's fraction of that rate.
   cpu_baseline  the CPU oracle (float64, numpy + BLAS) timed on the same full
                 workload on this host's cores, repeated for about --cpu-seconds
@@ -51,7 +51,8 @@ PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 
-from bit_quantized_gemm_amd.profsum import KERNELS, kernel_source_hash  # noqa: E402  (no native load)
+from profsum import KERNELS, kernel_source_hash  # noqa: E402  (no native load)
+from bit_quantized_gemm_amd import probes  # noqa: E402  (loads its library on first call)
 
 
 def committed_traffic(workload: str, fmt: str = "nvfp4"):
@@ -86,15 +87,15 @@ def cpu_model() -> str:
 
 
 def attainable_peak(w4, kind: int, dev, stream, iters: int = 2048, reps: int = 10) -> dict:
-    """Rate of one MFMA kind alone on every SIMD (gemm_w4a4_mfma_peak) and the
+    """Rate of one MFMA kind alone on every SIMD (w4a4_probe_mfma_peak) and the
     shader clock it ran at (median over workgroups)."""
     import numpy as np
     import torch
-    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=dev)
-    call = lambda: w4.mfma_peak_raw(kind, iters, clocks.data_ptr(), stream.cuda_stream)
+    clocks = torch.zeros(2 * probes.PEAK_GROUPS, dtype=torch.int64, device=dev)
+    call = lambda: probes.mfma_peak_raw(kind, iters, clocks.data_ptr(), stream.cuda_stream)
     for _ in range(3):
         if call() != 0:
-            raise RuntimeError("gemm_w4a4_mfma_peak failed")
+            raise RuntimeError("w4a4_probe_mfma_peak failed")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
         a.record(stream)
@@ -104,26 +105,26 @@ def attainable_peak(w4, kind: int, dev, stream, iters: int = 2048, reps: int = 1
     ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
     c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
     mhz = float(np.median(c[:, 0] / (c[:, 1] / 100.0)))
-    flops = w4.PEAK_GROUPS * 4 * iters * 8 * w4.PEAK_FLOP[kind]
+    flops = probes.PEAK_GROUPS * 4 * iters * 8 * probes.PEAK_FLOP[kind]
     return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_mhz": round(mhz, 1)}
 
 
 def route_rates(w4, dev, stream, blocks: int, reps: int = 10) -> dict:
     """The per-block arithmetic of both ways to run NVFP4 on the matrix cores
-    (gemm_w4a4_route_core): route 0 decodes to fp16 for the fp16 MFMA (what
+    (w4a4_probe_route_core): route 0 decodes to fp16 for the fp16 MFMA (what
     gemm_w4a4 does), route 1 feeds the scaled FP4 MFMA one 16-k block at a
     time and applies the scale product to each partial on the vector ALU.
     Register-resident operands, every SIMD busy; `blocks` 16-k blocks per wave."""
     import numpy as np
     import torch
-    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=dev)
+    clocks = torch.zeros(2 * probes.PEAK_GROUPS, dtype=torch.int64, device=dev)
     out = {}
     for route in (0, 1):
-        call = lambda: w4.route_core_raw(route, blocks, clocks.data_ptr(), stream.cuda_stream)
+        call = lambda: probes.route_core_raw(route, blocks, clocks.data_ptr(), stream.cuda_stream)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < 0.5:   # settle the clock under this load
             if call() != 0:
-                raise RuntimeError("gemm_w4a4_route_core failed")
+                raise RuntimeError("w4a4_probe_route_core failed")
             torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in ev:
@@ -133,7 +134,7 @@ def route_rates(w4, dev, stream, blocks: int, reps: int = 10) -> dict:
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
         c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
-        flops = w4.PEAK_GROUPS * 4 * blocks * w4.ROUTE_FLOP_PER_BLOCK
+        flops = probes.PEAK_GROUPS * 4 * blocks * probes.ROUTE_FLOP_PER_BLOCK
         out[f"route_{route}"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                                  "cycles_per_block": round(float(np.median(c[:, 0])) / blocks, 1),
                                  "clock_mhz": round(float(np.median(c[:, 0] / (c[:, 1] / 100.0))), 1)}
@@ -232,7 +233,7 @@ def main() -> int:
         rates = route_rates(w4, torch.device("cuda:0"), torch.cuda.current_stream(), blocks)
         print(json.dumps({"metric": "NVFP4 block arithmetic per route (no memory traffic), TFLOP/s",
                           "config": {"workload": wl.name, "blocks_per_wave": blocks,
-                                     "waves": w4.PEAK_GROUPS * 4, "wave_tile": "128x96"},
+                                     "waves": probes.PEAK_GROUPS * 4, "wave_tile": "128x96"},
                           **rates}))
         return 0
     mx = a.fmt == "mxfp4"

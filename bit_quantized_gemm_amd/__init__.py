@@ -12,15 +12,13 @@ in the library's HIP kernels. If the library is missing the calls raise.
 from __future__ import annotations
 
 from . import _native
-from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK, PEAK_FLOP,
-                      PEAK_GROUPS, ROUTE_FLOP_PER_BLOCK, gemm_mxfp4_f16_raw, gemm_mxfp4_raw, gemm_w4a4_f16_raw,
-                      gemm_w4a4_raw, library_path, mfma_peak_raw, plan, route_b_tile_raw,
-                      route_core_raw, strerror, variants)
+from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK,
+                      gemm_mxfp4_f16_raw, gemm_mxfp4_raw, gemm_w4a4_f16_raw, gemm_w4a4_raw,
+                      library_path, plan, strerror, variants)
 
 __all__ = ["gemm_w4a4", "gemm_mxfp4", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
            "gemm_mxfp4_f16_raw", "plan", "variants", "strerror", "library_path", "GemmError", "OK",
-           "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R", "FORMATS", "mfma_peak_raw",
-           "route_core_raw", "route_b_tile_raw", "ROUTE_FLOP_PER_BLOCK", "PEAK_GROUPS", "PEAK_FLOP"]
+           "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R", "FORMATS"]
 
 
 class GemmError(RuntimeError):

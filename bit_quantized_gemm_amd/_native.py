@@ -71,12 +71,6 @@ def load() -> ctypes.CDLL:
         lib.gemm_mxfp4_num_variants.restype = i
         lib.gemm_mxfp4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
         lib.gemm_mxfp4_variant_info.restype = i
-        lib.gemm_w4a4_mfma_peak.argtypes = [i, i, vp, vp]
-        lib.gemm_w4a4_mfma_peak.restype = i
-        lib.gemm_w4a4_route_core.argtypes = [i, i, vp, vp]
-        lib.gemm_w4a4_route_core.restype = i
-        lib.gemm_w4a4_route_b_tile.argtypes = [vp] * 5 + [i, vp]
-        lib.gemm_w4a4_route_b_tile.restype = i
         lib.gemm_w4a4_strerror.argtypes = [i]
         lib.gemm_w4a4_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -113,30 +107,6 @@ def gemm_mxfp4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, l
     """Direct call of the MXFP4 fp16 C entry point; returns its code."""
     return load().gemm_mxfp4_f16(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
                                  out, M, N, K, R, stream)
-
-
-PEAK_GROUPS = 256
-PEAK_FLOP = {0: 32768, 1: 131072, 2: 32768}   # per MFMA of each gemm_w4a4_mfma_peak kind
-
-
-def mfma_peak_raw(kind: int, iters: int, clocks, stream) -> int:
-    """Launch the attainable-MFMA-peak microbenchmark (measurement aid)."""
-    return load().gemm_w4a4_mfma_peak(kind, iters, clocks, stream)
-
-
-ROUTE_FLOP_PER_BLOCK = 12 * 32768   # useful flop per wave and 16-k block, either route
-ROUTE_B_MAX_K = 65536
-
-
-def route_core_raw(route: int, blocks: int, clocks, stream) -> int:
-    """Launch the per-block arithmetic of route 0 (decode + fp16 MFMA) or
-    route 1 (scaled FP4 MFMA + scale on partials) on every SIMD (measurement aid)."""
-    return load().gemm_w4a4_route_core(route, blocks, clocks, stream)
-
-
-def route_b_tile_raw(act, ascales, wgt, wscales, out, K: int, stream) -> int:
-    """One 32x32 NVFP4 tile by route 1 into float32 `out` (measurement aid)."""
-    return load().gemm_w4a4_route_b_tile(act, ascales, wgt, wscales, out, K, stream)
 
 
 FORMATS = ("nvfp4", "mxfp4")

@@ -1,9 +1,11 @@
-"""Build the gfx950 shared library in-tree with hipcc.
+"""Build the gfx950 shared libraries in-tree with hipcc.
 
     python -m bit_quantized_gemm_amd.build
 
-writes bit_quantized_gemm_amd/libgemm_w4a4.so. The kernels are compiled for
-gfx950 only, with packed-fp32 VALU instructions disabled.
+writes bit_quantized_gemm_amd/libgemm_w4a4.so (the operator: include/gemm_w4a4.h)
+and bit_quantized_gemm_amd/libw4a4_probes.so (measurement aids:
+include/w4a4_probes.h). The kernels are compiled for gfx950 only, with
+packed-fp32 VALU instructions disabled.
 """
 from __future__ import annotations
 
@@ -18,7 +20,12 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgemm_w4a4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, f) for f in ("gemm_w4a4.hip", "gemm_mxfp4.hip", "mfma_peak.hip", "route_probe.hip")]
+PROBES_LIB_PATH = os.path.join(PKG_DIR, "libw4a4_probes.so")
+# library -> the sources it is built from
+LIBS = {
+    LIB_PATH: ("gemm_w4a4.hip", "gemm_mxfp4.hip"),
+    PROBES_LIB_PATH: ("mfma_peak.hip", "route_probe.hip"),
+}
 ARCH = "gfx950"
 
 
@@ -39,10 +46,9 @@ def compile_flags() -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into the in-tree shared library; returns its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + compile_flags() + ["-o", tmp] + SOURCES
+def _build_one(path: str, sources, verbose: bool) -> None:
+    tmp = path + ".tmp"
+    cmd = [hipcc()] + compile_flags() + ["-o", tmp] + [os.path.join(CSRC, f) for f in sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,9 +58,17 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into the in-tree shared libraries; returns the
+    operator library's path."""
+    for path, sources in LIBS.items():
+        _build_one(path, sources, verbose)
     return LIB_PATH
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    build(verbose=True)
+    print("\n".join(LIBS))

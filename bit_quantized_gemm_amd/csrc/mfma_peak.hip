@@ -11,7 +11,7 @@
 
 #include <stdint.h>
 
-#include "gemm_w4a4.h"
+#include "w4a4_probes.h"
 #include "w4a4_common.hpp"
 #include "w4a4_host.hpp"
 #include "w4a4_layout.hpp"
@@ -69,14 +69,14 @@ __global__ __launch_bounds__(kPeakThreads, 1) void mfma_peak_kernel(int iters, u
 
 using namespace w4a4;
 
-extern "C" int gemm_w4a4_mfma_peak(int kind, int iters, uint64_t* clocks, void* stream) {
+extern "C" int w4a4_probe_mfma_peak(int kind, int iters, uint64_t* clocks, void* stream) {
   if (kind < 0 || kind > 2 || iters < 1 || !clocks) return GEMM_W4A4_EINVAL;
   if (reinterpret_cast<uintptr_t>(clocks) & 7u) return GEMM_W4A4_EALIGN;
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
   void (*k)(int, uint64_t*) = kind == 0 ? mfma_peak_kernel<0> : kind == 1 ? mfma_peak_kernel<1> : mfma_peak_kernel<2>;
   void* args[] = {&iters, &clocks};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(GEMM_W4A4_PEAK_GROUPS),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(W4A4_PROBE_GROUPS),
                                        dim3(kPeakThreads), args, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
 }

@@ -26,7 +26,7 @@
 
 #include <stdint.h>
 
-#include "gemm_w4a4.h"
+#include "w4a4_probes.h"
 #include "w4a4_common.hpp"
 #include "w4a4_host.hpp"
 
@@ -202,21 +202,21 @@ __global__ __launch_bounds__(64) void route_b_tile_kernel(const uint8_t* act, co
 
 using namespace w4a4;
 
-extern "C" int gemm_w4a4_route_core(int route, int blocks, uint64_t* clocks, void* stream) {
+extern "C" int w4a4_probe_route_core(int route, int blocks, uint64_t* clocks, void* stream) {
   if (route < 0 || route > 1 || blocks < 1 || !clocks) return GEMM_W4A4_EINVAL;
   if (reinterpret_cast<uintptr_t>(clocks) & 7u) return GEMM_W4A4_EALIGN;
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
   void (*k)(int, uint64_t*) = route == 0 ? route_core_kernel<0> : route_core_kernel<1>;
   void* args[] = {&blocks, &clocks};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(GEMM_W4A4_PEAK_GROUPS),
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(W4A4_PROBE_GROUPS),
                                        dim3(kRouteThreads), args, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
 }
 
-extern "C" int gemm_w4a4_route_b_tile(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
+extern "C" int w4a4_probe_route_b_tile(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
                                       const uint8_t* wscales, float* out, int K, void* stream) {
-  if (!act || !ascales || !wgt || !wscales || !out || K < 16 || K % 16 != 0 || K > GEMM_W4A4_ROUTE_B_MAX_K)
+  if (!act || !ascales || !wgt || !wscales || !out || K < 16 || K % 16 != 0 || K > W4A4_PROBE_ROUTE_B_MAX_K)
     return GEMM_W4A4_EINVAL;
   if (((reinterpret_cast<uintptr_t>(act) | reinterpret_cast<uintptr_t>(wgt) |
         reinterpret_cast<uintptr_t>(out)) & 3u) != 0)

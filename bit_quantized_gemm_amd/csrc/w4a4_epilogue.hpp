@@ -242,10 +242,13 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
     }
   }
 
-  // Per-column factor at columns ncol0 + 32j + 8q + (0..3), clamped at the N edge.
+  // Per-column factor at columns ncol0 + 32j + 8q + (0..3), clamped at the N
+  // edge. n is a multiple of 4, so one 16-byte read serves the four columns
+  // when both vectors are 16-byte aligned; the interface only promises 4 bytes.
+  const bool wb16 = ((reinterpret_cast<uintptr_t>(p.wcscale) | reinterpret_cast<uintptr_t>(p.bias)) & 15u) == 0;
   auto col4 = [&](const float* v, int j, int q) __attribute__((always_inline)) {
     const int n = ncol0 + 32 * j + 8 * q;
-    if (n_inside) return *reinterpret_cast<const f32x4*>(v + n);
+    if (n_inside && wb16) return *reinterpret_cast<const f32x4*>(v + n);
     return f32x4{v[min(n, N - 1)], v[min(n + 1, N - 1)], v[min(n + 2, N - 1)], v[min(n + 3, N - 1)]};
   };
 

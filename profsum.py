@@ -1,9 +1,9 @@
 """Summaries of rocprofv3 runs of the W4A4 kernels, as short text files.
 
-    python -m bit_quantized_gemm_amd.profsum trace DIR --workload qkv --command "..."
-    python -m bit_quantized_gemm_amd.profsum traffic FETCH_DIR WRITE_DIR --copy-mib 256 \
+    python profsum.py trace DIR --workload qkv --command "..."
+    python profsum.py traffic FETCH_DIR WRITE_DIR --copy-mib 256 \
         --workload qkv --command "..."
-    python -m bit_quantized_gemm_amd.profsum counters DIR --workload qkv --command "..."
+    python profsum.py counters DIR --workload qkv --command "..."
 
 `trace` reads the kernel statistics of a `--kernel-trace --stats` run; given
 the JSON line bench.py printed in that run (`--bench-json`), it also gives the
@@ -30,7 +30,7 @@ import statistics
 import sys
 from collections import defaultdict
 
-_HERE = os.path.dirname(os.path.abspath(__file__))
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_quantized_gemm_amd", "csrc")
 _SHARED = ("w4a4_common.hpp", "w4a4_epilogue.hpp", "w4a4_layout.hpp")
 # per format: (kernel name tag, summary file prefix, the sources the kernel is built from)
 KERNELS = {
@@ -44,7 +44,7 @@ def kernel_source_hash(fmt: str = "nvfp4") -> str:
     """First 16 hex digits of the sha256 over one kernel's sources."""
     h = hashlib.sha256()
     for f in KERNELS[fmt][2]:
-        p = os.path.join(_HERE, "csrc", f)
+        p = os.path.join(_CSRC, f)
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -1,4 +1,5 @@
-"""Helpers shared by the GPU parity tests: device upload, row sampling and the
+"""Helpers shared by the GPU parity tests: device upload, the full oracle, row
+sampling (only for outputs too large to hold twice on the host) and the
 tolerance check (oracle.check_output)."""
 import sys
 
@@ -32,16 +33,17 @@ def to_device(x):
     return d
 
 
+def full_reference(x, fmt="nvfp4"):
+    """(y, T) of the oracle over every output element."""
+    a = [x[k] for k in ARGS]
+    dt = x.get("dtype", "bf16")
+    if fmt == "mxfp4":
+        return ref.gemm_mxfp4_ref(*a, dtype=dt), ref.term_magnitude_mx(*a, dtype=dt)
+    return ref.gemm_w4a4_ref(*a, dtype=dt), ref.term_magnitude(*a, dtype=dt)
+
+
 def assert_parity(got, y, T, what, dtype="bf16"):
     res = ref.check_output(got, y, T, dtype)
-    _say(f"  {what}: max err/bound {res['max_ratio']:.3g}, failures {res['n_fail']}")
+    _say(f"  {what}: {got.size} elements, max err/bound {res['max_ratio']:.3g}, "
+         f"failures {res['n_fail']}")
     assert res["ok"], (what, res)
-
-
-def _sample_rows(M, block_m, rng):
-    rows = set(range(0, min(M, 40)))                          # first tile head
-    rows |= set(range(max(0, M - 40), M))                     # last (ragged) rows
-    for t in range(0, M, block_m):                            # tile boundaries
-        rows |= {t, min(M - 1, t + block_m - 1)}
-    rows |= set(rng.choice(M, size=min(M, 64), replace=False).tolist())
-    return np.array(sorted(rows))

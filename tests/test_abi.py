@@ -14,34 +14,45 @@ import subprocess
 import pytest
 
 import bit_quantized_gemm_amd as w4
+from bit_quantized_gemm_amd import probes
 from bit_quantized_gemm_amd import _native
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LLVM = "/opt/rocm/llvm/bin"
 
 
-def _declared_functions():
-    names = set()
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        text = open(h).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(gemm_(?:w4a4|mxfp4)\w*)\s*\(",
-                             text, flags=re.M):
-            names.add(m.group(1))
-    return sorted(names)
+# each header and the library that must export what it declares
+HEADERS = {"gemm_w4a4.h": w4.library_path, "w4a4_probes.h": probes.library_path}
 
 
-def test_library_exports_every_declared_symbol():
-    lib = _native.load()
-    names = _declared_functions()
-    assert {"gemm_w4a4", "gemm_w4a4_f16", "gemm_mxfp4", "gemm_mxfp4_f16"} <= set(names)
-    assert len(names) >= 11
+def _declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted({m.group(1) for m in re.finditer(
+        r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)})
+
+
+def test_every_header_is_checked():
+    assert sorted(HEADERS) == sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h")))
+
+
+@pytest.mark.parametrize("header", sorted(HEADERS))
+def test_library_exports_every_declared_symbol(header):
+    names = _declared_functions(header)
+    path = HEADERS[header]()
+    lib = ctypes.CDLL(path)
     for n in names:
         assert hasattr(lib, n), n
-    nm = subprocess.run(["nm", "-D", "--defined-only", w4.library_path()],
+    nm = subprocess.run(["nm", "-D", "--defined-only", path],
                         capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
     assert set(names) <= exported
+    if header == "gemm_w4a4.h":
+        assert {"gemm_w4a4", "gemm_w4a4_f16", "gemm_mxfp4", "gemm_mxfp4_f16"} <= set(names)
+        # the operator's library carries no measurement aid
+        assert not any(n.startswith("w4a4_probe") for n in exported)
+    else:
+        assert set(names) == {"w4a4_probe_mfma_peak", "w4a4_probe_route_core", "w4a4_probe_route_b_tile"}
 
 
 ENTRIES = {"bf16": w4.gemm_w4a4_raw, "f16": w4.gemm_w4a4_f16_raw,
@@ -229,14 +240,14 @@ def test_solver_lds_matches_code_objects():
     (3, 16, 0x1000, w4.EINVAL), (-1, 16, 0x1000, w4.EINVAL), (0, 0, 0x1000, w4.EINVAL),
     (1, 16, 0, w4.EINVAL), (2, 16, 0x1004, w4.EALIGN)])
 def test_mfma_peak_validation(kind, iters, clocks, want):
-    assert w4.mfma_peak_raw(kind, iters, clocks, 0) == want
+    assert probes.mfma_peak_raw(kind, iters, clocks, 0) == want
 
 
 @pytest.mark.parametrize("route,blocks,clocks,want", [
     (2, 16, 0x1000, w4.EINVAL), (-1, 16, 0x1000, w4.EINVAL), (0, 0, 0x1000, w4.EINVAL),
     (1, 16, 0, w4.EINVAL), (0, 16, 0x1004, w4.EALIGN)])
 def test_route_core_validation(route, blocks, clocks, want):
-    assert w4.route_core_raw(route, blocks, clocks, 0) == want
+    assert probes.route_core_raw(route, blocks, clocks, 0) == want
 
 
 _TILE = (0x1000, 0x2000, 0x3000, 0x4000, 0x5000)   # act, ascales, wgt, wscales, out
@@ -250,4 +261,4 @@ _TILE = (0x1000, 0x2000, 0x3000, 0x4000, 0x5000)   # act, ascales, wgt, wscales,
     ((0x1002,) + _TILE[1:], 64, w4.EALIGN), (_TILE[:2] + (0x3001,) + _TILE[3:], 64, w4.EALIGN),
     (_TILE[:4] + (0x5002,), 64, w4.EALIGN)])
 def test_route_b_tile_validation(ptrs, K, want):
-    assert w4.route_b_tile_raw(*ptrs, K, 0) == want
+    assert probes.route_b_tile_raw(*ptrs, K, 0) == want

@@ -9,10 +9,11 @@ import pytest
 import torch
 
 import bit_quantized_gemm_amd as w4
+from bit_quantized_gemm_amd import probes
 import oracle.w4a4_ref as ref
 import synthetic
 
-from gpu_helpers import ARGS, DEV, _say, _sample_rows, assert_parity, to_device
+from gpu_helpers import ARGS, DEV, _say, assert_parity, full_reference, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -59,31 +60,27 @@ def test_tiny_full():
 
 @pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "ragged", "prod_k3840_n3072",
                                   "prod_k3840_n15360", "prod_k15360_n3840", "prod_k10240_n3072"])
-def test_workload_full_size_sampled(name):
+def test_workload_full_size(name):
     wl = synthetic.workload(name)
-    _say(f"case: {name} {wl.shape}, full-size launch, sampled rows vs oracle")
+    _say(f"case: {name} {wl.shape}, full-size launch, every element vs oracle")
     x = synthetic.make_inputs(name)
     got = run_gpu(x)
-    plan = w4.plan(*wl.shape)
-    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(7))
-    y, T = ref.reference_rows(x, rows)
-    assert_parity(got[rows], y, T, f"{name} ({len(rows)} rows x {wl.N})")
+    y, T = full_reference(x)
+    assert_parity(got, y, T, f"{name} (all {wl.M} x {wl.N})")
     # every output is finite (no NaN scale bytes in these inputs)
     vals = (got.astype(np.uint32) << 16).view(np.float32)
     assert np.isfinite(vals).all()
 
 
 @pytest.mark.parametrize("name", ["qkv", "prod_k3840_n3072"])
-def test_ceiling_mode_sampled(name):
+def test_ceiling_mode_full_size(name):
     """LoRA and affine off (R = 0, wcscale = 1, bias = 0) at full size."""
     wl = synthetic.workload(name)
-    _say(f"case: {name} ceiling mode (no LoRA, no affine), sampled rows vs oracle")
+    _say(f"case: {name} ceiling mode (no LoRA, no affine), every element vs oracle")
     x = synthetic.no_lora_affine(synthetic.make_inputs(name))
     got = run_gpu(x)
-    plan = w4.plan(wl.M, wl.N, wl.K, 0)
-    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(8))
-    y, T = ref.reference_rows(x, rows)
-    assert_parity(got[rows], y, T, f"{name} ceiling ({len(rows)} rows x {wl.N})")
+    y, T = full_reference(x)
+    assert_parity(got, y, T, f"{name} ceiling (all {wl.M} x {wl.N})")
 
 
 def test_deterministic_bytes():
@@ -307,15 +304,13 @@ def test_f16_tiny_full():
 
 
 @pytest.mark.parametrize("name", ["qkv", "mlp_down", "prod_k3840_n3072"])
-def test_f16_workload_sampled(name):
+def test_f16_workload_full_size(name):
     wl = synthetic.workload(name)
-    _say(f"case: fp16 variant, {name} {wl.shape}, sampled rows vs oracle")
+    _say(f"case: fp16 variant, {name} {wl.shape}, every element vs oracle")
     x = synthetic.make_inputs(name, dtype="f16")
     got = run_gpu(x)
-    plan = w4.plan(*wl.shape)
-    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(9))
-    y, T = ref.reference_rows(x, rows)
-    assert_parity(got[rows], y, T, f"f16 {name} ({len(rows)} rows)", "f16")
+    y, T = full_reference(x)
+    assert_parity(got, y, T, f"f16 {name} (all {wl.M} x {wl.N})", "f16")
 
 
 def test_f16_zero_main_term_shows_lora_and_bias():
@@ -379,19 +374,19 @@ def test_mfma_peak_microbenchmark(kind):
     """The attainable-peak aid runs, every workgroup records its clocks, and
     its rate is positive and below the published dense peak at 2.4 GHz."""
     _say(f"case: MFMA peak microbenchmark, kind {kind}")
-    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=DEV)
+    clocks = torch.zeros(2 * probes.PEAK_GROUPS, dtype=torch.int64, device=DEV)
     s = torch.cuda.current_stream()
-    assert w4.mfma_peak_raw(kind, 64, clocks.data_ptr(), s.cuda_stream) == w4.OK
+    assert probes.mfma_peak_raw(kind, 64, clocks.data_ptr(), s.cuda_stream) == w4.OK
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    assert w4.mfma_peak_raw(kind, 512, clocks.data_ptr(), s.cuda_stream) == w4.OK
+    assert probes.mfma_peak_raw(kind, 512, clocks.data_ptr(), s.cuda_stream) == w4.OK
     b.record()
     torch.cuda.synchronize()
     c = clocks.view(-1, 2).cpu().numpy()
     assert (c[:, 0] > 0).all() and (c[:, 1] > 0).all()
     mhz = np.median(c[:, 0] / (c[:, 1] / 100.0))
     assert 500 < mhz < 2600
-    tf = w4.PEAK_GROUPS * 4 * 512 * 8 * w4.PEAK_FLOP[kind] / (a.elapsed_time(b) * 1e-3) / 1e12
+    tf = probes.PEAK_GROUPS * 4 * 512 * 8 * probes.PEAK_FLOP[kind] / (a.elapsed_time(b) * 1e-3) / 1e12
     published = {0: 2500.0, 1: 10100.0, 2: 2500.0}[kind]
     assert 0 < tf < 1.05 * published
 
@@ -463,16 +458,15 @@ TILE_256x128 = [(4320, 3064, 384, 40), (4316, 3064, 384, 40), (4300, 3000, 272, 
 
 
 @pytest.mark.parametrize("shape", TILE_256x128, ids=["x".join(map(str, s)) for s in TILE_256x128])
-def test_256x128_instance_sampled(shape):
+def test_256x128_instance(shape):
     M, N, K, R = shape
     plan = w4.plan(*shape)
     assert (plan["block_m"], plan["block_n"]) == (256, 128)
-    _say(f"case: 256x128 instance, M={M} N={N} K={K} R={R}, sampled rows")
+    _say(f"case: 256x128 instance, M={M} N={N} K={K} R={R}, every element")
     x = synthetic.custom_inputs(M, N, K, R, seed=M + N + K + R)
     got = run_gpu(x)
-    rows = _sample_rows(M, 256, np.random.default_rng(11))
-    y, T = ref.reference_rows(x, rows)
-    assert_parity(got[rows], y, T, f"256x128 {shape}")
+    y, T = full_reference(x)
+    assert_parity(got, y, T, f"256x128 {shape}")
 
 
 # token counts that are not a multiple of 8 on the large tiles: the fast
@@ -481,15 +475,13 @@ ODD_M = [(4095, 3072, 3072, 32), (4353, 3840, 3840, 128), (1001, 3072, 3072, 16)
 
 
 @pytest.mark.parametrize("shape", ODD_M, ids=["x".join(map(str, s)) for s in ODD_M])
-def test_odd_m_sampled(shape):
+def test_odd_m(shape):
     M, N, K, R = shape
-    _say(f"case: M % 8 != 0 on the fast flavour, M={M} N={N} K={K} R={R}, sampled rows")
+    _say(f"case: M % 8 != 0 on the fast flavour, M={M} N={N} K={K} R={R}, every element")
     x = synthetic.custom_inputs(M, N, K, R, seed=M + 2 * N + K + R)
     got = run_gpu(x)
-    plan = w4.plan(*shape)
-    rows = _sample_rows(M, plan["block_m"], np.random.default_rng(12))
-    y, T = ref.reference_rows(x, rows)
-    assert_parity(got[rows], y, T, f"odd M {shape}")
+    y, T = full_reference(x)
+    assert_parity(got, y, T, f"odd M {shape}")
 
 
 @pytest.mark.parametrize("shift", [4, 1])
@@ -514,6 +506,39 @@ def test_misaligned_act_scales(shift):
     assert torch.equal(out_a, out_b)
     y, T = oracle_full(x)
     assert_parity(out_b.view(torch.int16).cpu().numpy().view(np.uint16), y, T, f"act scales at offset {shift}")
+
+
+# wcscale / bias 4 bytes off 16-byte alignment (the interface asks for 4):
+# the epilogue's per-column reads, on the general flavour (K % 32 != 0) and
+# on the 128x128 instance (no side region), for both operand formats.
+WB_SHAPES = [(264, 200, 272, 24), (1000, 3072, 512, 16)]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("shape", WB_SHAPES, ids=["x".join(map(str, s)) for s in WB_SHAPES])
+def test_wcscale_bias_4byte_aligned(shape, fmt):
+    M, N, K, R = shape
+    if fmt == "mxfp4" and K % 32:
+        K += 16
+    _say(f"case: wcscale/bias at 16-byte offset 4, {fmt}, M={M} N={N} K={K} R={R}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=K + R, fmt=fmt)
+    d = to_device(x)
+    shifted = {}
+    for k in ("wcscale", "bias"):
+        buf = torch.zeros(N + 1, dtype=torch.float32, device=DEV)
+        buf[1:].copy_(d[k])
+        shifted[k] = buf[1:]
+        assert shifted[k].data_ptr() % 16 == 4
+    call = w4.gemm_mxfp4 if fmt == "mxfp4" else w4.gemm_w4a4
+    out_a = call(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+                 d["lora_act_in"], d["lora_up"])
+    out_b = call(d["act"], d["ascales"], d["wgt"], d["wscales"], shifted["wcscale"], shifted["bias"],
+                 d["lora_act_in"], d["lora_up"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    y, T = full_reference(x, fmt)
+    assert_parity(out_b.view(torch.int16).cpu().numpy().view(np.uint16), y, T,
+                  f"wcscale/bias at offset 4, {fmt} {shape}")
 
 
 # Tensors just under the 2^31-byte limit the entry points accept (the kernels
@@ -553,7 +578,7 @@ SIDE_PARTIAL = [((4096, 3072, 512, 16), "bf16"), ((4096, 3072, 512, 8), "f16"),
 
 @pytest.mark.parametrize("shape,dtype", SIDE_PARTIAL,
                          ids=["x".join(map(str, s)) + "-" + d for s, d in SIDE_PARTIAL])
-def test_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
+def test_prefetched_lora_chunk_partial_rank(shape, dtype):
     M, N, K, R = shape
     plan = w4.plan(*shape)
     assert plan["block_m"] == 256
@@ -561,6 +586,5 @@ def test_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
     x = synthetic.custom_inputs(M, N, K, R, seed=R + K, dtype=dtype)
     x["ascales"][:] = 0          # main term zero: the output is bias + LoRA
     got = run_gpu(x)
-    rows = _sample_rows(M, 256, np.random.default_rng(14))
-    y, T = ref.reference_rows(x, rows)
-    assert_parity(got[rows], y, T, f"side chunk R={R} {dtype}", dtype)
+    y, T = full_reference(x)
+    assert_parity(got, y, T, f"side chunk R={R} {dtype}", dtype)

@@ -12,7 +12,7 @@ import bit_quantized_gemm_amd as w4
 import oracle.w4a4_ref as ref
 import synthetic
 
-from gpu_helpers import ARGS, DEV, _say, _sample_rows, assert_parity, to_device
+from gpu_helpers import ARGS, DEV, _say, assert_parity, full_reference, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -48,37 +48,32 @@ def test_mx_tiny_full(dtype):
 
 @pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "ragged", "prod_k3840_n3072",
                                   "prod_k15360_n3840"])
-def test_mx_workload_full_size_sampled(name):
+def test_mx_workload_full_size(name):
     wl = synthetic.workload(name)
-    _say(f"case: MXFP4 {name} {wl.shape}, full-size launch, sampled rows vs oracle")
+    _say(f"case: MXFP4 {name} {wl.shape}, full-size launch, every element vs oracle")
     x = synthetic.make_inputs(name, fmt="mxfp4")
     got = run_mx(x)
-    plan = w4.plan(*wl.shape, fmt="mxfp4")
-    rows = _sample_rows(wl.M, plan["block_m"], np.random.default_rng(17))
-    y, T = ref.reference_rows_mx(x, rows)
-    assert_parity(got[rows], y, T, f"mx {name} ({len(rows)} rows x {wl.N})")
+    y, T = full_reference(x, "mxfp4")
+    assert_parity(got, y, T, f"mx {name} (all {wl.M} x {wl.N})")
     vals = (got.astype(np.uint32) << 16).view(np.float32)
     assert np.isfinite(vals).all()
 
 
-def test_mx_ceiling_mode_sampled():
-    wl = synthetic.workload("qkv")
-    _say("case: MXFP4 qkv ceiling mode (no LoRA, no affine), sampled rows vs oracle")
+def test_mx_ceiling_mode_full_size():
+    _say("case: MXFP4 qkv ceiling mode (no LoRA, no affine), every element vs oracle")
     x = synthetic.no_lora_affine(synthetic.make_inputs("qkv", fmt="mxfp4"))
     got = run_mx(x)
-    rows = _sample_rows(wl.M, 256, np.random.default_rng(18))
-    y, T = ref.reference_rows_mx(x, rows)
-    assert_parity(got[rows], y, T, "mx qkv ceiling")
+    y, T = full_reference(x, "mxfp4")
+    assert_parity(got, y, T, "mx qkv ceiling")
 
 
-def test_mx_f16_sampled():
+def test_mx_f16_full_size():
     wl = synthetic.workload("mlp_down")
-    _say(f"case: MXFP4 fp16 variant, mlp_down {wl.shape}, sampled rows")
+    _say(f"case: MXFP4 fp16 variant, mlp_down {wl.shape}, every element")
     x = synthetic.make_inputs("mlp_down", dtype="f16", fmt="mxfp4")
     got = run_mx(x)
-    rows = _sample_rows(wl.M, 256, np.random.default_rng(19))
-    y, T = ref.reference_rows_mx(x, rows)
-    assert_parity(got[rows], y, T, "mx f16 mlp_down", "f16")
+    y, T = full_reference(x, "mxfp4")
+    assert_parity(got, y, T, "mx f16 mlp_down", "f16")
 
 
 def test_mx_deterministic_bytes():
@@ -284,7 +279,7 @@ def test_mx_rejects_bad_arguments_on_device():
 
 
 @pytest.mark.parametrize("shape,dtype", [((4096, 3072, 512, 16), "bf16"), ((4096, 3072, 512, 8), "f16")])
-def test_mx_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
+def test_mx_prefetched_lora_chunk_partial_rank(shape, dtype):
     """The first LoRA chunk prefetched into LDS (act rows and lora_up rows)
     with R < 32: ranks past R must contribute nothing."""
     M, N, K, R = shape
@@ -294,9 +289,8 @@ def test_mx_prefetched_lora_chunk_partial_rank_sampled(shape, dtype):
     x = mx_inputs(M, N, K, R, seed=R + K + 1, dtype=dtype)
     x["act"][:] = 0              # main term zero: the output is bias + LoRA
     got = run_mx(x)
-    rows = _sample_rows(M, 256, np.random.default_rng(15))
-    y, T = ref.reference_rows_mx(x, rows)
-    assert_parity(got[rows], y, T, f"mx side chunk R={R} {dtype}", dtype)
+    y, T = full_reference(x, "mxfp4")
+    assert_parity(got, y, T, f"mx side chunk R={R} {dtype}", dtype)
 
 
 MX_ODD_M = [((4095, 3072, 3072, 32), "bf16"), ((4093, 3072, 512, 16), "bf16"),
@@ -304,7 +298,7 @@ MX_ODD_M = [((4095, 3072, 3072, 32), "bf16"), ((4093, 3072, 512, 16), "bf16"),
 
 
 @pytest.mark.parametrize("shape,dtype", MX_ODD_M, ids=["x".join(map(str, s)) + "-" + d for s, d in MX_ODD_M])
-def test_mx_odd_m_act_scale_windows_sampled(shape, dtype):
+def test_mx_odd_m_act_scale_windows(shape, dtype):
     """M % 4 != 0 on the 256x192 tile: the fast flavour reads each k-block row
     of act scales through a 4-byte aligned window (the last one clamped to
     the tensor's end), every row offset into it different."""
@@ -314,7 +308,5 @@ def test_mx_odd_m_act_scale_windows_sampled(shape, dtype):
     _say(f"case: MXFP4 odd M with act-scale windows {shape} {dtype}")
     x = mx_inputs(M, N, K, R, seed=M + K + R, dtype=dtype)
     got = run_mx(x)
-    rows = np.unique(np.concatenate([_sample_rows(M, 256, np.random.default_rng(M)),
-                                     np.arange(M - 5, M), np.arange(0, 3)]))
-    y, T = ref.reference_rows_mx(x, rows)
-    assert_parity(got[rows], y, T, f"mx odd M {shape} {dtype}", dtype)
+    y, T = full_reference(x, "mxfp4")
+    assert_parity(got, y, T, f"mx odd M {shape} {dtype}", dtype)

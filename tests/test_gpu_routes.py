@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import bit_quantized_gemm_amd as w4
+from bit_quantized_gemm_amd import probes
 import oracle.w4a4_ref as ref
 
 from gpu_helpers import DEV, _say
@@ -37,7 +38,7 @@ def test_route_b_tile_matches_the_reference(K, seed):
     d = [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in (act, asc, wgt, wsc)]
     out = torch.full((32, 32), float("nan"), dtype=torch.float32, device=DEV)
     s = torch.cuda.current_stream()
-    assert w4.route_b_tile_raw(*(v.data_ptr() for v in d), out.data_ptr(), K, s.cuda_stream) == w4.OK
+    assert probes.route_b_tile_raw(*(v.data_ptr() for v in d), out.data_ptr(), K, s.cuda_stream) == w4.OK
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     bound = (K // 16) * 2.0 ** -24 * mag
@@ -53,7 +54,7 @@ def test_route_b_tile_single_block_is_bit_exact():
     d = [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in (act, asc, wgt, wsc)]
     out = torch.empty((32, 32), dtype=torch.float32, device=DEV)
     s = torch.cuda.current_stream()
-    assert w4.route_b_tile_raw(*(v.data_ptr() for v in d), out.data_ptr(), 16, s.cuda_stream) == w4.OK
+    assert probes.route_b_tile_raw(*(v.data_ptr() for v in d), out.data_ptr(), 16, s.cuda_stream) == w4.OK
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), S)
 
@@ -61,9 +62,9 @@ def test_route_b_tile_single_block_is_bit_exact():
 @pytest.mark.parametrize("route", [0, 1])
 def test_route_core_runs_on_every_simd(route):
     _say(f"case: route core {route}")
-    clocks = torch.zeros(2 * w4.PEAK_GROUPS, dtype=torch.int64, device=DEV)
+    clocks = torch.zeros(2 * probes.PEAK_GROUPS, dtype=torch.int64, device=DEV)
     s = torch.cuda.current_stream()
-    assert w4.route_core_raw(route, 192, clocks.data_ptr(), s.cuda_stream) == w4.OK
+    assert probes.route_core_raw(route, 192, clocks.data_ptr(), s.cuda_stream) == w4.OK
     torch.cuda.synchronize()
     c = clocks.view(-1, 2).cpu().numpy()
     assert (c[:, 0] > 0).all() and (c[:, 1] > 0).all()

@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-from bit_quantized_gemm_amd import profsum  # noqa: E402
+import profsum  # noqa: E402
 
 KNAME = "void w4a4::gemm_w4a4_kernel<w4a4::TileCfg<256, 192, 2, 2, 4, 1>, false, false>(w4a4::Params)"
 
@@ -53,7 +53,7 @@ def test_trace_timed_region_picks_the_timed_dispatches(tmp_path):
     bench = tmp_path / "bench.json"
     bench.write_text("some log line\n" + json.dumps(
         {"warmup": W, "steps": K, "roofline": {"avg_launch_us": 0.115, "achieved": 1.0}}) + "\n")
-    out = subprocess.run([sys.executable, "-m", "bit_quantized_gemm_amd.profsum", "trace", str(d),
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "profsum.py"), "trace", str(d),
                           "--workload", "qkv", "--command", "cmd", "--bench-json", str(bench)],
                          cwd=ROOT, capture_output=True, text=True, check=True).stdout
     assert "dispatches 6 .. 9" in out
@@ -68,7 +68,7 @@ def test_trace_timed_region_rejects_a_short_trace(tmp_path):
     bench = tmp_path / "bench.json"
     bench.write_text(json.dumps({"warmup": 3, "steps": 4, "roofline": {"avg_launch_us": 0.1,
                                                                       "achieved": 1.0}}))
-    res = subprocess.run([sys.executable, "-m", "bit_quantized_gemm_amd.profsum", "trace", str(d),
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "profsum.py"), "trace", str(d),
                           "--workload", "qkv", "--command", "cmd", "--bench-json", str(bench)],
                          cwd=ROOT, capture_output=True, text=True)
     assert res.returncode != 0 and "expected 4 timed dispatches" in res.stderr
@@ -93,7 +93,7 @@ def test_traffic_scales_each_counter_by_the_copy_probe(tmp_path):
     # the probe copies 256 MiB; FETCH_SIZE reads half of it (scale 2), WRITE_SIZE all of it
     f = _pmc_dir(tmp_path, "F", "FETCH_SIZE", 131072.0, [1000.0, 1100.0, 1200.0])
     w = _pmc_dir(tmp_path, "W", "WRITE_SIZE", 262144.0, [500.0, 500.0, 500.0])
-    out = subprocess.run([sys.executable, "-m", "bit_quantized_gemm_amd.profsum", "traffic", str(f),
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "profsum.py"), "traffic", str(f),
                           str(w), "--copy-mib", "256", "--workload", "qkv", "--command-fetch", "a",
                           "--command-write", "b"], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout
@@ -144,7 +144,7 @@ def test_counters_labels_rocprof_derived_metrics(tmp_path):
         rows += [{"Dispatch_Id": 2 + i, "Kernel_Name": KNAME, "Counter_Name": "MfmaUtil", "Counter_Value": mu},
                  {"Dispatch_Id": 2 + i, "Kernel_Name": KNAME, "Counter_Name": "VALUBusy", "Counter_Value": vb}]
     _write_csv(d / "pmc_counter_collection.csv", rows)
-    out = subprocess.run([sys.executable, "-m", "bit_quantized_gemm_amd.profsum", "counters", str(d),
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "profsum.py"), "counters", str(d),
                           "--workload", "qkv", "--command", "cmd"], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout
     assert "derived metrics" in out and "Median over 3 dispatches" in out
