@@ -12,7 +12,9 @@ Warm-up: W untimed steps, continued until the GPU has run the step for at
 least --settle-ms (default 500 ms): the shader clock needs tens of
 milliseconds of continuous load to leave its idle state, and a timed region
 that starts earlier measures the ramp, not the kernel. "warmup" in the JSON is
-the number of untimed steps actually run.
+the requested W, "warmup_steps_run" the number of untimed steps actually run,
+"settle_ms" the settling time asked for, and "shader_clock_mhz_after_region"
+the shader clock a short MFMA-only probe saw right after the timed region.
 
 The JSON carries:
   roofline      achieved TFLOP/s of the kernel (average launch duration from
@@ -204,6 +206,8 @@ def main() -> int:
                     help="rotate input copies so that no launch finds its operands in the Infinity Cache")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter scale probe)")
+    ap.add_argument("--variant", type=int, default=-1,
+                    help="run this compiled tile instance (gemm_w4a4_run) instead of the solver's choice")
     ap.add_argument("--routes", action="store_true",
                     help="instead of the GEMM: the per-block arithmetic of the decode + fp16 MFMA route "
                          "and of the scaled-FP4-MFMA route, for the workload's K/16 blocks per wave")
@@ -267,7 +271,9 @@ def main() -> int:
                  sla.data_ptr(), slu.data_ptr(), out.data_ptr(), wl.M, wl.N, wl.K, wl.R,
                  stream.cuda_stream) for s, sla, slu in sets]
     counter = [0]
-    if mx:
+    if a.variant >= 0:
+        raw = lambda *args: w4.run_raw(a.fmt, a.dtype == "f16", a.variant, *args)
+    elif mx:
         raw = w4.gemm_mxfp4_f16_raw if a.dtype == "f16" else w4.gemm_mxfp4_raw
     else:
         raw = w4.gemm_w4a4_f16_raw if a.dtype == "f16" else w4.gemm_w4a4_raw
@@ -307,9 +313,17 @@ def main() -> int:
     for _ in range(a.steps):
         step()
     region1.record(stream)
+    # the shader clock right after the timed region, before the power manager
+    # can react to the end of the load: a short MFMA-only probe on the same
+    # stream (s_memtime cycles over s_memrealtime ticks, median over workgroups)
+    clk = torch.zeros(2 * probes.PEAK_GROUPS, dtype=torch.int64, device=dev)
+    if probes.mfma_peak_raw(0, 64, clk.data_ptr(), stream.cuda_stream) != 0:
+        raise RuntimeError("w4a4_probe_mfma_peak failed")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = region0.elapsed_time(region1)
+    c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+    clock_after_mhz = float(np.median(c[:, 0] / (c[:, 1] / 100.0)))
 
     if bad:
         print(f"{KERNELS[a.fmt][1]} returned {bad[0]} ({w4.strerror(bad[0])})", file=sys.stderr)
@@ -329,7 +343,7 @@ def main() -> int:
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     value = flops * a.steps / (region_ms * 1e-3) / 1e12
     traffic = None if a.shape else committed_traffic(a.workload, a.fmt)
-    plan = w4.plan(*wl.shape, fmt=a.fmt)
+    plan = w4.plan_variant(*wl.shape, a.variant, fmt=a.fmt)
     peak = PEAK_FP4_TFLOPS if mx else PEAK_F16_MFMA_TFLOPS
     attain = attainable_peak(w4, 1 if mx else 0, dev, stream)
     attain["frac"] = round(achieved / attain["tflops"], 4)
@@ -340,7 +354,10 @@ def main() -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
-        "warmup": warm_steps,
+        "warmup": a.warmup,
+        "warmup_steps_run": warm_steps,
+        "settle_ms": a.settle_ms,
+        "shader_clock_mhz_after_region": round(clock_after_mhz, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -352,7 +369,9 @@ def main() -> int:
                    "M": wl.M, "N": wl.N, "K": wl.K, "R": wl.R,
                    "operands": (("MXFP4 (E2M1 + UE8M0 per 32 k)" if mx else "NVFP4 (E2M1 + E4M3 per 16 k)")
                                 + f", LoRA {a.dtype}, out {a.dtype}"),
-                   "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"]},
+                   "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"],
+                   "variant": plan["variant"], "ring_stages": plan["stages"],
+                   "lora_place": plan["lora_place"], "solver_choice": a.variant < 0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),

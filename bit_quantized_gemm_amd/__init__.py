@@ -14,10 +14,10 @@ from __future__ import annotations
 from . import _native
 from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK,
                       gemm_mxfp4_f16_raw, gemm_mxfp4_raw, gemm_w4a4_f16_raw, gemm_w4a4_raw,
-                      library_path, plan, strerror, variants)
+                      library_path, plan, plan_variant, run_raw, strerror, variants)
 
 __all__ = ["gemm_w4a4", "gemm_mxfp4", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
-           "gemm_mxfp4_f16_raw", "plan", "variants", "strerror", "library_path", "GemmError", "OK",
+           "gemm_mxfp4_f16_raw", "run_raw", "plan", "plan_variant", "variants", "strerror", "library_path", "GemmError", "OK",
            "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R", "FORMATS"]
 
 

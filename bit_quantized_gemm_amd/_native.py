@@ -22,7 +22,9 @@ MAX_R = 1024
 
 _PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n",
                 "threads", "lds_bytes", "lds_stage_bytes", "lds_limit", "tiles_m", "tiles_n",
-                "grid", "k_stages", "lora_steps")
+                "grid", "k_stages", "lora_steps", "occupancy", "policy", "lora_place",
+                "lds_ring_bytes", "lds_side_bytes", "flavour", "vgprs", "agprs", "sgprs",
+                "regs_limit")
 
 
 class Plan(ctypes.Structure):
@@ -71,6 +73,10 @@ def load() -> ctypes.CDLL:
         lib.gemm_mxfp4_num_variants.restype = i
         lib.gemm_mxfp4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
         lib.gemm_mxfp4_variant_info.restype = i
+        lib.gemm_w4a4_run.argtypes = [i, i, i] + [vp] * 9 + [i, i, i, i, vp]
+        lib.gemm_w4a4_run.restype = i
+        lib.gemm_w4a4_plan_variant.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
+        lib.gemm_w4a4_plan_variant.restype = i
         lib.gemm_w4a4_strerror.argtypes = [i]
         lib.gemm_w4a4_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -109,6 +115,25 @@ def gemm_mxfp4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, l
                                  out, M, N, K, R, stream)
 
 
+def run_raw(fmt: str, out_f16: bool, variant: int, act, ascales, wgt, wscales, wcscale, bias,
+            lora_act_in, lora_up, out, M, N, K, R, stream) -> int:
+    """gemm_w4a4_run: the operator with the format, output type and compiled
+    instance (-1: the solver's choice) named explicitly; returns its code."""
+    return load().gemm_w4a4_run(_FMT_CODE[fmt], int(out_f16), variant, act, ascales, wgt,
+                                wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
+                                stream)
+
+
+def plan_variant(M: int, N: int, K: int, R: int, variant: int, fmt: str = "nvfp4") -> dict:
+    """The plan of compiled instance `variant` (-1: the solver's) for a shape."""
+    p = Plan()
+    rc = load().gemm_w4a4_plan_variant(_FMT_CODE[fmt], variant, M, N, K, R, ctypes.byref(p))
+    if rc != OK:
+        raise ValueError(f"gemm_w4a4_plan_variant: {strerror(rc)} ({rc})")
+    return p.as_dict()
+
+
+_FMT_CODE = {"nvfp4": 0, "mxfp4": 1}
 FORMATS = ("nvfp4", "mxfp4")
 _PREFIX = {"nvfp4": "gemm_w4a4", "mxfp4": "gemm_mxfp4"}
 

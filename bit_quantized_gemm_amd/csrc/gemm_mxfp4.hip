@@ -286,39 +286,26 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
 
 // ------------------------------------------------------------------ host side
 
-struct MxVariant {
-  void (*kernel[2][3])(const Params);   // [F16][flavour: general, fast, fast with act-scale windows]
-  bool awin;                            // the third flavour exists (room for the windows)
-  int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
-};
-
+// Rounds of the chip x the work of one round, as for NVFP4; nothing is
+// decoded, so the per-tile factor is the LDS operand traffic per MFMA, which
+// grows as (TM + TN) / (TM * TN) for a wave tile TM x TN.
 template <class C>
-constexpr MxVariant make_mx_variant() {
-  return MxVariant{{{gemm_mxfp4_kernel<C, true, false>, gemm_mxfp4_kernel<C, false, false>,
-                     gemm_mxfp4_kernel<C, false, false, kAwinRoom<C>>},
-                    {gemm_mxfp4_kernel<C, true, true>, gemm_mxfp4_kernel<C, false, true>,
-                     gemm_mxfp4_kernel<C, false, true, kAwinRoom<C>>}},
-                   kAwinRoom<C>, C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
-                   C::LDS_BYTES, C::STAGE_BYTES, C::OCC};
+VariantDesc mx_variant() {
+  static const void* const k[2][3] = {
+      {reinterpret_cast<const void*>(gemm_mxfp4_kernel<C, true, false>),
+       reinterpret_cast<const void*>(gemm_mxfp4_kernel<C, false, false>),
+       reinterpret_cast<const void*>(gemm_mxfp4_kernel<C, false, false, kAwinRoom<C>>)},
+      {reinterpret_cast<const void*>(gemm_mxfp4_kernel<C, true, true>),
+       reinterpret_cast<const void*>(gemm_mxfp4_kernel<C, false, true>),
+       reinterpret_cast<const void*>(gemm_mxfp4_kernel<C, false, true, kAwinRoom<C>>)}};
+  constexpr double tm = double(C::TM), tn = double(C::TN);
+  constexpr double per_elem = 1.0 + 16.0 * (tm + tn) / (tm * tn);
+  constexpr double ref = 1.0 + 16.0 * (128.0 + 96.0) / (128.0 * 96.0);   // the 128x96 wave tile
+  return describe<C>(k, kAwinRoom<C>, per_elem / ref);
 }
 
-static const MxVariant kMxVariants[] = {make_mx_variant<MxCfg256x192>(), make_mx_variant<MxCfg128x128>()};
+static const VariantDesc kMxVariants[] = {mx_variant<MxCfg256x192>(), mx_variant<MxCfg128x128>()};
 static constexpr int kNumMxVariants = int(sizeof(kMxVariants) / sizeof(kMxVariants[0]));
-
-static void mx_fill_static(const MxVariant& v, int idx, gemm_w4a4_plan_t* pl) {
-  memset(pl, 0, sizeof(*pl));
-  pl->variant = idx;
-  pl->block_m = v.block_m;
-  pl->block_n = v.block_n;
-  pl->block_k = v.block_k;
-  pl->stages = v.stages;
-  pl->waves_m = v.waves_m;
-  pl->waves_n = v.waves_n;
-  pl->threads = v.threads;
-  pl->lds_bytes = v.lds_bytes;
-  pl->lds_stage_bytes = v.stage_bytes;
-  pl->lds_limit = kLdsLimit;
-}
 
 // K a multiple of the 32-wide scale block; every tensor below 2^31 bytes.
 static bool mx_sizes_ok(int M, int N, int K, int R) {
@@ -328,100 +315,41 @@ static bool mx_sizes_ok(int M, int N, int K, int R) {
   return m * k / 2 < lim && n * k / 2 < lim && m * n * 2 < lim && m * r * 2 < lim && r * n * 2 < lim;
 }
 
-// Rounds of the chip x the work of one round, as for NVFP4; nothing is
-// decoded, so the per-tile factor is the LDS operand traffic per MFMA, which
-// grows as (TM + TN) / (TM * TN) for a wave tile TM x TN.
-static int mx_choose_variant(int M, int N) {
-  int best = 0;
-  double best_cost = 0.0;
-  for (int v = 0; v < kNumMxVariants; ++v) {
-    const MxVariant& x = kMxVariants[v];
-    const long tiles = long((M + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
-    const long slots = long(kNumCUs) * x.occ;
-    const long rounds = (tiles + slots - 1) / slots;
-    const long per_cu = std::min<long>(x.occ, (tiles + kNumCUs - 1) / kNumCUs);
-    const double tm = double(x.block_m / x.waves_m), tn = double(x.block_n / x.waves_n);
-    const double per_round = double(per_cu) * x.block_m * x.block_n * (1.0 + 16.0 * (tm + tn) / (tm * tn));
-    const double cost = double(rounds) * per_round;
-    if (v == 0 || cost < best_cost) {
-      best = v;
-      best_cost = cost;
-    }
-  }
-  return best;
+// Fast flavour: K % 128 == 0, N % 8 == 0, 4-byte aligned scales, LoRA as for
+// NVFP4; M % 4 != 0 takes the act-scale windows where the tile has room for
+// them and the tensor holds at least one window (K/32 * M >= BM + 4).
+static int mx_flavour(const VariantDesc& v, int M, int N, int K, int R, uintptr_t scales, uintptr_t lora) {
+  const bool fast = K % 128 == 0 && N % 8 == 0 && (scales & 3u) == 0 &&
+                    (R == 0 || (R % 8 == 0 && (lora & 15u) == 0));
+  const bool awin = v.has_window && int64_t(K / 32) * M >= v.block_m + 4;
+  return !fast ? 0 : M % 4 == 0 ? 1 : awin ? 2 : 0;
 }
 
-static int mx_plan_impl(int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
-  const int v = mx_choose_variant(M, N);
-  const MxVariant& x = kMxVariants[v];
-  mx_fill_static(x, v, pl);
-  pl->tiles_m = (M + x.block_m - 1) / x.block_m;
-  pl->tiles_n = (N + x.block_n - 1) / x.block_n;
-  const long grid = long(pl->tiles_m) * pl->tiles_n;
-  if (grid > 0x7fffffffL) return GEMM_W4A4_EINVAL;
-  pl->grid = int(grid);
-  pl->k_stages = (K + x.block_k - 1) / x.block_k;
-  pl->lora_steps = (R + 15) / 16;
-  return GEMM_W4A4_OK;
+int mx_plan(int variant, int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
+  if (!pl || !mx_sizes_ok(M, N, K, R) || variant < -1 || variant >= kNumMxVariants) return GEMM_W4A4_EINVAL;
+  const int v = variant >= 0 ? variant : choose_variant(kMxVariants, kNumMxVariants, M, N);
+  const int rc = plan_for(kMxVariants[v], v, M, N, K, R, pl);
+  if (rc == GEMM_W4A4_OK) fill_registers(kMxVariants[v], mx_flavour(kMxVariants[v], M, N, K, R, 0, 0), pl);
+  return rc;
 }
 
-static int mx_launch(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
-                     const uint8_t* wscales, const float* wcscale, const float* bias,
-                     const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
-                     int M, int N, int K, int R, void* stream, bool f16) {
-  if (!mx_sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
-  if (!act || !ascales || !wgt || !wscales || !wcscale || !bias || !out) return GEMM_W4A4_EINVAL;
-  if (R > 0 && (!lora_act_in || !lora_up)) return GEMM_W4A4_EINVAL;
-  if ((uintptr_t(act) | uintptr_t(wgt)) & 15u) return GEMM_W4A4_EALIGN;
-  if ((uintptr_t(wcscale) | uintptr_t(bias)) & 3u) return GEMM_W4A4_EALIGN;
-  if ((uintptr_t(out) | (R > 0 ? (uintptr_t(lora_act_in) | uintptr_t(lora_up)) : 0u)) & 1u)
-    return GEMM_W4A4_EALIGN;
-
-  const size_t Ms = size_t(M), Ns = size_t(N), Ks = size_t(K), Rs = size_t(R);
-  const size_t out_bytes = Ms * Ns * 2;
-  const struct { const void* p; size_t n; } ins[] = {
-      {act, Ms * Ks / 2},      {ascales, Ks / 32 * Ms}, {wgt, Ns * Ks / 2},
-      {wscales, Ks / 32 * Ns}, {wcscale, Ns * 4},       {bias, Ns * 4},
-      {lora_act_in, Ms * Rs * 2}, {lora_up, Rs * Ns * 2}};
-  for (const auto& in : ins)
-    if (overlaps(out, out_bytes, in.p, in.n)) return GEMM_W4A4_EOVERLAP;
-
+int mx_run(int variant, bool f16, const CallArgs& a) {
+  if (!mx_sizes_ok(a.M, a.N, a.K, a.R) || variant < -1 || variant >= kNumMxVariants) return GEMM_W4A4_EINVAL;
+  int rc = check_call(a, 32);
+  if (rc != GEMM_W4A4_OK) return rc;
   gemm_w4a4_plan_t pl;
-  if (mx_plan_impl(M, N, K, R, &pl) != GEMM_W4A4_OK) return GEMM_W4A4_EINVAL;
-  const int dev_rc = check_device();
-  if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-
-  Params prm;
-  prm.act = act;
-  prm.ascales = ascales;
-  prm.wgt = wgt;
-  prm.wscales = wscales;
-  prm.wcscale = wcscale;
-  prm.bias = bias;
-  prm.lora_act_in = lora_act_in;
-  prm.lora_up = lora_up;
-  prm.out = out;
-  prm.M = M;
-  prm.N = N;
-  prm.K = K;
-  prm.R = R;
-  prm.tiles_m = pl.tiles_m;
-  prm.tiles_n = pl.tiles_n;
-
-  const MxVariant& v = kMxVariants[pl.variant];
-  const bool fast = K % 128 == 0 && N % 8 == 0 &&
-                    ((uintptr_t(ascales) | uintptr_t(wscales)) & 3u) == 0 &&
-                    (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
-  // M % 4 != 0: act-scale windows where the tile has room for them and the
-  // tensor holds at least one window (K/32 * M >= BM + 4)
-  const bool awin = v.awin && int64_t(K / 32) * M >= v.block_m + 4;
-  const int flavour = !fast ? 0 : M % 4 == 0 ? 1 : awin ? 2 : 0;
-  void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][flavour]),
-                                       dim3(pl.grid), dim3(v.threads), args, 0,
-                                       static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+  if (mx_plan(variant, a.M, a.N, a.K, a.R, &pl) != GEMM_W4A4_OK) return GEMM_W4A4_EINVAL;
+  rc = check_device();
+  if (rc != GEMM_W4A4_OK) return rc;
+  const VariantDesc& v = kMxVariants[pl.variant];
+  const int flavour = mx_flavour(v, a.M, a.N, a.K, a.R, uintptr_t(a.ascales) | uintptr_t(a.wscales),
+                                 a.R > 0 ? (uintptr_t(a.lora_act_in) | uintptr_t(a.lora_up)) : 0u);
+  return launch_kernel(v.kernel[f16 ? 1 : 0][flavour], pl, a);
 }
+
+// The NVFP4 family's plan and launch (gemm_w4a4.hip), for the format-generic calls.
+int nv_plan(int variant, int M, int N, int K, int R, gemm_w4a4_plan_t* pl);
+int nv_run(int variant, bool f16, const CallArgs& a);
 
 }  // namespace w4a4
 
@@ -431,27 +359,45 @@ extern "C" int gemm_mxfp4(const uint8_t* act, const uint8_t* ascales, const uint
                           const uint8_t* wscales, const float* wcscale, const float* bias,
                           const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
                           int M, int N, int K, int R, void* stream) {
-  return mx_launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
-                   stream, false);
+  return mx_run(-1, false, CallArgs{act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                                    M, N, K, R, stream});
 }
 
 extern "C" int gemm_mxfp4_f16(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
                               const uint8_t* wscales, const float* wcscale, const float* bias,
                               const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
                               int M, int N, int K, int R, void* stream) {
-  return mx_launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
-                   stream, true);
+  return mx_run(-1, true, CallArgs{act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                                   M, N, K, R, stream});
 }
 
 extern "C" int gemm_mxfp4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan) {
-  if (!plan || !mx_sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
-  return mx_plan_impl(M, N, K, R, plan);
+  return mx_plan(-1, M, N, K, R, plan);
 }
 
 extern "C" int gemm_mxfp4_num_variants(void) { return kNumMxVariants; }
 
 extern "C" int gemm_mxfp4_variant_info(int variant, gemm_w4a4_plan_t* plan) {
   if (!plan || variant < 0 || variant >= kNumMxVariants) return GEMM_W4A4_EINVAL;
-  mx_fill_static(kMxVariants[variant], variant, plan);
+  fill_static(kMxVariants[variant], variant, plan);
   return GEMM_W4A4_OK;
+}
+
+extern "C" int gemm_w4a4_run(int format, int out_f16, int variant, const uint8_t* act,
+                             const uint8_t* ascales, const uint8_t* wgt, const uint8_t* wscales,
+                             const float* wcscale, const float* bias, const uint16_t* lora_act_in,
+                             const uint16_t* lora_up, uint16_t* out, int M, int N, int K, int R,
+                             void* stream) {
+  if (out_f16 != 0 && out_f16 != 1) return GEMM_W4A4_EINVAL;
+  const CallArgs a{act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R, stream};
+  if (format == GEMM_W4A4_FMT_NVFP4) return nv_run(variant, out_f16 == 1, a);
+  if (format == GEMM_W4A4_FMT_MXFP4) return mx_run(variant, out_f16 == 1, a);
+  return GEMM_W4A4_EINVAL;
+}
+
+extern "C" int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
+                                      gemm_w4a4_plan_t* plan) {
+  if (format == GEMM_W4A4_FMT_NVFP4) return nv_plan(variant, M, N, K, R, plan);
+  if (format == GEMM_W4A4_FMT_MXFP4) return mx_plan(variant, M, N, K, R, plan);
+  return GEMM_W4A4_EINVAL;
 }

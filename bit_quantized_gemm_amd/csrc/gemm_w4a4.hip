@@ -5,13 +5,14 @@
 // and 6.6; E2M1 bit layout: the DeepGEMM FP4 indexer page, "Step 0").
 //
 // Design (one workgroup per BM x BN output tile, WM x WN waves, 1 wave/SIMD):
-//  * Loader: a 4-deep LDS ring. Each stage (128 values of k) of packed act and
+//  * Loader: an LDS ring whose depth S the budget solver sets (3 or 4
+//    stages; w4a4_layout.hpp). Each stage (128 values of k) of packed act and
 //    wgt moves HBM -> LDS by direct-to-LDS DMA (global_load_lds), 16-byte
 //    chunks XOR-swizzled by row so the consumer's LDS reads do not conflict.
 //    The stage's E4M3 scale tiles are loaded by the workgroup with coalesced
 //    8-byte loads (12-byte windows when M % 8 != 0), converted once to fp16
 //    and stored [k-block][row] in LDS.
-//    A stage's DMA is issued three iterations before it is consumed.
+//    A stage's DMA is issued S-1 iterations before it is consumed.
 //  * Decode: NVFP4 is exact in fp16. Every E2M1 value times every E4M3 scale
 //    has at most 6 significant bits and lies in [2^-10, 2688], so each operand
 //    value is built exactly as fp16: v_cvt_scalef32_pk_f16_fp4 (scale 1.0;
@@ -374,25 +375,30 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 #pragma unroll
     for (int t = 0; t < C::MI + C::NI; ++t) decode_tile(t, R, s, d);
   };
-  // ---- pipeline over a 4-deep LDS ring. Iteration st computes stage st,
-  // DMAs stage st+3, loads the raw scales of stage st+2 (register set st % 2),
-  // stores the fp16 scales of stage st+1 (loaded one iteration earlier, set
-  // (st+1) % 2) into its buffer, and reads chunk 1 of stage st and chunk 0 of
-  // stage st+1 into registers. The one barrier sits in the middle of the
-  // iteration, right before the first read of stage st+1: it publishes stage
-  // st+1 (DMA and scales), and every read of stage st-1 (its chunk 1 is read
-  // in k-steps 0-1 of iteration st-1) happened before the previous one, so
-  // DMA(st+3) may refill buffer (st+3) % 4 = (st-1) % 4 from the start of
-  // iteration st. The prologue only waits for stage 0; stage 1 has three
-  // k-steps of stage 0's compute to arrive in.
+  // ---- pipeline over an S-deep LDS ring (S = C::STAGES >= 3). Iteration st
+  // computes stage st, DMAs stage st+S-1, loads the raw scales of stage st+2
+  // (register set st % 2), stores the fp16 scales of stage st+1 (loaded one
+  // iteration earlier, set (st+1) % 2) into its buffer, and reads chunk 1 of
+  // stage st and chunk 0 of stage st+1 into registers. The one barrier sits in
+  // the middle of the iteration, right before the first read of stage st+1:
+  // it publishes stage st+1 (DMA and scales), and every read of stage st-1
+  // (its chunk 1 is read in k-steps 0-2 of iteration st-1) happened before the
+  // previous one, so DMA(st+S-1) may refill buffer (st+S-1) % S = (st-1) % S
+  // from the start of iteration st. The prologue issues DMA(0 .. S-2) and only
+  // waits for stage 0; stage 1 has three k-steps of stage 0's compute to
+  // arrive in.
   //
   // Prefetches past the last stage read clamped, in-range addresses into
   // buffers nobody reads again, and stages past K get zero scales, which keeps
   // the loop body free of branches. Vector-memory ops complete in issue
-  // order: per iteration SCL(st+2) then DMA(st+3), so at the scale store of
-  // iteration st the ops issued after SCL(st+1) are DMA(st+2), SCL(st+2) and
-  // DMA(st+3); waiting until at most that many remain completes SCL(st+1)
-  // and everything before it, DMA(st+1) included.
+  // order: the prologue issues SCL(0), DMA(0), SCL(1), DMA(1 .. S-2), and
+  // iteration j issues SCL(j+2) then DMA(j+S-1). The scale store of iteration
+  // st needs SCL(st+1) and DMA(st+1). With S >= 4, DMA(st+1) is older than
+  // SCL(st+1), and the ops issued after SCL(st+1) are DMA(st+S-2), SCL(st+2)
+  // and DMA(st+S-1); with S = 3, DMA(st+1) is the younger one and SCL(st+2),
+  // DMA(st+2) follow it. Waiting until at most min(S-2, 2) DMA rounds plus one
+  // scale load pair remain completes both (for st = 0 more may remain; the
+  // smaller count is the stricter wait and serves every st).
   //
   // Inside an iteration every instruction has a fixed slot: k-step S (0..7)
   // runs G MFMA groups; group q issues MFMA q, decodes
@@ -414,7 +420,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   constexpr int SLOT_RD1 = 2 + DMA_SLOTS, SLOT_RD0 = 4 * G, SLOT_SCL = 3 * G + G / 2;
   // ops issued after SCL(st+1): DMA(st+2), SCL(st+2) (2 loads per thread in
   // the fast flavour; the general one counts none, which waits longer), DMA(st+3)
-  constexpr int VM_AFTER_SCL = 2 * DMA_N + (GENERAL ? 0 : 2);
+  constexpr int VM_AFTER_SCL = std::min(C::STAGES - 2, 2) * DMA_N + (GENERAL ? 0 : 2);
+  static_assert(VM_AFTER_SCL < 64, "vmcnt range");
   static_assert(T <= G, "one decode per MFMA group");
   static_assert(SLOT_RD1 + T <= 3 * G, "chunk 1 must be requested before k-step 3 decodes it");
   static_assert(SLOT_RD1 + T <= SLOT_SCL, "slots overlap");
@@ -425,9 +432,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   load_scales(0, s_raw[0]);
   issue_dma(0, 0);
   load_scales(min(1, last), s_raw[1]);
-  issue_dma(min(1, last), 1);
-  issue_dma(min(2, last), 2);
-  wait_vm_lgkm0<2 * DMA_N + (GENERAL ? 0 : 2)>();   // SCL(0), DMA(0)
+#pragma unroll
+  for (int j = 1; j < C::STAGES - 1; ++j) issue_dma(min(j, last), j);
+  // SCL(0), DMA(0): after them come SCL(1) and DMA(1 .. S-2)
+  wait_vm_lgkm0<std::min(63, (C::STAGES - 2) * DMA_N + (GENERAL ? 0 : 2))>();
   store_scales(0, 0, s_raw[0]);
   wait_vm_lgkm0<63>();
   wg_barrier();
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 
   // PAR = st & 1, fixed per call site of the two-way unrolled loop.
   auto iteration = [&]<int PAR>(int st) __attribute__((always_inline)) {
-    const int st_scl = min(st + 2, last), st_dma = min(st + 3, last);
+    const int st_scl = min(st + 2, last), st_dma = min(st + C::STAGES - 1, last);
     // k-step S: Sv is an int, or (general flavour) a std::integral_constant
     auto kstep = [&](auto Sv) __attribute__((always_inline)) {
       const int S = Sv;
@@ -458,7 +466,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
           load_scale_half(st_scl, s_raw[PAR], slot);
         else if (slot < SLOT_RD1)
 #pragma unroll
-          for (int u = 0; u < DMA_PER_SLOT; ++u) dma_part(st_dma, st + 3, (slot - 2) * DMA_PER_SLOT + u);
+          for (int u = 0; u < DMA_PER_SLOT; ++u)
+            dma_part(st_dma, st + C::STAGES - 1, (slot - 2) * DMA_PER_SLOT + u);
         else if (slot < SLOT_RD1 + T)
           read_tile(st, 1, slot - SLOT_RD1, C1);
         else if (slot == SLOT_SCL) {
@@ -493,44 +502,29 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
 
 // ------------------------------------------------------------------ host side
 
-struct Variant {
-  void (*kernel[2][3])(const Params);   // [F16][flavour: general, fast, fast with act scales byte by byte]
-  int block_m, block_n, block_k, stages, waves_m, waves_n, threads, lds_bytes, stage_bytes, occ;
-  double cost;   // time per output element of a full round, relative to 256x192
-};
-
 template <class C>
-constexpr Variant make_variant(double cost) {
-  return Variant{{{gemm_w4a4_kernel<C, true, false, false>, gemm_w4a4_kernel<C, false, false, false>,
-                   gemm_w4a4_kernel<C, false, false, true>},
-                  {gemm_w4a4_kernel<C, true, true, false>, gemm_w4a4_kernel<C, false, true, false>,
-                   gemm_w4a4_kernel<C, false, true, true>}},
-                 C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN, C::THREADS,
-                 C::LDS_BYTES, C::STAGE_BYTES, C::OCC, cost};
+VariantDesc nv_variant(double cost) {
+  static const void* const k[2][3] = {
+      {reinterpret_cast<const void*>(gemm_w4a4_kernel<C, true, false, false>),
+       reinterpret_cast<const void*>(gemm_w4a4_kernel<C, false, false, false>),
+       reinterpret_cast<const void*>(gemm_w4a4_kernel<C, false, false, true>)},
+      {reinterpret_cast<const void*>(gemm_w4a4_kernel<C, true, true, false>),
+       reinterpret_cast<const void*>(gemm_w4a4_kernel<C, false, true, false>),
+       reinterpret_cast<const void*>(gemm_w4a4_kernel<C, false, true, true>)}};
+  return describe<C>(k, true, cost);
 }
 
-// Relative costs measured on MI355X at the M = 4352 shapes (K = 3840..15360),
-// where each instance needs whole rounds: a 256x192 tile-round per output
-// element 1.00, 256x128 1.16, two 128x128 tiles sharing a CU 1.22. Smaller
-// wave tiles decode more operand tiles per MFMA (0.58, 0.75 and 1.0 per MFMA).
-static const Variant kVariants[] = {make_variant<Cfg256x192>(1.00), make_variant<Cfg128x128>(1.22),
-                                    make_variant<Cfg256x128>(1.16)};
+// Relative costs per output element of a full round, measured on MI355X at
+// the M = 4352 shapes (K = 3840..15360), where each instance needs whole
+// rounds: 256x192 1.00, 256x128 1.16, two 128x128 tiles sharing a CU 1.22
+// with a 4-deep ring and no side region, 1.20 with a 3-deep ring and the
+// whole side region (1.5-2.2 % faster than the 4-deep ring at every shape
+// where 128x128 tiles win: the first LoRA chunk and wcscale/bias arrive during
+// the K-loop, and three stages still cover the DMA latency). Smaller wave
+// tiles decode more operand tiles per MFMA (0.58, 0.75 and 1.0 per MFMA).
+static const VariantDesc kVariants[] = {nv_variant<Cfg256x192>(1.00), nv_variant<Cfg128x128>(1.22),
+                                        nv_variant<Cfg256x128>(1.16), nv_variant<Cfg128x128S>(1.20)};
 static constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
-
-static void fill_static(const Variant& v, int idx, gemm_w4a4_plan_t* pl) {
-  memset(pl, 0, sizeof(*pl));
-  pl->variant = idx;
-  pl->block_m = v.block_m;
-  pl->block_n = v.block_n;
-  pl->block_k = v.block_k;
-  pl->stages = v.stages;
-  pl->waves_m = v.waves_m;
-  pl->waves_n = v.waves_n;
-  pl->threads = v.threads;
-  pl->lds_bytes = v.lds_bytes;
-  pl->lds_stage_bytes = v.stage_bytes;
-  pl->lds_limit = kLdsLimit;
-}
 
 // Size rules. Besides the operator's own (K a multiple of the 16-wide scale
 // block), every tensor must stay below 2^31 bytes: the kernels address them
@@ -544,44 +538,38 @@ static bool sizes_ok(int M, int N, int K, int R) {
          r * n * 2 < lim;
 }
 
-// Budget solver: for each compiled instance, the number of rounds the chip
-// needs (tiles / (CUs * workgroups resident per CU)) times the time of one
-// round (the workgroups resident on the busiest CU, times the tile's elements,
-// times the instance's measured relative cost); picks the instance with the
-// smallest estimate. Ties go to the earlier instance.
-static int choose_variant(int M, int N) {
-  int best = 0;
-  double best_cost = 0.0;
-  for (int v = 0; v < kNumVariants; ++v) {
-    const Variant& x = kVariants[v];
-    const long tiles = long((M + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
-    const long slots = long(kNumCUs) * x.occ;
-    const long rounds = (tiles + slots - 1) / slots;
-    // workgroups sharing the busiest compute unit in a round (fewer than occ
-    // when the tiles do not fill the chip)
-    const long per_cu = std::min<long>(x.occ, (tiles + kNumCUs - 1) / kNumCUs);
-    const double per_round = double(per_cu) * x.block_m * x.block_n * x.cost;
-    const double cost = double(rounds) * per_round;
-    if (v == 0 || cost < best_cost) {
-      best = v;
-      best_cost = cost;
-    }
-  }
-  return best;
+// Flavour: fast where packed rows, wgt scales and LoRA operands allow wide
+// accesses; within it, act scales in 8-byte loads when their rows are
+// 8-byte aligned, else in 12-byte windows (needs a 4-byte aligned act-scale
+// tensor of a multiple of 4 bytes, at least 12); general otherwise.
+static int nv_flavour(int M, int N, int K, int R, uintptr_t ascales, uintptr_t wscales, uintptr_t lora) {
+  const bool fast = K % 32 == 0 && N % 8 == 0 && (wscales & 7u) == 0 &&
+                    (R == 0 || (R % 8 == 0 && (lora & 15u) == 0));
+  const size_t a_bytes = size_t(K) / 16 * size_t(M);
+  const bool a_rows8 = M % 8 == 0 && (ascales & 7u) == 0;
+  const bool a_window = (ascales & 3u) == 0 && a_bytes % 4 == 0 && a_bytes >= 12;
+  return !fast ? 0 : a_rows8 ? 1 : a_window ? 2 : 0;
 }
 
-static int plan_impl(int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
-  const int v = choose_variant(M, N);
-  const Variant& x = kVariants[v];
-  fill_static(x, v, pl);
-  pl->tiles_m = (M + x.block_m - 1) / x.block_m;
-  pl->tiles_n = (N + x.block_n - 1) / x.block_n;
-  const long grid = long(pl->tiles_m) * pl->tiles_n;
-  if (grid > 0x7fffffffL) return GEMM_W4A4_EINVAL;
-  pl->grid = int(grid);
-  pl->k_stages = (K + x.block_k - 1) / x.block_k;
-  pl->lora_steps = (R + 15) / 16;
-  return GEMM_W4A4_OK;
+int nv_plan(int variant, int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
+  if (!pl || !sizes_ok(M, N, K, R) || variant < -1 || variant >= kNumVariants) return GEMM_W4A4_EINVAL;
+  const int v = variant >= 0 ? variant : choose_variant(kVariants, kNumVariants, M, N);
+  const int rc = plan_for(kVariants[v], v, M, N, K, R, pl);
+  if (rc == GEMM_W4A4_OK) fill_registers(kVariants[v], nv_flavour(M, N, K, R, 0, 0, 0), pl);
+  return rc;
+}
+
+int nv_run(int variant, bool f16, const CallArgs& a) {
+  if (!sizes_ok(a.M, a.N, a.K, a.R) || variant < -1 || variant >= kNumVariants) return GEMM_W4A4_EINVAL;
+  int rc = check_call(a, 16);
+  if (rc != GEMM_W4A4_OK) return rc;
+  gemm_w4a4_plan_t pl;
+  if (nv_plan(variant, a.M, a.N, a.K, a.R, &pl) != GEMM_W4A4_OK) return GEMM_W4A4_EINVAL;
+  rc = check_device();
+  if (rc != GEMM_W4A4_OK) return rc;
+  const int flavour = nv_flavour(a.M, a.N, a.K, a.R, uintptr_t(a.ascales), uintptr_t(a.wscales),
+                                 a.R > 0 ? (uintptr_t(a.lora_act_in) | uintptr_t(a.lora_up)) : 0u);
+  return launch_kernel(kVariants[pl.variant].kernel[f16 ? 1 : 0][flavour], pl, a);
 }
 
 }  // namespace w4a4
@@ -589,8 +577,7 @@ static int plan_impl(int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
 using namespace w4a4;
 
 extern "C" int gemm_w4a4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan) {
-  if (!plan || !sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
-  return plan_impl(M, N, K, R, plan);
+  return nv_plan(-1, M, N, K, R, plan);
 }
 
 extern "C" int gemm_w4a4_num_variants(void) { return kNumVariants; }
@@ -613,80 +600,18 @@ extern "C" const char* gemm_w4a4_strerror(int code) {
   }
 }
 
-// Validation and launch shared by the bf16 and the fp16 entry points.
-static int launch(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
-                  const uint8_t* wscales, const float* wcscale, const float* bias,
-                  const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
-                  int M, int N, int K, int R, void* stream, bool f16) {
-  if (!sizes_ok(M, N, K, R)) return GEMM_W4A4_EINVAL;
-  if (!act || !ascales || !wgt || !wscales || !wcscale || !bias || !out) return GEMM_W4A4_EINVAL;
-  if (R > 0 && (!lora_act_in || !lora_up)) return GEMM_W4A4_EINVAL;
-  if ((uintptr_t(act) | uintptr_t(wgt)) & 15u) return GEMM_W4A4_EALIGN;
-  if ((uintptr_t(wcscale) | uintptr_t(bias)) & 3u) return GEMM_W4A4_EALIGN;
-  if ((uintptr_t(out) | (R > 0 ? (uintptr_t(lora_act_in) | uintptr_t(lora_up)) : 0u)) & 1u)
-    return GEMM_W4A4_EALIGN;
-
-  const size_t Ms = size_t(M), Ns = size_t(N), Ks = size_t(K), Rs = size_t(R);
-  const size_t out_bytes = Ms * Ns * 2;
-  const struct { const void* p; size_t n; } ins[] = {
-      {act, Ms * Ks / 2},     {ascales, Ks / 16 * Ms}, {wgt, Ns * Ks / 2},
-      {wscales, Ks / 16 * Ns}, {wcscale, Ns * 4},      {bias, Ns * 4},
-      {lora_act_in, Ms * Rs * 2}, {lora_up, Rs * Ns * 2}};
-  for (const auto& in : ins)
-    if (overlaps(out, out_bytes, in.p, in.n)) return GEMM_W4A4_EOVERLAP;
-
-  gemm_w4a4_plan_t pl;
-  if (plan_impl(M, N, K, R, &pl) != GEMM_W4A4_OK) return GEMM_W4A4_EINVAL;
-  const int dev_rc = check_device();
-  if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-
-  Params prm;
-  prm.act = act;
-  prm.ascales = ascales;
-  prm.wgt = wgt;
-  prm.wscales = wscales;
-  prm.wcscale = wcscale;
-  prm.bias = bias;
-  prm.lora_act_in = lora_act_in;
-  prm.lora_up = lora_up;
-  prm.out = out;
-  prm.M = M;
-  prm.N = N;
-  prm.K = K;
-  prm.R = R;
-  prm.tiles_m = pl.tiles_m;
-  prm.tiles_n = pl.tiles_n;
-
-  const Variant& v = kVariants[pl.variant];
-  // Flavour: fast where packed rows, wgt scales and LoRA operands allow wide
-  // accesses; within it, act scales in 8-byte loads when their rows are
-  // 8-byte aligned, else in 12-byte windows (needs a 4-byte aligned act-scale
-  // tensor of a multiple of 4 bytes, at least 12); general otherwise.
-  const bool fast = K % 32 == 0 && N % 8 == 0 && (uintptr_t(wscales) & 7u) == 0 &&
-                    (R == 0 || (R % 8 == 0 && ((uintptr_t(lora_act_in) | uintptr_t(lora_up)) & 15u) == 0));
-  const size_t a_bytes = Ks / 16 * Ms;
-  const bool a_rows8 = M % 8 == 0 && (uintptr_t(ascales) & 7u) == 0;
-  const bool a_window = (uintptr_t(ascales) & 3u) == 0 && a_bytes % 4 == 0 && a_bytes >= 12;
-  const int flavour = !fast ? 0 : a_rows8 ? 1 : a_window ? 2 : 0;
-  void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(v.kernel[f16 ? 1 : 0][flavour]),
-                                       dim3(pl.grid), dim3(v.threads), args, 0,
-                                       static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
-}
-
 extern "C" int gemm_w4a4(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
                          const uint8_t* wscales, const float* wcscale, const float* bias,
                          const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
                          int M, int N, int K, int R, void* stream) {
-  return launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
-                stream, false);
+  return nv_run(-1, false, CallArgs{act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                                    M, N, K, R, stream});
 }
 
 extern "C" int gemm_w4a4_f16(const uint8_t* act, const uint8_t* ascales, const uint8_t* wgt,
                              const uint8_t* wscales, const float* wcscale, const float* bias,
                              const uint16_t* lora_act_in, const uint16_t* lora_up, uint16_t* out,
                              int M, int N, int K, int R, void* stream) {
-  return launch(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out, M, N, K, R,
-                stream, true);
+  return nv_run(-1, true, CallArgs{act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up, out,
+                                   M, N, K, R, stream});
 }

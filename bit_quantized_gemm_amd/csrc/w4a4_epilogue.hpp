@@ -36,6 +36,10 @@ template <class C, bool GENERAL>
 __device__ __forceinline__ void epilogue_prefetch(const Params& p, uint8_t* smem, const int tid,
                                                   const int m0, const int n0, EpiRegs& regs) {
   using S = typename C::Side;
+  // each piece's DMA footprint is exactly the bytes the budget solver counted
+  static_assert(S::WB_SLOTS / C::THREADS * C::THREADS * 4 == S::WB_BYTES, "WB footprint");
+  static_assert(C::BM * 4 / C::THREADS * C::THREADS * 16 == S::LA_BYTES, "LA footprint");
+  static_assert(32 * (C::BN / 8) / C::THREADS * C::THREADS * 16 == S::LU_BYTES, "LU footprint");
   if constexpr (!GENERAL && S::ON) {
     const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = p.N, R = p.R;

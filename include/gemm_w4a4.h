@@ -117,27 +117,49 @@ int gemm_mxfp4_f16(const uint8_t* act, const uint8_t* ascales,
                    uint16_t* out, int M, int N, int K, int R, void* stream);
 
 /*
- * Launch plan chosen by the LDS/register budget solver for one problem size.
- * Filled by gemm_w4a4_plan; pure host arithmetic (no HIP call), so it also
- * runs on a machine without a GPU.
+ * Launch plan chosen by the solver for one problem size: which compiled tile
+ * instance runs, and how that instance's LDS budget was solved — the ring
+ * depth (stages of K in flight) and where the epilogue's first LoRA chunk and
+ * per-column factors live — with the registers its code object uses. The
+ * SVDQuant W4A4 on Blackwell page (section 7) shows what a miscounted buffer
+ * in such a budget does: a silently shallower pipeline. Here the kernels carve
+ * LDS from the same solved budget that these fields report. Pure host
+ * arithmetic and table lookups (no HIP call), so it also runs without a GPU.
  */
 typedef struct {
   int variant;        /* index of the compiled kernel instance */
   int block_m;        /* output rows per workgroup tile */
   int block_n;        /* output columns per workgroup tile */
   int block_k;        /* k per pipeline stage */
-  int stages;         /* LDS stages of the operand ring */
+  int stages;         /* ring depth: LDS stages of K in flight, set by the budget solve */
   int waves_m;        /* wave grid inside a workgroup */
   int waves_n;
   int threads;        /* threads per workgroup */
-  int lds_bytes;      /* LDS the instance uses, from the same layout the kernel carves */
-  int lds_stage_bytes;/* bytes of one ring stage (packed A + packed B) */
+  int lds_bytes;      /* LDS the instance uses: lds_ring_bytes + lds_side_bytes */
+  int lds_stage_bytes;/* bytes of one ring stage (packed operands and their scales) */
   int lds_limit;      /* LDS available to one workgroup on gfx950 */
   int tiles_m;
   int tiles_n;
   int grid;           /* workgroups launched */
   int k_stages;       /* pipeline iterations over K */
   int lora_steps;     /* 16-deep LoRA MFMA steps (ceil(R/16)) */
+  int occupancy;      /* workgroups of this instance per compute unit (LDS share = lds_limit / occupancy) */
+  int policy;         /* budget solve: 0 deepest ring first, 1 whole side region first */
+  int lora_place;     /* where the first 32 LoRA ranks and wcscale/bias wait for the epilogue:
+                         0 nowhere: loaded by the epilogue and staged through the drained ring;
+                         1 side region with wcscale/bias and the lora_act_in rows (lora_up in
+                           registers held through the K-loop);
+                         2 side region with the lora_up rows too.
+                         Ranks past 32 always go through the drained ring. */
+  int lds_ring_bytes; /* stages * lds_stage_bytes */
+  int lds_side_bytes; /* side region beside the ring (0 when lora_place == 0) */
+  int flavour;        /* kernel flavour the shape gets when every tensor is 16-byte aligned:
+                         0 general, 1 fast, 2 fast with act-scale windows; -1 in variant_info */
+  int vgprs;          /* vector registers a lane of that kernel (bf16 output) holds, architectural and
+                         accumulation together, from its code object; -1 if unknown */
+  int agprs;          /* of which accumulation registers */
+  int sgprs;          /* scalar registers, same kernel */
+  int regs_limit;     /* VGPR + AGPR a lane may hold at this occupancy (512 per SIMD lane, shared) */
 } gemm_w4a4_plan_t;
 
 /* Fill *plan for (M, N, K, R). Returns GEMM_W4A4_OK or GEMM_W4A4_EINVAL
@@ -154,6 +176,32 @@ int gemm_w4a4_variant_info(int variant, gemm_w4a4_plan_t* plan);
 int gemm_mxfp4_plan(int M, int N, int K, int R, gemm_w4a4_plan_t* plan);
 int gemm_mxfp4_num_variants(void);
 int gemm_mxfp4_variant_info(int variant, gemm_w4a4_plan_t* plan);
+
+/* Operand formats and output types of gemm_w4a4_run / gemm_w4a4_plan_variant. */
+enum { GEMM_W4A4_FMT_NVFP4 = 0, GEMM_W4A4_FMT_MXFP4 = 1 };
+
+/*
+ * gemm_w4a4_run — the same operator with every choice explicit, for callers
+ * that pick the tiling per shape themselves (the solver's choice is a model;
+ * this runs any compiled instance):
+ *   format   GEMM_W4A4_FMT_NVFP4 (as gemm_w4a4) or GEMM_W4A4_FMT_MXFP4 (as gemm_mxfp4)
+ *   out_f16  0: LoRA operands and output bfloat16; 1: binary16 (as the _f16 calls)
+ *   variant  a compiled instance of that format, 0 <= variant < its
+ *            num_variants, or -1 for the solver's choice
+ * Every other argument, layout, rule and return code is the named entry
+ * point's; an unknown format or variant returns GEMM_W4A4_EINVAL.
+ */
+int gemm_w4a4_run(int format, int out_f16, int variant,
+                  const uint8_t* act, const uint8_t* ascales,
+                  const uint8_t* wgt, const uint8_t* wscales,
+                  const float* wcscale, const float* bias,
+                  const uint16_t* lora_act_in, const uint16_t* lora_up,
+                  uint16_t* out, int M, int N, int K, int R, void* stream);
+
+/* The plan gemm_w4a4_run would follow for (format, variant, M, N, K, R);
+ * variant -1 gives the solver's choice (the format's _plan call). */
+int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
+                           gemm_w4a4_plan_t* plan);
 
 /* Static string for a return code (never NULL). */
 const char* gemm_w4a4_strerror(int code);

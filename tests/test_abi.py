@@ -221,8 +221,8 @@ def test_solver_lds_matches_code_objects():
     cases = [(v, "7TileCfgI", 6) for v in w4.variants("nvfp4")] + \
             [(v, "9MxTileCfgI", 6 if v["block_m"] == 256 else 4) for v in w4.variants("mxfp4")]
     for v, tag, count in cases:
-        key = tag + "Li%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
-                                                  v["waves_n"], v["stages"])
+        key = tag + "Li%dELi%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
+                                                       v["waves_n"], v["occupancy"], v["policy"])
         hits = [m for n, m in meta.items() if key in n]
         assert len(hits) == count, (key, list(meta))
         for m in hits:
@@ -262,3 +262,28 @@ _TILE = (0x1000, 0x2000, 0x3000, 0x4000, 0x5000)   # act, ascales, wgt, wscales,
     (_TILE[:4] + (0x5002,), 64, w4.EALIGN)])
 def test_route_b_tile_validation(ptrs, K, want):
     assert probes.route_b_tile_raw(*ptrs, K, 0) == want
+
+
+@pytest.mark.parametrize("fmt,out_f16,variant", [("nvfp4", 0, 99), ("nvfp4", 0, -2), ("mxfp4", 1, 7),
+                                                 ("nvfp4", 2, 0)])
+def test_run_rejects_unknown_variant_or_type(fmt, out_f16, variant):
+    rc = w4.run_raw(fmt, out_f16, variant, 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000,
+                    0x70000, 0x80000, 0x90000000, 64, 64, 128, 16, 0)
+    assert rc == w4.EINVAL
+
+
+def test_run_rejects_unknown_format():
+    lib = _native.load()
+    assert lib.gemm_w4a4_run(5, 0, -1, 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000,
+                             0x70000, 0x80000, 0x90000000, 64, 64, 128, 16, None) == w4.EINVAL
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_plan_variant_matches_plan(fmt):
+    for shape in [(4096, 3072, 3072, 32), (1000, 3072, 3072, 16), (4352, 3840, 3840, 128)]:
+        assert w4.plan_variant(*shape, -1, fmt=fmt) == w4.plan(*shape, fmt=fmt)
+        for v in range(len(w4.variants(fmt))):
+            q = w4.plan_variant(*shape, v, fmt=fmt)
+            assert q["variant"] == v and q["grid"] == q["tiles_m"] * q["tiles_n"]
+    with pytest.raises(ValueError):
+        w4.plan_variant(64, 64, 128, 0, len(w4.variants(fmt)), fmt=fmt)

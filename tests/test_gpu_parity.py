@@ -508,6 +508,42 @@ def test_misaligned_act_scales(shift):
     assert_parity(out_b.view(torch.int16).cpu().numpy().view(np.uint16), y, T, f"act scales at offset {shift}")
 
 
+# Every compiled tile instance of both formats through gemm_w4a4_run, on the
+# fast flavour (aligned), the act-scale window flavour (M % 8 != 0) and the
+# general one (K % 32 != 0, R % 8 != 0), bf16 and fp16: the solver may pick
+# any of them, and callers may name one.
+EVERY_VARIANT_SHAPES = [(520, 392, 640, 32), (517, 392, 640, 24), (264, 200, 272, 20)]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", EVERY_VARIANT_SHAPES, ids=["x".join(map(str, s)) for s in EVERY_VARIANT_SHAPES])
+def test_every_variant(shape, dtype, fmt):
+    M, N, K, R = shape
+    if fmt == "mxfp4" and K % 32:
+        K += 16
+    x = synthetic.custom_inputs(M, N, K, R, seed=M + K + R, dtype=dtype, fmt=fmt)
+    x["dtype"] = dtype
+    d = to_device(x)
+    y, T = full_reference(x, fmt)
+    half = torch.float16 if dtype == "f16" else torch.bfloat16
+    for v in range(len(w4.variants(fmt))):
+        p = w4.plan_variant(M, N, K, R, v, fmt=fmt)
+        _say(f"case: {fmt} variant {v} ({p['block_m']}x{p['block_n']}, ring {p['stages']}, "
+             f"side {p['lora_place']}), M={M} N={N} K={K} R={R} {dtype}")
+        out = torch.empty((M, N), dtype=half, device=DEV)
+        la = d["lora_act_in"].data_ptr() if R else 0
+        lu = d["lora_up"].data_ptr() if R else 0
+        rc = w4.run_raw(fmt, dtype == "f16", v, d["act"].data_ptr(), d["ascales"].data_ptr(),
+                        d["wgt"].data_ptr(), d["wscales"].data_ptr(), d["wcscale"].data_ptr(),
+                        d["bias"].data_ptr(), la, lu, out.data_ptr(), M, N, K, R,
+                        torch.cuda.current_stream().cuda_stream)
+        assert rc == w4.OK, rc
+        torch.cuda.synchronize()
+        assert_parity(out.view(torch.int16).cpu().numpy().view(np.uint16), y, T,
+                      f"{fmt} variant {v} {shape} {dtype}", dtype)
+
+
 # wcscale / bias 4 bytes off 16-byte alignment (the interface asks for 4):
 # the epilogue's per-column reads, on the general flavour (K % 32 != 0) and
 # on the 128x128 instance (no side region), for both operand formats.
