@@ -30,7 +30,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "custom_inputs", "no_lora_affine",
-           "bf16_bits_from_f32", "f16_bits_from_f32", "e4m3_scale_byte", "large_inputs"]
+           "bf16_bits_from_f32", "f16_bits_from_f32", "e4m3_scale_byte", "large_inputs",
+           "producer_inputs", "producer_workload_inputs", "PRODUCER_SEED_OFFSET"]
 
 
 @dataclass(frozen=True)
@@ -232,3 +233,34 @@ def large_inputs(M: int, N: int, K: int, R: int, seed: int, fmt: str = "nvfp4") 
     lora_up = bf16_bits_from_f32((rng.standard_normal(size=(R, N)) * 0.1).astype(np.float32))
     return dict(act=act, ascales=ascales, wgt=wgt, wscales=wscales, wcscale=wcscale, bias=bias,
                 lora_act_in=lora_act_in, lora_up=lora_up, M=M, N=N, K=K, R=R, dtype="bf16", fmt=fmt)
+
+
+# ---------------------------------------------------------------- producer inputs
+#
+# The other half of the layer: bf16 activations x [M, K] (the tensor the fused
+# GEMM's act / ascales are quantised from) and the LoRA-down weights
+# lora_down [R, K] (one rank per row). The pages give no activation
+# statistics; the recipe: x[m, k] = N(0, 1) * c[k] with a per-channel
+# magnitude c[k] = 2^U(-3, 3) and 1 % of the channels 32x larger (outlier
+# channels, the structure low-rank branches absorb), rounded to bf16;
+# lora_down = bf16 of N(0, 0.02). The shapes are the GEMM workloads' M x K, R.
+
+PRODUCER_SEED_OFFSET = 500
+
+
+def producer_inputs(M: int, K: int, R: int, seed: int) -> dict:
+    """Seeded producer inputs: x bf16 bits [M, K], lora_down bf16 bits [R, K]."""
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    rng = np.random.default_rng(seed)
+    c = np.exp2(rng.uniform(-3.0, 3.0, size=K))
+    c[rng.random(size=K) < 0.01] *= 32.0
+    x = rng.standard_normal(size=(M, K)).astype(np.float32) * c.astype(np.float32)[None, :]
+    lora_down = (rng.standard_normal(size=(R, K)) * 0.02).astype(np.float32)
+    return dict(x=bf16_bits_from_f32(x), lora_down=bf16_bits_from_f32(lora_down), M=M, K=K, R=R)
+
+
+def producer_workload_inputs(name: str) -> dict:
+    """Producer inputs at a GEMM workload's M x K and rank R (the x it would quantise)."""
+    wl = WORKLOADS[name]
+    return producer_inputs(wl.M, wl.K, wl.R, seed=wl.seed + PRODUCER_SEED_OFFSET)
