@@ -184,6 +184,111 @@ def cpu_baseline(inputs: dict, seconds: float, fmt: str = "nvfp4", got_rows=None
     return base, parity
 
 
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+
+
+def producer_bytes(M: int, K: int, R: int) -> int:
+    """Algorithmic HBM bytes of one quantize_w4a4_act call: x read once, lora_down
+    once, act + ascales + lora_act_in written once."""
+    return 2 * M * K + 2 * R * K + M * K // 2 + M * K // 16 + 2 * M * R
+
+
+def settle_and_time(step, stream, steps, warmup, settle_ms):
+    """Warm-up (W steps, then until the step has kept the GPU busy settle_ms),
+    then exactly `steps` steps between two events on the launch stream;
+    returns (warm-up steps run, region ms, wall s)."""
+    import torch
+    warm = 0
+    t_warm = time.perf_counter()
+    while True:
+        for _ in range(max(1, warmup) if warm == 0 else 16):
+            step()
+            warm += 1
+        torch.cuda.synchronize()
+        if warm >= warmup and (time.perf_counter() - t_warm) * 1e3 >= settle_ms:
+            break
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return warm, e0.elapsed_time(e1), time.perf_counter() - t0
+
+
+def bench_producer(a, wl) -> int:
+    """quantize_w4a4_act at the workload's M x K, rank R: GB/s of algorithmic
+    traffic against the HBM peak; the oracle on a bounded row sample beside it."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_gemm_amd as w4
+    import synthetic
+    M, K, R = wl.M, wl.K, wl.R
+    d = synthetic.producer_inputs(M, K, R, seed=wl.seed + synthetic.PRODUCER_SEED_OFFSET)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    ld = torch.from_numpy(d["lora_down"].view(np.int16)).view(torch.bfloat16).to(dev) if R else None
+    act, asc, la = w4.quantize_w4a4_act(x, ld)
+    stream = torch.cuda.current_stream(dev)
+    args = (x.data_ptr(), ld.data_ptr() if R else 0, act.data_ptr(), asc.data_ptr(),
+            la.data_ptr() if R else 0, M, K, R, stream.cuda_stream)
+    bad = []
+
+    def step():
+        rc = w4.quantize_raw(*args)
+        if rc != 0:
+            bad.append(rc)
+
+    warm, region_ms, wall = settle_and_time(step, stream, a.steps, a.warmup, a.settle_ms)
+    if bad:
+        print(f"quantize_w4a4_act returned {bad[0]} ({w4.strerror(bad[0])})", file=sys.stderr)
+        return 1
+    nbytes = producer_bytes(M, K, R)
+    us = region_ms * 1e3 / a.steps
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "metric": f"W4A4 producer (NVFP4 quantize + LoRA-down) GB/s, M={M} K={K} R={R}",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "warmup_steps_run": warm, "settle_ms": a.settle_ms, "ms_per_step": round(region_ms / a.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} producer", "M": M, "K": K, "R": R},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes, "avg_launch_us": round(us, 3)},
+        "wall_s": round(wall, 3),
+    }
+    if a.cpu_seconds > 0:
+        import oracle.quantize_ref as qref
+        rows = min(M, 256)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            qref.quantize_nvfp4_ref(d["x"][:rows])
+            qref.lora_down_ref(d["x"][:rows], d["lora_down"])
+            reps += 1
+            if time.perf_counter() - t0 >= a.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(producer_bytes(rows, K, R) * reps / dt / 1e9, 4),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the first {rows} rows of x, {reps} times in {dt:.1f} s "
+                                         f"(numpy, float64 comparisons; {cpu_model()})"}
+        got_a = act[:rows].cpu().numpy()
+        got_s = asc[:, :rows].cpu().numpy()
+        ra, rs = qref.quantize_nvfp4_ref(d["x"][:rows])
+        res["parity_sample"] = {"rows": rows, "act_equal": bool(np.array_equal(got_a, ra)),
+                                "ascales_equal": bool(np.array_equal(got_s, rs))}
+    print(json.dumps(res), flush=True)
+    ok = res.get("parity_sample") is None or (res["parity_sample"]["act_equal"] and
+                                               res["parity_sample"]["ascales_equal"])
+    return 0 if ok else 3
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +313,9 @@ def main() -> int:
                     help="also run one device copy of this many MiB (counter scale probe)")
     ap.add_argument("--variant", type=int, default=-1,
                     help="run this compiled tile instance (gemm_w4a4_run) instead of the solver's choice")
+    ap.add_argument("--op", default="gemm", choices=["gemm", "producer"],
+                    help="gemm: the fused W4A4 GEMM (default); producer: quantize_w4a4_act, the "
+                         "layer's memory-bound half, at the workload's M x K and rank R")
     ap.add_argument("--routes", action="store_true",
                     help="instead of the GEMM: the per-block arithmetic of the decode + fp16 MFMA route "
                          "and of the scaled-FP4-MFMA route, for the workload's K/16 blocks per wave")
@@ -240,6 +348,8 @@ def main() -> int:
                                      "waves": probes.PEAK_GROUPS * 4, "wave_tile": "128x96"},
                           **rates}))
         return 0
+    if a.op == "producer":
+        return bench_producer(a, wl)
     mx = a.fmt == "mxfp4"
     x = synthetic.make_inputs(wl, dtype=a.dtype, fmt=a.fmt)
     if a.ceiling:

@@ -3,7 +3,9 @@
     y = scaled_mma(act4, wgt4) * wcscale + bias + lora_act_in @ lora_up
 
 with E2M1 operands and either NVFP4 block scales (FP8-E4M3, one per 16 k:
-gemm_w4a4) or MXFP4 block scales (UE8M0, one per 32 k: gemm_mxfp4).
+gemm_w4a4) or MXFP4 block scales (UE8M0, one per 32 k: gemm_mxfp4); and the
+layer's other half, quantize_w4a4_act: bf16 activations -> the NVFP4 act /
+ascales operand plus lora_act_in = x @ lora_down^T, in one pass over x.
 
 Python binding over the C ABI of libgemm_w4a4.so (include/gemm_w4a4.h).
 PyTorch supplies device memory and the stream; every step of the operator runs
@@ -12,11 +14,12 @@ in the library's HIP kernels. If the library is missing the calls raise.
 from __future__ import annotations
 
 from . import _native
-from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK,
+from ._native import (EALIGN, EDEVICE, EINVAL, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK, QUANTIZE_MAX_R,
+                      quantize_raw,
                       gemm_mxfp4_f16_raw, gemm_mxfp4_raw, gemm_w4a4_f16_raw, gemm_w4a4_raw,
                       library_path, plan, plan_variant, run_raw, strerror, variants)
 
-__all__ = ["gemm_w4a4", "gemm_mxfp4", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
+__all__ = ["gemm_w4a4", "gemm_mxfp4", "quantize_w4a4_act", "quantize_raw", "QUANTIZE_MAX_R", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
            "gemm_mxfp4_f16_raw", "run_raw", "plan", "plan_variant", "variants", "strerror", "library_path", "GemmError", "OK",
            "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "MAX_R", "FORMATS"]
 
@@ -125,3 +128,41 @@ def _launch(fmt, act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up
     if rc != OK:
         raise GemmError(rc)
     return out
+
+
+def quantize_w4a4_act(x, lora_down=None, act=None, ascales=None, lora_act_in=None, stream=None):
+    """Enqueue the producer half on `stream`: x bfloat16 [M, K] (K % 16 == 0)
+    -> act uint8 [M, K/2], ascales uint8 [K/16, M] (the NVFP4 operand of
+    gemm_w4a4) and, when lora_down bfloat16 [R, K] is given, lora_act_in
+    bfloat16 [M, R] = x @ lora_down^T. Outputs are allocated when None.
+    Returns (act, ascales, lora_act_in or None)."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K), device)
+    R = 0 if lora_down is None else lora_down.shape[0]
+    if lora_down is not None:
+        _check(lora_down, "lora_down", torch.bfloat16, (R, K), device)
+    if act is None:
+        act = torch.empty((M, K // 2), dtype=torch.uint8, device=device)
+    if ascales is None:
+        ascales = torch.empty((K // 16, M), dtype=torch.uint8, device=device)
+    if R > 0 and lora_act_in is None:
+        lora_act_in = torch.empty((M, R), dtype=torch.bfloat16, device=device)
+    _check(act, "act", torch.uint8, (M, K // 2), device)
+    _check(ascales, "ascales", torch.uint8, (K // 16, M), device)
+    if R > 0:
+        _check(lora_act_in, "lora_act_in", torch.bfloat16, (M, R), device)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(device):
+        rc = quantize_raw(x.data_ptr(), lora_down.data_ptr() if R else 0, act.data_ptr(),
+                          ascales.data_ptr(), lora_act_in.data_ptr() if R else 0, M, K, R, handle)
+    if rc != OK:
+        raise GemmError(rc)
+    return act, ascales, (lora_act_in if R else None)

@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_mxfp4_num_variants.restype = i
         lib.gemm_mxfp4_variant_info.argtypes = [i, ctypes.POINTER(Plan)]
         lib.gemm_mxfp4_variant_info.restype = i
+        lib.quantize_w4a4_act.argtypes = [vp] * 5 + [i, i, i, vp]
+        lib.quantize_w4a4_act.restype = i
         lib.gemm_w4a4_run.argtypes = [i, i, i] + [vp] * 9 + [i, i, i, i, vp]
         lib.gemm_w4a4_run.restype = i
         lib.gemm_w4a4_plan_variant.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
@@ -113,6 +115,14 @@ def gemm_mxfp4_f16_raw(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, l
     """Direct call of the MXFP4 fp16 C entry point; returns its code."""
     return load().gemm_mxfp4_f16(act, ascales, wgt, wscales, wcscale, bias, lora_act_in, lora_up,
                                  out, M, N, K, R, stream)
+
+
+QUANTIZE_MAX_R = 128
+
+
+def quantize_raw(x, lora_down, act, ascales, lora_act_in, M, K, R, stream) -> int:
+    """Direct call of quantize_w4a4_act with integer addresses; returns its code."""
+    return load().quantize_w4a4_act(x, lora_down, act, ascales, lora_act_in, M, K, R, stream)
 
 
 def run_raw(fmt: str, out_f16: bool, variant: int, act, ascales, wgt, wscales, wcscale, bias,

@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 PROBES_LIB_PATH = os.path.join(PKG_DIR, "libw4a4_probes.so")
 # library -> (the sources it is built from, whether it carries the resource table)
 LIBS = {
-    LIB_PATH: (("gemm_w4a4.hip", "gemm_mxfp4.hip"), True),
+    LIB_PATH: (("gemm_w4a4.hip", "gemm_mxfp4.hip", "w4a4_producer.hip"), True),
     PROBES_LIB_PATH: (("mfma_peak.hip", "route_probe.hip"), False),
 }
 ARCH = "gfx950"

@@ -203,6 +203,41 @@ int gemm_w4a4_run(int format, int out_f16, int variant,
 int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
                            gemm_w4a4_plan_t* plan);
 
+/*
+ * quantize_w4a4_act — the other half of an SVDQuant W4A4 layer (the SVDQuant
+ * W4A4 on Blackwell page, section 1, calls gemm_w4a4 the compute-bound half):
+ * from the bf16 activations x, the NVFP4 operand gemm_w4a4 consumes and the
+ * rank-R LoRA input, in one pass over x.
+ *
+ *   x            uint16  [M, K]     bfloat16 bit patterns (read)
+ *   lora_down    uint16  [R, K]     bfloat16 bit patterns, one rank per row (read);
+ *                                   may be NULL iff R == 0
+ *   act          uint8   [M, K/2]   written: two E2M1 codes per byte, low nibble = even k
+ *   ascales      uint8   [K/16, M]  written: OCP E4M3FN scale of (m, k) at [k/16][m]
+ *   lora_act_in  uint16  [M, R]     written: bfloat16 bits of sum_k x[m,k] * lora_down[r,k]
+ *                                   (float32 accumulation, rounded to nearest even);
+ *                                   may be NULL iff R == 0
+ *
+ * The pages fix these layouts (section 2; single-level scaling, section 3.1)
+ * but not how a block's scale is chosen or its codes rounded. This library's
+ * reading, per row and block of 16 consecutive k:
+ *   - a block holding a NaN or an infinity gets scale byte 0x7F (NaN) and zero codes;
+ *   - otherwise scale = E4M3FN nearest-even of max|x| / 6, saturating at 448;
+ *   - code = sign bit of x | E2M1 magnitude of |x| / scale, nearest with ties
+ *     to the even code, saturating at 6; a zero scale keeps only the sign bit.
+ * Every rounding decision is exact (the same as on the real numbers).
+ *
+ * M >= 1; K >= 16 with K % 16 == 0; 0 <= R <= QUANTIZE_W4A4_MAX_R; every
+ * tensor below 2^31 bytes. Alignment: x and lora_down 16 bytes, act 8,
+ * lora_act_in 2. No output may overlap an input or another output
+ * (GEMM_W4A4_EOVERLAP). Device pointers owned by the caller; nothing is
+ * allocated or synchronised; return codes as for gemm_w4a4.
+ */
+#define QUANTIZE_W4A4_MAX_R 128
+int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
+                      uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
+                      void* stream);
+
 /* Static string for a return code (never NULL). */
 const char* gemm_w4a4_strerror(int code);
 
