@@ -322,3 +322,15 @@ def test_quantize_overlap(over):
 def test_quantize_rank_zero_needs_no_lora_pointers():
     rc = _q(R=0, lora_down=0, lora_act_in=0)
     assert rc in (w4.EDEVICE, w4.ELAUNCH, w4.OK)
+
+
+@pytest.mark.skipif(not os.path.exists(f"{LLVM}/clang-offload-bundler"), reason="no ROCm llvm")
+def test_no_kernel_spills():
+    """No compiled kernel of the operator library spills registers or uses
+    scratch memory (the build's resource table, read from the code objects)."""
+    from bit_quantized_gemm_amd.build import BUILD_DIR
+    src = open(os.path.join(BUILD_DIR, "libgemm_w4a4_resources.cpp")).read()
+    rows = re.findall(r'\{"(\w+)", (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\}', src)
+    assert len(rows) >= 40
+    for name, vgpr, agpr, sgpr, lds, spill, scratch in rows:
+        assert int(spill) == 0 and int(scratch) == 0, name

@@ -58,11 +58,11 @@ def test_producer_workloads(name):
     check_producer(d["x"], d["lora_down"], name)
 
 
-# rows not a multiple of 16 or 32, K % 128 != 0 and K % 32 == 16 (8-byte act
-# stores), every rank instance (R = 0, <= 16, <= 32, <= 128) with R not a
-# multiple of 16
+# rows not a multiple of 16, K % 128 != 0 and K % 32 == 16 (8-byte act
+# stores), every compiled instance (8 or 16 waves per 16 rows; R = 0, <= 16,
+# <= 32, <= 128) with R not a multiple of 16
 EDGE = [(1, 16, 0), (17, 48, 1), (33, 144, 17), (100, 528, 32), (130, 1040, 100), (31, 2064, 128),
-        (256, 128, 16), (47, 4096, 64), (64, 272, 0), (2, 16, 128)]
+        (256, 128, 16), (47, 4096, 64), (64, 272, 0), (2, 16, 128), (3072, 272, 0), (3100, 400, 8)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
