@@ -18,6 +18,7 @@ EALIGN = -2
 ELAUNCH = -3
 EOVERLAP = -4
 EDEVICE = -5
+ENOMEM = -6
 MAX_R = 1024
 
 _PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n",

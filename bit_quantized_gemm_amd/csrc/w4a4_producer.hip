@@ -7,30 +7,40 @@
 // (sections 2 and 3.1); the scale and rounding rule is this library's
 // reading, stated in gemm_w4a4.h.
 //
-// Design (one workgroup of WAVES waves per 16 rows of x):
-//  * x is read once. The workgroup's rows are cut into spans of 128 k; wave w
-//    takes spans w, w+WAVES, ... and streams them through a private LDS ring
-//    (DEPTH spans, 128 KiB / WAVES) by direct-to-LDS DMA, so the loop needs no
-//    workgroup barrier. Each 256-byte row of a span is stored with its 16-byte
-//    chunks XOR-swizzled by row, so that the reads below hit distinct banks.
-//    More waves per workgroup (up to 16) keep every SIMD busy when M / 16 is
-//    small. A span's lora_down operands are loaded at its start; their L2
-//    latency hides behind the span's LDS read and quantisation.
-//  * Lane (r, g) holds row r, k = 32g .. 32g+31 of the
-//    span: two whole 16-value blocks, so a block's amax needs no cross-lane
-//    step. Scale and codes are decided exactly (see quantize_block), codes are
-//    packed by the FP4 conversion, act is written as 16 (or 2 x 8) bytes per
-//    lane and the scale bytes are gathered through LDS into 16-byte rows of
-//    ascales.
+// Design (one workgroup of 8 waves, or 4 at the largest ranks, per 16 rows
+// of x and one slice of K):
+//  * x is read once. K is cut into spans of 128; a workgroup takes the spans
+//    of its K slice, wave w the spans w, w+WAVES, ... of them, streamed through a
+//    private LDS ring of DEPTH slots by direct-to-LDS DMA, so the loop needs
+//    no workgroup barrier. Each 256-byte row of a span is stored with its
+//    16-byte chunks XOR-swizzled by row, so that the reads below hit distinct
+//    banks. Loads are buffer loads: a per-lane offset fixed for the whole
+//    kernel into a descriptor of the span's base and the tensor's remaining
+//    bytes, in scalar registers. Reads past the tensor's end return zeros and
+//    reads past K in the span that crosses it land in the next row, zeroed at
+//    use, so no address is clamped.
+//  * When there are fewer row blocks (M / 16) than workgroup slots on the
+//    chip, K is split into slices over several workgroups: each writes its
+//    float32 LoRA partial sums to a scratch buffer, and the last of them to
+//    finish (a counter per row block) adds the slices in slice order and
+//    writes lora_act_in, so the result does not depend on the order the
+//    workgroups ran in.
+//  * Lane (r, g) holds row r, k = 32g .. 32g+31 of the span: two whole
+//    16-value blocks, so a block's amax needs no cross-lane step. Scale and
+//    codes are decided exactly (see quantize_block), codes are packed by the
+//    FP4 conversion, act is written as 16 (or 2 x 8) bytes per lane and the
+//    scale bytes are gathered through LDS into 16-byte rows of ascales.
 //  * The same registers are the A operand of v_mfma_f32_16x16x32_bf16: in
 //    k-step i lane (r, g) supplies x[r][32g + 8i .. +7] and, as B operand,
 //    lora_down[rank][32g + 8i .. +7] (any k order works if both sides agree).
-//    The four waves' partial sums meet once through LDS at the end.
+//    The waves' partial sums meet once through LDS at the end.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "gemm_w4a4.h"
 #include "w4a4_common.hpp"
@@ -40,42 +50,43 @@ namespace w4a4 {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// WAVES waves per 16-row workgroup, RTILES rank tiles of 16 (R <= 16 * RTILES).
-template <int WAVES_, int RTILES_>
+// WAVES waves per workgroup, RTILES rank tiles of 16 (R <= 16 * RTILES),
+// DEPTH ring slots per wave.
+template <int WAVES_, int RTILES_, int DEPTH_>
 struct ProdCfg {
-  static constexpr int WAVES = WAVES_, RTILES = RTILES_, RT = 1;
+  static constexpr int WAVES = WAVES_, RTILES = RTILES_, DEPTH = DEPTH_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int ROWS = 16;
   static constexpr int SPAN_K = 128;
-  static constexpr int TILE_BYTES = 16 * SPAN_K * 2;            // one 16-row tile of a span (4 KiB)
-  static constexpr int SPAN_BYTES = TILE_BYTES;
-  static constexpr int RING = 131072 / WAVES;                     // per wave
-  static constexpr int DEPTH = RING / SPAN_BYTES;                 // spans in flight per wave
+  static constexpr int SPAN_BYTES = ROWS * SPAN_K * 2;            // one span of 16 rows (4 KiB)
+  static constexpr int RING = DEPTH * SPAN_BYTES;                 // per wave
   static constexpr int SC_BYTES = 8 * ROWS;                       // staged scale bytes of a span
   static constexpr int SC_OFF = WAVES * RING;
   static constexpr int RED_BYTES = WAVES * RTILES * kWave * 16;   // end-of-loop partial sums
   static constexpr int LDS = SC_OFF + WAVES * SC_BYTES;
   static constexpr int D = SPAN_BYTES / (kWave * 16);             // 16-byte DMA rounds per span
   static constexpr int NL = 4 * RTILES;                           // lora_down loads per span
-  // lora_down operands are loaded PL spans ahead into NSETS = PL + 1 register
-  // sets (the span loop is unrolled NSETS times so that every set index is a
-  // constant): as deep as the x ring for R <= 32; at the start of their own
-  // span for the largest ranks, whose one set already takes half the
-  // register file.
-  static constexpr int PL = RTILES <= 2 ? (RTILES == 0 ? 0 : DEPTH - 1) : 0;
-  static constexpr int NSETS = PL + 1;
-  // Issue order: the prologue issues DMA(0 .. DEPTH-1) and L(0 .. PL-1); span
-  // j issues the stores S(j-1) of the previous span's results, L(j + PL),
-  // then the refill DMA(j + DEPTH) of its ring slot. Loads complete in issue
-  // order (a store can only make a count of loads stricter), so waiting until
-  // at most X vector-memory ops remain completes every load with at least X
-  // younger loads:
-  //   DMA(j): at least DEPTH-1 younger DMA groups and min(PL, DEPTH-1) L groups;
-  //   L(j):   at least PL younger L groups and one DMA group.
+  // lora_down operands of a span, L(j), go to register set j % NSETS. With
+  // two sets (R <= 32) L(j+1) is issued early in span j, beside the refill
+  // DMA(j + DEPTH); with one set (the largest ranks, whose set alone is 128
+  // registers) both are issued at the end of span j, after its MFMAs.
+  static constexpr int NSETS = RTILES >= 1 && RTILES <= 2 ? 2 : 1;
+  static constexpr bool EARLY = NSETS == 2;
+  // Issue order: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); then per span j the
+  // stores S(j-1) of the previous span's results and the pair L(j+1),
+  // DMA(j+DEPTH). A pair past the wave's last span is issued as the
+  // same loads on an empty descriptor (they read nothing), so that every
+  // count below is the same in every span. Loads complete in issue order and a store can only make a
+  // count of loads stricter, so waiting until at most X vector-memory ops
+  // remain completes every load with at least X younger loads:
+  //   DMA(j): DEPTH-1 younger pairs (DMA(0): one L fewer, waited for by the
+  //           prologue itself);
+  //   L(j):   EARLY: DMA(j-1+DEPTH) and span j's pair; else DMA(j-1+DEPTH).
   // (Counts above the counter's 63 are capped: a stricter wait.)
-  static constexpr int VM_DMA = (DEPTH - 1) * D + (PL < DEPTH - 1 ? PL : DEPTH - 1) * NL < 63
-                                    ? (DEPTH - 1) * D + (PL < DEPTH - 1 ? PL : DEPTH - 1) * NL : 63;
-  static constexpr int VM_L = PL * NL + D < 63 ? PL * NL + D : 63;
+  static constexpr int cap(int v) { return v < 63 ? v : 63; }
+  static constexpr int VM_X = cap((DEPTH - 1) * (D + NL));
+  static constexpr int VM_X0 = cap((DEPTH - 1) * D + NL);
+  static constexpr int VM_L = cap(EARLY ? 2 * D + NL : D);
   static_assert(DEPTH >= 2, "ring depth");
   static_assert(RED_BYTES <= WAVES * RING, "partial sums fit in the drained rings");
   static_assert(LDS <= kLdsLimit, "LDS budget");
@@ -88,6 +99,9 @@ struct ProdParams {
   uint8_t* ascales;
   uint16_t* lora_act_in;
   int M, K, R;
+  int ks, sps;          // K slices per row block, spans per slice
+  float* part;          // ks > 1 and R > 0: float32 partial sums [row block][slice][16][R]
+  uint32_t* count;      // ks > 1 and R > 0: arrivals per row block, zero between calls
 };
 
 // OCP E4M3FN byte of v, 0 <= v <= 448, rounded to nearest even (integer
@@ -115,13 +129,17 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 //    fma(-q, 6, amax) return the exact quotient whenever it is a float32 (the
 //    only case in which it can sit on an E4M3 midpoint: a tie) and otherwise
 //    a value within an ulp of it, while every other quotient lies at least
-//    2^-13 relative from every E4M3 midpoint; the integer rounding above is
+//    2^-9 relative from every E4M3 midpoint; the integer rounding above is
 //    exact.
-//  * |x| / s: within 2^-22 relative of the exact quotient, which is either
-//    exactly an E2M1 midpoint (a multiple of 0.25) or at least 2^-10 away from
-//    every one; snapping to the 2^-12 grid (adding and subtracting 2048)
-//    restores the exact midpoints and keeps every other quotient on its side,
-//    so the conversion's nearest-even rounding decides like the exact one.
+//  * x / s: P = x * (4096 / s), with 4096 / s from the reciprocal, is within
+//    2^-21 relative of 4096 x / s. For |x| / s <= 6.5 that exact quotient is
+//    either exactly an E2M1 midpoint (a multiple of 1024) or at least 4 away
+//    from every one, so rounding P to an integer (nearest even) gives the
+//    midpoints exactly and keeps every other quotient on its side. The FP4
+//    conversion divides by its scale's power of two (4096) exactly and rounds
+//    to nearest even, so it decides like the exact quotient; larger
+//    quotients saturate either way. The rounding keeps the sign of zero, and
+//    an infinite P converts to the largest code.
 // A block holding a NaN or an infinity gets 0x7F and zero codes (computed
 // branch-free: the arithmetic runs on whatever the block holds and is
 // replaced at the end).
@@ -141,27 +159,47 @@ __device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], uint32_t&
   const float q = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, amax), sixth, q0);
   const uint32_t sb = e4m3_rne(fminf(q, 448.0f));
   const float s = e4m3_value(sb);
-  const float r = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+  const float c = s > 0.0f ? __builtin_amdgcn_rcpf(s) * 4096.0f : 0.0f;
   uint32_t w[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t xl = d[i] << 16, xh = d[i] & 0xFFFF0000u;
-    // |x| * r snapped to the 2^-12 grid (never negative), then the sign of x
-    const float ql = __builtin_fmaf(__builtin_fabsf(__builtin_bit_cast(float, xl)), r, 2048.0f) - 2048.0f;
-    const float qh = __builtin_fmaf(__builtin_fabsf(__builtin_bit_cast(float, xh)), r, 2048.0f) - 2048.0f;
-    const float sl = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, ql) | (xl & 0x80000000u));
-    const float sh = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, qh) | (xh & 0x80000000u));
-    // element 2i is k even (low nibble of byte i), 2i+1 odd; byte i of the 8
+    // element 2i (k even) is the low half of the dword: low nibble of byte i
+    const float pl = __builtin_rintf(__builtin_bit_cast(float, d[i] << 16) * c);
+    const float ph = __builtin_rintf(__builtin_bit_cast(float, d[i] & 0xFFFF0000u) * c);
     switch (i & 3) {   // byte select must be an immediate; folds after unrolling
-      case 0: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], sl, sh, 1.0f, 0); break;
-      case 1: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], sl, sh, 1.0f, 1); break;
-      case 2: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], sl, sh, 1.0f, 2); break;
-      default: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], sl, sh, 1.0f, 3); break;
+      case 0: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], pl, ph, 4096.0f, 0); break;
+      case 1: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], pl, ph, 4096.0f, 1); break;
+      case 2: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], pl, ph, 4096.0f, 2); break;
+      default: w[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[i >> 2], pl, ph, 4096.0f, 3); break;
     }
   }
   sbyte = finite ? sb : 0x7Fu;
   lo = finite ? w[0] : 0u;
   hi = finite ? w[1] : 0u;
+}
+
+// Raw buffer descriptor of `bytes` bytes from `base` (gfx9 format word).
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// 16-byte buffer load the compiler does not track (see load_lora): per-lane
+// offset + immediate into the descriptor's range (zeros past its end).
+template <int IMM>
+__device__ __forceinline__ void load_untracked(u32x4& dst, uint32_t voff, const u32x4& desc) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3"
+               : "=v"(dst) : "v"(voff), "s"(desc), "i"(IMM) : "memory");
+}
+
+// The same descriptor for the buffer builtins.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// Direct-to-LDS 16-byte buffer load: lane l writes lds + 16 l.
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
 template <class C>
@@ -173,114 +211,137 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int r = lane & 15, g = lane >> 4;
   const int M = p.M, K = p.K, R = p.R;
-  const int m0 = blockIdx.x * C::ROWS;
+  const int rb = blockIdx.x / p.ks, z = blockIdx.x - rb * p.ks;
+  const int m0 = rb * C::ROWS;
   const int nsp = (K + C::SPAN_K - 1) / C::SPAN_K;
-  const int nmine = wave_u < nsp ? (nsp - 1 - wave_u) / C::WAVES + 1 : 0;   // spans of this wave
+  const int s_end = min(nsp, (z + 1) * p.sps);
+  const int first = z * p.sps + wave_u;                                  // this wave's first span
+  const int n = first < s_end ? (s_end - 1 - first) / C::WAVES + 1 : 0;   // and its number of spans
+  const int tail_span = (K % C::SPAN_K) != 0 ? nsp - 1 : -1;             // the span crossing K
   const uint32_t row_bytes = uint32_t(K) * 2u;
   uint8_t* ring = smem + wave_u * C::RING;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x);
 
-  // DMA of this wave's j-th span into ring slot j % DEPTH. Round u:
-  // lane l writes slot position (row 4u + l/16, chunk l%16) and reads data
-  // chunk (l%16) ^ row of that row. Spans past the wave's last one re-read it
-  // (never consumed); k past K and rows past M read clamped in-range bytes.
+  // DMA round u of a span: lane l writes slot position (row 4u + l/16, chunk
+  // l%16) and reads data chunk (l%16) ^ row of that row; rows past M read
+  // row M-1 (never stored).
+  const uint32_t x_bytes = uint32_t(M) * row_bytes;
+  uint32_t xoff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int lr = 4 * u + g;
+    xoff[u] = uint32_t(min(m0 + lr, M - 1)) * row_bytes + uint32_t((r ^ lr) << 4);
+  }
+  // span j of this wave into slot j % DEPTH; j >= n: a dummy of the same
+  // shape on an empty descriptor (reads nothing, writes zeros to the slot,
+  // which holds no span still to be read)
   auto dma_span = [&](int j) __attribute__((always_inline)) {
-    const int jj = nmine > 0 ? min(j, nmine - 1) : 0;
-    const int span = wave_u + C::WAVES * jj;
+    const bool valid = j < n;
+    const uint32_t sb = valid ? uint32_t(first + C::WAVES * j) * uint32_t(C::SPAN_K * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t desc = buffer_rsrc(xb + sb, valid ? x_bytes - sb : 0u);
     uint8_t* slot = ring + (j % C::DEPTH) * C::SPAN_BYTES;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int lr = 4 * u + (lane >> 4);                         // row inside the tile
-      const int row = min(m0 + lr, M - 1);
-      const int chunk = (lane & 15) ^ lr;                         // 16-byte chunk = 8 k
-      const int kk = span * C::SPAN_K + 8 * chunk;
-      const uint32_t kb = kk < K ? uint32_t(kk) * 2u : 0u;
-      dma<16>(reinterpret_cast<const uint8_t*>(p.x) + uint32_t(row) * row_bytes + kb, slot + u * 1024);
-    }
+    for (int u = 0; u < 4; ++u) dma_buf(desc, xoff[u], slot + u * 1024);
   };
 
   f32x4_t acc[C::RTILES > 0 ? C::RTILES : 1];
 #pragma unroll
   for (int jt = 0; jt < (C::RTILES > 0 ? C::RTILES : 1); ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // LoRA-down operands of this wave's j-th span into register set `SET` (B:
-  // lora_down[rank][k0 + 8i .. +7]); ranks past R re-read rank R-1 (their sums
-  // are not stored), k past K re-reads the row's last 8 and is zeroed at use,
-  // spans past the wave's last re-read that one (never used).
+  // LoRA-down operands of this wave's j-th span into a register set (B:
+  // lora_down[rank][k0 + 8i .. +7]); ranks past R re-read rank R-1 (their
+  // sums are not stored), and in the span crossing K, k past K reads the next
+  // rank's values or zeros (zeroed at use).
   //
-  // Issued as explicit global_load_dwordx4, which the compiler does not track:
-  // with stores in flight it would otherwise wait for every outstanding
-  // vector-memory op (vmcnt(0)) before the first use, the ring's DMAs
-  // included. The explicit waits below count loads only, and scheduling
-  // fences keep every use after its wait.
+  // Issued as explicit buffer_load_dwordx4, which the compiler does not
+  // track: with stores in flight it would otherwise wait for every
+  // outstanding vector-memory op (vmcnt(0)) before the first use, the ring's
+  // DMAs included. The explicit waits count loads only, and scheduling fences
+  // keep every use after its wait.
   constexpr int LT = C::RTILES > 0 ? C::RTILES : 1;
   u32x4 lb[C::NSETS][LT][4];
+  uint32_t loff[LT];
+#pragma unroll
+  for (int jt = 0; jt < LT; ++jt)
+    loff[jt] = uint32_t(min(16 * jt + r, max(R, 1) - 1)) * row_bytes + uint32_t(64 * g);
+  const uint8_t* ldb = reinterpret_cast<const uint8_t*>(p.lora_down);
+  const uint32_t ld_bytes = uint32_t(R) * row_bytes;
+  // j >= n: a dummy on an empty descriptor (reads nothing; the set is not used)
   auto load_lora = [&](u32x4 (&dst)[LT][4], int j) __attribute__((always_inline)) {
     if constexpr (C::RTILES > 0) {
-      const int jj = nmine > 0 ? min(j, nmine - 1) : 0;
-      const int k0 = (wave_u + C::WAVES * jj) * C::SPAN_K + 32 * g;
+      const bool valid = j < n;
+      const uint32_t sb = valid ? uint32_t(first + C::WAVES * j) * uint32_t(C::SPAN_K * 2) : 0u;
+      const u32x4 desc = buffer_desc(ldb + sb, valid ? ld_bytes - sb : 0u);
 #pragma unroll
-      for (int jt = 0; jt < C::RTILES; ++jt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rank = min(16 * jt + r, R - 1);
-          const int kk = min(k0 + 8 * i, K - 8);
-          const uint16_t* src = p.lora_down + uint32_t(rank) * uint32_t(K) + uint32_t(kk);
-          asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst[jt][i]) : "v"(src) : "memory");
-        }
+      for (int jt = 0; jt < C::RTILES; ++jt) {
+        load_untracked<0>(dst[jt][0], loff[jt], desc);
+        load_untracked<16>(dst[jt][1], loff[jt], desc);
+        load_untracked<32>(dst[jt][2], loff[jt], desc);
+        load_untracked<48>(dst[jt][3], loff[jt], desc);
+      }
     }
   };
+  // the pair of span t: L(t+1), DMA(t+DEPTH)
+  auto issue_pair = [&]<int NEXT_SET>(int t) __attribute__((always_inline)) {
+    load_lora(lb[NEXT_SET], t + 1);
+    dma_span(t + C::DEPTH);
+  };
 
+  // prologue: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1)
 #pragma unroll
-  for (int j = 0; j < C::DEPTH; ++j) dma_span(j);
-  static_for<0, C::PL>([&]<int S>() __attribute__((always_inline)) { load_lora(lb[S], S); });
+  for (int t = 0; t < C::DEPTH - 1; ++t) dma_span(t);
+  load_lora(lb[0], 0);
+  dma_span(C::DEPTH - 1);
+  wait_vm_lgkm0<C::VM_X0>();   // DMA(0): its count differs from the loop's
 
+  // output addresses: act row m0 + r from k0 / 2; ascales row (block) lane
+  // of the span, 16 consecutive m
+  const bool row_ok = m0 + r < M;
+  const uint32_t aoff = uint32_t(min(m0 + r, M - 1)) * uint32_t(K / 2) + uint32_t(16 * g);
+  const uint32_t soff = uint32_t(lane & 7) * uint32_t(M) + uint32_t(m0);
   const bool act16 = (K & 31) == 0 && (reinterpret_cast<uintptr_t>(p.act) & 15u) == 0;
   const bool sc16 = (M & 15) == 0 && (reinterpret_cast<uintptr_t>(p.ascales) & 15u) == 0;
   uint8_t* sc_stage = smem + C::SC_OFF + wave_u * C::SC_BYTES;
 
   // The results of a span are stored at the start of the next one, before its
-  // lora_down loads and refill DMA, so that no store lies between a lora_down
-  // load group and the ops its wait counts.
+  // pair of loads, so that no store lies between a load and the ops its
+  // wait counts.
   uint32_t code[4] = {0u, 0u, 0u, 0u};   // the previous span's 32 codes of this lane
   u32x4 scv = {0u, 0u, 0u, 0u};          // lanes 0..7: one 16-byte row of its scales
-  int prev_span = -1;
-  auto store_span = [&]() __attribute__((always_inline)) {
-    const int k0 = prev_span * C::SPAN_K + 32 * g;
-    const bool ok0 = k0 < K, ok1 = k0 + 16 < K;
-    const int row = m0 + r;
-    if (row < M) {
-      uint8_t* dst = p.act + uint32_t(row) * uint32_t(K / 2) + uint32_t(k0 / 2);
-      if (act16 && ok1) {
-        *reinterpret_cast<u32x4*>(dst) = u32x4{code[0], code[1], code[2], code[3]};
+  const int nv = min(C::ROWS, M - m0);   // valid rows of the block
+  auto store_span = [&](int span) __attribute__((always_inline)) {
+    uint8_t* abase = p.act + uint32_t(span) * uint32_t(C::SPAN_K / 2);
+    uint8_t* sbase = p.ascales + uint32_t(span) * uint32_t(C::SPAN_K / 16) * uint32_t(M);
+    const bool tail = span == tail_span;
+    const int k0 = span * C::SPAN_K + 32 * g;
+    if (row_ok) {
+      if (act16 && !tail) {
+        *reinterpret_cast<u32x4*>(abase + aoff) = u32x4{code[0], code[1], code[2], code[3]};
       } else {
-        if (ok0) *reinterpret_cast<u32x2*>(dst) = u32x2{code[0], code[1]};
-        if (ok1) *reinterpret_cast<u32x2*>(dst + 8) = u32x2{code[2], code[3]};
+        if (k0 < K) *reinterpret_cast<u32x2*>(abase + aoff) = u32x2{code[0], code[1]};
+        if (k0 + 16 < K) *reinterpret_cast<u32x2*>(abase + aoff + 8) = u32x2{code[2], code[3]};
       }
     }
-    const int kb = prev_span * (C::SPAN_K / 16) + lane;
-    if (lane < 8 && kb < K / 16) {
-      uint8_t* dst = p.ascales + uint32_t(kb) * uint32_t(M) + uint32_t(m0);
-      if (sc16 && m0 + 16 <= M) {
-        *reinterpret_cast<u32x4*>(dst) = scv;
+    if (lane < 8 && span * (C::SPAN_K / 16) + lane < K / 16) {
+      if (sc16) {
+        *reinterpret_cast<u32x4*>(sbase + soff) = scv;
       } else {
-        const uint32_t w4[4] = {scv.x, scv.y, scv.z, scv.w};
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (m0 + e < M) dst[e] = uint8_t(w4[e >> 2] >> (8 * (e & 3)));
+        const uint64_t lo = uint64_t(scv.x) | (uint64_t(scv.y) << 32), hi = uint64_t(scv.z) | (uint64_t(scv.w) << 32);
+#pragma unroll 1
+        for (int e = 0; e < nv; ++e) sbase[soff + e] = uint8_t((e < 8 ? lo : hi) >> (8 * (e & 7)));
       }
     }
   };
 
-  // span j uses lora_down set j % NSETS; j0 is a multiple of NSETS
+  // span j uses lora_down set j % NSETS; the loop below is unrolled NSETS times
   auto one_span = [&]<int SET>(int j) __attribute__((always_inline)) {
-    const int span = wave_u + C::WAVES * j;
-    const int k0 = span * C::SPAN_K + 32 * g;                 // this lane's first k
-    wait_vm_lgkm0<C::VM_DMA>();                               // DMA(j) has landed
+    constexpr int NEXT = (SET + 1) % C::NSETS;
+    const int span = first + C::WAVES * j;
+    const bool tail = span == tail_span;
+    wait_vm_lgkm0<C::VM_X>();                                 // DMA(j) has landed
     // scheduling fences keep the issue order the wait counts rely on
     __builtin_amdgcn_sched_barrier(0);
-    if (prev_span >= 0) store_span();                         // S(j-1)
-    __builtin_amdgcn_sched_barrier(0);
-    load_lora(lb[(SET + C::PL) % C::NSETS], j + C::PL);      // L(j + PL)
+    if (j > 0) store_span(span - C::WAVES);                   // S(j-1)
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* slot = ring + (j % C::DEPTH) * C::SPAN_BYTES;
     uint32_t xd[16];
@@ -292,14 +353,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       xd[4 * i + 2] = v.z;
       xd[4 * i + 3] = v.w;
     }
-    wait_vm_lgkm0<63>();                                      // the slot is read: refill it
-    __builtin_amdgcn_sched_barrier(0);
-    dma_span(j + C::DEPTH);
-    __builtin_amdgcn_sched_barrier(0);
-    // a span reaching past K (only the last, when K % 128 != 0): zero this
-    // lane's blocks past K (they add nothing to the LoRA sums and are not stored)
-    const bool tail = (span + 1) * C::SPAN_K > K;   // uniform
+    wait_vm_lgkm0<63>();                                      // the slot is read
+    if constexpr (C::EARLY) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_pair.template operator()<NEXT>(j);                // L(j+1), DMA(j+DEPTH)
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (tail) {
+      // this lane's blocks past K: zero (they add nothing to the LoRA sums
+      // and are not stored)
+      const int k0 = span * C::SPAN_K + 32 * g;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (k0 + 16 * (i >> 3) >= K) xd[i] = 0u;
@@ -313,6 +376,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       for (int i = 0; i < 8; ++i) d[i] = xd[8 * b + i];
       quantize_block(d, sb[b], code[2 * b], code[2 * b + 1]);
     }
+    // scales: staged [block 0..7 of the span][16 rows] in this wave's LDS;
+    // lanes 0..7 take one 16-byte row each for the store
+#pragma unroll
+    for (int b = 0; b < 2; ++b) sc_stage[(2 * g + b) * C::ROWS + r] = uint8_t(sb[b]);
 
     if constexpr (C::RTILES > 0) {
       __builtin_amdgcn_sched_barrier(0);
@@ -321,6 +388,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       asm volatile("" ::: "memory");                          // nothing reads lb[SET] before this point
       if (tail) {
         // k past K: a zero operand (a NaN weight there must not reach valid sums)
+        const int k0 = span * C::SPAN_K + 32 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -337,25 +405,29 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
                                                             acc[jt], 0, 0, 0);
       }
     }
-    // scales: staged [block 0..7 of the span][16 rows] in this wave's LDS;
-    // lanes 0..7 keep one 16-byte row each for the store
-#pragma unroll
-    for (int b = 0; b < 2; ++b) sc_stage[(2 * g + b) * C::ROWS + r] = uint8_t(sb[b]);
+    if constexpr (!C::EARLY) {
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (C::RTILES > 0) {
+        // the loads below overwrite the operands of the MFMAs just issued
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+      }
+      issue_pair.template operator()<NEXT>(j);                // L(j+1), DMA(j+DEPTH)
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_vm_lgkm0<63>();
     if (lane < 8) scv = *reinterpret_cast<const u32x4*>(sc_stage + lane * C::ROWS);
     wait_vm_lgkm0<63>();                                      // staging read done before the next span's writes
-    prev_span = span;
   };
   int j0 = 0;
-  for (; j0 + C::NSETS <= nmine; j0 += C::NSETS)
+  for (; j0 + C::NSETS <= n; j0 += C::NSETS)
     static_for<0, C::NSETS>([&]<int S>() __attribute__((always_inline)) { one_span.template operator()<S>(j0 + S); });
   static_for<0, C::NSETS - 1>([&]<int S>() __attribute__((always_inline)) {
-    if (j0 + S < nmine) one_span.template operator()<S>(j0 + S);
+    if (j0 + S < n) one_span.template operator()<S>(j0 + S);
   });
-  if (prev_span >= 0) store_span();                           // S(last)
-  wait_vm_lgkm0<0>();                                         // drain the DMAs past the last span
+  if (n > 0) store_span(first + C::WAVES * (n - 1));          // S(last)
+  wait_vm_lgkm0<0>();                                         // drain the loads past the last span
   // Every lora_down register set stays allocated until here: a set loaded
-  // for a span past the wave's last is never read, and without this use the
+  // past the wave's last span is never read, and without this use the
   // compiler could hand its registers to other values while the (untracked)
   // load is still in flight.
   if constexpr (C::RTILES > 0) {
@@ -376,6 +448,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
     __syncthreads();
     // wave w finishes rank tiles w, w + WAVES, ...: lane (col, g) holds rows
     // 4g .. 4g+3 of rank 16 jt + col
+    const bool split = p.ks > 1;
     for (int jt = wave; jt < C::RTILES; jt += C::WAVES) {
       f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -386,11 +459,43 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = m0 + 4 * g + e;
-          if (row < M) {
+          if (split) {
+            __hip_atomic_store(p.part + (uint32_t(blockIdx.x) * 16u + uint32_t(4 * g + e)) * uint32_t(R) + uint32_t(rank),
+                               s[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else if (row < M) {
             const __bf16 v = __bf16(s[e]);   // round to nearest even
             p.lora_act_in[uint32_t(row) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, v);
           }
         }
+      }
+    }
+    if (split) {
+      // The last workgroup of the row block to finish adds the slices. The
+      // partial sums and the counter are device-scope atomic accesses, each
+      // coherent across the compute dies by itself; every wave waits until
+      // its stores are acknowledged before the barrier, which orders the
+      // sums before the count, so no cache write-back or invalidation is
+      // needed.
+      uint32_t* last = reinterpret_cast<uint32_t*>(smem + C::SC_OFF);   // the staging area is free
+      wait_vm<0>();
+      __syncthreads();
+      if (tid == 0)
+        *last = __hip_atomic_fetch_add(p.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                uint32_t(p.ks - 1);
+      __syncthreads();
+      if (*last) {
+        const int nel = 16 * R;
+        const float* base = p.part + uint32_t(rb) * uint32_t(p.ks) * uint32_t(nel);
+        for (int e = tid; e < nel; e += C::THREADS) {
+          float s = 0.f;
+          for (int q = 0; q < p.ks; ++q)
+            s += __hip_atomic_load(base + q * nel + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (m0 + e / R < M) {
+            const __bf16 v = __bf16(s);
+            p.lora_act_in[uint32_t(m0) * uint32_t(R) + uint32_t(e)] = __builtin_bit_cast(uint16_t, v);
+          }
+        }
+        if (tid == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -400,28 +505,109 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 
 struct ProdVariant {
   const void* kernel;
-  int waves, rtiles, lds;
+  int rtiles, threads, lds;
 };
 
-template <int WAVES, int RTILES>
+template <int WAVES, int RTILES, int DEPTH>
 ProdVariant prod_variant() {
-  using C = ProdCfg<WAVES, RTILES>;
-  return ProdVariant{reinterpret_cast<const void*>(producer_kernel<C>), WAVES, RTILES, C::LDS};
+  using C = ProdCfg<WAVES, RTILES, DEPTH>;
+  return ProdVariant{reinterpret_cast<const void*>(producer_kernel<C>), RTILES, C::THREADS, C::LDS};
 }
 
-// By rank: R == 0, R <= 16, R <= 32 with 8 waves per 16 rows; R == 0 and
-// R <= 16 also with 16 waves, for when M / 16 workgroups would leave compute
-// units idle (at R <= 32 sixteen waves' registers would spill); R <= 128 with
-// 4 waves (its double-buffered lora_down operands need the register file of
-// one wave per SIMD).
-static const ProdVariant kProdVariants[] = {prod_variant<8, 0>(),  prod_variant<8, 1>(), prod_variant<8, 2>(),
-                                            prod_variant<16, 0>(), prod_variant<16, 1>(), prod_variant<4, 8>()};
+// By rank: R == 0, R <= 16, R <= 32 with 8 waves (two per SIMD) and two
+// ring slots each; R <= 128 with 4 waves (its operand set and partial sums
+// need the register file of one wave per SIMD) and three slots.
+static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(), prod_variant<8, 1, 2>(),
+                                            prod_variant<8, 2, 2>(), prod_variant<4, 8, 3>()};
 
-static int prod_variant_index(int M, int R) {
-  if (R > 32) return 5;
-  const int rank = R == 0 ? 0 : R <= 16 ? 1 : 2;
-  const bool few_rows = (M + 15) / 16 < 192;
-  return few_rows && rank < 2 ? 3 + rank : rank;
+static int prod_variant_index(int R) { return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : 3; }
+
+// Workgroups of a variant resident on one compute unit, from the compiled
+// kernel's registers and its LDS.
+static int prod_occupancy(const ProdVariant& v) {
+  const KernelResources* kr = find_resources(v.kernel);
+  int per_simd = 1;
+  if (kr) {
+    const int regs = ((kr->vgpr + 7) & ~7) + ((kr->agpr + 7) & ~7);   // one file of 512, granules of 8
+    per_simd = regs > 0 ? 512 / regs : 1;
+  }
+  const int by_regs = max(1, per_simd / max(1, v.threads / kWave / 4));
+  const int by_lds = max(1, kLdsLimit / v.lds);
+  return min(by_regs, by_lds);
+}
+
+static std::atomic<int> g_cus[64];
+
+static int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return 256;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+// Scratch of the split-K reduction: a fixed region of arrival counters (one
+// per row block; the same bytes in every call, so they stay zero between
+// calls), then the partial sums.
+constexpr int kProdMaxCounters = 1024;
+constexpr size_t kProdCountBytes = kProdMaxCounters * 4;
+
+struct ProdLaunch {
+  int ks, sps;
+  size_t part_bytes;   // partial sums after the counters; 0: no scratch
+};
+
+// K slices: one when the row blocks alone fill every compute unit, else
+// enough to fill the workgroup slots (no slice left empty).
+static ProdLaunch prod_plan(const ProdVariant& v, int M, int K, int R) {
+  const int rbs = (M + 15) / 16, nsp = (K + 127) / 128;
+  const int cus = compute_units();
+  ProdLaunch pl{1, nsp, 0};
+  if (rbs < cus && rbs <= kProdMaxCounters) {
+    const int slots = cus * prod_occupancy(v);
+    int ks = min(nsp, (slots + rbs - 1) / rbs);
+    const int sps = (nsp + ks - 1) / ks;
+    ks = (nsp + sps - 1) / sps;
+    pl.ks = ks;
+    pl.sps = sps;
+  }
+  if (pl.ks > 1 && R > 0) pl.part_bytes = size_t(rbs) * size_t(pl.ks) * 16 * size_t(R) * 4;
+  return pl;
+}
+
+// Scratch of the split-K reduction, per device: grown on demand and zeroed
+// when allocated (the counters return to zero at the end of every call).
+struct ProdScratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+static ProdScratch g_prod_scratch[64];
+static std::mutex g_prod_scratch_mu;
+
+static int prod_scratch(size_t need, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_W4A4_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_prod_scratch_mu);
+  ProdScratch& s = g_prod_scratch[dev];
+  if (s.bytes < need) {
+    if (s.ptr && hipFree(s.ptr) != hipSuccess) return GEMM_W4A4_ENOMEM;   // waits for the device
+    s.ptr = nullptr;
+    s.bytes = 0;
+    void* ptr = nullptr;
+    if (hipMalloc(&ptr, need) != hipSuccess) return GEMM_W4A4_ENOMEM;
+    if (hipMemset(ptr, 0, need) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(ptr);
+      return GEMM_W4A4_ENOMEM;
+    }
+    s.ptr = ptr;
+    s.bytes = need;
+  }
+  *out = s.ptr;
+  return GEMM_W4A4_OK;
 }
 
 }  // namespace w4a4
@@ -450,10 +636,18 @@ extern "C" int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, u
   }
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-  const ProdVariant& v = kProdVariants[prod_variant_index(M, R)];
-  ProdParams prm{x, lora_down, act, ascales, lora_act_in, M, K, R};
+  const ProdVariant& v = kProdVariants[prod_variant_index(R)];
+  const ProdLaunch pl = prod_plan(v, M, K, R);
+  void* scratch = nullptr;
+  if (pl.part_bytes > 0) {
+    const int rc = prod_scratch(kProdCountBytes + pl.part_bytes, &scratch);
+    if (rc != GEMM_W4A4_OK) return rc;
+  }
+  uint8_t* sb = static_cast<uint8_t*>(scratch);
+  ProdParams prm{x, lora_down, act, ascales, lora_act_in, M, K, R, pl.ks, pl.sps,
+                 sb ? reinterpret_cast<float*>(sb + kProdCountBytes) : nullptr, reinterpret_cast<uint32_t*>(sb)};
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(v.kernel, dim3((M + 15) / 16), dim3(v.waves * kWave), args, 0,
+  const hipError_t e = hipLaunchKernel(v.kernel, dim3(((M + 15) / 16) * pl.ks), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
 }

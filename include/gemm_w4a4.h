@@ -51,7 +51,8 @@ enum {
                                  lora/out not 2-byte aligned */
   GEMM_W4A4_ELAUNCH = -3,     /* the HIP launch itself failed */
   GEMM_W4A4_EOVERLAP = -4,    /* out overlaps an input */
-  GEMM_W4A4_EDEVICE = -5      /* the current device is not gfx950 */
+  GEMM_W4A4_EDEVICE = -5,     /* the current device is not gfx950 */
+  GEMM_W4A4_ENOMEM = -6       /* quantize_w4a4_act could not allocate its scratch buffer */
 };
 
 #define GEMM_W4A4_MAX_R 1024

@@ -120,7 +120,7 @@ def test_output_overlapping_an_input(target, entry):
 
 
 def test_strerror():
-    for code in (w4.OK, w4.EINVAL, w4.EALIGN, w4.ELAUNCH, w4.EOVERLAP, w4.EDEVICE, -99):
+    for code in (w4.OK, w4.EINVAL, w4.EALIGN, w4.ELAUNCH, w4.EOVERLAP, w4.EDEVICE, w4.ENOMEM, -99):
         assert isinstance(w4.strerror(code), str) and w4.strerror(code)
 
 
@@ -331,6 +331,6 @@ def test_no_kernel_spills():
     from bit_quantized_gemm_amd.build import BUILD_DIR
     src = open(os.path.join(BUILD_DIR, "libgemm_w4a4_resources.cpp")).read()
     rows = re.findall(r'\{"(\w+)", (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\}', src)
-    assert len(rows) >= 40
+    assert len(rows) >= 38 and sum("producer_kernel" in r[0] for r in rows) >= 4
     for name, vgpr, agpr, sgpr, lds, spill, scratch in rows:
         assert int(spill) == 0 and int(scratch) == 0, name

@@ -186,3 +186,14 @@ def test_layer_end_to_end(name):
                  lora_act_in=la.view(torch.int16).cpu().numpy().view(np.uint16))
     y, T = full_reference(chain)
     assert_parity(out.view(torch.int16).cpu().numpy().view(np.uint16), y, T, f"layer {name}")
+
+
+def test_split_calls_of_different_sizes():
+    """Consecutive calls whose K is split over workgroups, with different
+    numbers of row blocks and ranks: the arrival counters live in the same
+    scratch bytes in every call and must be back at zero after each."""
+    for shape in [(1000, 3072, 16), (3100, 400, 8), (33, 144, 17), (3100, 400, 8), (200, 1024, 128)]:
+        M, K, R = shape
+        _say(f"case: producer split sequence M={M} K={K} R={R}")
+        d = synthetic.producer_inputs(M, K, R, seed=M * 7 + K + R)
+        check_producer(d["x"], d["lora_down"], f"sequence {shape}")
