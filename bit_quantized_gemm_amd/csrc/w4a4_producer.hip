@@ -178,10 +178,14 @@ __device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], uint32_t&
   hi = finite ? w[1] : 0u;
 }
 
-// Raw buffer descriptor of `bytes` bytes from `base` (gfx9 format word).
+// Raw buffer descriptor of `bytes` bytes from `base` (gfx9 format word),
+// in scalar registers (the values are wave-uniform; readfirstlane says so
+// where the compiler cannot prove it).
 __device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  return u32x4{uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a))),
+               uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xFFFFu)),
+               uint32_t(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000u};
 }
 
 // 16-byte buffer load the compiler does not track (see load_lora): per-lane
@@ -300,7 +304,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   const uint32_t aoff = uint32_t(min(m0 + r, M - 1)) * uint32_t(K / 2) + uint32_t(16 * g);
   const uint32_t soff = uint32_t(lane & 7) * uint32_t(M) + uint32_t(m0);
   const bool act16 = (K & 31) == 0 && (reinterpret_cast<uintptr_t>(p.act) & 15u) == 0;
-  const bool sc16 = (M & 15) == 0 && (reinterpret_cast<uintptr_t>(p.ascales) & 15u) == 0;
+  // widest store a scale row allows: rows of ascales are M bytes apart
+  const uintptr_t sc_align = reinterpret_cast<uintptr_t>(p.ascales) | uintptr_t(M);
+  const int sc_w = (sc_align & 15u) == 0 ? 16 : (sc_align & 7u) == 0 ? 8 : (sc_align & 3u) == 0 ? 4 : 1;
   uint8_t* sc_stage = smem + C::SC_OFF + wave_u * C::SC_BYTES;
 
   // The results of a span are stored at the start of the next one, before its
@@ -323,8 +329,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       }
     }
     if (lane < 8 && span * (C::SPAN_K / 16) + lane < K / 16) {
-      if (sc16) {
+      if (sc_w == 16) {
         *reinterpret_cast<u32x4*>(sbase + soff) = scv;
+      } else if (sc_w == 8 && nv == C::ROWS) {
+        *reinterpret_cast<u32x2*>(sbase + soff) = u32x2{scv.x, scv.y};
+        *reinterpret_cast<u32x2*>(sbase + soff + 8) = u32x2{scv.z, scv.w};
+      } else if (sc_w == 4 && nv == C::ROWS) {
+        uint32_t* d = reinterpret_cast<uint32_t*>(sbase + soff);
+        d[0] = scv.x;
+        d[1] = scv.y;
+        d[2] = scv.z;
+        d[3] = scv.w;
       } else {
         const uint64_t lo = uint64_t(scv.x) | (uint64_t(scv.y) << 32), hi = uint64_t(scv.z) | (uint64_t(scv.w) << 32);
 #pragma unroll 1
@@ -523,8 +538,13 @@ static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(), prod_varian
 static int prod_variant_index(int R) { return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : 3; }
 
 // Workgroups of a variant resident on one compute unit, from the compiled
-// kernel's registers and its LDS.
-static int prod_occupancy(const ProdVariant& v) {
+// kernel's registers and its LDS (looked up once per variant).
+static std::atomic<int> g_prod_occ[sizeof(kProdVariants) / sizeof(kProdVariants[0])];
+
+static int prod_occupancy(int vi) {
+  int occ = g_prod_occ[vi].load(std::memory_order_relaxed);
+  if (occ > 0) return occ;
+  const ProdVariant& v = kProdVariants[vi];
   const KernelResources* kr = find_resources(v.kernel);
   int per_simd = 1;
   if (kr) {
@@ -533,7 +553,9 @@ static int prod_occupancy(const ProdVariant& v) {
   }
   const int by_regs = max(1, per_simd / max(1, v.threads / kWave / 4));
   const int by_lds = max(1, kLdsLimit / v.lds);
-  return min(by_regs, by_lds);
+  occ = min(by_regs, by_lds);
+  g_prod_occ[vi].store(occ, std::memory_order_relaxed);
+  return occ;
 }
 
 static std::atomic<int> g_cus[64];
@@ -561,15 +583,19 @@ struct ProdLaunch {
   size_t part_bytes;   // partial sums after the counters; 0: no scratch
 };
 
-// K slices: one when the row blocks alone fill every compute unit, else
-// enough to fill the workgroup slots (no slice left empty).
-static ProdLaunch prod_plan(const ProdVariant& v, int M, int K, int R) {
+// K slices: one when the row blocks alone fill every compute unit, or when
+// the waves of a workgroup would have fewer than 4 spans each (the split's
+// reduction costs about two memory round trips, more than it saves there);
+// else enough to fill the workgroup slots, keeping 2 spans per wave (no
+// slice left empty).
+static ProdLaunch prod_plan(int vi, int M, int K, int R) {
   const int rbs = (M + 15) / 16, nsp = (K + 127) / 128;
+  const int waves = kProdVariants[vi].threads / kWave;
   const int cus = compute_units();
   ProdLaunch pl{1, nsp, 0};
-  if (rbs < cus && rbs <= kProdMaxCounters) {
-    const int slots = cus * prod_occupancy(v);
-    int ks = min(nsp, (slots + rbs - 1) / rbs);
+  if (rbs < cus && rbs <= kProdMaxCounters && nsp >= 4 * waves) {
+    const int slots = cus * prod_occupancy(vi);
+    int ks = min(nsp / (2 * waves), (slots + rbs - 1) / rbs);
     const int sps = (nsp + ks - 1) / ks;
     ks = (nsp + sps - 1) / sps;
     pl.ks = ks;
@@ -636,8 +662,9 @@ extern "C" int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, u
   }
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-  const ProdVariant& v = kProdVariants[prod_variant_index(R)];
-  const ProdLaunch pl = prod_plan(v, M, K, R);
+  const int vi = prod_variant_index(R);
+  const ProdVariant& v = kProdVariants[vi];
+  const ProdLaunch pl = prod_plan(vi, M, K, R);
   void* scratch = nullptr;
   if (pl.part_bytes > 0) {
     const int rc = prod_scratch(kProdCountBytes + pl.part_bytes, &scratch);

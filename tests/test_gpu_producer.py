@@ -189,10 +189,12 @@ def test_layer_end_to_end(name):
 
 
 def test_split_calls_of_different_sizes():
-    """Consecutive calls whose K is split over workgroups, with different
-    numbers of row blocks and ranks: the arrival counters live in the same
-    scratch bytes in every call and must be back at zero after each."""
-    for shape in [(1000, 3072, 16), (3100, 400, 8), (33, 144, 17), (3100, 400, 8), (200, 1024, 128)]:
+    """Consecutive calls whose K is split over workgroups (few row blocks, many
+    spans), with different numbers of row blocks and ranks: the arrival
+    counters live in the same scratch bytes in every call and must be back at
+    zero after each."""
+    for shape in [(1000, 8192, 16), (3100, 4096, 8), (33, 4160, 17), (3100, 4096, 8), (200, 2048, 128),
+                  (1000, 8192, 16)]:
         M, K, R = shape
         _say(f"case: producer split sequence M={M} K={K} R={R}")
         d = synthetic.producer_inputs(M, K, R, seed=M * 7 + K + R)
