@@ -19,6 +19,7 @@ ELAUNCH = -3
 EOVERLAP = -4
 EDEVICE = -5
 ENOMEM = -6
+ESCRATCH = -7
 MAX_R = 1024
 
 _PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m", "waves_n",
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_mxfp4_variant_info.restype = i
         lib.quantize_w4a4_act.argtypes = [vp] * 5 + [i, i, i, vp]
         lib.quantize_w4a4_act.restype = i
+        lib.quantize_w4a4_act_noalloc.argtypes = [vp] * 5 + [i, i, i, vp]
+        lib.quantize_w4a4_act_noalloc.restype = i
         lib.gemm_w4a4_run.argtypes = [i, i, i] + [vp] * 9 + [i, i, i, i, vp]
         lib.gemm_w4a4_run.restype = i
         lib.gemm_w4a4_plan_variant.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
@@ -124,6 +127,12 @@ QUANTIZE_MAX_R = 128
 def quantize_raw(x, lora_down, act, ascales, lora_act_in, M, K, R, stream) -> int:
     """Direct call of quantize_w4a4_act with integer addresses; returns its code."""
     return load().quantize_w4a4_act(x, lora_down, act, ascales, lora_act_in, M, K, R, stream)
+
+
+def quantize_noalloc_raw(x, lora_down, act, ascales, lora_act_in, M, K, R, stream) -> int:
+    """Direct call of quantize_w4a4_act_noalloc (no device allocation; its
+    scratch is a fixed array per GPU) with integer addresses; returns its code."""
+    return load().quantize_w4a4_act_noalloc(x, lora_down, act, ascales, lora_act_in, M, K, R, stream)
 
 
 def run_raw(fmt: str, out_f16: bool, variant: int, act, ascales, wgt, wscales, wcscale, bias,

@@ -597,6 +597,7 @@ extern "C" const char* gemm_w4a4_strerror(int code) {
     case GEMM_W4A4_EOVERLAP: return "output overlaps an input";
     case GEMM_W4A4_EDEVICE: return "current device is not gfx950";
     case GEMM_W4A4_ENOMEM: return "scratch allocation failed";
+    case GEMM_W4A4_ESCRATCH: return "needs more scratch than the no-allocation entry point holds";
     default: return "unknown error";
   }
 }

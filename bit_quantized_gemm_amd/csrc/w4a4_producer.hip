@@ -638,11 +638,40 @@ static int prod_scratch(size_t need, void** out) {
 
 }  // namespace w4a4
 
-using namespace w4a4;
+// Scratch of quantize_w4a4_act_noalloc: one copy per GPU, held until the
+// process ends. The arrival counters at its start are zero when the module
+// is loaded and every call returns them to zero. Host code must not pass
+// `scratch` itself to a kernel (it names a host-side stand-in): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES];
 
-extern "C" int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
-                                 uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
-                                 void* stream) {
+namespace w4a4 {
+
+static std::atomic<uintptr_t> g_noalloc_scratch[64];
+static std::mutex g_noalloc_mu;
+
+static int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_W4A4_EDEVICE;
+  uintptr_t ptr = g_noalloc_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    ptr = g_noalloc_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      void* sym = nullptr;   // this device's copy of the array (the device is current)
+      if (hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch)) != hipSuccess || !sym) return GEMM_W4A4_EDEVICE;
+      ptr = reinterpret_cast<uintptr_t>(sym);
+      g_noalloc_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = reinterpret_cast<void*>(ptr);
+  return GEMM_W4A4_OK;
+}
+
+// Checks, plan, scratch and launch shared by both entry points; `noalloc`
+// takes the scratch from the fixed array instead of the library's buffer.
+static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* act, uint8_t* ascales,
+                        uint16_t* lora_act_in, int M, int K, int R, void* stream, bool noalloc) {
   if (!(M >= 1 && K >= 16 && K % 16 == 0 && R >= 0 && R <= QUANTIZE_W4A4_MAX_R)) return GEMM_W4A4_EINVAL;
   const int64_t lim = int64_t(1) << 31;
   if (int64_t(M) * K * 2 >= lim || int64_t(R) * K * 2 >= lim || int64_t(M) * R * 2 >= lim)
@@ -665,16 +694,37 @@ extern "C" int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, u
   const int vi = prod_variant_index(R);
   const ProdVariant& v = kProdVariants[vi];
   const ProdLaunch pl = prod_plan(vi, M, K, R);
-  void* scratch = nullptr;
+  void* buf = nullptr;
   if (pl.part_bytes > 0) {
-    const int rc = prod_scratch(kProdCountBytes + pl.part_bytes, &scratch);
+    const size_t need = kProdCountBytes + pl.part_bytes;
+    int rc;
+    if (noalloc) {
+      if (need > size_t(QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES)) return GEMM_W4A4_ESCRATCH;
+      rc = noalloc_scratch(&buf);
+    } else {
+      rc = prod_scratch(need, &buf);
+    }
     if (rc != GEMM_W4A4_OK) return rc;
   }
-  uint8_t* sb = static_cast<uint8_t*>(scratch);
+  uint8_t* sb = static_cast<uint8_t*>(buf);
   ProdParams prm{x, lora_down, act, ascales, lora_act_in, M, K, R, pl.ks, pl.sps,
                  sb ? reinterpret_cast<float*>(sb + kProdCountBytes) : nullptr, reinterpret_cast<uint32_t*>(sb)};
   void* args[] = {&prm};
   const hipError_t e = hipLaunchKernel(v.kernel, dim3(((M + 15) / 16) * pl.ks), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}
+
+}  // namespace w4a4
+
+extern "C" int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
+                                 uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
+                                 void* stream) {
+  return w4a4::quantize_run(x, lora_down, act, ascales, lora_act_in, M, K, R, stream, false);
+}
+
+extern "C" int quantize_w4a4_act_noalloc(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
+                                         uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
+                                         void* stream) {
+  return w4a4::quantize_run(x, lora_down, act, ascales, lora_act_in, M, K, R, stream, true);
 }

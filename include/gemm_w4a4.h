@@ -52,7 +52,9 @@ enum {
   GEMM_W4A4_ELAUNCH = -3,     /* the HIP launch itself failed */
   GEMM_W4A4_EOVERLAP = -4,    /* out overlaps an input */
   GEMM_W4A4_EDEVICE = -5,     /* the current device is not gfx950 */
-  GEMM_W4A4_ENOMEM = -6       /* quantize_w4a4_act could not allocate its scratch buffer */
+  GEMM_W4A4_ENOMEM = -6,      /* quantize_w4a4_act could not allocate its scratch buffer */
+  GEMM_W4A4_ESCRATCH = -7     /* the call needs more scratch than quantize_w4a4_act_noalloc's
+                                 fixed array (QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES) */
 };
 
 #define GEMM_W4A4_MAX_R 1024
@@ -238,6 +240,31 @@ int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
 int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
                       uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
                       void* stream);
+
+/*
+ * quantize_w4a4_act_noalloc — quantize_w4a4_act for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, kernels and results as
+ * quantize_w4a4_act; it calls no allocating routine.
+ *
+ * When K is split over several workgroups (few rows, long K), the kernel
+ * keeps float32 partial sums and one arrival counter per 16 rows in scratch
+ * memory; quantize_w4a4_act allocates that buffer on first need, this entry
+ * point uses a fixed device array of QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES
+ * (4 KiB of counters + 4 MiB of partial sums) that each GPU holds until the
+ * process ends. A call that would need more returns GEMM_W4A4_ESCRATCH with
+ * nothing enqueued. The counters are zero at load and every completed call
+ * returns them to zero.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, or host threads) race on it and must be ordered
+ * by the caller. Return codes as for quantize_w4a4_act, plus
+ * GEMM_W4A4_ESCRATCH.
+ */
+#define QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES (4096 + (4 << 20))
+int quantize_w4a4_act_noalloc(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
+                              uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
+                              void* stream);
 
 /* Static string for a return code (never NULL). */
 const char* gemm_w4a4_strerror(int code);

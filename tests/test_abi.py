@@ -120,7 +120,7 @@ def test_output_overlapping_an_input(target, entry):
 
 
 def test_strerror():
-    for code in (w4.OK, w4.EINVAL, w4.EALIGN, w4.ELAUNCH, w4.EOVERLAP, w4.EDEVICE, w4.ENOMEM, -99):
+    for code in (w4.OK, w4.EINVAL, w4.EALIGN, w4.ELAUNCH, w4.EOVERLAP, w4.EDEVICE, w4.ENOMEM, w4.ESCRATCH, -99):
         assert isinstance(w4.strerror(code), str) and w4.strerror(code)
 
 
@@ -291,36 +291,43 @@ def test_plan_variant_matches_plan(fmt):
 
 # ---------------------------------------------------------------- quantize_w4a4_act
 
-def _q(**over):
+QENTRIES = ["quantize_raw", "quantize_noalloc_raw"]   # quantize_w4a4_act and its no-allocation twin
+
+
+def _q(qentry="quantize_raw", **over):
     a = dict(x=0x10000, lora_down=0x200000, act=0x300000, ascales=0x400000, lora_act_in=0x500000,
              M=64, K=128, R=16, stream=0)
     a.update(over)
-    return w4.quantize_raw(a["x"], a["lora_down"], a["act"], a["ascales"], a["lora_act_in"],
-                           a["M"], a["K"], a["R"], a["stream"])
+    return getattr(w4, qentry)(a["x"], a["lora_down"], a["act"], a["ascales"], a["lora_act_in"],
+                               a["M"], a["K"], a["R"], a["stream"])
 
 
 @pytest.mark.parametrize("over", [dict(M=0), dict(K=0), dict(K=8), dict(K=24), dict(R=-1),
                                   dict(R=w4.QUANTIZE_MAX_R + 1), dict(x=0), dict(act=0),
                                   dict(ascales=0), dict(lora_down=0), dict(lora_act_in=0),
                                   dict(M=1 << 20, K=1 << 11)])
-def test_quantize_invalid_arguments(over):
-    assert _q(**over) == w4.EINVAL
+@pytest.mark.parametrize("qentry", QENTRIES)
+def test_quantize_invalid_arguments(over, qentry):
+    assert _q(qentry, **over) == w4.EINVAL
 
 
 @pytest.mark.parametrize("over", [dict(x=0x10008), dict(lora_down=0x200004), dict(act=0x300004),
                                   dict(lora_act_in=0x500001)])
-def test_quantize_misaligned(over):
-    assert _q(**over) == w4.EALIGN
+@pytest.mark.parametrize("qentry", QENTRIES)
+def test_quantize_misaligned(over, qentry):
+    assert _q(qentry, **over) == w4.EALIGN
 
 
 @pytest.mark.parametrize("over", [dict(act=0x10000 + 64), dict(ascales=0x200000 + 16),
                                   dict(lora_act_in=0x300000 + 32), dict(ascales=0x300000 + 8)])
-def test_quantize_overlap(over):
-    assert _q(**over) == w4.EOVERLAP
+@pytest.mark.parametrize("qentry", QENTRIES)
+def test_quantize_overlap(over, qentry):
+    assert _q(qentry, **over) == w4.EOVERLAP
 
 
-def test_quantize_rank_zero_needs_no_lora_pointers():
-    rc = _q(R=0, lora_down=0, lora_act_in=0)
+@pytest.mark.parametrize("qentry", QENTRIES)
+def test_quantize_rank_zero_needs_no_lora_pointers(qentry):
+    rc = _q(qentry, R=0, lora_down=0, lora_act_in=0)
     assert rc in (w4.EDEVICE, w4.ELAUNCH, w4.OK)
 
 
