@@ -26,7 +26,7 @@ _PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m",
                 "threads", "lds_bytes", "lds_stage_bytes", "lds_limit", "tiles_m", "tiles_n",
                 "grid", "k_stages", "lora_steps", "occupancy", "policy", "lora_place",
                 "lds_ring_bytes", "lds_side_bytes", "flavour", "vgprs", "agprs", "sgprs",
-                "regs_limit")
+                "regs_limit", "k_groups")
 
 
 class Plan(ctypes.Structure):

@@ -142,7 +142,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const int g = lane >> 5;                 // which half of the wave (k group)
   const int wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy (for M0)
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  // wave = (wm * KG + kg) * WN + wn: k-group kg of wave tile (wm, wn)
+  const int wn = wave % C::WN, wm = wave / C::WN / C::KG;
+  const int kg = (wave_u / C::WN) % C::KG;   // uniform
 
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -428,18 +430,37 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const int last = nst - 1;
   Chunk C0, C1;
   EpiRegs epi_regs;
+  // DEEP (KG == 2, fast flavours): raw scales of stage j in set j % 4,
+  // loaded with the DMA of the same stage (S-1 stages ahead: a k-group
+  // iteration is a quarter of a single-group one, too short to cover a load
+  // issued one stage ahead). The general flavour keeps the single-group
+  // prefetch (the deeper one's unrolling costs it scalar registers).
+  constexpr bool DEEP = C::KG == 2 && !GENERAL;
+  RawT s_raw4[DEEP ? 4 : 1][2] = {};
   epilogue_prefetch<C, GENERAL>(p, smem, tid, m0, n0, epi_regs);   // older than every ring op below
-  load_scales(0, s_raw[0]);
-  issue_dma(0, 0);
-  load_scales(min(1, last), s_raw[1]);
+  if constexpr (!DEEP) {
+    load_scales(0, s_raw[0]);
+    issue_dma(0, 0);
+    load_scales(min(1, last), s_raw[1]);
 #pragma unroll
-  for (int j = 1; j < C::STAGES - 1; ++j) issue_dma(min(j, last), j);
-  // SCL(0), DMA(0): after them come SCL(1) and DMA(1 .. S-2)
-  wait_vm_lgkm0<std::min(63, (C::STAGES - 2) * DMA_N + (GENERAL ? 0 : 2))>();
-  store_scales(0, 0, s_raw[0]);
+    for (int j = 1; j < C::STAGES - 1; ++j) issue_dma(min(j, last), j);
+    // SCL(0), DMA(0): after them come SCL(1) and DMA(1 .. S-2)
+    wait_vm_lgkm0<std::min(63, (C::STAGES - 2) * DMA_N + (GENERAL ? 0 : 2))>();
+    store_scales(0, 0, s_raw[0]);
+  } else {
+    static_assert(C::STAGES <= 4, "scale sets cover S-1 stages ahead");
+#pragma unroll
+    for (int j = 0; j < C::STAGES - 1; ++j) {
+      load_scales(min(j, last), s_raw4[j]);
+      issue_dma(min(j, last), j);
+    }
+    // SCL(0), DMA(0): after them come SCL(j), DMA(j) for j = 1 .. S-2
+    wait_vm_lgkm0<std::min(63, (C::STAGES - 2) * (DMA_N + (GENERAL ? 0 : 2)))>();
+    store_scales(0, 0, s_raw4[0]);
+  }
   wait_vm_lgkm0<63>();
   wg_barrier();
-  read_chunk(0, 0, C0);
+  read_chunk(0, kg, C0);   // KG == 1: chunk 0; KG == 2: the k-group's own chunk
   decode_all(C0, 0, D[0]);
 
   // PAR = st & 1, fixed per call site of the two-way unrolled loop.
@@ -489,15 +510,147 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
       for (int S = 0; S < 8; ++S) kstep(S);
     }
   };
+  // ---- KG == 2: k-group kg runs k-steps 4kg .. 4kg+3 of every stage, from
+  // chunk kg of its operand rows, 4 k-steps of G MFMA groups per iteration.
+  // The memory ops keep the order and waits of the single-group schedule:
+  // slots 0, 1 scale loads of stage st+2, then the DMA rounds of stage st+S-1,
+  // slot SLOT_SCL2 the fp16 scales of stage st+1, slot SLOT_RD2 (k-step 2)
+  // the barrier that publishes stage st+1, then the k-group's T tiles of
+  // stage st+1 (decoded in k-step 3). The k-group reads nothing else, so
+  // every read of stage st-1 precedes the barrier of iteration st-1, and
+  // DMA(st+S-1) may refill its buffer from the start of iteration st.
+  constexpr int SLOT_SCL2 = G + G / 2, SLOT_RD2 = 2 * G;
+  // ops issued after DMA(st+1) when stage st+1's scales are stored: the S-2
+  // later pairs SCL(j), DMA(j) (the general flavour counts no scale loads,
+  // which waits longer); SCL(st+1) precedes DMA(st+1)
+  constexpr int VM_KG = DEEP ? std::min(63, (C::STAGES - 2) * (DMA_N + 2)) : VM_AFTER_SCL;
+  auto iteration_kg = [&]<int PAR>(int st) __attribute__((always_inline)) {
+    // stage st's chunk is in C0 for even st, C1 for odd; stage st+1's goes to the other
+    Chunk& Cc = *[&]() { if constexpr (PAR % 2 == 0) return &C0; else return &C1; }();
+    Chunk& Cn = *[&]() { if constexpr (PAR % 2 == 0) return &C1; else return &C0; }();
+    // scales: DEEP loads stage st+S-1 into set (st+S-1) % 4 and stores stage
+    // st+1 from set (st+1) % 4; otherwise stage st+2 into s_raw[st % 2], as
+    // the single-group loop
+    RawT (&sc_load)[2] = *[&]() { if constexpr (DEEP) return &s_raw4[(PAR + C::STAGES - 1) % 4]; else return &s_raw[PAR % 2]; }();
+    RawT (&sc_store)[2] = *[&]() { if constexpr (DEEP) return &s_raw4[(PAR + 1) % 4]; else return &s_raw[1 - PAR % 2]; }();
+    const int st_scl = min(st + (DEEP ? C::STAGES - 1 : 2), last);
+    const int st_dma = min(st + C::STAGES - 1, last);
+    auto kstep = [&](auto Sv) __attribute__((always_inline)) {
+      const int S = Sv;
+      const Dec& cur = D[S & 1];
+      Dec& nxt = D[(S + 1) & 1];
+      const Chunk& Rn = S + 1 < 4 ? Cc : Cn;
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        const int j = q / C::MI, i = q % C::MI;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[j][i], 0, 0, 0);
+        const int slot = S * G + q;
+        if (slot == SLOT_RD2) {
+          wait_vm_lgkm0<63>();   // this wave's scale stores
+          wg_barrier();
+        }
+#pragma unroll
+        for (int pr = 4 * T * q / G; pr < 4 * T * (q + 1) / G; ++pr) decode_pair(pr, Rn, (S + 1) & 3, nxt);
+        if (slot < 2)
+          load_scale_half(st_scl, sc_load, slot);
+        else if (slot < SLOT_RD1)
+#pragma unroll
+          for (int u = 0; u < DMA_PER_SLOT; ++u)
+            dma_part(st_dma, st + C::STAGES - 1, (slot - 2) * DMA_PER_SLOT + u);
+        else if (slot == SLOT_SCL2) {
+          wait_vm<VM_KG>();
+          store_scales(st + 1, st + 1, sc_store);
+        } else if (slot >= SLOT_RD2 && slot < SLOT_RD2 + T)
+          read_tile(st + 1, kg, slot - SLOT_RD2, Cn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (GENERAL) {
+      static_for<0, 4>([&]<int S>() __attribute__((always_inline)) { kstep(std::integral_constant<int, S>{}); });
+    } else {
+#pragma unroll
+      for (int S = 0; S < 4; ++S) kstep(S);
+    }
+  };
+
   int st = 0;
-  for (; st + 1 < nst; st += 2) {
-    iteration.template operator()<0>(st);
-    iteration.template operator()<1>(st + 1);
+  if constexpr (C::KG == 1) {
+    for (; st + 1 < nst; st += 2) {
+      iteration.template operator()<0>(st);
+      iteration.template operator()<1>(st + 1);
+    }
+    if (st < nst) iteration.template operator()<0>(st);
+  } else {
+    static_assert(C::KG == 2, "one or two k-groups");
+    static_assert(SLOT_RD1 <= SLOT_SCL2 && SLOT_SCL2 < SLOT_RD2 && SLOT_RD2 + T <= 3 * G,
+                  "k-group schedule: scales, DMA, scale store, barrier, then the next stage's chunk");
+    if constexpr (DEEP) {
+      for (; st + 3 < nst; st += 4) {
+        iteration_kg.template operator()<0>(st);
+        iteration_kg.template operator()<1>(st + 1);
+        iteration_kg.template operator()<2>(st + 2);
+        iteration_kg.template operator()<3>(st + 3);
+      }
+      if (st < nst) iteration_kg.template operator()<0>(st);
+      if (st + 1 < nst) iteration_kg.template operator()<1>(st + 1);
+      if (st + 2 < nst) iteration_kg.template operator()<2>(st + 2);
+    } else {
+      for (; st + 1 < nst; st += 2) {
+        iteration_kg.template operator()<0>(st);
+        iteration_kg.template operator()<1>(st + 1);
+      }
+      if (st < nst) iteration_kg.template operator()<0>(st);
+    }
   }
-  if (st < nst) iteration.template operator()<0>(st);
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
-  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0, epi_regs);
+  if constexpr (C::KG == 1) {
+    epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0, epi_regs);
+  } else {
+    // k-group kg keeps m-tiles [kg MIH, (kg+1) MIH) of the wave tile and adds
+    // its partner's partial sums of them; it hands the other half to the
+    // partner. Through the drained ring: wave w's outgoing tiles at
+    // [w][tile][quarter][lane] (16 bytes per lane, consecutive lanes
+    // consecutive: no bank conflicts).
+    constexpr int MIH = C::MI / 2;
+    using E = EpiView<C>;
+    f32x16 kept[C::NI][MIH];
+    const int partner = wave + (kg == 0 ? C::WN : -C::WN);
+    float* xbuf = reinterpret_cast<float*>(smem);
+    constexpr int TILE_F = 16 * kWave;   // floats per exchanged tile
+    static_assert(C::THREADS / kWave * C::NI * MIH * TILE_F * 4 <= C::RING_BYTES, "exchange fits the ring");
+    auto exchange = [&]<int KGC>() __attribute__((always_inline)) {
+      f32x4* out = reinterpret_cast<f32x4*>(xbuf + wave * (C::NI * MIH * TILE_F));
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int ii = 0; ii < MIH; ++ii) {
+          const f32x16& a = acc[j][(1 - KGC) * MIH + ii];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            out[((j * MIH + ii) * 4 + qq) * kWave + lane] = f32x4{a[4 * qq], a[4 * qq + 1], a[4 * qq + 2], a[4 * qq + 3]};
+        }
+      __syncthreads();
+      const f32x4* in = reinterpret_cast<const f32x4*>(xbuf + partner * (C::NI * MIH * TILE_F));
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int ii = 0; ii < MIH; ++ii) {
+          const f32x16& a = acc[j][KGC * MIH + ii];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4 b = in[((j * MIH + ii) * 4 + qq) * kWave + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kept[j][ii][4 * qq + e] = a[4 * qq + e] + b[e];
+          }
+        }
+    };
+    __syncthreads();   // every wave is done with the ring
+    if (kg == 0) exchange.template operator()<0>();
+    else exchange.template operator()<1>();
+    __syncthreads();   // the epilogue reuses the ring
+    epilogue<E, GENERAL, F16>(kept, p, smem, tid, m0, n0, epi_regs);
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -522,8 +675,12 @@ VariantDesc nv_variant(double cost) {
 // where 128x128 tiles win: the first LoRA chunk and wcscale/bias arrive during
 // the K-loop, and three stages still cover the DMA latency). Smaller wave
 // tiles decode more operand tiles per MFMA (0.58, 0.75 and 1.0 per MFMA).
+// 64x192 with two k-groups (0.83 per MFMA, one workgroup per CU): 1.30,
+// from 1000x3072x3072, where it and 128x128 both need one round (22.4 against
+// 27.5 us).
 static const VariantDesc kVariants[] = {nv_variant<Cfg256x192>(1.00), nv_variant<Cfg128x128>(1.22),
-                                        nv_variant<Cfg256x128>(1.16), nv_variant<Cfg128x128S>(1.20)};
+                                        nv_variant<Cfg256x128>(1.16), nv_variant<Cfg128x128S>(1.20),
+                                        nv_variant<Cfg64x192K>(1.30)};
 static constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 // Size rules. Besides the operator's own (K a multiple of the 16-wide scale

@@ -56,7 +56,7 @@ inline const KernelResources* find_resources(const void* kernel) {
 struct VariantDesc {
   const void* kernel[2][3];   // [F16][flavour: general, fast, fast with act-scale windows]
   bool has_window;            // the third flavour exists
-  int block_m, block_n, block_k, waves_m, waves_n, threads, occ, stage_bytes, policy;
+  int block_m, block_n, block_k, waves_m, waves_n, k_groups, threads, occ, stage_bytes, policy;
   Budget budget;
   double cost;                // time per output element of a full round, relative to 256x192
 };
@@ -64,7 +64,7 @@ struct VariantDesc {
 template <class C>
 VariantDesc describe(const void* const (&k)[2][3], bool has_window, double cost) {
   return VariantDesc{{{k[0][0], k[0][1], k[0][2]}, {k[1][0], k[1][1], k[1][2]}}, has_window, C::BM, C::BN,
-                     C::BK, C::WM, C::WN, C::THREADS, C::OCC, C::STAGE_BYTES, C::POLICY, C::BUDGET, cost};
+                     C::BK, C::WM, C::WN, C::KG, C::THREADS, C::OCC, C::STAGE_BYTES, C::POLICY, C::BUDGET, cost};
 }
 
 inline void fill_static(const VariantDesc& v, int idx, gemm_w4a4_plan_t* pl) {
@@ -76,6 +76,7 @@ inline void fill_static(const VariantDesc& v, int idx, gemm_w4a4_plan_t* pl) {
   pl->stages = v.budget.depth;
   pl->waves_m = v.waves_m;
   pl->waves_n = v.waves_n;
+  pl->k_groups = v.k_groups;
   pl->threads = v.threads;
   pl->lds_bytes = v.budget.lds_bytes;
   pl->lds_stage_bytes = v.stage_bytes;
@@ -87,7 +88,7 @@ inline void fill_static(const VariantDesc& v, int idx, gemm_w4a4_plan_t* pl) {
   pl->lds_side_bytes = v.budget.side_bytes;
   // registers a lane may hold: 512 (VGPR + AGPR) per SIMD lane, shared by the
   // waves resident on that SIMD
-  const int waves_per_simd = std::max(1, (v.waves_m * v.waves_n * v.occ + 3) / 4);
+  const int waves_per_simd = std::max(1, (v.waves_m * v.waves_n * v.k_groups * v.occ + 3) / 4);
   pl->regs_limit = 512 / waves_per_simd;
   pl->flavour = -1;
   pl->vgprs = pl->agprs = pl->sgprs = -1;

@@ -115,6 +115,10 @@ struct EpiSide {
 // BM x BN output tile per workgroup, WM x WN waves, each wave owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles. Every pipeline stage covers
 // BK = 128 values of k, i.e. 8 NVFP4 scale blocks and 8 MFMA k-steps of 16.
+// With KG = 2 k-groups, each wave block is computed by two waves, one taking
+// k-steps 0-3 of every stage and the other k-steps 4-7, whose partial sums
+// meet in LDS after the K-loop (a tile with few rows then still occupies
+// every SIMD with a wave tile big enough to keep the decode per MFMA low).
 // OCC workgroups share a compute unit; POLICY steers the budget solve, which
 // sets the ring depth (STAGES) and the side region.
 //
@@ -124,11 +128,11 @@ struct EpiSide {
 //   SA act scales  fp16 [4 k-block pairs][BM rows][2]
 //   SB wgt scales  fp16 [4 k-block pairs][BN rows][2]
 // The geometry of a tile (what one ring stage holds), apart from its budget.
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int KG_ = 1>
 struct TileShape {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KG = KG_;
   static constexpr int BK = 128;
-  static constexpr int THREADS = WM * WN * kWave;
+  static constexpr int THREADS = WM * WN * KG * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
   static constexpr int MI = TM / 32, NI = TN / 32;   // 32x32 MFMA tiles per wave
   static constexpr int ROW_BYTES = BK / 2;      // packed bytes of one row per stage
@@ -140,11 +144,12 @@ struct TileShape {
   static constexpr int STAGE_BYTES = SB_OFF + KBLK * BN * 2;
   static constexpr int PACKED_BYTES = SA_OFF;   // bytes moved by DMA per stage
   using Pieces = SidePieces<BM, BN, THREADS>;
+  static_assert(KG == 1 || (KG == 2 && MI % 2 == 0), "k-groups split the 8 k-steps and the m-tiles in two");
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int OCC_, int POLICY_>
-struct TileCfg : TileShape<BM_, BN_, WM_, WN_> {
-  using G = TileShape<BM_, BN_, WM_, WN_>;
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int POLICY_, int KG_ = 1>
+struct TileCfg : TileShape<BM_, BN_, WM_, WN_, KG_> {
+  using G = TileShape<BM_, BN_, WM_, WN_, KG_>;
   using G::BM, G::BN, G::THREADS, G::TM, G::TN, G::BK, G::STAGE_BYTES, G::PACKED_BYTES;
   static constexpr int OCC = OCC_;              // workgroups per CU the variant is built for
   static constexpr int POLICY = POLICY_;
@@ -168,11 +173,21 @@ struct TileCfg : TileShape<BM_, BN_, WM_, WN_> {
   static_assert(LDS_BYTES * OCC <= kLdsLimit, "occupancy target exceeds the LDS budget");
 };
 
+// The tile as the epilogue sees it once the k-groups have exchanged partial
+// sums: k-group kg of wave row wm keeps m-tiles [kg MI/KG, (kg+1) MI/KG) of
+// that row's wave tile, i.e. it is wave row wm*KG + kg of a KG-times finer
+// grid of waves (same LDS layout, same threads).
+template <class C>
+struct EpiView : C {
+  static constexpr int WM = C::WM * C::KG, TM = C::TM / C::KG, MI = C::MI / C::KG;
+};
+
 // The compiled instances, in variant order. The solver picks among them.
 using Cfg256x192 = TileCfg<256, 192, 2, 2, 1, kDepthFirst>;   // ring 4, side WB+LA
 using Cfg128x128 = TileCfg<128, 128, 2, 2, 2, kDepthFirst>;   // ring 4, no side region
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 1, kDepthFirst>;   // ring 4, side WB+LA+LU
 using Cfg128x128S = TileCfg<128, 128, 2, 2, 2, kSideFirst>;   // ring 3, side WB+LA+LU
+using Cfg64x192K = TileCfg<64, 192, 1, 2, 1, kDepthFirst, 2>; // ring 4, side WB+LA+LU; 2 k-groups
 
 // MXFP4 kernel: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN), 32x32x64
 // scaled FP4 MFMAs. A stage covers BK = 128 values of k = 2 MFMA k-steps = 4
@@ -183,7 +198,7 @@ using Cfg128x128S = TileCfg<128, 128, 2, 2, 2, kSideFirst>;   // ring 3, side WB
 //      the global layout's order), padded to whole 4-byte DMA rounds
 template <int BM_, int BN_, int WM_, int WN_>
 struct MxTileShape {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KG = 1;
   static constexpr int BK = 128;
   static constexpr int THREADS = WM * WN * kWave;
   static constexpr int TM = BM / WM, TN = BN / WN;

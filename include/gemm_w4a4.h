@@ -163,6 +163,8 @@ typedef struct {
   int agprs;          /* of which accumulation registers */
   int sgprs;          /* scalar registers, same kernel */
   int regs_limit;     /* VGPR + AGPR a lane may hold at this occupancy (512 per SIMD lane, shared) */
+  int k_groups;       /* waves sharing each wave tile, splitting every stage's k-steps between them
+                         (threads = 64 * waves_m * waves_n * k_groups) */
 } gemm_w4a4_plan_t;
 
 /* Fill *plan for (M, N, K, R). Returns GEMM_W4A4_OK or GEMM_W4A4_EINVAL

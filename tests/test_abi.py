@@ -136,7 +136,7 @@ def test_plan(shape):
     assert p["k_stages"] == -(-K // p["block_k"])
     assert p["lora_steps"] == -(-R // 16)
     assert p["lds_bytes"] <= p["lds_limit"] == 163840
-    assert p["threads"] == 64 * p["waves_m"] * p["waves_n"]
+    assert p["threads"] == 64 * p["waves_m"] * p["waves_n"] * p["k_groups"]
     with pytest.raises(ValueError):
         w4.plan(M, N, K + 8, R)
 
@@ -230,7 +230,7 @@ def test_solver_lds_matches_code_objects():
             assert int(m[".vgpr_spill_count"]) == 0, (key, m)
             assert int(m.get(".private_segment_fixed_size", 0)) == 0, (key, m)
             regs = int(m[".vgpr_count"])
-            waves_per_simd = max(1, (v["waves_m"] * v["waves_n"] + 3) // 4)
+            waves_per_simd = max(1, (v["waves_m"] * v["waves_n"] * v["k_groups"] + 3) // 4)
             occ = v["lds_limit"] // v["lds_bytes"]
             assert regs * waves_per_simd <= 512, (key, regs)
             assert occ >= 1
