@@ -193,6 +193,76 @@ def producer_bytes(M: int, K: int, R: int) -> int:
     return 2 * M * K + 2 * R * K + M * K // 2 + M * K // 16 + 2 * M * R
 
 
+CAL_SHAPES = ["ragged", (2000, 3072, 3072, 16), "qkv", "prod_k3840_n3072", "prod_k3840_n15360",
+              "prod_k15360_n3840", "prod_k10240_n3072"]
+
+
+def calibrate(w4, synthetic, rounds=3, reps=20) -> int:
+    """Every compiled tile instance of each format at CAL_SHAPES. One JSON
+    line per (format, shape): average launch time of each instance (best of
+    `rounds` interleaved rounds of `reps` launches, after clock settling), the
+    solver's pick, the fastest, and each instance's measured time per output
+    element of one round of tiles on the busiest compute unit, relative to
+    instance 0 -- the quantity the solver's cost table holds."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for fmt in ("nvfp4", "mxfp4"):
+        nvar = len(w4.variants(fmt))
+        for shape in CAL_SHAPES:
+            if isinstance(shape, str):
+                wl = synthetic.workload(shape)
+                x = synthetic.make_inputs(wl, fmt=fmt)
+                name = shape
+            else:
+                x = synthetic.custom_inputs(*shape, seed=3000, fmt=fmt)
+                name = "x".join(map(str, shape))
+            M, N, K, R = x["M"], x["N"], x["K"], x["R"]
+            t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+                 for k in ("act", "ascales", "wgt", "wscales", "wcscale", "bias")}
+            la = torch.from_numpy(x["lora_act_in"].view(np.int16)).to(dev)
+            lu = torch.from_numpy(x["lora_up"].view(np.int16)).to(dev)
+            out = torch.empty((M, N), dtype=torch.int16, device=dev)
+            args = (t["act"].data_ptr(), t["ascales"].data_ptr(), t["wgt"].data_ptr(), t["wscales"].data_ptr(),
+                    t["wcscale"].data_ptr(), t["bias"].data_ptr(), la.data_ptr(), lu.data_ptr(),
+                    out.data_ptr(), M, N, K, R, stream.cuda_stream)
+
+            def run(v, n):
+                for _ in range(n):
+                    if w4.run_raw(fmt, False, v, *args) != 0:
+                        raise RuntimeError(f"gemm_w4a4_run failed for variant {v}")
+
+            t0 = time.perf_counter()
+            while (time.perf_counter() - t0) < 0.3:
+                run(0, 8)
+                torch.cuda.synchronize()
+            us = [float("inf")] * nvar
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for r in range(rounds):
+                for v in [(r + i) % nvar for i in range(nvar)]:
+                    run(v, 3)
+                    e0.record(stream)
+                    run(v, reps)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us[v] = min(us[v], e0.elapsed_time(e1) * 1e3 / reps)
+            per_elem = []
+            for v in range(nvar):
+                p = w4.plan_variant(M, N, K, R, v, fmt=fmt)
+                slots = 256 * p["occupancy"]
+                rounds_v = -(-p["grid"] // slots)
+                per_cu = min(p["occupancy"], -(-p["grid"] // 256))
+                per_elem.append(us[v] / (rounds_v * per_cu * p["block_m"] * p["block_n"]))
+            pick = w4.plan(M, N, K, R, fmt=fmt)["variant"]
+            print(json.dumps({"calibrate": fmt, "shape": name, "M": M, "N": N, "K": K, "R": R,
+                              "us": [round(v, 2) for v in us], "pick": pick,
+                              "fastest": int(np.argmin(us)),
+                              "pick_vs_fastest": round(us[pick] / min(us), 3),
+                              "cost_rel_v0": [round(c / per_elem[0], 3) for c in per_elem]}), flush=True)
+    return 0
+
+
 def settle_and_time(step, stream, steps, warmup, settle_ms):
     """Warm-up (W steps, then until the step has kept the GPU busy settle_ms),
     then exactly `steps` steps between two events on the launch stream;
@@ -316,6 +386,10 @@ def main() -> int:
     ap.add_argument("--op", default="gemm", choices=["gemm", "producer"],
                     help="gemm: the fused W4A4 GEMM (default); producer: quantize_w4a4_act, the "
                          "layer's memory-bound half, at the workload's M x K and rank R")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead of one launch configuration: every compiled tile instance of both "
+                         "formats timed at the shapes where the solver's choice matters, with the "
+                         "measured cost per output element that the solver's table approximates")
     ap.add_argument("--routes", action="store_true",
                     help="instead of the GEMM: the per-block arithmetic of the decode + fp16 MFMA route "
                          "and of the scaled-FP4-MFMA route, for the workload's K/16 blocks per wave")
@@ -348,6 +422,8 @@ def main() -> int:
                                      "waves": probes.PEAK_GROUPS * 4, "wave_tile": "128x96"},
                           **rates}))
         return 0
+    if a.calibrate:
+        return calibrate(w4, synthetic)
     if a.op == "producer":
         return bench_producer(a, wl)
     mx = a.fmt == "mxfp4"
