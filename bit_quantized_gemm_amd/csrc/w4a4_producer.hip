@@ -51,10 +51,11 @@ namespace w4a4 {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // WAVES waves per workgroup, RTILES rank tiles of 16 (R <= 16 * RTILES),
-// DEPTH ring slots per wave.
-template <int WAVES_, int RTILES_, int DEPTH_>
+// DEPTH ring slots per wave, HALVES register sets a span's lora_down
+// operands are split over (1, or 2 for the largest ranks).
+template <int WAVES_, int RTILES_, int DEPTH_, int HALVES_ = 1>
 struct ProdCfg {
-  static constexpr int WAVES = WAVES_, RTILES = RTILES_, DEPTH = DEPTH_;
+  static constexpr int WAVES = WAVES_, RTILES = RTILES_, DEPTH = DEPTH_, HALVES = HALVES_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int ROWS = 16;
   static constexpr int SPAN_K = 128;
@@ -68,13 +69,21 @@ struct ProdCfg {
   static constexpr int NL = 4 * RTILES;                           // lora_down loads per span
   // lora_down operands of a span, L(j), go to register set j % NSETS. With
   // two sets (R <= 32) L(j+1) is issued early in span j, beside the refill
-  // DMA(j + DEPTH); with one set (the largest ranks, whose set alone is 128
-  // registers) both are issued at the end of span j, after its MFMAs.
-  static constexpr int NSETS = RTILES >= 1 && RTILES <= 2 ? 2 : 1;
-  static constexpr bool EARLY = NSETS == 2;
-  // Issue order: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); then per span j the
-  // stores S(j-1) of the previous span's results and the pair L(j+1),
-  // DMA(j+DEPTH). A pair past the wave's last span is issued as the
+  // DMA(j + DEPTH); with one set both are issued at the end of span j, after
+  // its MFMAs. SPLIT (HALVES == 2, the largest ranks, whose whole operand
+  // set is 128 registers): set h holds rank tiles [h RTILES/2, (h+1)
+  // RTILES/2) of a span, L(j, h); span j issues L(j, 1) early, beside the
+  // refill DMA, and L(j+1, 0) once its MFMAs on set 0 are issued, so that
+  // two waves of 128 operand registers each fit one SIMD.
+  static constexpr bool SPLIT = HALVES == 2;
+  static constexpr int NSETS = SPLIT ? 2 : RTILES >= 1 && RTILES <= 2 ? 2 : 1;
+  static constexpr bool EARLY = !SPLIT && NSETS == 2;
+  static constexpr int UNROLL = SPLIT ? 1 : NSETS;   // set indices constant in the unrolled loop
+  static constexpr int PH = RTILES / HALVES;          // rank tiles per set
+  static constexpr int NLH = 4 * PH;                  // loads per set
+  // Issue order (not SPLIT): DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); then per
+  // span j the stores S(j-1) of the previous span's results and the pair
+  // L(j+1), DMA(j+DEPTH). A pair past the wave's last span is issued as the
   // same loads on an empty descriptor (they read nothing), so that every
   // count below is the same in every span. Loads complete in issue order and a store can only make a
   // count of loads stricter, so waiting until at most X vector-memory ops
@@ -84,9 +93,14 @@ struct ProdCfg {
   //   L(j):   EARLY: DMA(j-1+DEPTH) and span j's pair; else DMA(j-1+DEPTH).
   // (Counts above the counter's 63 are capped: a stricter wait.)
   static constexpr int cap(int v) { return v < 63 ? v : 63; }
-  static constexpr int VM_X = cap((DEPTH - 1) * (D + NL));
-  static constexpr int VM_X0 = cap((DEPTH - 1) * D + NL);
-  static constexpr int VM_L = cap(EARLY ? 2 * D + NL : D);
+  // SPLIT: DMA(0 .. DEPTH-1), L(0, 0); then per span j: S(j-1), L(j, 1),
+  // DMA(j+DEPTH), and after the first MFMAs L(j+1, 0). DMA(j) is then
+  // followed by L(j-DEPTH+1, 0) and DEPTH-1 whole spans; L(j, 0) and L(j, 1)
+  // each by one half-set and one DMA.
+  static constexpr int VM_X = cap(SPLIT ? NLH + (DEPTH - 1) * (2 * NLH + D) : (DEPTH - 1) * (D + NL));
+  static constexpr int VM_X0 = cap((DEPTH - 1) * D + (SPLIT ? NLH : NL));
+  static constexpr int VM_L = cap(SPLIT ? NLH + D : EARLY ? 2 * D + NL : D);
+  static_assert(!SPLIT || RTILES % 2 == 0, "two halves of rank tiles");
   static_assert(DEPTH >= 2, "ring depth");
   static_assert(RED_BYTES <= WAVES * RING, "partial sums fit in the drained rings");
   static_assert(LDS <= kLdsLimit, "LDS budget");
@@ -206,6 +220,78 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// Split-K partial sums: float32, [row block][slice][rank][ROWS rows], so
+// that the four rows an MFMA lane holds for one rank are one 16-byte piece,
+// stored and loaded as two 8-byte device-scope atomic accesses.
+constexpr int kProdMaxSlices = 8;
+
+// (The whole vector is reinterpreted: this compiler's bit-cast of a single
+// vector element reads the vector's first element.)
+__device__ __forceinline__ void store_partial4(float* dst, const f32x4_t& v) {
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  const u64x2 w = __builtin_bit_cast(u64x2, v);
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+  __hip_atomic_store(d, uint64_t(w.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, uint64_t(w.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// K split over workgroups: the last workgroup of row block rb (rows m0 ..
+// m0+ROWS-1) to finish adds the slices' partial sums in slice order and
+// writes lora_act_in. The partial sums and the counter are device-scope
+// atomic accesses, each coherent across the compute dies by itself; every
+// wave waits until its stores are acknowledged before the barrier, which
+// orders the sums before the count, so no cache write-back or invalidation
+// is needed. The adding loop issues every slice's loads of GR groups before
+// it adds them (the loads' latency, not bandwidth, bounds it). `flag` is one
+// word of free LDS.
+template <int ROWS, int THREADS, int GR>
+__device__ __forceinline__ void finish_split(const ProdParams& p, int rb, int m0, uint32_t* flag) {
+  wait_vm<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(p.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            uint32_t(p.ks - 1);
+  __syncthreads();
+  if (*flag) {
+    const int R = p.R, ks = p.ks;
+    const int ng = (ROWS / 4) * R;   // groups of four rows of one rank, per slice
+    const uint64_t* base = reinterpret_cast<const uint64_t*>(p.part + uint32_t(rb) * uint32_t(ks) * uint32_t(ROWS * R));
+    for (int g0 = threadIdx.x; g0 < ng; g0 += GR * THREADS) {
+      uint64_t v[GR][kProdMaxSlices][2];
+#pragma unroll
+      for (int u = 0; u < GR; ++u) {
+        const int gi = g0 + u * THREADS;
+#pragma unroll
+        for (int q = 0; q < kProdMaxSlices; ++q)
+          if (q < ks && gi < ng) {
+            const uint64_t* src = base + 2 * (uint32_t(q) * uint32_t(ng) + uint32_t(gi));
+            v[u][q][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v[u][q][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < GR; ++u) {
+        const int gi = g0 + u * THREADS;
+        if (gi >= ng) continue;
+        float sm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < kProdMaxSlices; ++q)
+          if (q < ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm[e] += __builtin_bit_cast(float, uint32_t(v[u][q][e >> 1] >> (32 * (e & 1))));
+        const int rank = gi / (ROWS / 4), row = m0 + 4 * (gi % (ROWS / 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (row + e < p.M) {
+            const __bf16 b = __bf16(sm[e]);   // round to nearest even
+            p.lora_act_in[uint32_t(row + e) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, b);
+          }
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -263,39 +349,48 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   // DMAs included. The explicit waits count loads only, and scheduling fences
   // keep every use after its wait.
   constexpr int LT = C::RTILES > 0 ? C::RTILES : 1;
-  u32x4 lb[C::NSETS][LT][4];
+  constexpr int LTS = C::RTILES > 0 ? C::PH : 1;   // rank tiles per register set
+  u32x4 lb[C::NSETS][LTS][4];
   uint32_t loff[LT];
 #pragma unroll
   for (int jt = 0; jt < LT; ++jt)
     loff[jt] = uint32_t(min(16 * jt + r, max(R, 1) - 1)) * row_bytes + uint32_t(64 * g);
   const uint8_t* ldb = reinterpret_cast<const uint8_t*>(p.lora_down);
   const uint32_t ld_bytes = uint32_t(R) * row_bytes;
-  // j >= n: a dummy on an empty descriptor (reads nothing; the set is not used)
-  auto load_lora = [&](u32x4 (&dst)[LT][4], int j) __attribute__((always_inline)) {
+  // rank tiles [h PH, (h+1) PH) of span j; j >= n: a dummy on an empty
+  // descriptor (reads nothing; the set is not used)
+  auto load_lora = [&](u32x4 (&dst)[LTS][4], int j, int h) __attribute__((always_inline)) {
     if constexpr (C::RTILES > 0) {
       const bool valid = j < n;
       const uint32_t sb = valid ? uint32_t(first + C::WAVES * j) * uint32_t(C::SPAN_K * 2) : 0u;
       const u32x4 desc = buffer_desc(ldb + sb, valid ? ld_bytes - sb : 0u);
 #pragma unroll
-      for (int jt = 0; jt < C::RTILES; ++jt) {
-        load_untracked<0>(dst[jt][0], loff[jt], desc);
-        load_untracked<16>(dst[jt][1], loff[jt], desc);
-        load_untracked<32>(dst[jt][2], loff[jt], desc);
-        load_untracked<48>(dst[jt][3], loff[jt], desc);
+      for (int jt = 0; jt < LTS; ++jt) {
+        const uint32_t off = loff[h * LTS + jt];
+        load_untracked<0>(dst[jt][0], off, desc);
+        load_untracked<16>(dst[jt][1], off, desc);
+        load_untracked<32>(dst[jt][2], off, desc);
+        load_untracked<48>(dst[jt][3], off, desc);
       }
     }
   };
   // the pair of span t: L(t+1), DMA(t+DEPTH)
   auto issue_pair = [&]<int NEXT_SET>(int t) __attribute__((always_inline)) {
-    load_lora(lb[NEXT_SET], t + 1);
+    load_lora(lb[NEXT_SET], t + 1, 0);
     dma_span(t + C::DEPTH);
   };
 
-  // prologue: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1)
+  // prologue: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); SPLIT: DMA(0 .. DEPTH-1), L(0, 0)
+  if constexpr (C::SPLIT) {
 #pragma unroll
-  for (int t = 0; t < C::DEPTH - 1; ++t) dma_span(t);
-  load_lora(lb[0], 0);
-  dma_span(C::DEPTH - 1);
+    for (int t = 0; t < C::DEPTH; ++t) dma_span(t);
+    load_lora(lb[0], 0, 0);
+  } else {
+#pragma unroll
+    for (int t = 0; t < C::DEPTH - 1; ++t) dma_span(t);
+    load_lora(lb[0], 0, 0);
+    dma_span(C::DEPTH - 1);
+  }
   wait_vm_lgkm0<C::VM_X0>();   // DMA(0): its count differs from the loop's
 
   // output addresses: act row m0 + r from k0 / 2; ascales row (block) lane
@@ -373,6 +468,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       __builtin_amdgcn_sched_barrier(0);
       issue_pair.template operator()<NEXT>(j);                // L(j+1), DMA(j+DEPTH)
       __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (C::SPLIT) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7" ::: "memory");                   // set 1's last MFMAs (span j-1) are behind
+      load_lora(lb[1], j, 1);                                 // L(j, 1)
+      dma_span(j + C::DEPTH);                                 // DMA(j+DEPTH)
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (tail) {
       // this lane's blocks past K: zero (they add nothing to the LoRA sums
@@ -396,31 +497,41 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 #pragma unroll
     for (int b = 0; b < 2; ++b) sc_stage[(2 * g + b) * C::ROWS + r] = uint8_t(sb[b]);
 
-    if constexpr (C::RTILES > 0) {
+    // the MFMAs of register set Q, rank tiles from T0, once its loads landed
+    auto lora_mfma = [&]<int Q, int T0>() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<C::VM_L>();                                     // L(j)
+      wait_vm<C::VM_L>();                                     // L(j) (SPLIT: L(j, Q))
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");                          // nothing reads lb[SET] before this point
+      asm volatile("" ::: "memory");                          // nothing reads lb[Q] before this point
       if (tail) {
         // k past K: a zero operand (a NaN weight there must not reach valid sums)
         const int k0 = span * C::SPAN_K + 32 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int jt = 0; jt < C::RTILES; ++jt)
-            if (k0 + 8 * i >= K) lb[SET][jt][i] = u32x4{0u, 0u, 0u, 0u};
+          for (int jt = 0; jt < LTS; ++jt)
+            if (k0 + 8 * i >= K) lb[Q][jt][i] = u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32x4 a = {xd[4 * i], xd[4 * i + 1], xd[4 * i + 2], xd[4 * i + 3]};
 #pragma unroll
-        for (int jt = 0; jt < C::RTILES; ++jt)
-          acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                            __builtin_bit_cast(bf16x8, lb[SET][jt][i]),
-                                                            acc[jt], 0, 0, 0);
+        for (int jt = 0; jt < LTS; ++jt)
+          acc[T0 + jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                 __builtin_bit_cast(bf16x8, lb[Q][jt][i]),
+                                                                 acc[T0 + jt], 0, 0, 0);
       }
+    };
+    if constexpr (C::SPLIT) {
+      lora_mfma.template operator()<0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");     // the loads below overwrite set 0's operands
+      load_lora(lb[0], j + 1, 0);                             // L(j+1, 0)
+      lora_mfma.template operator()<1, C::PH>();
+    } else if constexpr (C::RTILES > 0) {
+      lora_mfma.template operator()<SET, 0>();
     }
-    if constexpr (!C::EARLY) {
+    if constexpr (!C::EARLY && !C::SPLIT) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (C::RTILES > 0) {
         // the loads below overwrite the operands of the MFMAs just issued
@@ -434,9 +545,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
     wait_vm_lgkm0<63>();                                      // staging read done before the next span's writes
   };
   int j0 = 0;
-  for (; j0 + C::NSETS <= n; j0 += C::NSETS)
-    static_for<0, C::NSETS>([&]<int S>() __attribute__((always_inline)) { one_span.template operator()<S>(j0 + S); });
-  static_for<0, C::NSETS - 1>([&]<int S>() __attribute__((always_inline)) {
+  for (; j0 + C::UNROLL <= n; j0 += C::UNROLL)
+    static_for<0, C::UNROLL>([&]<int S>() __attribute__((always_inline)) { one_span.template operator()<S>(j0 + S); });
+  static_for<0, C::UNROLL - 1>([&]<int S>() __attribute__((always_inline)) {
     if (j0 + S < n) one_span.template operator()<S>(j0 + S);
   });
   if (n > 0) store_span(first + C::WAVES * (n - 1));          // S(last)
@@ -449,7 +560,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 #pragma unroll
     for (int q = 0; q < C::NSETS; ++q)
 #pragma unroll
-      for (int jt = 0; jt < LT; ++jt)
+      for (int jt = 0; jt < LTS; ++jt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(lb[q][jt][i]));
   }
@@ -471,49 +582,284 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
         s += *reinterpret_cast<const f32x4_t*>(smem + ((w * C::RTILES + jt) * kWave + lane) * 16);
       const int rank = 16 * jt + (lane & 15);
       if (rank < R) {
+        if (split) {
+          store_partial4(p.part + (uint32_t(blockIdx.x) * uint32_t(R) + uint32_t(rank)) * uint32_t(C::ROWS) +
+                             uint32_t(4 * g), s);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = m0 + 4 * g + e;
-          if (split) {
-            __hip_atomic_store(p.part + (uint32_t(blockIdx.x) * 16u + uint32_t(4 * g + e)) * uint32_t(R) + uint32_t(rank),
-                               s[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else if (row < M) {
-            const __bf16 v = __bf16(s[e]);   // round to nearest even
-            p.lora_act_in[uint32_t(row) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, v);
+          for (int e = 0; e < 4; ++e) {
+            const int row = m0 + 4 * g + e;
+            if (row < M) {
+              const __bf16 v = __bf16(s[e]);   // round to nearest even
+              p.lora_act_in[uint32_t(row) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, v);
+            }
           }
         }
       }
     }
-    if (split) {
-      // The last workgroup of the row block to finish adds the slices. The
-      // partial sums and the counter are device-scope atomic accesses, each
-      // coherent across the compute dies by itself; every wave waits until
-      // its stores are acknowledged before the barrier, which orders the
-      // sums before the count, so no cache write-back or invalidation is
-      // needed.
-      uint32_t* last = reinterpret_cast<uint32_t*>(smem + C::SC_OFF);   // the staging area is free
-      wait_vm<0>();
-      __syncthreads();
-      if (tid == 0)
-        *last = __hip_atomic_fetch_add(p.count + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                uint32_t(p.ks - 1);
-      __syncthreads();
-      if (*last) {
-        const int nel = 16 * R;
-        const float* base = p.part + uint32_t(rb) * uint32_t(p.ks) * uint32_t(nel);
-        for (int e = tid; e < nel; e += C::THREADS) {
-          float s = 0.f;
-          for (int q = 0; q < p.ks; ++q)
-            s += __hip_atomic_load(base + q * nel + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (m0 + e / R < M) {
-            const __bf16 v = __bf16(s);
-            p.lora_act_in[uint32_t(m0) * uint32_t(R) + uint32_t(e)] = __builtin_bit_cast(uint16_t, v);
-          }
-        }
-        if (tid == 0) __hip_atomic_store(p.count + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    // at most 4R groups, one per thread
+    if (split) finish_split<C::ROWS, C::THREADS, 1>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
   }
+}
+
+// ------------------------------------------------------------------ wide variant
+//
+// The largest ranks (32 < R <= 128). Read per 16 rows, a span's lora_down
+// tile (R x 128 values) outweighs its x by R/16 and its loads touch two
+// cache lines per 32 bytes used; here one workgroup of 4 waves takes 128
+// rows (32 per wave, two 16-row MFMA tiles sharing each operand) and every
+// wave the same span: the span's lora_down tile is brought into LDS once per
+// workgroup by direct-to-LDS DMA of whole rows (each wave a quarter of its
+// rank rows), and each wave reads its B operands from there. x moves through
+// a private ring per wave as in the narrow kernel; K is split over
+// workgroups when the row blocks alone do not fill the chip.
+template <int RTILES_>
+struct WideCfg {
+  static constexpr int WAVES = 4, RTILES = RTILES_;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int ROWS_W = 32, ROWS = WAVES * ROWS_W;    // rows per wave, per workgroup
+  static constexpr int SPAN_K = 128, ROW_SPAN = SPAN_K * 2;  // bytes of one row in a span
+  static constexpr int X_SLOT = ROWS_W * ROW_SPAN;           // one span of a wave's rows (8 KiB)
+  static constexpr int X_RING = 2 * X_SLOT;                  // per wave
+  static constexpr int L_ROWS = 16 * RTILES;                 // rank rows of a lora_down tile
+  static constexpr int L_SLOT = L_ROWS * ROW_SPAN;           // one span's tile
+  static constexpr int L_OFF = WAVES * X_RING;
+  static constexpr int SC_OFF = L_OFF + 2 * L_SLOT;
+  static constexpr int SC_BYTES = 2 * 8 * 16;                // staged scales of a span, per wave
+  static constexpr int LDS = SC_OFF + WAVES * SC_BYTES;
+  static constexpr int DX = X_SLOT / (kWave * 16);           // x DMA rounds per wave and span
+  static constexpr int DL = L_SLOT / WAVES / (kWave * 16);   // lora_down DMA rounds per wave and span
+  // Issue order: X(0), L(0), X(1); then per span j, after its barrier,
+  // L(j+1) and, once the wave has read its x slot, X(j+2). At the start of
+  // span j, L(j) (this wave's part) is followed by X(j+1) only, and X(j) is
+  // older than L(j): waiting until DX ops remain completes both.
+  static constexpr int VM_J = DX;
+  static_assert(DX <= 63 && RTILES % 1 == 0, "wait counts");
+  static_assert(LDS <= kLdsLimit, "LDS budget");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void producer_wide_kernel(const ProdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int r = lane & 15, g = lane >> 4;
+  const int M = p.M, K = p.K, R = p.R;
+  const int rb = blockIdx.x / p.ks, z = blockIdx.x - rb * p.ks;
+  const int m0 = rb * C::ROWS;
+  const int mw = m0 + wave_u * C::ROWS_W;                                // this wave's first row
+  const int nsp = (K + C::SPAN_K - 1) / C::SPAN_K;
+  const int s_beg = z * p.sps;
+  const int n = max(0, min(nsp, s_beg + p.sps) - s_beg);               // spans of the slice
+  const int tail_span = (K % C::SPAN_K) != 0 ? nsp - 1 : -1;
+  const uint32_t row_bytes = uint32_t(K) * 2u;
+  const uint32_t x_bytes = uint32_t(M) * row_bytes, ld_bytes = uint32_t(R) * row_bytes;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x);
+  const uint8_t* ldb = reinterpret_cast<const uint8_t*>(p.lora_down);
+  uint8_t* xring = smem + wave_u * C::X_RING;
+  uint8_t* lring = smem + C::L_OFF;
+
+  // DMA round u: lane l writes slot position (row 4u + l/16, chunk l%16) of
+  // its region and reads data chunk (l%16) ^ (row % 16) of that row. x: this
+  // wave's rows (past M: row M-1, never stored); lora_down: rank rows 32w ..
+  // 32w+31 of the tile (past R: beyond the tensor, read as zeros).
+  uint32_t xoff[C::DX], loff[C::DL];
+#pragma unroll
+  for (int u = 0; u < C::DX; ++u) {
+    const int rl = 4 * u + g;
+    xoff[u] = uint32_t(min(mw + rl, M - 1)) * row_bytes + uint32_t((r ^ (rl & 15)) << 4);
+  }
+#pragma unroll
+  for (int u = 0; u < C::DL; ++u) {
+    const int rank = wave_u * (C::L_ROWS / C::WAVES) + 4 * u + g;
+    loff[u] = uint32_t(rank) * row_bytes + uint32_t((r ^ (rank & 15)) << 4);
+  }
+  // span j of the slice; j >= n: the same loads on an empty descriptor
+  auto dma_x = [&](int j) __attribute__((always_inline)) {
+    const bool valid = j < n;
+    const uint32_t sb = valid ? uint32_t(s_beg + j) * uint32_t(C::ROW_SPAN) : 0u;
+    const __amdgpu_buffer_rsrc_t desc = buffer_rsrc(xb + sb, valid ? x_bytes - sb : 0u);
+    uint8_t* slot = xring + (j & 1) * C::X_SLOT;
+#pragma unroll
+    for (int u = 0; u < C::DX; ++u) dma_buf(desc, xoff[u], slot + u * 1024);
+  };
+  auto dma_l = [&](int j) __attribute__((always_inline)) {
+    const bool valid = j < n;
+    const uint32_t sb = valid ? uint32_t(s_beg + j) * uint32_t(C::ROW_SPAN) : 0u;
+    const __amdgpu_buffer_rsrc_t desc = buffer_rsrc(ldb + sb, valid ? ld_bytes - sb : 0u);
+    uint8_t* slot = lring + (j & 1) * C::L_SLOT + wave_u * (C::L_SLOT / C::WAVES);
+#pragma unroll
+    for (int u = 0; u < C::DL; ++u) dma_buf(desc, loff[u], slot + u * 1024);
+  };
+
+  f32x4_t acc[2][C::RTILES];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int jt = 0; jt < C::RTILES; ++jt) acc[t][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  dma_x(0);
+  dma_l(0);
+  dma_x(1);
+
+  // outputs: act rows mw + 16t + r from k0 / 2; lanes 0..15 store scale row
+  // (block) lane % 8 of the span for row tile lane / 8, 16 consecutive m
+  const bool act16 = (K & 31) == 0 && (reinterpret_cast<uintptr_t>(p.act) & 15u) == 0;
+  const uintptr_t sc_align = reinterpret_cast<uintptr_t>(p.ascales) | uintptr_t(M);
+  const int sc_w = (sc_align & 15u) == 0 ? 16 : (sc_align & 7u) == 0 ? 8 : (sc_align & 3u) == 0 ? 4 : 1;
+  const int st_t = (lane >> 3) & 1;
+  const int st_row0 = mw + 16 * st_t;
+  const int st_nv = max(0, min(16, M - st_row0));
+  const uint32_t soff = uint32_t(lane & 7) * uint32_t(M) + uint32_t(min(st_row0, M - 1));
+  uint8_t* sc_stage = smem + C::SC_OFF + wave_u * C::SC_BYTES;
+  uint32_t code[2][4] = {};
+  u32x4 scv = {0u, 0u, 0u, 0u};
+  auto store_span = [&](int span) __attribute__((always_inline)) {
+    uint8_t* abase = p.act + uint32_t(span) * uint32_t(C::SPAN_K / 2);
+    uint8_t* sbase = p.ascales + uint32_t(span) * uint32_t(C::SPAN_K / 16) * uint32_t(M);
+    const bool tail = span == tail_span;
+    const int k0 = span * C::SPAN_K + 32 * g;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = mw + 16 * t + r;
+      if (row < M) {
+        uint8_t* dst = abase + uint32_t(row) * uint32_t(K / 2) + uint32_t(16 * g);
+        if (act16 && !tail) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{code[t][0], code[t][1], code[t][2], code[t][3]};
+        } else {
+          if (k0 < K) *reinterpret_cast<u32x2*>(dst) = u32x2{code[t][0], code[t][1]};
+          if (k0 + 16 < K) *reinterpret_cast<u32x2*>(dst + 8) = u32x2{code[t][2], code[t][3]};
+        }
+      }
+    }
+    if (lane < 16 && st_nv > 0 && span * (C::SPAN_K / 16) + (lane & 7) < K / 16) {
+      if (sc_w == 16 && st_nv == 16) {
+        *reinterpret_cast<u32x4*>(sbase + soff) = scv;
+      } else if (sc_w == 8 && st_nv == 16) {
+        *reinterpret_cast<u32x2*>(sbase + soff) = u32x2{scv.x, scv.y};
+        *reinterpret_cast<u32x2*>(sbase + soff + 8) = u32x2{scv.z, scv.w};
+      } else if (sc_w == 4 && st_nv == 16) {
+        uint32_t* d = reinterpret_cast<uint32_t*>(sbase + soff);
+        d[0] = scv.x;
+        d[1] = scv.y;
+        d[2] = scv.z;
+        d[3] = scv.w;
+      } else {
+        const uint64_t lo = uint64_t(scv.x) | (uint64_t(scv.y) << 32), hi = uint64_t(scv.z) | (uint64_t(scv.w) << 32);
+#pragma unroll 1
+        for (int e = 0; e < st_nv; ++e) sbase[soff + e] = uint8_t((e < 8 ? lo : hi) >> (8 * (e & 7)));
+      }
+    }
+  };
+
+  for (int j = 0; j < n; ++j) {
+    const int span = s_beg + j;
+    const bool tail = span == tail_span;
+    wait_vm_lgkm0<C::VM_J>();                                 // X(j), this wave's part of L(j)
+    __builtin_amdgcn_sched_barrier(0);
+    if (j > 0) store_span(span - 1);                          // S(j-1)
+    __builtin_amdgcn_sched_barrier(0);
+    wg_barrier();                                             // all of L(j) landed; every wave past span j-1
+    __builtin_amdgcn_sched_barrier(0);
+    dma_l(j + 1);                                             // L(j+1) into span j-1's slot
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* xs = xring + (j & 1) * C::X_SLOT;
+    uint32_t xd[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xs + (16 * t + r) * C::ROW_SPAN + (((4 * g + i) ^ r) << 4));
+        xd[t][4 * i] = v.x;
+        xd[t][4 * i + 1] = v.y;
+        xd[t][4 * i + 2] = v.z;
+        xd[t][4 * i + 3] = v.w;
+      }
+    wait_vm_lgkm0<63>();                                      // the x slot is read
+    __builtin_amdgcn_sched_barrier(0);
+    dma_x(j + 2);                                             // X(j+2) into it
+    __builtin_amdgcn_sched_barrier(0);
+    const int k0 = span * C::SPAN_K + 32 * g;
+    if (tail) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (k0 + 16 * (i >> 3) >= K) xd[t][i] = 0u;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint32_t d[8], sbv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = xd[t][8 * b + i];
+        quantize_block(d, sbv, code[t][2 * b], code[t][2 * b + 1]);
+        sc_stage[(8 * t + 2 * g + b) * 16 + r] = uint8_t(sbv);
+      }
+    // LoRA-down: B operands of rank tile jt, k-step i from the shared tile,
+    // those of k-step i+1 read while k-step i's MFMAs run
+    const uint8_t* ls = lring + (j & 1) * C::L_SLOT + r * C::ROW_SPAN;
+    auto read_b = [&](int i, u32x4 (&b)[C::RTILES]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jt = 0; jt < C::RTILES; ++jt)
+        b[jt] = *reinterpret_cast<const u32x4*>(ls + 16 * jt * C::ROW_SPAN + (((4 * g + i) ^ r) << 4));
+    };
+    auto lora_mfma = [&]<bool TAIL>() __attribute__((always_inline)) {
+      u32x4 bb[2][C::RTILES];
+      read_b(0, bb[0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i + 1 < 4) read_b(i + 1, bb[(i + 1) & 1]);
+        const u32x4 a0 = {xd[0][4 * i], xd[0][4 * i + 1], xd[0][4 * i + 2], xd[0][4 * i + 3]};
+        const u32x4 a1 = {xd[1][4 * i], xd[1][4 * i + 1], xd[1][4 * i + 2], xd[1][4 * i + 3]};
+#pragma unroll
+        for (int jt = 0; jt < C::RTILES; ++jt) {
+          u32x4 b = bb[i & 1][jt];
+          // k past K: a zero operand (a NaN weight there must not reach valid sums)
+          if constexpr (TAIL) b = k0 + 8 * i < K ? b : u32x4{0u, 0u, 0u, 0u};
+          acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                               __builtin_bit_cast(bf16x8, b), acc[0][jt], 0, 0, 0);
+          acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                               __builtin_bit_cast(bf16x8, b), acc[1][jt], 0, 0, 0);
+        }
+      }
+    };
+    if (tail) lora_mfma.template operator()<true>();
+    else lora_mfma.template operator()<false>();
+    wait_vm_lgkm0<63>();
+    if (lane < 16) scv = *reinterpret_cast<const u32x4*>(sc_stage + lane * 16);
+    wait_vm_lgkm0<63>();                                      // staging read done before the next span's writes
+  }
+  if (n > 0) store_span(s_beg + n - 1);                       // S(last)
+
+  // lane (col, g) of tile (t, jt) holds rows 16t + 4g .. +3 of this wave's
+  // rows, rank 16 jt + col (stored before the drain: the two overlap)
+  const bool split = p.ks > 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int jt = 0; jt < C::RTILES; ++jt) {
+      const int rank = 16 * jt + (lane & 15);
+      const int rl = wave * C::ROWS_W + 16 * t + 4 * g;   // first of the lane's four rows in the block
+      if (rank < R) {
+        if (split) {
+          store_partial4(p.part + (uint32_t(blockIdx.x) * uint32_t(R) + uint32_t(rank)) * uint32_t(C::ROWS) +
+                             uint32_t(rl), acc[t][jt]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m0 + rl + e < M) {
+              const __bf16 v = __bf16(acc[t][jt][e]);   // round to nearest even
+              p.lora_act_in[uint32_t(m0 + rl + e) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, v);
+            }
+        }
+      }
+    }
+  wait_vm_lgkm0<0>();                                         // drain the loads past the last span
+  if (split) finish_split<C::ROWS, C::THREADS, 4>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
 }
 
 // ------------------------------------------------------------------ host side
@@ -521,21 +867,44 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 struct ProdVariant {
   const void* kernel;
   int rtiles, threads, lds;
+  int rows;    // rows per workgroup
+  bool wide;   // every wave on the same span (producer_wide_kernel)
 };
 
-template <int WAVES, int RTILES, int DEPTH>
+template <int WAVES, int RTILES, int DEPTH, int HALVES = 1>
 ProdVariant prod_variant() {
-  using C = ProdCfg<WAVES, RTILES, DEPTH>;
-  return ProdVariant{reinterpret_cast<const void*>(producer_kernel<C>), RTILES, C::THREADS, C::LDS};
+  using C = ProdCfg<WAVES, RTILES, DEPTH, HALVES>;
+  return ProdVariant{reinterpret_cast<const void*>(producer_kernel<C>), RTILES, C::THREADS, C::LDS, C::ROWS, false};
 }
 
-// By rank: R == 0, R <= 16, R <= 32 with 8 waves (two per SIMD) and two
-// ring slots each; R <= 128 with 4 waves (its operand set and partial sums
-// need the register file of one wave per SIMD) and three slots.
-static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(), prod_variant<8, 1, 2>(),
-                                            prod_variant<8, 2, 2>(), prod_variant<4, 8, 3>()};
+template <int RTILES>
+ProdVariant prod_wide_variant() {
+  using C = WideCfg<RTILES>;
+  return ProdVariant{reinterpret_cast<const void*>(producer_wide_kernel<C>), RTILES, C::THREADS, C::LDS, C::ROWS,
+                     true};
+}
 
-static int prod_variant_index(int R) { return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : 3; }
+// By rank: R == 0, R <= 16, R <= 32, R <= 128 with 8 waves (two per SIMD)
+// and two ring slots each (at R <= 128 a span's operands come in two halves,
+// SPLIT); and the wide kernel for R <= 128 (128 rows per workgroup, the
+// lora_down tile shared through LDS).
+//
+// Above R = 32 the wide kernel reads lora_down once per 128 rows instead of
+// once per 16, but its single wave per SIMD hides less latency and its split
+// reduction covers 8x the rows: it was measured faster from about 2^24
+// elements of x up (8192x3072 R=128: 44 against 55 us; 4096x12288: 62
+// against 94) and slower below (4096x3072: 36 against 28; 1000x12288: 55
+// against 49). At R <= 32 the narrow kernels were faster at every size
+// measured (up to 8192x12288).
+static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(), prod_variant<8, 1, 2>(),
+                                            prod_variant<8, 2, 2>(), prod_variant<8, 8, 2, 2>(),
+                                            prod_wide_variant<8>()};
+
+constexpr size_t kProdWideElems = size_t(1) << 24;
+
+static int prod_variant_index(int M, int K, int R) {
+  return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : size_t(M) * size_t(K) >= kProdWideElems ? 4 : 3;
+}
 
 // Workgroups of a variant resident on one compute unit, from the compiled
 // kernel's registers and its LDS (looked up once per variant).
@@ -574,34 +943,50 @@ static int compute_units() {
 
 // Scratch of the split-K reduction: a fixed region of arrival counters (one
 // per row block; the same bytes in every call, so they stay zero between
-// calls), then the partial sums.
+// calls), then the partial sums, at most kProdMaxPartBytes (K is split fewer
+// ways where more would be needed; both entry points plan alike).
 constexpr int kProdMaxCounters = 1024;
 constexpr size_t kProdCountBytes = kProdMaxCounters * 4;
+constexpr size_t kProdMaxPartBytes = size_t(QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES) - kProdCountBytes;
+static_assert(QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES > int(kProdCountBytes), "counters fit the fixed scratch");
 
 struct ProdLaunch {
   int ks, sps;
   size_t part_bytes;   // partial sums after the counters; 0: no scratch
 };
 
-// K slices: one when the row blocks alone fill every compute unit, or when
-// the waves of a workgroup would have fewer than 4 spans each (the split's
-// reduction costs about two memory round trips, more than it saves there);
-// else enough to fill the workgroup slots, keeping 2 spans per wave (no
-// slice left empty).
+// K slices. Narrow kernel: one when the row blocks alone fill every compute
+// unit, or when the waves of a workgroup would have fewer than 4 spans each
+// (the split's reduction costs about two memory round trips, more than it
+// saves there); else enough to fill the workgroup slots, keeping 2 spans per
+// wave. Wide kernel (its waves share every span): enough to give every
+// compute unit a workgroup, keeping 4 spans per slice. Both: no slice left
+// empty, and partial sums within kProdMaxPartBytes.
 static ProdLaunch prod_plan(int vi, int M, int K, int R) {
-  const int rbs = (M + 15) / 16, nsp = (K + 127) / 128;
-  const int waves = kProdVariants[vi].threads / kWave;
+  const ProdVariant& v = kProdVariants[vi];
+  const int rbs = (M + v.rows - 1) / v.rows, nsp = (K + 127) / 128;
+  const int waves = v.threads / kWave;
   const int cus = compute_units();
   ProdLaunch pl{1, nsp, 0};
-  if (rbs < cus && rbs <= kProdMaxCounters && nsp >= 4 * waves) {
-    const int slots = cus * prod_occupancy(vi);
-    int ks = min(nsp / (2 * waves), (slots + rbs - 1) / rbs);
+  int ks = 1;
+  if (rbs < cus && rbs <= kProdMaxCounters) {
+    if (v.wide) {
+      ks = min(max(1, nsp / 4), (cus + rbs - 1) / rbs);
+    } else if (nsp >= 4 * waves) {
+      const int slots = cus * prod_occupancy(vi);
+      ks = min(nsp / (2 * waves), (slots + rbs - 1) / rbs);
+    }
+    if (R > 0) {
+      const size_t per_slice = size_t(rbs) * size_t(v.rows) * size_t(R) * 4;
+      ks = int(min(size_t(min(ks, kProdMaxSlices)), max(size_t(1), kProdMaxPartBytes / per_slice)));
+    }
+  }
+  if (ks > 1) {
     const int sps = (nsp + ks - 1) / ks;
-    ks = (nsp + sps - 1) / sps;
-    pl.ks = ks;
+    pl.ks = (nsp + sps - 1) / sps;
     pl.sps = sps;
   }
-  if (pl.ks > 1 && R > 0) pl.part_bytes = size_t(rbs) * size_t(pl.ks) * 16 * size_t(R) * 4;
+  if (pl.ks > 1 && R > 0) pl.part_bytes = size_t(rbs) * size_t(pl.ks) * size_t(v.rows) * size_t(R) * 4;
   return pl;
 }
 
@@ -691,7 +1076,7 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
   }
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-  const int vi = prod_variant_index(R);
+  const int vi = prod_variant_index(M, K, R);
   const ProdVariant& v = kProdVariants[vi];
   const ProdLaunch pl = prod_plan(vi, M, K, R);
   void* buf = nullptr;
@@ -710,7 +1095,7 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
   ProdParams prm{x, lora_down, act, ascales, lora_act_in, M, K, R, pl.ks, pl.sps,
                  sb ? reinterpret_cast<float*>(sb + kProdCountBytes) : nullptr, reinterpret_cast<uint32_t*>(sb)};
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(v.kernel, dim3(((M + 15) / 16) * pl.ks), dim3(v.threads), args, 0,
+  const hipError_t e = hipLaunchKernel(v.kernel, dim3(((M + v.rows - 1) / v.rows) * pl.ks), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
 }

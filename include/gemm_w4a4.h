@@ -253,9 +253,10 @@ int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act
  * keeps float32 partial sums and one arrival counter per 16 rows in scratch
  * memory; quantize_w4a4_act allocates that buffer on first need, this entry
  * point uses a fixed device array of QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES
- * (4 KiB of counters + 4 MiB of partial sums) that each GPU holds until the
- * process ends. A call that would need more returns GEMM_W4A4_ESCRATCH with
- * nothing enqueued. The counters are zero at load and every completed call
+ * (4 KiB of counters + 16 MiB of partial sums) that each GPU holds until the
+ * process ends. Both entry points split K only as far as 16 MiB of partial
+ * sums allow; a call that would still need more returns GEMM_W4A4_ESCRATCH
+ * with nothing enqueued. The counters are zero at load and every completed call
  * returns them to zero.
  *
  * Every call on one GPU shares that GPU's array: calls that overlap on one
@@ -263,7 +264,7 @@ int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act
  * by the caller. Return codes as for quantize_w4a4_act, plus
  * GEMM_W4A4_ESCRATCH.
  */
-#define QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES (4096 + (4 << 20))
+#define QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES (4096 + (16 << 20))
 int quantize_w4a4_act_noalloc(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
                               uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
                               void* stream);

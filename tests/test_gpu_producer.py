@@ -60,9 +60,12 @@ def test_producer_workloads(name):
 
 # rows not a multiple of 16, K % 128 != 0 and K % 32 == 16 (8-byte act
 # stores), every compiled instance (8 or 16 waves per 16 rows; R = 0, <= 16,
-# <= 32, <= 128) with R not a multiple of 16
+# <= 32, <= 128) with R not a multiple of 16; the wide kernel (R > 32 and
+# M*K >= 2^24) with K split (4100 rows: 33 row blocks, the last of 4 rows)
+# and unsplit (257 row blocks, the last of 32 rows)
 EDGE = [(1, 16, 0), (17, 48, 1), (33, 144, 17), (100, 528, 32), (130, 1040, 100), (31, 2064, 128),
-        (256, 128, 16), (47, 4096, 64), (64, 272, 0), (2, 16, 128), (3072, 272, 0), (3100, 400, 8)]
+        (256, 128, 16), (47, 4096, 64), (64, 272, 0), (2, 16, 128), (3072, 272, 0), (3100, 400, 8),
+        (4100, 4112, 100), (32800, 528, 64)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
@@ -193,8 +196,8 @@ def test_split_calls_of_different_sizes():
     spans), with different numbers of row blocks and ranks: the arrival
     counters live in the same scratch bytes in every call and must be back at
     zero after each."""
-    for shape in [(1000, 8192, 16), (3100, 4096, 8), (33, 4160, 17), (3100, 4096, 8), (200, 2048, 128),
-                  (1000, 8192, 16)]:
+    for shape in [(1000, 8192, 16), (3100, 4096, 8), (33, 4160, 17), (4160, 4096, 128), (3100, 4096, 8),
+                  (200, 2048, 128), (4100, 4112, 100), (1000, 8192, 16)]:
         M, K, R = shape
         _say(f"case: producer split sequence M={M} K={K} R={R}")
         d = synthetic.producer_inputs(M, K, R, seed=M * 7 + K + R)
