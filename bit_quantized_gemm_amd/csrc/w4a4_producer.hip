@@ -51,11 +51,10 @@ namespace w4a4 {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // WAVES waves per workgroup, RTILES rank tiles of 16 (R <= 16 * RTILES),
-// DEPTH ring slots per wave, HALVES register sets a span's lora_down
-// operands are split over (1, or 2 for the largest ranks).
-template <int WAVES_, int RTILES_, int DEPTH_, int HALVES_ = 1>
+// DEPTH ring slots per wave.
+template <int WAVES_, int RTILES_, int DEPTH_>
 struct ProdCfg {
-  static constexpr int WAVES = WAVES_, RTILES = RTILES_, DEPTH = DEPTH_, HALVES = HALVES_;
+  static constexpr int WAVES = WAVES_, RTILES = RTILES_, DEPTH = DEPTH_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int ROWS = 16;
   static constexpr int SPAN_K = 128;
@@ -69,19 +68,12 @@ struct ProdCfg {
   static constexpr int NL = 4 * RTILES;                           // lora_down loads per span
   // lora_down operands of a span, L(j), go to register set j % NSETS. With
   // two sets (R <= 32) L(j+1) is issued early in span j, beside the refill
-  // DMA(j + DEPTH); with one set both are issued at the end of span j, after
-  // its MFMAs. SPLIT (HALVES == 2, the largest ranks, whose whole operand
-  // set is 128 registers): set h holds rank tiles [h RTILES/2, (h+1)
-  // RTILES/2) of a span, L(j, h); span j issues L(j, 1) early, beside the
-  // refill DMA, and L(j+1, 0) once its MFMAs on set 0 are issued, so that
-  // two waves of 128 operand registers each fit one SIMD.
-  static constexpr bool SPLIT = HALVES == 2;
-  static constexpr int NSETS = SPLIT ? 2 : RTILES >= 1 && RTILES <= 2 ? 2 : 1;
-  static constexpr bool EARLY = !SPLIT && NSETS == 2;
-  static constexpr int UNROLL = SPLIT ? 1 : NSETS;   // set indices constant in the unrolled loop
-  static constexpr int PH = RTILES / HALVES;          // rank tiles per set
-  static constexpr int NLH = 4 * PH;                  // loads per set
-  // Issue order (not SPLIT): DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); then per
+  // DMA(j + DEPTH); with one set (no LoRA) the refill is issued at the end
+  // of span j.
+  static constexpr int NSETS = RTILES >= 1 && RTILES <= 2 ? 2 : 1;
+  static constexpr bool EARLY = NSETS == 2;
+  static constexpr int UNROLL = NSETS;   // set indices constant in the unrolled loop
+  // Issue order: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); then per
   // span j the stores S(j-1) of the previous span's results and the pair
   // L(j+1), DMA(j+DEPTH). A pair past the wave's last span is issued as the
   // same loads on an empty descriptor (they read nothing), so that every
@@ -93,14 +85,10 @@ struct ProdCfg {
   //   L(j):   EARLY: DMA(j-1+DEPTH) and span j's pair; else DMA(j-1+DEPTH).
   // (Counts above the counter's 63 are capped: a stricter wait.)
   static constexpr int cap(int v) { return v < 63 ? v : 63; }
-  // SPLIT: DMA(0 .. DEPTH-1), L(0, 0); then per span j: S(j-1), L(j, 1),
-  // DMA(j+DEPTH), and after the first MFMAs L(j+1, 0). DMA(j) is then
-  // followed by L(j-DEPTH+1, 0) and DEPTH-1 whole spans; L(j, 0) and L(j, 1)
-  // each by one half-set and one DMA.
-  static constexpr int VM_X = cap(SPLIT ? NLH + (DEPTH - 1) * (2 * NLH + D) : (DEPTH - 1) * (D + NL));
-  static constexpr int VM_X0 = cap((DEPTH - 1) * D + (SPLIT ? NLH : NL));
-  static constexpr int VM_L = cap(SPLIT ? NLH + D : EARLY ? 2 * D + NL : D);
-  static_assert(!SPLIT || RTILES % 2 == 0, "two halves of rank tiles");
+  static constexpr int VM_X = cap((DEPTH - 1) * (D + NL));
+  static constexpr int VM_X0 = cap((DEPTH - 1) * D + NL);
+  static constexpr int VM_L = cap(EARLY ? 2 * D + NL : D);
+  static_assert(RTILES <= 2, "R <= 32: larger ranks run the wide kernel");
   static_assert(DEPTH >= 2, "ring depth");
   static_assert(RED_BYTES <= WAVES * RING, "partial sums fit in the drained rings");
   static_assert(LDS <= kLdsLimit, "LDS budget");
@@ -221,9 +209,11 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff
 }
 
 // Split-K partial sums: float32, [row block][slice][rank][ROWS rows], so
-// that the four rows an MFMA lane holds for one rank are one 16-byte piece,
-// stored and loaded as two 8-byte device-scope atomic accesses.
-constexpr int kProdMaxSlices = 8;
+// that the four rows an MFMA lane holds for one rank are one 16-byte piece
+// (in the narrow kernels stored and loaded as two 8-byte device-scope atomic
+// accesses).
+constexpr int kProdMaxSlices = 8;        // narrow kernels: one register per slice and group
+constexpr int kProdMaxWideSlices = 64;   // the wide kernel (a second launch adds them)
 
 // (The whole vector is reinterpreted: this compiler's bit-cast of a single
 // vector element reads the vector's first element.)
@@ -235,17 +225,18 @@ __device__ __forceinline__ void store_partial4(float* dst, const f32x4_t& v) {
   __hip_atomic_store(d + 1, uint64_t(w.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// K split over workgroups: the last workgroup of row block rb (rows m0 ..
-// m0+ROWS-1) to finish adds the slices' partial sums in slice order and
-// writes lora_act_in. The partial sums and the counter are device-scope
-// atomic accesses, each coherent across the compute dies by itself; every
-// wave waits until its stores are acknowledged before the barrier, which
-// orders the sums before the count, so no cache write-back or invalidation
-// is needed. The adding loop issues every slice's loads of GR groups before
-// it adds them (the loads' latency, not bandwidth, bounds it). `flag` is one
-// word of free LDS.
-template <int ROWS, int THREADS, int GR>
+// K split over the narrow kernels' workgroups: the last workgroup of row
+// block rb (rows m0 .. m0+ROWS-1) to finish adds the slices' partial sums in
+// slice order and writes lora_act_in (16 rows: at most 4R groups, one per
+// thread). The partial sums and the counter are device-scope atomic
+// accesses, each coherent across the compute dies by itself; every wave
+// waits until its stores are acknowledged before the barrier, which orders
+// the sums before the count, so no cache write-back or invalidation is
+// needed. Every slice's loads are issued before they are added. `flag` is
+// one word of free LDS.
+template <int ROWS, int THREADS>
 __device__ __forceinline__ void finish_split(const ProdParams& p, int rb, int m0, uint32_t* flag) {
+  constexpr int GR = 1;
   wait_vm<0>();
   __syncthreads();
   if (threadIdx.x == 0)
@@ -349,24 +340,23 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   // DMAs included. The explicit waits count loads only, and scheduling fences
   // keep every use after its wait.
   constexpr int LT = C::RTILES > 0 ? C::RTILES : 1;
-  constexpr int LTS = C::RTILES > 0 ? C::PH : 1;   // rank tiles per register set
-  u32x4 lb[C::NSETS][LTS][4];
+  u32x4 lb[C::NSETS][LT][4];
   uint32_t loff[LT];
 #pragma unroll
   for (int jt = 0; jt < LT; ++jt)
     loff[jt] = uint32_t(min(16 * jt + r, max(R, 1) - 1)) * row_bytes + uint32_t(64 * g);
   const uint8_t* ldb = reinterpret_cast<const uint8_t*>(p.lora_down);
   const uint32_t ld_bytes = uint32_t(R) * row_bytes;
-  // rank tiles [h PH, (h+1) PH) of span j; j >= n: a dummy on an empty
-  // descriptor (reads nothing; the set is not used)
-  auto load_lora = [&](u32x4 (&dst)[LTS][4], int j, int h) __attribute__((always_inline)) {
+  // span j; j >= n: a dummy on an empty descriptor (reads nothing; the set
+  // is not used)
+  auto load_lora = [&](u32x4 (&dst)[LT][4], int j) __attribute__((always_inline)) {
     if constexpr (C::RTILES > 0) {
       const bool valid = j < n;
       const uint32_t sb = valid ? uint32_t(first + C::WAVES * j) * uint32_t(C::SPAN_K * 2) : 0u;
       const u32x4 desc = buffer_desc(ldb + sb, valid ? ld_bytes - sb : 0u);
 #pragma unroll
-      for (int jt = 0; jt < LTS; ++jt) {
-        const uint32_t off = loff[h * LTS + jt];
+      for (int jt = 0; jt < LT; ++jt) {
+        const uint32_t off = loff[jt];
         load_untracked<0>(dst[jt][0], off, desc);
         load_untracked<16>(dst[jt][1], off, desc);
         load_untracked<32>(dst[jt][2], off, desc);
@@ -376,21 +366,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   };
   // the pair of span t: L(t+1), DMA(t+DEPTH)
   auto issue_pair = [&]<int NEXT_SET>(int t) __attribute__((always_inline)) {
-    load_lora(lb[NEXT_SET], t + 1, 0);
+    load_lora(lb[NEXT_SET], t + 1);
     dma_span(t + C::DEPTH);
   };
 
-  // prologue: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); SPLIT: DMA(0 .. DEPTH-1), L(0, 0)
-  if constexpr (C::SPLIT) {
+  // prologue: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1)
 #pragma unroll
-    for (int t = 0; t < C::DEPTH; ++t) dma_span(t);
-    load_lora(lb[0], 0, 0);
-  } else {
-#pragma unroll
-    for (int t = 0; t < C::DEPTH - 1; ++t) dma_span(t);
-    load_lora(lb[0], 0, 0);
-    dma_span(C::DEPTH - 1);
-  }
+  for (int t = 0; t < C::DEPTH - 1; ++t) dma_span(t);
+  load_lora(lb[0], 0);
+  dma_span(C::DEPTH - 1);
   wait_vm_lgkm0<C::VM_X0>();   // DMA(0): its count differs from the loop's
 
   // output addresses: act row m0 + r from k0 / 2; ascales row (block) lane
@@ -468,12 +452,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       __builtin_amdgcn_sched_barrier(0);
       issue_pair.template operator()<NEXT>(j);                // L(j+1), DMA(j+DEPTH)
       __builtin_amdgcn_sched_barrier(0);
-    } else if constexpr (C::SPLIT) {
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_nop 7" ::: "memory");                   // set 1's last MFMAs (span j-1) are behind
-      load_lora(lb[1], j, 1);                                 // L(j, 1)
-      dma_span(j + C::DEPTH);                                 // DMA(j+DEPTH)
-      __builtin_amdgcn_sched_barrier(0);
     }
     if (tail) {
       // this lane's blocks past K: zero (they add nothing to the LoRA sums
@@ -497,10 +475,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 #pragma unroll
     for (int b = 0; b < 2; ++b) sc_stage[(2 * g + b) * C::ROWS + r] = uint8_t(sb[b]);
 
-    // the MFMAs of register set Q, rank tiles from T0, once its loads landed
-    auto lora_mfma = [&]<int Q, int T0>() __attribute__((always_inline)) {
+    // the MFMAs of register set Q once its loads landed
+    auto lora_mfma = [&]<int Q>() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<C::VM_L>();                                     // L(j) (SPLIT: L(j, Q))
+      wait_vm<C::VM_L>();                                     // L(j)
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");                          // nothing reads lb[Q] before this point
       if (tail) {
@@ -509,29 +487,20 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int jt = 0; jt < LTS; ++jt)
+          for (int jt = 0; jt < LT; ++jt)
             if (k0 + 8 * i >= K) lb[Q][jt][i] = u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32x4 a = {xd[4 * i], xd[4 * i + 1], xd[4 * i + 2], xd[4 * i + 3]};
 #pragma unroll
-        for (int jt = 0; jt < LTS; ++jt)
-          acc[T0 + jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                 __builtin_bit_cast(bf16x8, lb[Q][jt][i]),
-                                                                 acc[T0 + jt], 0, 0, 0);
+        for (int jt = 0; jt < LT; ++jt)
+          acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                            __builtin_bit_cast(bf16x8, lb[Q][jt][i]), acc[jt], 0, 0, 0);
       }
     };
-    if constexpr (C::SPLIT) {
-      lora_mfma.template operator()<0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");     // the loads below overwrite set 0's operands
-      load_lora(lb[0], j + 1, 0);                             // L(j+1, 0)
-      lora_mfma.template operator()<1, C::PH>();
-    } else if constexpr (C::RTILES > 0) {
-      lora_mfma.template operator()<SET, 0>();
-    }
-    if constexpr (!C::EARLY && !C::SPLIT) {
+    if constexpr (C::RTILES > 0) lora_mfma.template operator()<SET>();
+    if constexpr (!C::EARLY) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (C::RTILES > 0) {
         // the loads below overwrite the operands of the MFMAs just issued
@@ -560,7 +529,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
 #pragma unroll
     for (int q = 0; q < C::NSETS; ++q)
 #pragma unroll
-      for (int jt = 0; jt < LTS; ++jt)
+      for (int jt = 0; jt < LT; ++jt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(lb[q][jt][i]));
   }
@@ -597,8 +566,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
         }
       }
     }
-    // at most 4R groups, one per thread
-    if (split) finish_split<C::ROWS, C::THREADS, 1>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
+    if (split) finish_split<C::ROWS, C::THREADS>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
   }
 }
 
@@ -836,7 +804,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_wide_kernel(const Prod
   if (n > 0) store_span(s_beg + n - 1);                       // S(last)
 
   // lane (col, g) of tile (t, jt) holds rows 16t + 4g .. +3 of this wave's
-  // rows, rank 16 jt + col (stored before the drain: the two overlap)
+  // rows, rank 16 jt + col (stored before the drain: the two overlap). A K
+  // slice stores plain partial sums, [slice workgroup][ROWS rows][R ranks];
+  // producer_reduce_kernel, launched after this kernel, adds them up.
   const bool split = p.ks > 1;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -846,8 +816,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_wide_kernel(const Prod
       const int rl = wave * C::ROWS_W + 16 * t + 4 * g;   // first of the lane's four rows in the block
       if (rank < R) {
         if (split) {
-          store_partial4(p.part + (uint32_t(blockIdx.x) * uint32_t(R) + uint32_t(rank)) * uint32_t(C::ROWS) +
-                             uint32_t(rl), acc[t][jt]);
+          float* dst = p.part + (uint32_t(blockIdx.x) * uint32_t(C::ROWS) + uint32_t(rl)) * uint32_t(R) + uint32_t(rank);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e * R] = acc[t][jt][e];
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -859,7 +830,45 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_wide_kernel(const Prod
       }
     }
   wait_vm_lgkm0<0>();                                         // drain the loads past the last span
-  if (split) finish_split<C::ROWS, C::THREADS, 4>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
+}
+
+// The wide kernel's split-K reduction: thread u adds VEC consecutive ranks
+// of one row over the K slices' partial sums ([row block][slice][ROWS
+// rows][R ranks], fp32) in slice order, then rounds them to bf16. Lanes
+// take consecutive rank groups, so loads and stores are coalesced; the slice
+// loop issues eight slices' loads before it adds them.
+constexpr int kReduceThreads = 256;
+
+template <int ROWS, int VEC>
+__global__ __launch_bounds__(kReduceThreads) void producer_reduce_kernel(const ProdParams p) {
+  const int R = p.R, ks = p.ks;
+  const int groups = R / VEC;   // VEC divides R
+  const uint32_t u = blockIdx.x * uint32_t(kReduceThreads) + threadIdx.x;
+  const uint32_t row_all = u / uint32_t(groups);   // row of the padded row blocks
+  const int rb = int(row_all / ROWS), row = int(row_all % ROWS);
+  const int r0 = int(u % uint32_t(groups)) * VEC;
+  const int m = rb * ROWS + row;
+  if (m >= p.M) return;
+  const uint32_t slice = uint32_t(ROWS) * uint32_t(R);
+  const float* src = p.part + uint32_t(rb) * uint32_t(ks) * slice + uint32_t(row) * uint32_t(R) + uint32_t(r0);
+  float s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+#pragma unroll 8
+  for (int q = 0; q < ks; ++q) {
+    const float* v = static_cast<const float*>(__builtin_assume_aligned(src + uint32_t(q) * slice, 4 * VEC));
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[e] += v[e];
+  }
+  uint16_t* dst = p.lora_act_in + uint32_t(m) * uint32_t(R) + uint32_t(r0);
+  uint16_t b[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) b[e] = __builtin_bit_cast(uint16_t, __bf16(s[e]));   // round to nearest even
+  if constexpr (VEC == 4) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{uint32_t(b[0]) | (uint32_t(b[1]) << 16), uint32_t(b[2]) | (uint32_t(b[3]) << 16)};
+  } else {
+    dst[0] = b[0];
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -871,9 +880,9 @@ struct ProdVariant {
   bool wide;   // every wave on the same span (producer_wide_kernel)
 };
 
-template <int WAVES, int RTILES, int DEPTH, int HALVES = 1>
+template <int WAVES, int RTILES, int DEPTH>
 ProdVariant prod_variant() {
-  using C = ProdCfg<WAVES, RTILES, DEPTH, HALVES>;
+  using C = ProdCfg<WAVES, RTILES, DEPTH>;
   return ProdVariant{reinterpret_cast<const void*>(producer_kernel<C>), RTILES, C::THREADS, C::LDS, C::ROWS, false};
 }
 
@@ -884,48 +893,19 @@ ProdVariant prod_wide_variant() {
                      true};
 }
 
-// By rank: R == 0, R <= 16, R <= 32, R <= 128 with 8 waves (two per SIMD)
-// and two ring slots each (at R <= 128 a span's operands come in two halves,
-// SPLIT); and the wide kernel for R <= 128 (128 rows per workgroup, the
-// lora_down tile shared through LDS).
-//
-// Above R = 32 the wide kernel reads lora_down once per 128 rows instead of
-// once per 16, but its single wave per SIMD hides less latency and its split
-// reduction covers 8x the rows: it was measured faster from about 2^24
-// elements of x up (8192x3072 R=128: 44 against 55 us; 4096x12288: 62
-// against 94) and slower below (4096x3072: 36 against 28; 1000x12288: 55
-// against 49). At R <= 32 the narrow kernels were faster at every size
-// measured (up to 8192x12288).
+// By rank: R == 0, R <= 16, R <= 32 with 8 waves of 16 rows (two per SIMD)
+// and two ring slots each; above R = 32 the wide kernel (128 rows per
+// workgroup, the lora_down tile shared through LDS, 8 rank tiles). A narrow
+// kernel for R <= 128 (its operands in two register halves per span) was
+// measured slower than the wide one at every shape tried, 256x3072 to
+// 8192x12288 at R = 64 and 128 (1000x3072 R=128: 26.2 against 14.4 us;
+// 4096x12288 R=128: 93.3 against 41.3), and is not built; at R <= 32 the
+// narrow kernels are faster (4096x3072 R=32: 12.4 against 24.4 us for the
+// wide kernel, whose 8 rank tiles would do 4x the MFMA work).
 static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(), prod_variant<8, 1, 2>(),
-                                            prod_variant<8, 2, 2>(), prod_variant<8, 8, 2, 2>(),
-                                            prod_wide_variant<8>()};
+                                            prod_variant<8, 2, 2>(), prod_wide_variant<8>()};
 
-constexpr size_t kProdWideElems = size_t(1) << 24;
-
-static int prod_variant_index(int M, int K, int R) {
-  return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : size_t(M) * size_t(K) >= kProdWideElems ? 4 : 3;
-}
-
-// Workgroups of a variant resident on one compute unit, from the compiled
-// kernel's registers and its LDS (looked up once per variant).
-static std::atomic<int> g_prod_occ[sizeof(kProdVariants) / sizeof(kProdVariants[0])];
-
-static int prod_occupancy(int vi) {
-  int occ = g_prod_occ[vi].load(std::memory_order_relaxed);
-  if (occ > 0) return occ;
-  const ProdVariant& v = kProdVariants[vi];
-  const KernelResources* kr = find_resources(v.kernel);
-  int per_simd = 1;
-  if (kr) {
-    const int regs = ((kr->vgpr + 7) & ~7) + ((kr->agpr + 7) & ~7);   // one file of 512, granules of 8
-    per_simd = regs > 0 ? 512 / regs : 1;
-  }
-  const int by_regs = max(1, per_simd / max(1, v.threads / kWave / 4));
-  const int by_lds = max(1, kLdsLimit / v.lds);
-  occ = min(by_regs, by_lds);
-  g_prod_occ[vi].store(occ, std::memory_order_relaxed);
-  return occ;
-}
+static int prod_variant_index(int R) { return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : 3; }
 
 static std::atomic<int> g_cus[64];
 
@@ -942,9 +922,10 @@ static int compute_units() {
 }
 
 // Scratch of the split-K reduction: a fixed region of arrival counters (one
-// per row block; the same bytes in every call, so they stay zero between
-// calls), then the partial sums, at most kProdMaxPartBytes (K is split fewer
-// ways where more would be needed; both entry points plan alike).
+// per row block of a narrow kernel; the same bytes in every call, so they
+// stay zero between calls), then the partial sums, at most kProdMaxPartBytes
+// (K is split fewer ways where more would be needed; both entry points plan
+// alike). The wide kernel's reduction is a second launch and uses no counter.
 constexpr int kProdMaxCounters = 1024;
 constexpr size_t kProdCountBytes = kProdMaxCounters * 4;
 constexpr size_t kProdMaxPartBytes = size_t(QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES) - kProdCountBytes;
@@ -955,13 +936,19 @@ struct ProdLaunch {
   size_t part_bytes;   // partial sums after the counters; 0: no scratch
 };
 
-// K slices. Narrow kernel: one when the row blocks alone fill every compute
-// unit, or when the waves of a workgroup would have fewer than 4 spans each
-// (the split's reduction costs about two memory round trips, more than it
-// saves there); else enough to fill the workgroup slots, keeping 2 spans per
-// wave. Wide kernel (its waves share every span): enough to give every
-// compute unit a workgroup, keeping 4 spans per slice. Both: no slice left
-// empty, and partial sums within kProdMaxPartBytes.
+// K slices, so that the workgroups of all row blocks spread over the compute
+// units in one round. Narrow kernel: one slice when the row blocks alone
+// fill every compute unit or its waves would have a single span each; else
+// up to one workgroup per compute unit, down to one span per wave (measured
+// against splitting only from 4 spans per wave, 2 kept, with the workgroup
+// slots of two per CU: 1000x3072 R=16 6.8 against 8.2 us, 2048x3072 R=32
+// 9.3 against 11.1, 3000x12288 R=32 32.4 against 37.3; filling both slots
+// per CU was slower from 1500 rows on). Wide kernel (its waves share every
+// span, and its LDS fills a compute unit): likewise, down to one span per
+// slice (256x3072 R=64 9.5 us against 16.3 at four spans per slice,
+// 1000x12288 R=128 19.9 against 38.7 with at most 8 slices);
+// producer_reduce_kernel then adds the slices. Both: no slice left empty,
+// and partial sums within kProdMaxPartBytes.
 static ProdLaunch prod_plan(int vi, int M, int K, int R) {
   const ProdVariant& v = kProdVariants[vi];
   const int rbs = (M + v.rows - 1) / v.rows, nsp = (K + 127) / 128;
@@ -971,14 +958,14 @@ static ProdLaunch prod_plan(int vi, int M, int K, int R) {
   int ks = 1;
   if (rbs < cus && rbs <= kProdMaxCounters) {
     if (v.wide) {
-      ks = min(max(1, nsp / 4), (cus + rbs - 1) / rbs);
-    } else if (nsp >= 4 * waves) {
-      const int slots = cus * prod_occupancy(vi);
-      ks = min(nsp / (2 * waves), (slots + rbs - 1) / rbs);
+      ks = min(nsp, max(1, cus / rbs));
+    } else if (nsp >= 2 * waves) {
+      ks = min(nsp / waves, max(1, cus / rbs));
     }
     if (R > 0) {
       const size_t per_slice = size_t(rbs) * size_t(v.rows) * size_t(R) * 4;
-      ks = int(min(size_t(min(ks, kProdMaxSlices)), max(size_t(1), kProdMaxPartBytes / per_slice)));
+      const int cap = v.wide ? kProdMaxWideSlices : kProdMaxSlices;
+      ks = int(min(size_t(min(ks, cap)), max(size_t(1), kProdMaxPartBytes / per_slice)));
     }
   }
   if (ks > 1) {
@@ -1076,7 +1063,7 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
   }
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-  const int vi = prod_variant_index(M, K, R);
+  const int vi = prod_variant_index(R);
   const ProdVariant& v = kProdVariants[vi];
   const ProdLaunch pl = prod_plan(vi, M, K, R);
   void* buf = nullptr;
@@ -1095,8 +1082,17 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
   ProdParams prm{x, lora_down, act, ascales, lora_act_in, M, K, R, pl.ks, pl.sps,
                  sb ? reinterpret_cast<float*>(sb + kProdCountBytes) : nullptr, reinterpret_cast<uint32_t*>(sb)};
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(v.kernel, dim3(((M + v.rows - 1) / v.rows) * pl.ks), dim3(v.threads), args, 0,
-                                       static_cast<hipStream_t>(stream));
+  const int rbs = (M + v.rows - 1) / v.rows;
+  hipError_t e = hipLaunchKernel(v.kernel, dim3(rbs * pl.ks), dim3(v.threads), args, 0, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && v.wide && pl.part_bytes > 0) {
+    // four ranks per thread (8-byte stores) where R and lora_act_in allow
+    const bool vec4 = R % 4 == 0 && (reinterpret_cast<uintptr_t>(lora_act_in) & 7u) == 0;
+    const size_t units = size_t(rbs) * size_t(v.rows) * size_t(vec4 ? R / 4 : R);
+    const void* rk = vec4 ? reinterpret_cast<const void*>(producer_reduce_kernel<WideCfg<8>::ROWS, 4>)
+                          : reinterpret_cast<const void*>(producer_reduce_kernel<WideCfg<8>::ROWS, 1>);
+    e = hipLaunchKernel(rk, dim3(unsigned((units + kReduceThreads - 1) / kReduceThreads)), dim3(kReduceThreads), args,
+                        0, static_cast<hipStream_t>(stream));
+  }
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
 }
 

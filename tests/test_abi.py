@@ -338,6 +338,7 @@ def test_no_kernel_spills():
     from bit_quantized_gemm_amd.build import BUILD_DIR
     src = open(os.path.join(BUILD_DIR, "libgemm_w4a4_resources.cpp")).read()
     rows = re.findall(r'\{"(\w+)", (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\}', src)
-    assert len(rows) >= 38 and sum("producer_kernel" in r[0] for r in rows) >= 4
+    # the producer: three narrow kernels, the wide kernel and its two reductions
+    assert len(rows) >= 38 and sum("producer_" in r[0] for r in rows) >= 6
     for name, vgpr, agpr, sgpr, lds, spill, scratch in rows:
         assert int(spill) == 0 and int(scratch) == 0, name

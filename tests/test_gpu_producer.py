@@ -58,14 +58,15 @@ def test_producer_workloads(name):
     check_producer(d["x"], d["lora_down"], name)
 
 
-# rows not a multiple of 16, K % 128 != 0 and K % 32 == 16 (8-byte act
-# stores), every compiled instance (8 or 16 waves per 16 rows; R = 0, <= 16,
-# <= 32, <= 128) with R not a multiple of 16; the wide kernel (R > 32 and
-# M*K >= 2^24) with K split (4100 rows: 33 row blocks, the last of 4 rows)
-# and unsplit (257 row blocks, the last of 32 rows)
+# rows not a multiple of 16 (narrow kernels) or 128 (wide kernel), K % 128
+# != 0 and K % 32 == 16 (8-byte act stores), every compiled instance (R = 0,
+# <= 16, <= 32 narrow; R > 32 wide) with R not a multiple of 16 or of 4
+# (the reduction's one-rank path); the wide kernel with K split (4100 rows:
+# 33 row blocks, the last of 4 rows) and unsplit (257 row blocks, the last
+# of 32 rows)
 EDGE = [(1, 16, 0), (17, 48, 1), (33, 144, 17), (100, 528, 32), (130, 1040, 100), (31, 2064, 128),
         (256, 128, 16), (47, 4096, 64), (64, 272, 0), (2, 16, 128), (3072, 272, 0), (3100, 400, 8),
-        (4100, 4112, 100), (32800, 528, 64)]
+        (4100, 4112, 100), (32800, 528, 64), (300, 3072, 33), (1000, 12288, 128)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
@@ -196,7 +197,7 @@ def test_split_calls_of_different_sizes():
     spans), with different numbers of row blocks and ranks: the arrival
     counters live in the same scratch bytes in every call and must be back at
     zero after each."""
-    for shape in [(1000, 8192, 16), (3100, 4096, 8), (33, 4160, 17), (4160, 4096, 128), (3100, 4096, 8),
+    for shape in [(1000, 8192, 16), (2000, 4096, 8), (33, 4160, 17), (4160, 4096, 128), (2000, 4096, 8),
                   (200, 2048, 128), (4100, 4112, 100), (1000, 8192, 16)]:
         M, K, R = shape
         _say(f"case: producer split sequence M={M} K={K} R={R}")

@@ -1,7 +1,9 @@
 """quantize_w4a4_act_noalloc, the entry point that allocates nothing (its
 split-K scratch is a fixed device array per GPU), against quantize_w4a4_act
-through the C ABI: two calls in a row whose K is split over workgroups, so
-that the scratch is used, the second on a smaller input. act, ascales and
+through the C ABI: calls in a row whose K is split over workgroups, so
+that the scratch is used, each pair's second on a smaller input (narrow
+kernels with arrival counters, then the wide kernel with its reduction
+launch, whose partial sums are larger than the first pair's). act, ascales and
 lora_act_in must equal quantize_w4a4_act's bit for bit (same kernels, same
 order of additions), and meet the oracle's bar (byte-exact act / ascales,
 lora_act_in within 4e-3 T + 1 ulp). Needs a gfx950 GPU."""
@@ -36,7 +38,7 @@ def _run(entry, x, ld, M, K, R):
 
 
 def test_noalloc_matches_quantize_w4a4_act():
-    for M, K, R in [(1000, 8192, 32), (200, 4096, 16)]:
+    for M, K, R in [(1000, 8192, 32), (200, 4096, 16), (4160, 4096, 128), (300, 2048, 64)]:
         _say(f"case: no-allocation entry point M={M} K={K} R={R}")
         d = synthetic.producer_inputs(M, K, R, seed=M + 3 * K + R)
         x, ld = _bits_dev(d["x"]), _bits_dev(d["lora_down"])
