@@ -289,6 +289,17 @@ def settle_and_time(step, stream, steps, warmup, settle_ms):
     return warm, e0.elapsed_time(e1), time.perf_counter() - t0
 
 
+def copy_probe(a, dev) -> None:
+    """One device copy of --copy-probe-mb MiB: the known traffic that scales
+    rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    if a.copy_probe_mb > 0:
+        import torch
+        src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+
 def bench_producer(a, wl) -> int:
     """quantize_w4a4_act at the workload's M x K, rank R: GB/s of algorithmic
     traffic against the HBM peak; the oracle on a bounded row sample beside it."""
@@ -304,6 +315,7 @@ def bench_producer(a, wl) -> int:
     ld = torch.from_numpy(d["lora_down"].view(np.int16)).view(torch.bfloat16).to(dev) if R else None
     act, asc, la = w4.quantize_w4a4_act(x, ld)
     stream = torch.cuda.current_stream(dev)
+    copy_probe(a, dev)
     args = (x.data_ptr(), ld.data_ptr() if R else 0, act.data_ptr(), asc.data_ptr(),
             la.data_ptr() if R else 0, M, K, R, stream.cuda_stream)
     bad = []
@@ -328,7 +340,7 @@ def bench_producer(a, wl) -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name} producer", "M": M, "K": K, "R": R},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(wl.name, "producer"),
                      "algorithmic_bytes": nbytes, "avg_launch_us": round(us, 3)},
         "wall_s": round(wall, 3),
     }
@@ -471,11 +483,7 @@ def main() -> int:
         if rc != 0:
             bad.append(rc)
 
-    if a.copy_probe_mb > 0:
-        src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_probe(a, dev)
 
     # Untimed warm-up: W steps, then more until the GPU has been busy with
     # this step for settle_ms (checked every few steps, so the GPU never idles

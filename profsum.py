@@ -13,8 +13,10 @@ include the warm-up, whose first launches run before the clock has settled).
 that also made one device copy of COPY_MIB MiB (bench.py --copy-probe-mb): each
 counter is scaled by (true bytes of that copy) / (what the counter read for
 it), and the GEMM's HBM bytes per launch are the scaled median over its
-dispatches. `counters` tabulates the SQ/GRBM counters of one `--pmc` run. `--fmt mxfp4`
-selects the MXFP4 kernel (default: the NVFP4 one).
+dispatches (per kernel name, summed: a producer step with a split K is two
+launches). `counters` tabulates the counters of one `--pmc` run. `--fmt mxfp4`
+selects the MXFP4 kernel, `--fmt producer` the activation producer's kernels
+(default: the NVFP4 GEMM).
 The file carries the hash of the kernel sources it was taken on, so a reader
 (bench.py) can tell whether it still describes the current kernel.
 """
@@ -36,6 +38,8 @@ _SHARED = ("w4a4_common.hpp", "w4a4_epilogue.hpp", "w4a4_layout.hpp")
 KERNELS = {
     "nvfp4": ("gemm_w4a4_kernel", "gemm_w4a4", ("gemm_w4a4.hip",) + _SHARED),
     "mxfp4": ("gemm_mxfp4_kernel", "gemm_mxfp4", ("gemm_mxfp4.hip",) + _SHARED),
+    "producer": ("producer_", "quantize_w4a4_act",
+                 ("w4a4_producer.hip", "w4a4_common.hpp", "w4a4_host.hpp", "w4a4_layout.hpp")),
 }
 COPY_TAG = "copyBuffer"
 
@@ -70,6 +74,7 @@ def _per_dispatch(directory: str):
 
 def trace(args) -> str:
     tag, name, _ = KERNELS[args.fmt]
+    tag = args.tag or tag
     stats = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_stats.csv")))))
     rows = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_trace.csv")))))
     g = [r for r in rows if tag in r["Kernel_Name"]]
@@ -99,8 +104,10 @@ def trace(args) -> str:
 
 def timed_region(gs, bench_json: str) -> list:
     """Statistics of the timed region's dispatches. bench.py launches the
-    kernel once through the checked binding, then `warmup` untimed steps, then
-    the `steps` timed ones (then one more for its parity sample)."""
+    kernel once through the checked binding, then its untimed warm-up steps
+    (`warmup_steps_run`: the requested `warmup`, continued until the clock has
+    settled), then the `steps` timed ones (then one more for its parity
+    sample). A step is one dispatch of the selected kernel."""
     b = None
     with open(bench_json) as f:
         for line in f:
@@ -108,19 +115,20 @@ def timed_region(gs, bench_json: str) -> list:
                 b = json.loads(line)
     if b is None:
         raise SystemExit(f"no JSON line in {bench_json}")
-    first, k = 1 + int(b["warmup"]), int(b["steps"])
+    warm = int(b.get("warmup_steps_run", b["warmup"]))
+    first, k = 1 + warm, int(b["steps"])
     sel = gs[first:first + k]
     if len(sel) != k:
         raise SystemExit(f"expected {k} timed dispatches after {first}, found {len(sel)}")
     d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
     span = int(sel[-1]["End_Timestamp"]) - int(sel[0]["Start_Timestamp"])
     return ["", f"Timed region of that bench run: dispatches {first} .. {first + k - 1} of the kernel "
-                f"({k} launches after {b['warmup']} warm-up steps):", "",
+                f"({k} launches after {warm} warm-up steps):", "",
             "| Average ns | Median ns | Min ns | Max ns | Span / launches ns |", "|---|---|---|---|---|",
             f"| {statistics.mean(d):.1f} | {statistics.median(d):.0f} | {min(d)} | {max(d)} | {span / k:.1f} |",
             "", f"bench.py's own figure in that run (HIP events at the ends of the timed region): "
-                f"{b['roofline']['avg_launch_us'] * 1e3:.0f} ns per launch, "
-                f"{b['roofline']['achieved']:.1f} TFLOP/s."]
+                f"{b['roofline']['avg_launch_us'] * 1e3:.0f} ns per step, "
+                f"{b['roofline']['achieved']:.1f} {b['roofline'].get('unit', 'TFLOP/s')}."]
 
 
 def traffic(args) -> str:
@@ -133,10 +141,14 @@ def traffic(args) -> str:
         if not copies:
             raise SystemExit(f"no copy dispatch found for {counter}")
         probe = max(copies)   # the probe is by far the largest copy
-        gemm = [v[counter] for n, v in runs.values() if tag in n]
-        if not gemm:
-            raise SystemExit(f"no gemm dispatch found for {counter}")
-        return probe, true_kib / probe, statistics.median(gemm), len(gemm)
+        per_kernel = defaultdict(list)
+        for n, v in runs.values():
+            if tag in n:
+                per_kernel[n].append(v[counter])
+        if not per_kernel:
+            raise SystemExit(f"no {tag} dispatch found for {counter}")
+        med = sum(statistics.median(x) for x in per_kernel.values())   # one launch of each per step
+        return probe, true_kib / probe, med, min(len(x) for x in per_kernel.values())
 
     fp, ff, fg, fn = scale(fetch, "FETCH_SIZE")
     wp, wf, wg, wn = scale(write, "WRITE_SIZE")
@@ -146,9 +158,9 @@ def traffic(args) -> str:
              f"#   {args.command_fetch}", f"#   {args.command_write}",
              f"# copy probe: one device copy of {args.copy_mib} MiB = {true_kib:.0f} KiB read and written",
              f"# FETCH_SIZE read {fp:.1f} KiB for the probe -> scale {ff:.4f}; "
-             f"gemm median over {fn} dispatches {fg:.1f} KiB",
+             f"kernel median over {fn} dispatches {fg:.1f} KiB",
              f"# WRITE_SIZE read {wp:.1f} KiB for the probe -> scale {wf:.4f}; "
-             f"gemm median over {wn} dispatches {wg:.1f} KiB",
+             f"kernel median over {wn} dispatches {wg:.1f} KiB",
              f"kernel_source_sha256: {kernel_source_hash(args.fmt)}",
              f"fetch_bytes_per_launch: {fetch_b:.0f}",
              f"write_bytes_per_launch: {write_b:.0f}",
@@ -164,6 +176,9 @@ DERIVED = {
     "LDSBankConflict": "100 * SQ_LDS_BANK_CONFLICT / (GRBM_GUI_ACTIVE * CU count): % of time the LDS stalls on bank conflicts",
     "LdsUtil": "100 * SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * CU count): % of time the LDS is busy",
     "LdsBankConflict": "SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT): conflict cycles per LDS access cycle",
+    "VmemLatency": "accumulated SQ_INST_LEVEL_VMEM / SQ_INSTS_VMEM: average cycles a vector memory instruction is in flight",
+    "LdsLatency": "accumulated SQ_INST_LEVEL_LDS / SQ_INSTS_LDS: average cycles an LDS instruction is in flight",
+    "MemUnitStalled": "100 * TCP_TCP_TA_DATA_STALL_CYCLES (max) / GRBM_GUI_ACTIVE / SE count: % of time the memory unit is stalled",
 }
 
 
@@ -173,7 +188,7 @@ def counters(args) -> str:
     g = [v for n, v in runs.values() if tag in n]
     names = sorted(g[0]) if g else []
     derived = bool(names) and all(c in DERIVED for c in names)
-    title = "rocprofv3 derived metrics" if derived else "SQ/GRBM counters"
+    title = "rocprofv3 derived metrics" if derived else "hardware counters"
     what = ("values as rocprofv3 computes them per dispatch" if derived
             else "values summed over the device")
     lines = [f"# {name} {title}, {args.workload} workload", "",
@@ -200,6 +215,7 @@ def main(argv=None) -> int:
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--bench-json", default=None, help="bench.py's output of the traced run")
+    t.add_argument("--tag", default=None, help="kernel-name substring of the launch to time (default: the format's)")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_dir")
     f.add_argument("write_dir")

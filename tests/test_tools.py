@@ -63,6 +63,21 @@ def test_trace_timed_region_picks_the_timed_dispatches(tmp_path):
     assert "Median gap between consecutive launches under the tracer: 0 ns." in out
 
 
+def test_trace_timed_region_counts_the_settled_warmup(tmp_path):
+    # bench.py's JSON: `warmup` is the requested count, `warmup_steps_run` what
+    # its settle loop ran; the timed dispatches follow the latter
+    durations = [900] * (1 + 5) + [100, 110, 120, 130] + [700]
+    d = _trace_dir(tmp_path, durations)
+    bench = tmp_path / "bench.json"
+    bench.write_text(json.dumps({"warmup": 2, "warmup_steps_run": 5, "steps": 4,
+                                 "roofline": {"avg_launch_us": 0.115, "achieved": 9.0, "unit": "GB/s"}}))
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "profsum.py"), "trace", str(d),
+                          "--workload", "qkv", "--command", "cmd", "--bench-json", str(bench)],
+                         cwd=ROOT, capture_output=True, text=True, check=True).stdout
+    assert "dispatches 6 .. 9" in out and "after 5 warm-up steps" in out
+    assert "| 115.0 | 115 | 100 | 130 | 115.0 |" in out and "9.0 GB/s" in out
+
+
 def test_trace_timed_region_rejects_a_short_trace(tmp_path):
     d = _trace_dir(tmp_path, [100] * 5)
     bench = tmp_path / "bench.json"
