@@ -7,8 +7,8 @@
 // (sections 2 and 3.1); the scale and rounding rule is this library's
 // reading, stated in gemm_w4a4.h.
 //
-// Design (one workgroup of 8 waves, or 4 at the largest ranks, per 16 rows
-// of x and one slice of K):
+// Design. Ranks R <= 32 run a narrow kernel: one workgroup of 8 waves per 16
+// rows of x and one slice of K.
 //  * x is read once. K is cut into spans of 128; a workgroup takes the spans
 //    of its K slice, wave w the spans w, w+WAVES, ... of them, streamed through a
 //    private LDS ring of DEPTH slots by direct-to-LDS DMA, so the loop needs
@@ -19,12 +19,15 @@
 //    bytes, in scalar registers. Reads past the tensor's end return zeros and
 //    reads past K in the span that crosses it land in the next row, zeroed at
 //    use, so no address is clamped.
-//  * When there are fewer row blocks (M / 16) than workgroup slots on the
-//    chip, K is split into slices over several workgroups: each writes its
-//    float32 LoRA partial sums to a scratch buffer, and the last of them to
-//    finish (a counter per row block) adds the slices in slice order and
-//    writes lora_act_in, so the result does not depend on the order the
-//    workgroups ran in.
+//  * When the row blocks (M / 16) do not fill the chip, K is split into
+//    slices over several workgroups: each writes its float32 LoRA partial
+//    sums to a scratch buffer, and the last of them to finish (a counter per
+//    row block) adds the slices in slice order and writes lora_act_in, so
+//    the result does not depend on the order the workgroups ran in.
+// Ranks R > 32 run the wide kernel (producer_wide_kernel): four waves share
+// 128 rows, each streaming its own 32 rows of x, while the span's lora_down
+// tile is DMA'd once per workgroup into a shared LDS ring; its K slices'
+// partial sums are added by a second launch (producer_reduce_kernel).
 //  * Lane (r, g) holds row r, k = 32g .. 32g+31 of the span: two whole
 //    16-value blocks, so a block's amax needs no cross-lane step. Scale and
 //    codes are decided exactly (see quantize_block), codes are packed by the

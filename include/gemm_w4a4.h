@@ -235,8 +235,18 @@ int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
  * M >= 1; K >= 16 with K % 16 == 0; 0 <= R <= QUANTIZE_W4A4_MAX_R; every
  * tensor below 2^31 bytes. Alignment: x and lora_down 16 bytes, act 8,
  * lora_act_in 2. No output may overlap an input or another output
- * (GEMM_W4A4_EOVERLAP). Device pointers owned by the caller; nothing is
- * allocated or synchronised; return codes as for gemm_w4a4.
+ * (GEMM_W4A4_EOVERLAP). Device pointers owned by the caller; the work is
+ * enqueued on `stream` (one launch, or two when R > 32 and K is split: the
+ * second adds the slices' partial sums).
+ *
+ * Scratch: when few rows meet a long K, K is split over workgroups and
+ * float32 partial sums go to a scratch buffer that the library allocates per
+ * device on the first call that needs it (or more than it holds) and keeps
+ * until the process ends. That call allocates, zeroes the buffer and
+ * synchronises the device before it enqueues anything (GEMM_W4A4_ENOMEM if
+ * the allocation fails); every other call allocates and synchronises
+ * nothing. quantize_w4a4_act_noalloc never allocates. Other return codes as
+ * for gemm_w4a4.
  */
 #define QUANTIZE_W4A4_MAX_R 128
 int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
@@ -249,9 +259,10 @@ int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act
  * harnesses that forbid hipMalloc. Same arguments, kernels and results as
  * quantize_w4a4_act; it calls no allocating routine.
  *
- * When K is split over several workgroups (few rows, long K), the kernel
- * keeps float32 partial sums and one arrival counter per 16 rows in scratch
- * memory; quantize_w4a4_act allocates that buffer on first need, this entry
+ * When K is split over several workgroups (few rows, long K), the kernels
+ * keep float32 partial sums (and, for R <= 32, one arrival counter per 16
+ * rows) in scratch memory; quantize_w4a4_act allocates that buffer on first
+ * need, this entry
  * point uses a fixed device array of QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES
  * (4 KiB of counters + 16 MiB of partial sums) that each GPU holds until the
  * process ends. Both entry points split K only as far as 16 MiB of partial
