@@ -105,7 +105,8 @@ struct ProdParams {
   uint16_t* lora_act_in;
   int M, K, R;
   int ks, sps;          // K slices per row block, spans per slice
-  float* part;          // ks > 1 and R > 0: float32 partial sums [row block][slice][16][R]
+  float* part;          // ks > 1 and R > 0: float32 partial sums, [row block][slice][rank][16 rows]
+                        // (narrow kernels) or [row block][slice][128 rows][rank] (wide kernel)
   uint32_t* count;      // ks > 1 and R > 0: arrivals per row block, zero between calls
 };
 
@@ -656,8 +657,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_wide_kernel(const Prod
 #pragma unroll
     for (int u = 0; u < C::DX; ++u) dma_buf(desc, xoff[u], slot + u * 1024);
   };
+  // (R == 0: lora_down may be null and every descriptor is empty)
   auto dma_l = [&](int j) __attribute__((always_inline)) {
-    const bool valid = j < n;
+    const bool valid = j < n && R > 0;
     const uint32_t sb = valid ? uint32_t(s_beg + j) * uint32_t(C::ROW_SPAN) : 0u;
     const __amdgpu_buffer_rsrc_t desc = buffer_rsrc(ldb + sb, valid ? ld_bytes - sb : 0u);
     uint8_t* slot = lring + (j & 1) * C::L_SLOT + wave_u * (C::L_SLOT / C::WAVES);
@@ -896,19 +898,38 @@ ProdVariant prod_wide_variant() {
                      true};
 }
 
-// By rank: R == 0, R <= 16, R <= 32 with 8 waves of 16 rows (two per SIMD)
-// and two ring slots each; above R = 32 the wide kernel (128 rows per
-// workgroup, the lora_down tile shared through LDS, 8 rank tiles). A narrow
-// kernel for R <= 128 (its operands in two register halves per span) was
-// measured slower than the wide one at every shape tried, 256x3072 to
-// 8192x12288 at R = 64 and 128 (1000x3072 R=128: 26.2 against 14.4 us;
-// 4096x12288 R=128: 93.3 against 41.3), and is not built; at R <= 32 the
-// narrow kernels are faster (4096x3072 R=32: 12.4 against 24.4 us for the
-// wide kernel, whose 8 rank tiles would do 4x the MFMA work).
-static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(), prod_variant<8, 1, 2>(),
-                                            prod_variant<8, 2, 2>(), prod_wide_variant<8>()};
+// Instances: narrow kernels for R == 0, R <= 16, R <= 32 (8 waves of 16
+// rows, two per SIMD, two ring slots each); the wide kernel (128 rows per
+// workgroup, the lora_down tile shared through LDS) with 8, 1 and 2 rank
+// tiles. Above R = 32 the wide kernel always: a narrow kernel for R <= 128
+// (its operands in two register halves per span) was measured slower at
+// every shape tried, 256x3072 to 8192x12288 at R = 64 and 128 (1000x3072
+// R=128: 26.2 against 14.4 us; 4096x12288 R=128: 93.3 against 41.3), and
+// is not built. At R <= 32 each narrow wave reads its own copy of the
+// span's lora_down, 8x the L2 traffic of the wide kernel's shared tile, but
+// hides latency with two waves per SIMD; measured:
+//  * R <= 32: wide faster from M > 4096 rows or 2^25 elements of x up
+//    (16384x3072: 28.5 against 36.2 us; 4096x12288: 28.7 against 33.3;
+//    4352x10240: 29.8 against 51.7), narrow faster below (4096x3072: 12.1
+//    against 12.5; 1000x3072: 8.1 against 9.2);
+//  * R <= 16: narrow faster or equal except where its 16-row blocks
+//    overfill the compute units unevenly (4352x10240, 272 blocks: wide 27.6
+//    against 36.6 us; 8192x3072, 512 blocks: narrow 15.5 against 18.2). The
+//    same holds without LoRA (R == 0: the wide kernel's one rank tile then
+//    multiplies zeros).
+static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(),  prod_variant<8, 1, 2>(),
+                                            prod_variant<8, 2, 2>(),  prod_wide_variant<8>(),
+                                            prod_wide_variant<1>(), prod_wide_variant<2>()};
 
-static int prod_variant_index(int R) { return R == 0 ? 0 : R <= 16 ? 1 : R <= 32 ? 2 : 3; }
+static int prod_variant_index(int M, int K, int R, int cus) {
+  if (R > 32) return 3;
+  const int rbs = (M + 15) / 16;                        // narrow row blocks
+  const int full = rbs / cus, part = rbs % cus;         // whole rounds, the last round's blocks
+  const bool uneven = full >= 1 && part > 0 && part * 4 <= cus * 3;   // last round <= 3/4 full
+  if (R == 0) return uneven ? 4 : 0;
+  if (R <= 16) return uneven ? 4 : 1;
+  return rbs > cus || size_t(M) * size_t(K) >= (size_t(1) << 25) ? 5 : 2;
+}
 
 static std::atomic<int> g_cus[64];
 
@@ -1066,7 +1087,7 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
   }
   const int dev_rc = check_device();
   if (dev_rc != GEMM_W4A4_OK) return dev_rc;
-  const int vi = prod_variant_index(R);
+  const int vi = prod_variant_index(M, K, R, compute_units());
   const ProdVariant& v = kProdVariants[vi];
   const ProdLaunch pl = prod_plan(vi, M, K, R);
   void* buf = nullptr;

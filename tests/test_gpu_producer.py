@@ -58,15 +58,18 @@ def test_producer_workloads(name):
     check_producer(d["x"], d["lora_down"], name)
 
 
-# rows not a multiple of 16 (narrow kernels) or 128 (wide kernel), K % 128
-# != 0 and K % 32 == 16 (8-byte act stores), every compiled instance (R = 0,
-# <= 16, <= 32 narrow; R > 32 wide) with R not a multiple of 16 or of 4
-# (the reduction's one-rank path); the wide kernel with K split (4100 rows:
-# 33 row blocks, the last of 4 rows) and unsplit (257 row blocks, the last
-# of 32 rows)
+# rows not a multiple of 16 (narrow kernels) or 128 (wide kernels), K % 128
+# != 0 and K % 32 == 16 (8-byte act stores), every compiled instance with R
+# not a multiple of 16 or of 4 (the reduction's one-rank path): narrow for
+# R = 0, <= 16, <= 32; wide with 8 rank tiles for R > 32, with 1 where
+# 16-row blocks would overfill the chip unevenly (4352 rows, also at R = 0)
+# and with 2 from 4097 rows or 2^25 elements at R <= 32; the wide kernels
+# with K split (4100 rows: 33 row blocks, the last of 4 rows) and unsplit
+# (257 or 258 row blocks)
 EDGE = [(1, 16, 0), (17, 48, 1), (33, 144, 17), (100, 528, 32), (130, 1040, 100), (31, 2064, 128),
         (256, 128, 16), (47, 4096, 64), (64, 272, 0), (2, 16, 128), (3072, 272, 0), (3100, 400, 8),
-        (4100, 4112, 100), (32800, 528, 64), (300, 3072, 33), (1000, 12288, 128)]
+        (4100, 4112, 100), (32800, 528, 64), (300, 3072, 33), (1000, 12288, 128),
+        (4352, 1040, 9), (8200, 528, 32), (4100, 8208, 24), (33000, 272, 20), (4352, 1040, 0)]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=["x".join(map(str, s)) for s in EDGE])
