@@ -43,7 +43,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "gemm_w4a4.h"
 #include "w4a4_common.hpp"
@@ -1001,20 +1003,23 @@ static ProdLaunch prod_plan(int vi, int M, int K, int R) {
   return pl;
 }
 
-// Scratch of the split-K reduction, per device: grown on demand and zeroed
-// when allocated (the counters return to zero at the end of every call).
+// Scratch of the split-K reduction, one per (device, stream): calls on one
+// stream run in order, so each call finds the counters it needs at zero
+// (every call returns them there) and no other call's partial sums in its
+// way; calls on different streams never share one. Grown on demand, zeroed
+// when allocated, kept until the process ends.
 struct ProdScratch {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-static ProdScratch g_prod_scratch[64];
+static std::map<std::pair<int, void*>, ProdScratch> g_prod_scratch;
 static std::mutex g_prod_scratch_mu;
 
-static int prod_scratch(size_t need, void** out) {
+static int prod_scratch(size_t need, void* stream, void** out) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_W4A4_EDEVICE;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_W4A4_EDEVICE;
   std::lock_guard<std::mutex> lock(g_prod_scratch_mu);
-  ProdScratch& s = g_prod_scratch[dev];
+  ProdScratch& s = g_prod_scratch[{dev, stream}];
   if (s.bytes < need) {
     if (s.ptr && hipFree(s.ptr) != hipSuccess) return GEMM_W4A4_ENOMEM;   // waits for the device
     s.ptr = nullptr;
@@ -1098,7 +1103,7 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
       if (need > size_t(QUANTIZE_W4A4_NOALLOC_SCRATCH_BYTES)) return GEMM_W4A4_ESCRATCH;
       rc = noalloc_scratch(&buf);
     } else {
-      rc = prod_scratch(need, &buf);
+      rc = prod_scratch(need, stream, &buf);
     }
     if (rc != GEMM_W4A4_OK) return rc;
   }

@@ -241,12 +241,13 @@ int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
  *
  * Scratch: when few rows meet a long K, K is split over workgroups and
  * float32 partial sums go to a scratch buffer that the library allocates per
- * device on the first call that needs it (or more than it holds) and keeps
- * until the process ends. That call allocates, zeroes the buffer and
- * synchronises the device before it enqueues anything (GEMM_W4A4_ENOMEM if
- * the allocation fails); every other call allocates and synchronises
- * nothing. quantize_w4a4_act_noalloc never allocates. Other return codes as
- * for gemm_w4a4.
+ * device and stream on the first call on that stream that needs it (or more
+ * than it holds) and keeps until the process ends. That call allocates,
+ * zeroes the buffer and synchronises the device before it enqueues anything
+ * (GEMM_W4A4_ENOMEM if the allocation fails); every other call allocates and
+ * synchronises nothing. Calls on different streams use different buffers, so
+ * they may overlap. quantize_w4a4_act_noalloc never allocates. Other return
+ * codes as for gemm_w4a4.
  */
 #define QUANTIZE_W4A4_MAX_R 128
 int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,

@@ -206,3 +206,33 @@ def test_split_calls_of_different_sizes():
         _say(f"case: producer split sequence M={M} K={K} R={R}")
         d = synthetic.producer_inputs(M, K, R, seed=M * 7 + K + R)
         check_producer(d["x"], d["lora_down"], f"sequence {shape}")
+
+
+def test_split_calls_on_two_streams_overlap_safely():
+    """Split calls on two streams, enqueued alternately with no ordering
+    between the streams: each stream has its own scratch (counters and
+    partial sums), so both results equal those of the same calls made one
+    after another."""
+    shapes = [(1000, 8192, 16), (2000, 4096, 8)]   # both split K (narrow kernels, arrival counters)
+    dev = torch.device("cuda:0")
+    bufs = []
+    for M, K, R in shapes:
+        d = synthetic.producer_inputs(M, K, R, seed=M * 5 + K + R)
+        x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ld = torch.from_numpy(d["lora_down"].view(np.int16)).view(torch.bfloat16).to(dev)
+        bufs.append((x, ld, w4.quantize_w4a4_act(x, ld)))
+    torch.cuda.synchronize()
+    want = [tuple(t.clone() for t in b[2]) for b in bufs]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    for _ in range(20):
+        for (x, ld, outs), s in zip(bufs, streams):
+            act, asc, la = outs
+            M, K = x.shape
+            rc = w4.quantize_raw(x.data_ptr(), ld.data_ptr(), act.data_ptr(), asc.data_ptr(), la.data_ptr(),
+                                 M, K, ld.shape[0], s.cuda_stream)
+            assert rc == w4.OK, w4.strerror(rc)
+    torch.cuda.synchronize()
+    for (x, ld, outs), w, shape in zip(bufs, want, shapes):
+        _say(f"case: producer on two streams {shape}")
+        for got, exp in zip(outs, w):
+            assert torch.equal(got, exp), shape
