@@ -80,6 +80,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   constexpr int PF = C::STAGES - 1;                              // prefetch distance in stages
   static_assert((PF - 1) * DMA_N < 64, "vmcnt range");
   static_assert(ROWS_PER_ROUND % 32 == 0, "the chunk swizzle repeats every 32 rows");
+  // each MFMA group issues at most one operand read, tile q - (G - T) (k-step
+  // 0) or q (k-step 1): every tile needs a group (a 32x96 wave tile, 4 tiles
+  // for 3 MFMAs, would leave one unread)
+  static_assert(T <= G, "one operand tile read per MFMA group");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
