@@ -341,7 +341,8 @@ def bench_producer(a, wl) -> int:
         "config": {"workload": f"{wl.name} producer", "M": M, "K": K, "R": R},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(wl.name, "producer"),
-                     "algorithmic_bytes": nbytes, "avg_launch_us": round(us, 3)},
+                     "algorithmic_bytes": nbytes, "avg_launch_us": round(us, 3),
+                     "kernel_source_sha256": kernel_source_hash("producer")},
         "wall_s": round(wall, 3),
     }
     if a.cpu_seconds > 0:

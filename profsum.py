@@ -18,7 +18,11 @@ launches). `counters` tabulates the counters of one `--pmc` run. `--fmt mxfp4`
 selects the MXFP4 kernel, `--fmt producer` the activation producer's kernels
 (default: the NVFP4 GEMM).
 The file carries the hash of the kernel sources it was taken on, so a reader
-(bench.py) can tell whether it still describes the current kernel.
+(bench.py) can tell whether it still describes the current kernel. That hash
+is the one bench.py recorded in the profiled run's JSON line (`--bench-json`,
+or `--bench-out` for a counter run's output): a run whose kernel sources
+differ from the current ones is refused, not summarised under the current
+hash.
 """
 from __future__ import annotations
 
@@ -54,6 +58,28 @@ def kernel_source_hash(fmt: str = "nvfp4") -> str:
     return h.hexdigest()[:16]
 
 
+def _bench_line(path: str) -> dict:
+    """The last JSON line bench.py printed into `path`."""
+    b = None
+    with open(path) as f:
+        for line in f:
+            if line.lstrip().startswith("{"):
+                b = json.loads(line)
+    if b is None:
+        raise SystemExit(f"no JSON line in {path}")
+    return b
+
+
+def _check_sources(path, fmt: str) -> None:
+    """Refuse a profiled run whose recorded kernel sources are not the current ones."""
+    if path is None:
+        return
+    rec = _bench_line(path).get("roofline", {}).get("kernel_source_sha256")
+    if rec is not None and rec != kernel_source_hash(fmt):
+        raise SystemExit(f"{path}: the profiled run used kernel sources {rec}, the current ones are "
+                         f"{kernel_source_hash(fmt)}: profile again")
+
+
 def _one(pattern: str) -> str:
     hits = sorted(glob.glob(pattern))
     if not hits:
@@ -75,6 +101,7 @@ def _per_dispatch(directory: str):
 def trace(args) -> str:
     tag, name, _ = KERNELS[args.fmt]
     tag = args.tag or tag
+    _check_sources(args.bench_json, args.fmt)
     stats = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_stats.csv")))))
     rows = list(csv.DictReader(open(_one(os.path.join(args.dir, "*kernel_trace.csv")))))
     g = [r for r in rows if tag in r["Kernel_Name"]]
@@ -108,13 +135,7 @@ def timed_region(gs, bench_json: str) -> list:
     (`warmup_steps_run`: the requested `warmup`, continued until the clock has
     settled), then the `steps` timed ones (then one more for its parity
     sample). A step is one dispatch of the selected kernel."""
-    b = None
-    with open(bench_json) as f:
-        for line in f:
-            if line.lstrip().startswith("{"):
-                b = json.loads(line)
-    if b is None:
-        raise SystemExit(f"no JSON line in {bench_json}")
+    b = _bench_line(bench_json)
     warm = int(b.get("warmup_steps_run", b["warmup"]))
     first, k = 1 + warm, int(b["steps"])
     sel = gs[first:first + k]
@@ -133,6 +154,8 @@ def timed_region(gs, bench_json: str) -> list:
 
 def traffic(args) -> str:
     tag, name, _ = KERNELS[args.fmt]
+    for out in args.bench_out or []:
+        _check_sources(out, args.fmt)
     fetch, write = _per_dispatch(args.fetch_dir), _per_dispatch(args.write_dir)
     true_kib = args.copy_mib * 1024.0
 
@@ -184,6 +207,8 @@ DERIVED = {
 
 def counters(args) -> str:
     tag, name, _ = KERNELS[args.fmt]
+    for out in args.bench_out or []:
+        _check_sources(out, args.fmt)
     runs = _per_dispatch(args.dir)
     g = [v for n, v in runs.values() if tag in n]
     names = sorted(g[0]) if g else []
@@ -223,10 +248,12 @@ def main(argv=None) -> int:
     f.add_argument("--workload", required=True)
     f.add_argument("--command-fetch", required=True)
     f.add_argument("--command-write", required=True)
+    f.add_argument("--bench-out", nargs="*", help="bench.py's output of the profiled runs (source check)")
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--workload", required=True)
     c.add_argument("--command", required=True)
+    c.add_argument("--bench-out", nargs="*", help="bench.py's output of the profiled run (source check)")
     for p in (t, f, c):
         p.add_argument("--fmt", default="nvfp4", choices=sorted(KERNELS))
     a = ap.parse_args(argv)

@@ -78,6 +78,17 @@ def test_trace_timed_region_counts_the_settled_warmup(tmp_path):
     assert "| 115.0 | 115 | 100 | 130 | 115.0 |" in out and "9.0 GB/s" in out
 
 
+def test_trace_refuses_a_run_on_other_kernel_sources(tmp_path):
+    d = _trace_dir(tmp_path, [100] * 10)
+    bench = tmp_path / "bench.json"
+    bench.write_text(json.dumps({"warmup": 2, "steps": 4, "roofline": {
+        "avg_launch_us": 0.1, "achieved": 1.0, "kernel_source_sha256": "0123456789abcdef"}}))
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "profsum.py"), "trace", str(d),
+                          "--workload", "qkv", "--command", "cmd", "--bench-json", str(bench)],
+                         cwd=ROOT, capture_output=True, text=True)
+    assert res.returncode != 0 and "profile again" in res.stderr
+
+
 def test_trace_timed_region_rejects_a_short_trace(tmp_path):
     d = _trace_dir(tmp_path, [100] * 5)
     bench = tmp_path / "bench.json"
