@@ -15,11 +15,11 @@ from __future__ import annotations
 
 from . import _native
 from ._native import (EALIGN, EDEVICE, EINVAL, ENOMEM, ESCRATCH, ELAUNCH, EOVERLAP, FORMATS, MAX_R, OK, QUANTIZE_MAX_R,
-                      quantize_noalloc_raw, quantize_raw,
+                      quantize_noalloc_raw, quantize_plan, quantize_raw,
                       gemm_mxfp4_f16_raw, gemm_mxfp4_raw, gemm_w4a4_f16_raw, gemm_w4a4_raw,
                       library_path, plan, plan_variant, run_raw, strerror, variants)
 
-__all__ = ["gemm_w4a4", "gemm_mxfp4", "quantize_w4a4_act", "quantize_raw", "quantize_noalloc_raw", "QUANTIZE_MAX_R", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
+__all__ = ["gemm_w4a4", "gemm_mxfp4", "quantize_w4a4_act", "quantize_raw", "quantize_noalloc_raw", "quantize_plan", "QUANTIZE_MAX_R", "gemm_w4a4_raw", "gemm_w4a4_f16_raw", "gemm_mxfp4_raw",
            "gemm_mxfp4_f16_raw", "run_raw", "plan", "plan_variant", "variants", "strerror", "library_path", "GemmError", "OK",
            "EINVAL", "EALIGN", "ELAUNCH", "EOVERLAP", "EDEVICE", "ENOMEM", "ESCRATCH", "MAX_R", "FORMATS"]
 

@@ -29,6 +29,17 @@ _PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m",
                 "regs_limit", "k_groups")
 
 
+_QPLAN_FIELDS = ("variant", "wide", "rank_tiles", "rows", "threads", "lds_bytes", "row_blocks", "k_slices",
+                 "spans_per_slice", "grid", "launches")
+
+
+class QuantizePlan(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in _QPLAN_FIELDS] + [("scratch_bytes", ctypes.c_longlong)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f in _QPLAN_FIELDS + ("scratch_bytes",)}
+
+
 class Plan(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in _PLAN_FIELDS]
 
@@ -79,6 +90,8 @@ def load() -> ctypes.CDLL:
         lib.quantize_w4a4_act.restype = i
         lib.quantize_w4a4_act_noalloc.argtypes = [vp] * 5 + [i, i, i, vp]
         lib.quantize_w4a4_act_noalloc.restype = i
+        lib.quantize_w4a4_act_plan.argtypes = [i, i, i, ctypes.POINTER(QuantizePlan)]
+        lib.quantize_w4a4_act_plan.restype = i
         lib.gemm_w4a4_run.argtypes = [i, i, i] + [vp] * 9 + [i, i, i, i, vp]
         lib.gemm_w4a4_run.restype = i
         lib.gemm_w4a4_plan_variant.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
@@ -133,6 +146,15 @@ def quantize_noalloc_raw(x, lora_down, act, ascales, lora_act_in, M, K, R, strea
     """Direct call of quantize_w4a4_act_noalloc (no device allocation; its
     scratch is a fixed array per GPU) with integer addresses; returns its code."""
     return load().quantize_w4a4_act_noalloc(x, lora_down, act, ascales, lora_act_in, M, K, R, stream)
+
+
+def quantize_plan(M: int, K: int, R: int) -> dict:
+    """The launch quantize_w4a4_act would make for (M, K, R) (host only)."""
+    p = QuantizePlan()
+    rc = load().quantize_w4a4_act_plan(M, K, R, ctypes.byref(p))
+    if rc != OK:
+        raise ValueError(f"quantize_w4a4_act_plan: {strerror(rc)} ({rc})")
+    return p.as_dict()
 
 
 def run_raw(fmt: str, out_f16: bool, variant: int, act, ascales, wgt, wscales, wcscale, bias,

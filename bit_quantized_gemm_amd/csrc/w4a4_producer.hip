@@ -1069,14 +1069,17 @@ static int noalloc_scratch(void** out) {
   return GEMM_W4A4_OK;
 }
 
+static bool prod_sizes_ok(int M, int K, int R) {
+  if (!(M >= 1 && K >= 16 && K % 16 == 0 && R >= 0 && R <= QUANTIZE_W4A4_MAX_R)) return false;
+  const int64_t lim = int64_t(1) << 31;
+  return int64_t(M) * K * 2 < lim && int64_t(R) * K * 2 < lim && int64_t(M) * R * 2 < lim;
+}
+
 // Checks, plan, scratch and launch shared by both entry points; `noalloc`
 // takes the scratch from the fixed array instead of the library's buffer.
 static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* act, uint8_t* ascales,
                         uint16_t* lora_act_in, int M, int K, int R, void* stream, bool noalloc) {
-  if (!(M >= 1 && K >= 16 && K % 16 == 0 && R >= 0 && R <= QUANTIZE_W4A4_MAX_R)) return GEMM_W4A4_EINVAL;
-  const int64_t lim = int64_t(1) << 31;
-  if (int64_t(M) * K * 2 >= lim || int64_t(R) * K * 2 >= lim || int64_t(M) * R * 2 >= lim)
-    return GEMM_W4A4_EINVAL;
+  if (!prod_sizes_ok(M, K, R)) return GEMM_W4A4_EINVAL;
   if (!x || !act || !ascales || (R > 0 && (!lora_down || !lora_act_in))) return GEMM_W4A4_EINVAL;
   if ((uintptr_t(x) | (R > 0 ? uintptr_t(lora_down) : 0u)) & 15u) return GEMM_W4A4_EALIGN;
   if ((uintptr_t(act) & 7u) || (R > 0 && (uintptr_t(lora_act_in) & 1u))) return GEMM_W4A4_EALIGN;
@@ -1125,7 +1128,34 @@ static int quantize_run(const uint16_t* x, const uint16_t* lora_down, uint8_t* a
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
 }
 
+static int quantize_plan(int M, int K, int R, quantize_w4a4_plan_t* out) {
+  if (!out || !prod_sizes_ok(M, K, R)) return GEMM_W4A4_EINVAL;
+  const int vi = prod_variant_index(M, K, R, compute_units());
+  const ProdVariant& v = kProdVariants[vi];
+  const ProdLaunch pl = prod_plan(vi, M, K, R);
+  const int rbs = (M + v.rows - 1) / v.rows;
+  quantize_w4a4_plan_t q{};
+  q.variant = vi;
+  q.wide = v.wide ? 1 : 0;
+  q.rank_tiles = v.rtiles;
+  q.rows = v.rows;
+  q.threads = v.threads;
+  q.lds_bytes = v.lds;
+  q.row_blocks = rbs;
+  q.k_slices = pl.ks;
+  q.spans_per_slice = pl.sps;
+  q.grid = rbs * pl.ks;
+  q.launches = v.wide && pl.part_bytes > 0 ? 2 : 1;
+  q.scratch_bytes = pl.part_bytes > 0 ? (long long)(kProdCountBytes + pl.part_bytes) : 0;
+  *out = q;
+  return GEMM_W4A4_OK;
+}
+
 }  // namespace w4a4
+
+extern "C" int quantize_w4a4_act_plan(int M, int K, int R, quantize_w4a4_plan_t* plan) {
+  return w4a4::quantize_plan(M, K, R, plan);
+}
 
 extern "C" int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act,
                                  uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,

@@ -254,6 +254,30 @@ int quantize_w4a4_act(const uint16_t* x, const uint16_t* lora_down, uint8_t* act
                       uint8_t* ascales, uint16_t* lora_act_in, int M, int K, int R,
                       void* stream);
 
+/* The launch quantize_w4a4_act would make for (M, K, R): host only, nothing
+ * enqueued. The instance follows the rank and, at R <= 32, the shape; K is
+ * split over workgroups so that all row blocks' workgroups spread over the
+ * compute units in one round (the device's count; 256 when no device is
+ * current). */
+typedef struct {
+  int variant;          /* compiled producer instance */
+  int wide;             /* 1: the waves of a workgroup share each span (lora_down tile in LDS) */
+  int rank_tiles;       /* 16-rank tiles the instance covers (R <= 16 * rank_tiles) */
+  int rows;             /* rows of x per workgroup */
+  int threads;          /* threads per workgroup */
+  int lds_bytes;        /* LDS per workgroup */
+  int row_blocks;       /* ceil(M / rows) */
+  int k_slices;         /* workgroups sharing a row block's K */
+  int spans_per_slice;  /* 128-wide spans of K per slice */
+  int grid;             /* workgroups of the first launch (row_blocks * k_slices) */
+  int launches;         /* 2 when a wide kernel's slices are added by a second launch */
+  long long scratch_bytes;  /* scratch the call needs (arrival counters + partial sums); 0 unsplit */
+} quantize_w4a4_plan_t;
+
+/* Fill *plan. Returns GEMM_W4A4_OK, or GEMM_W4A4_EINVAL for sizes
+ * quantize_w4a4_act rejects or a NULL plan. */
+int quantize_w4a4_act_plan(int M, int K, int R, quantize_w4a4_plan_t* plan);
+
 /*
  * quantize_w4a4_act_noalloc — quantize_w4a4_act for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
