@@ -236,3 +236,17 @@ def test_split_calls_on_two_streams_overlap_safely():
         _say(f"case: producer on two streams {shape}")
         for got, exp in zip(outs, w):
             assert torch.equal(got, exp), shape
+
+
+def test_plan_on_the_device_matches_the_host_model():
+    """On the GPU the planner reads the device's compute-unit count (256 on
+    MI355X): the choices pinned on the CPU (tests/test_producer_plan.py, which
+    assume 256) hold here too."""
+    import torch as _t
+    cus = _t.cuda.get_device_properties(0).multi_processor_count
+    _say(f"case: producer plan on the device ({cus} compute units)")
+    if cus != 256:
+        pytest.skip(f"{cus} compute units: the pinned plans assume 256")
+    assert w4.quantize_plan(4096, 12288, 128)["k_slices"] == 8
+    assert w4.quantize_plan(1000, 3072, 16)["k_slices"] == 3
+    assert w4.quantize_plan(4352, 10240, 32)["variant"] == 5

@@ -51,6 +51,8 @@ def test_plan_consistency_over_shapes():
             assert p["grid"] <= 256, (M, K, R, p)
         assert 0 <= p["scratch_bytes"] <= NOALLOC
         assert (p["scratch_bytes"] > 0) == (ks > 1 and R > 0), (M, K, R, p)
+        if p["scratch_bytes"]:   # 4 KiB of arrival counters, then fp32 partial sums of every slice
+            assert p["scratch_bytes"] == 4096 + p["row_blocks"] * ks * p["rows"] * R * 4, (M, K, R, p)
         assert p["launches"] == (2 if p["wide"] and p["scratch_bytes"] > 0 else 1)
 
 
