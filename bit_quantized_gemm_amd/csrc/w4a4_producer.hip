@@ -7,8 +7,8 @@
 // (sections 2 and 3.1); the scale and rounding rule is this library's
 // reading, stated in gemm_w4a4.h.
 //
-// Design. Ranks R <= 32 run a narrow kernel: one workgroup of 8 waves per 16
-// rows of x and one slice of K.
+// Design. Ranks 0 < R <= 32 run a narrow kernel: one workgroup of 8 waves per
+// 16 rows of x and one slice of K.
 //  * x is read once. K is cut into spans of 128; a workgroup takes the spans
 //    of its K slice, wave w the spans w, w+WAVES, ... of them, streamed through a
 //    private LDS ring of DEPTH slots by direct-to-LDS DMA, so the loop needs
@@ -24,10 +24,10 @@
 //    sums to a scratch buffer, and the last of them to finish (a counter per
 //    row block) adds the slices in slice order and writes lora_act_in, so
 //    the result does not depend on the order the workgroups ran in.
-// Ranks R > 32 run the wide kernel (producer_wide_kernel): four waves share
-// 128 rows, each streaming its own 32 rows of x, while the span's lora_down
-// tile is DMA'd once per workgroup into a shared LDS ring; its K slices'
-// partial sums are added by a second launch (producer_reduce_kernel).
+// Ranks R > 32, and R = 0, run the wide kernel (producer_wide_kernel): four
+// waves share 128 rows, each streaming its own 32 rows of x, while the span's
+// lora_down tile is DMA'd once per workgroup into a shared LDS ring; its K
+// slices' partial sums are added by a second launch (producer_reduce_kernel).
 //  * Lane (r, g) holds row r, k = 32g .. 32g+31 of the span: two whole
 //    16-value blocks, so a block's amax needs no cross-lane step. Scale and
 //    codes are decided exactly (see quantize_block), codes are packed by the
@@ -55,8 +55,8 @@ namespace w4a4 {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// WAVES waves per workgroup, RTILES rank tiles of 16 (R <= 16 * RTILES),
-// DEPTH ring slots per wave.
+// WAVES waves per workgroup, RTILES rank tiles of 16 (1 or 2: 0 < R <= 16 *
+// RTILES), DEPTH ring slots per wave.
 template <int WAVES_, int RTILES_, int DEPTH_>
 struct ProdCfg {
   static constexpr int WAVES = WAVES_, RTILES = RTILES_, DEPTH = DEPTH_;
@@ -71,30 +71,25 @@ struct ProdCfg {
   static constexpr int LDS = SC_OFF + WAVES * SC_BYTES;
   static constexpr int D = SPAN_BYTES / (kWave * 16);             // 16-byte DMA rounds per span
   static constexpr int NL = 4 * RTILES;                           // lora_down loads per span
-  // lora_down operands of a span, L(j), go to register set j % NSETS. With
-  // two sets (R <= 32) L(j+1) is issued early in span j, beside the refill
-  // DMA(j + DEPTH); with one set (no LoRA) the refill is issued at the end
-  // of span j.
-  static constexpr int NSETS = RTILES >= 1 && RTILES <= 2 ? 2 : 1;
-  static constexpr bool EARLY = NSETS == 2;
-  static constexpr int UNROLL = NSETS;   // set indices constant in the unrolled loop
-  // Issue order: DMA(0 .. DEPTH-2), L(0), DMA(DEPTH-1); then per
-  // span j the stores S(j-1) of the previous span's results and the pair
-  // L(j+1), DMA(j+DEPTH). A pair past the wave's last span is issued as the
-  // same loads on an empty descriptor (they read nothing), so that every
-  // count below is the same in every span. Loads complete in issue order and a store can only make a
-  // count of loads stricter, so waiting until at most X vector-memory ops
-  // remain completes every load with at least X younger loads:
-  //   DMA(j): DEPTH-1 younger pairs (DMA(0): one L fewer, waited for by the
+  // lora_down operands of a span, L(j), go to register set j % 2: L(j+1) is
+  // issued early in span j, beside the refill DMA(j + DEPTH).
+  static constexpr int NSETS = 2;
+  // Issue order: DMA(0), L(0), DMA(1); then per span j the stores S(j-1) of
+  // the previous span's results and the pair L(j+1), DMA(j+2). A pair past
+  // the wave's last span is issued as the same loads on an empty descriptor
+  // (they read nothing), so that every count below is the same in every
+  // span. Loads complete in issue order and a store can only make a count of
+  // loads stricter, so waiting until at most X vector-memory ops remain
+  // completes every load with at least X younger loads:
+  //   DMA(j): one younger pair (DMA(0): L(0) and DMA(1), waited for by the
   //           prologue itself);
-  //   L(j):   EARLY: DMA(j-1+DEPTH) and span j's pair; else DMA(j-1+DEPTH).
-  // (Counts above the counter's 63 are capped: a stricter wait.)
-  static constexpr int cap(int v) { return v < 63 ? v : 63; }
-  static constexpr int VM_X = cap((DEPTH - 1) * (D + NL));
-  static constexpr int VM_X0 = cap((DEPTH - 1) * D + NL);
-  static constexpr int VM_L = cap(EARLY ? 2 * D + NL : D);
-  static_assert(RTILES <= 2, "R <= 32: larger ranks run the wide kernel");
-  static_assert(DEPTH >= 2, "ring depth");
+  //   L(j):   DMA(j+1) and span j's pair.
+  static constexpr int VM_X = D + NL;
+  static constexpr int VM_X0 = D + NL;
+  static constexpr int VM_L = 2 * D + NL;
+  static_assert(RTILES >= 1 && RTILES <= 2, "0 < R <= 32: R = 0 and larger ranks run the wide kernel");
+  static_assert(DEPTH == 2, "the wait counts above are those of a two-slot ring");
+  static_assert(VM_L < 64, "vmcnt range");
   static_assert(RED_BYTES <= WAVES * RING, "partial sums fit in the drained rings");
   static_assert(LDS <= kLdsLimit, "LDS budget");
 };
@@ -331,9 +326,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
     for (int u = 0; u < 4; ++u) dma_buf(desc, xoff[u], slot + u * 1024);
   };
 
-  f32x4_t acc[C::RTILES > 0 ? C::RTILES : 1];
+  f32x4_t acc[C::RTILES];
 #pragma unroll
-  for (int jt = 0; jt < (C::RTILES > 0 ? C::RTILES : 1); ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int jt = 0; jt < C::RTILES; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // LoRA-down operands of this wave's j-th span into a register set (B:
   // lora_down[rank][k0 + 8i .. +7]); ranks past R re-read rank R-1 (their
@@ -345,29 +340,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   // outstanding vector-memory op (vmcnt(0)) before the first use, the ring's
   // DMAs included. The explicit waits count loads only, and scheduling fences
   // keep every use after its wait.
-  constexpr int LT = C::RTILES > 0 ? C::RTILES : 1;
+  constexpr int LT = C::RTILES;
   u32x4 lb[C::NSETS][LT][4];
   uint32_t loff[LT];
 #pragma unroll
   for (int jt = 0; jt < LT; ++jt)
-    loff[jt] = uint32_t(min(16 * jt + r, max(R, 1) - 1)) * row_bytes + uint32_t(64 * g);
+    loff[jt] = uint32_t(min(16 * jt + r, R - 1)) * row_bytes + uint32_t(64 * g);
   const uint8_t* ldb = reinterpret_cast<const uint8_t*>(p.lora_down);
   const uint32_t ld_bytes = uint32_t(R) * row_bytes;
   // span j; j >= n: a dummy on an empty descriptor (reads nothing; the set
   // is not used)
   auto load_lora = [&](u32x4 (&dst)[LT][4], int j) __attribute__((always_inline)) {
-    if constexpr (C::RTILES > 0) {
-      const bool valid = j < n;
-      const uint32_t sb = valid ? uint32_t(first + C::WAVES * j) * uint32_t(C::SPAN_K * 2) : 0u;
-      const u32x4 desc = buffer_desc(ldb + sb, valid ? ld_bytes - sb : 0u);
+    const bool valid = j < n;
+    const uint32_t sb = valid ? uint32_t(first + C::WAVES * j) * uint32_t(C::SPAN_K * 2) : 0u;
+    const u32x4 desc = buffer_desc(ldb + sb, valid ? ld_bytes - sb : 0u);
 #pragma unroll
-      for (int jt = 0; jt < LT; ++jt) {
-        const uint32_t off = loff[jt];
-        load_untracked<0>(dst[jt][0], off, desc);
-        load_untracked<16>(dst[jt][1], off, desc);
-        load_untracked<32>(dst[jt][2], off, desc);
-        load_untracked<48>(dst[jt][3], off, desc);
-      }
+    for (int jt = 0; jt < LT; ++jt) {
+      const uint32_t off = loff[jt];
+      load_untracked<0>(dst[jt][0], off, desc);
+      load_untracked<16>(dst[jt][1], off, desc);
+      load_untracked<32>(dst[jt][2], off, desc);
+      load_untracked<48>(dst[jt][3], off, desc);
     }
   };
   // the pair of span t: L(t+1), DMA(t+DEPTH)
@@ -433,7 +426,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
     }
   };
 
-  // span j uses lora_down set j % NSETS; the loop below is unrolled NSETS times
+  // span j uses lora_down set j % 2; the loop below is unrolled twice
   auto one_span = [&]<int SET>(int j) __attribute__((always_inline)) {
     constexpr int NEXT = (SET + 1) % C::NSETS;
     const int span = first + C::WAVES * j;
@@ -454,11 +447,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
       xd[4 * i + 3] = v.w;
     }
     wait_vm_lgkm0<63>();                                      // the slot is read
-    if constexpr (C::EARLY) {
-      __builtin_amdgcn_sched_barrier(0);
-      issue_pair.template operator()<NEXT>(j);                // L(j+1), DMA(j+DEPTH)
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_pair.template operator()<NEXT>(j);                  // L(j+1), DMA(j+DEPTH)
+    __builtin_amdgcn_sched_barrier(0);
     if (tail) {
       // this lane's blocks past K: zero (they add nothing to the LoRA sums
       // and are not stored)
@@ -505,24 +496,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
                                                             __builtin_bit_cast(bf16x8, lb[Q][jt][i]), acc[jt], 0, 0, 0);
       }
     };
-    if constexpr (C::RTILES > 0) lora_mfma.template operator()<SET>();
-    if constexpr (!C::EARLY) {
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (C::RTILES > 0) {
-        // the loads below overwrite the operands of the MFMAs just issued
-        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-      }
-      issue_pair.template operator()<NEXT>(j);                // L(j+1), DMA(j+DEPTH)
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    lora_mfma.template operator()<SET>();
     wait_vm_lgkm0<63>();
     if (lane < 8) scv = *reinterpret_cast<const u32x4*>(sc_stage + lane * C::ROWS);
     wait_vm_lgkm0<63>();                                      // staging read done before the next span's writes
   };
   int j0 = 0;
-  for (; j0 + C::UNROLL <= n; j0 += C::UNROLL)
-    static_for<0, C::UNROLL>([&]<int S>() __attribute__((always_inline)) { one_span.template operator()<S>(j0 + S); });
-  static_for<0, C::UNROLL - 1>([&]<int S>() __attribute__((always_inline)) {
+  for (; j0 + C::NSETS <= n; j0 += C::NSETS)
+    static_for<0, C::NSETS>([&]<int S>() __attribute__((always_inline)) { one_span.template operator()<S>(j0 + S); });
+  static_for<0, C::NSETS - 1>([&]<int S>() __attribute__((always_inline)) {
     if (j0 + S < n) one_span.template operator()<S>(j0 + S);
   });
   if (n > 0) store_span(first + C::WAVES * (n - 1));          // S(last)
@@ -531,49 +513,45 @@ __global__ __launch_bounds__(C::THREADS, 1) void producer_kernel(const ProdParam
   // past the wave's last span is never read, and without this use the
   // compiler could hand its registers to other values while the (untracked)
   // load is still in flight.
-  if constexpr (C::RTILES > 0) {
 #pragma unroll
-    for (int q = 0; q < C::NSETS; ++q)
+  for (int q = 0; q < C::NSETS; ++q)
 #pragma unroll
-      for (int jt = 0; jt < LT; ++jt)
+    for (int jt = 0; jt < LT; ++jt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(lb[q][jt][i]));
-  }
+      for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(lb[q][jt][i]));
 
-  if constexpr (C::RTILES > 0) {
-    // partial sums of the waves through the drained rings: red[wave][jt][lane]
-    __syncthreads();
+  // partial sums of the waves through the drained rings: red[wave][jt][lane]
+  __syncthreads();
 #pragma unroll
-    for (int jt = 0; jt < C::RTILES; ++jt)
-      *reinterpret_cast<f32x4_t*>(smem + ((wave * C::RTILES + jt) * kWave + lane) * 16) = acc[jt];
-    __syncthreads();
-    // wave w finishes rank tiles w, w + WAVES, ...: lane (col, g) holds rows
-    // 4g .. 4g+3 of rank 16 jt + col
-    const bool split = p.ks > 1;
-    for (int jt = wave; jt < C::RTILES; jt += C::WAVES) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int jt = 0; jt < C::RTILES; ++jt)
+    *reinterpret_cast<f32x4_t*>(smem + ((wave * C::RTILES + jt) * kWave + lane) * 16) = acc[jt];
+  __syncthreads();
+  // wave w finishes rank tiles w, w + WAVES, ...: lane (col, g) holds rows
+  // 4g .. 4g+3 of rank 16 jt + col
+  const bool split = p.ks > 1;
+  for (int jt = wave; jt < C::RTILES; jt += C::WAVES) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < C::WAVES; ++w)
-        s += *reinterpret_cast<const f32x4_t*>(smem + ((w * C::RTILES + jt) * kWave + lane) * 16);
-      const int rank = 16 * jt + (lane & 15);
-      if (rank < R) {
-        if (split) {
-          store_partial4(p.part + (uint32_t(blockIdx.x) * uint32_t(R) + uint32_t(rank)) * uint32_t(C::ROWS) +
-                             uint32_t(4 * g), s);
-        } else {
+    for (int w = 0; w < C::WAVES; ++w)
+      s += *reinterpret_cast<const f32x4_t*>(smem + ((w * C::RTILES + jt) * kWave + lane) * 16);
+    const int rank = 16 * jt + (lane & 15);
+    if (rank < R) {
+      if (split) {
+        store_partial4(p.part + (uint32_t(blockIdx.x) * uint32_t(R) + uint32_t(rank)) * uint32_t(C::ROWS) +
+                           uint32_t(4 * g), s);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = m0 + 4 * g + e;
-            if (row < M) {
-              const __bf16 v = __bf16(s[e]);   // round to nearest even
-              p.lora_act_in[uint32_t(row) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, v);
-            }
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + 4 * g + e;
+          if (row < M) {
+            const __bf16 v = __bf16(s[e]);   // round to nearest even
+            p.lora_act_in[uint32_t(row) * uint32_t(R) + uint32_t(rank)] = __builtin_bit_cast(uint16_t, v);
           }
         }
       }
     }
-    if (split) finish_split<C::ROWS, C::THREADS>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
   }
+  if (split) finish_split<C::ROWS, C::THREADS>(p, rb, m0, reinterpret_cast<uint32_t*>(smem + C::SC_OFF));
 }
 
 // ------------------------------------------------------------------ wide variant
@@ -900,12 +878,13 @@ ProdVariant prod_wide_variant() {
                      true};
 }
 
-// Instances: narrow kernels for R == 0, R <= 16, R <= 32 (8 waves of 16
-// rows, two per SIMD, two ring slots each); the wide kernel (128 rows per
-// workgroup, the lora_down tile shared through LDS) with 8, 1 and 2 rank
-// tiles. Above R = 32 the wide kernel always: a narrow kernel for R <= 128
-// (its operands in two register halves per span) was measured slower at
-// every shape tried, 256x3072 to 8192x12288 at R = 64 and 128 (1000x3072
+// Instances: narrow kernels for R <= 16 and R <= 32 (8 waves of 16 rows, two
+// per SIMD, two ring slots each); the wide kernel (128 rows per workgroup,
+// the lora_down tile shared through LDS) with 8, 1 and 2 rank tiles. R = 0
+// runs the wide kernel with one rank tile (its lora_down loads read nothing
+// and it stores no LoRA sums). Above R = 32 the wide kernel always: a
+// narrow kernel for R <= 128 (its operands in two register halves per span)
+// was measured slower at every shape tried, 256x3072 to 8192x12288 at R = 64 and 128 (1000x3072
 // R=128: 26.2 against 14.4 us; 4096x12288 R=128: 93.3 against 41.3), and
 // is not built. At R <= 32 each narrow wave reads its own copy of the
 // span's lora_down, 8x the L2 traffic of the wide kernel's shared tile, but
@@ -916,21 +895,19 @@ ProdVariant prod_wide_variant() {
 //    against 12.5; 1000x3072: 8.1 against 9.2);
 //  * R <= 16: narrow faster or equal except where its 16-row blocks
 //    overfill the compute units unevenly (4352x10240, 272 blocks: wide 27.6
-//    against 36.6 us; 8192x3072, 512 blocks: narrow 15.5 against 18.2). The
-//    same holds without LoRA (R == 0: the wide kernel's one rank tile then
-//    multiplies zeros).
-static const ProdVariant kProdVariants[] = {prod_variant<8, 0, 2>(),  prod_variant<8, 1, 2>(),
-                                            prod_variant<8, 2, 2>(),  prod_wide_variant<8>(),
-                                            prod_wide_variant<1>(), prod_wide_variant<2>()};
+//    against 36.6 us; 8192x3072, 512 blocks: narrow 15.5 against 18.2).
+static const ProdVariant kProdVariants[] = {prod_variant<8, 1, 2>(), prod_variant<8, 2, 2>(),
+                                            prod_wide_variant<8>(), prod_wide_variant<1>(),
+                                            prod_wide_variant<2>()};
 
 static int prod_variant_index(int M, int K, int R, int cus) {
-  if (R > 32) return 3;
+  if (R > 32) return 2;
+  if (R == 0) return 3;
   const int rbs = (M + 15) / 16;                        // narrow row blocks
   const int full = rbs / cus, part = rbs % cus;         // whole rounds, the last round's blocks
   const bool uneven = full >= 1 && part > 0 && part * 4 <= cus * 3;   // last round <= 3/4 full
-  if (R == 0) return uneven ? 4 : 0;
-  if (R <= 16) return uneven ? 4 : 1;
-  return rbs > cus || size_t(M) * size_t(K) >= (size_t(1) << 25) ? 5 : 2;
+  if (R <= 16) return uneven ? 3 : 0;
+  return rbs > cus || size_t(M) * size_t(K) >= (size_t(1) << 25) ? 4 : 1;
 }
 
 static std::atomic<int> g_cus[64];

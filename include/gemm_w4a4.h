@@ -236,8 +236,9 @@ int gemm_w4a4_plan_variant(int format, int variant, int M, int N, int K, int R,
  * tensor below 2^31 bytes. Alignment: x and lora_down 16 bytes, act 8,
  * lora_act_in 2. No output may overlap an input or another output
  * (GEMM_W4A4_EOVERLAP). Device pointers owned by the caller; the work is
- * enqueued on `stream` (one launch, or two when R > 32 and K is split: the
- * second adds the slices' partial sums).
+ * enqueued on `stream` (one launch, or two when a 128-row instance splits K
+ * with R > 0: the second adds the slices' partial sums; quantize_w4a4_act_plan
+ * says which).
  *
  * Scratch: when few rows meet a long K, K is split over workgroups and
  * float32 partial sums go to a scratch buffer that the library allocates per

@@ -61,9 +61,10 @@ def test_producer_workloads(name):
 # rows not a multiple of 16 (narrow kernels) or 128 (wide kernels), K % 128
 # != 0 and K % 32 == 16 (8-byte act stores), every compiled instance with R
 # not a multiple of 16 or of 4 (the reduction's one-rank path): narrow for
-# R = 0, <= 16, <= 32; wide with 8 rank tiles for R > 32, with 1 where
-# 16-row blocks would overfill the chip unevenly (4352 rows, also at R = 0)
-# and with 2 from 4097 rows or 2^25 elements at R <= 32; the wide kernels
+# R <= 16, <= 32; wide with 8 rank tiles for R > 32, with 1 at R = 0 (split
+# and unsplit, one and two spans a slice) and where 16-row blocks would
+# overfill the chip unevenly (4352 rows), and with 2 from 4097 rows or 2^25
+# elements at R <= 32; the wide kernels
 # with K split (4100 rows: 33 row blocks, the last of 4 rows) and unsplit
 # (257 or 258 row blocks)
 EDGE = [(1, 16, 0), (17, 48, 1), (33, 144, 17), (100, 528, 32), (130, 1040, 100), (31, 2064, 128),
@@ -249,4 +250,4 @@ def test_plan_on_the_device_matches_the_host_model():
         pytest.skip(f"{cus} compute units: the pinned plans assume 256")
     assert w4.quantize_plan(4096, 12288, 128)["k_slices"] == 8
     assert w4.quantize_plan(1000, 3072, 16)["k_slices"] == 3
-    assert w4.quantize_plan(4352, 10240, 32)["variant"] == 5
+    assert w4.quantize_plan(4352, 10240, 32)["variant"] == 4

@@ -96,7 +96,7 @@ def test_no_register_touched_while_its_load_is_in_flight(asm):
     # the narrow kernels (R = 0, <= 16, <= 32) load lora_down untracked; the
     # wide kernel moves every operand by DMA into LDS
     starts = [i for i, l in enumerate(asm) if re.match(r"^_ZN4w4a415producer_kernel\S*:", l)]
-    assert len(starts) >= 3
+    assert len(starts) >= 2
     total = 0
     for s in starts:
         e = next(i for i in range(s, len(asm)) if "s_endpgm" in asm[i])

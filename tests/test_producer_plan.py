@@ -1,9 +1,9 @@
 """The producer's launch plan (quantize_w4a4_act_plan, host only; CPU).
 
 The instance and K split follow measurements on MI355X (the kernel source's
-notes): narrow kernels at R <= 32 unless their 16-row blocks overfill the
-compute units unevenly or, at R <= 32, from 4097 rows or 2^25 elements; the
-wide kernel with 8 rank tiles above R = 32; K split so that every row block's
+notes): narrow kernels at 0 < R <= 32 unless their 16-row blocks overfill
+the compute units unevenly or, at R > 16, from 4097 rows or 2^25 elements;
+the wide kernel with one rank tile at R = 0 and with 8 above R = 32; K split so that every row block's
 workgroups fit one round on the compute units (256 here: no device is
 current on the CPU, and MI355X has 256). These tests pin those decisions and
 the plan's own consistency."""
@@ -17,17 +17,18 @@ NOALLOC = 4096 + (16 << 20)
 
 
 @pytest.mark.parametrize("shape,variant,wide,rank_tiles,k_slices,launches", [
-    ((4096, 3072, 32), 2, 0, 2, 1, 1),      # qkv: narrow, 256 row blocks fill the chip
-    ((4096, 3072, 16), 1, 0, 1, 1, 1),
-    ((4096, 3072, 0), 0, 0, 0, 1, 1),
-    ((1000, 3072, 16), 1, 0, 1, 3, 1),      # ragged: narrow, one span per wave
-    ((4096, 12288, 128), 3, 1, 8, 8, 2),    # mlp_down: wide, reduction launch
-    ((4096, 12288, 32), 5, 1, 2, 8, 2),     # 2^25.6 elements at R = 32: wide
-    ((4352, 10240, 16), 4, 1, 1, 7, 2),     # 272 narrow blocks for 256 CUs: wide
-    ((4352, 10240, 0), 4, 1, 1, 7, 1),      # the same without LoRA: no partial sums
-    ((8192, 3072, 16), 1, 0, 1, 1, 1),      # 512 narrow blocks, two even rounds: narrow
-    ((8192, 3072, 32), 5, 1, 2, 4, 2),      # more than 4096 rows at R = 32: wide
-    ((256, 3072, 64), 3, 1, 8, 24, 2),      # two row blocks: one span per slice
+    ((4096, 3072, 32), 1, 0, 2, 1, 1),      # qkv: narrow, 256 row blocks fill the chip
+    ((4096, 3072, 16), 0, 0, 1, 1, 1),
+    ((4096, 3072, 0), 3, 1, 1, 8, 1),       # no LoRA: the wide kernel, no partial sums
+    ((1000, 3072, 16), 0, 0, 1, 3, 1),      # ragged: narrow, one span per wave
+    ((4096, 12288, 128), 2, 1, 8, 8, 2),    # mlp_down: wide, reduction launch
+    ((4096, 12288, 32), 4, 1, 2, 8, 2),     # 2^25.6 elements at R = 32: wide
+    ((4352, 10240, 16), 3, 1, 1, 7, 2),     # 272 narrow blocks for 256 CUs: wide
+    ((4352, 10240, 0), 3, 1, 1, 7, 1),      # the same without LoRA: no partial sums
+    ((8192, 3072, 16), 0, 0, 1, 1, 1),      # 512 narrow blocks, two even rounds: narrow
+    ((8192, 3072, 32), 4, 1, 2, 4, 2),      # more than 4096 rows at R = 32: wide
+    ((256, 3072, 64), 2, 1, 8, 24, 2),      # two row blocks: one span per slice
+    ((1, 16, 0), 3, 1, 1, 1, 1),            # R = 0 always runs the wide kernel
 ])
 def test_plan_choices(shape, variant, wide, rank_tiles, k_slices, launches):
     p = w4.quantize_plan(*shape)
