@@ -511,8 +511,11 @@ def test_misaligned_act_scales(shift):
 # Every compiled tile instance of both formats through gemm_w4a4_run, on the
 # fast flavour (aligned), the act-scale window flavour (M % 8 != 0) and the
 # general one (K % 32 != 0, R % 8 != 0), bf16 and fp16: the solver may pick
-# any of them, and callers may name one.
-EVERY_VARIANT_SHAPES = [(520, 392, 640, 32), (517, 392, 640, 24), (264, 200, 272, 20)]
+# any of them, and callers may name one. The fast and window flavours also
+# with a partial last stage (K % 128 == 96: pieces past K read the next row
+# or, past the tensor's end, nothing).
+EVERY_VARIANT_SHAPES = [(520, 392, 640, 32), (517, 392, 640, 24), (264, 200, 272, 20), (520, 392, 608, 32),
+                        (517, 392, 608, 32)]
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
