@@ -409,8 +409,8 @@ def main() -> int:
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this operator needs no cross-GPU work and "
-              "this build runs on a single MI355X (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the operator needs no cross-GPU work, and a "
+              "sharded layer runs one independent launch per GPU (use --gpus 1)", file=sys.stderr)
         return 2
 
     import numpy as np
