@@ -201,9 +201,11 @@ def calibrate(w4, synthetic, rounds=3, reps=20) -> int:
     """Every compiled tile instance of each format at CAL_SHAPES. One JSON
     line per (format, shape): average launch time of each instance (best of
     `rounds` interleaved rounds of `reps` launches, after clock settling), the
-    solver's pick, the fastest, and each instance's measured time per output
-    element of one round of tiles on the busiest compute unit, relative to
-    instance 0 -- the quantity the solver's cost table holds."""
+    solver's plan (one instance, or a main instance and a tail instance over
+    the last rows) timed the same way, the fastest single instance, and each
+    instance's measured time per output element of one round of tiles on the
+    busiest compute unit, relative to instance 0 -- the quantity the solver's
+    cost table holds."""
     import numpy as np
     import torch
     dev = torch.device("cuda:0")
@@ -237,16 +239,18 @@ def calibrate(w4, synthetic, rounds=3, reps=20) -> int:
             while (time.perf_counter() - t0) < 0.3:
                 run(0, 8)
                 torch.cuda.synchronize()
-            us = [float("inf")] * nvar
+            us = [float("inf")] * (nvar + 1)          # the last entry: the solver's plan
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             for r in range(rounds):
-                for v in [(r + i) % nvar for i in range(nvar)]:
+                for i in [(r + i) % (nvar + 1) for i in range(nvar + 1)]:
+                    v = -1 if i == nvar else i
                     run(v, 3)
                     e0.record(stream)
                     run(v, reps)
                     e1.record(stream)
                     torch.cuda.synchronize()
-                    us[v] = min(us[v], e0.elapsed_time(e1) * 1e3 / reps)
+                    us[i] = min(us[i], e0.elapsed_time(e1) * 1e3 / reps)
+            plan_us = us.pop()
             per_elem = []
             for v in range(nvar):
                 p = w4.plan_variant(M, N, K, R, v, fmt=fmt)
@@ -254,11 +258,13 @@ def calibrate(w4, synthetic, rounds=3, reps=20) -> int:
                 rounds_v = -(-p["grid"] // slots)
                 per_cu = min(p["occupancy"], -(-p["grid"] // 256))
                 per_elem.append(us[v] / (rounds_v * per_cu * p["block_m"] * p["block_n"]))
-            pick = w4.plan(M, N, K, R, fmt=fmt)["variant"]
+            pl = w4.plan(M, N, K, R, fmt=fmt)
+            plan = f"{pl['variant']}" + (f" + {pl['tail_variant']} on {pl['tail_rows']} rows"
+                                         if pl["tail_variant"] >= 0 else "")
             print(json.dumps({"calibrate": fmt, "shape": name, "M": M, "N": N, "K": K, "R": R,
-                              "us": [round(v, 2) for v in us], "pick": pick,
+                              "us": [round(v, 2) for v in us], "plan": plan, "plan_us": round(plan_us, 2),
                               "fastest": int(np.argmin(us)),
-                              "pick_vs_fastest": round(us[pick] / min(us), 3),
+                              "plan_vs_fastest": round(plan_us / min(us), 3),
                               "cost_rel_v0": [round(c / per_elem[0], 3) for c in per_elem]}), flush=True)
     return 0
 
@@ -534,7 +540,9 @@ def main() -> int:
 
     flops = wl.flops()
     ms_per_step = region_ms / a.steps
-    avg_launch_ms = ms_per_step   # one launch per step, back to back
+    # one operator call per step, back to back: one launch, or two when the
+    # plan runs a tail instance over the last rows (their sum, then)
+    avg_launch_ms = ms_per_step
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     value = flops * a.steps / (region_ms * 1e-3) / 1e12
     traffic = None if a.shape else committed_traffic(a.workload, a.fmt)
@@ -566,7 +574,10 @@ def main() -> int:
                                 + f", LoRA {a.dtype}, out {a.dtype}"),
                    "tile": f"{plan['block_m']}x{plan['block_n']}", "grid": plan["grid"],
                    "variant": plan["variant"], "ring_stages": plan["stages"],
-                   "lora_place": plan["lora_place"], "solver_choice": a.variant < 0},
+                   "lora_place": plan["lora_place"], "solver_choice": a.variant < 0,
+                   "tail": (None if plan["tail_variant"] < 0 else
+                            f"{plan['tail_block_m']}x{plan['tail_block_n']} (variant {plan['tail_variant']}) over "
+                            f"the last {plan['tail_rows']} rows, grid {plan['tail_grid']}, a second launch")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),

@@ -29,7 +29,8 @@ struct Params {
   const uint16_t* lora_up;
   uint16_t* out;
   int M, N, K, R;
-  int tiles_m, tiles_n;
+  int tiles_m, tiles_n;   // tile rows and columns of this launch
+  int tm0;                // its first tile row (in this instance's BM rows) within the M rows
 };
 
 // 16-byte chunk c of a 64-byte row is stored at chunk position c ^ swz(row).

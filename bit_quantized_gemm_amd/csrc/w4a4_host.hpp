@@ -92,6 +92,7 @@ inline void fill_static(const VariantDesc& v, int idx, gemm_w4a4_plan_t* pl) {
   pl->regs_limit = 512 / waves_per_simd;
   pl->flavour = -1;
   pl->vgprs = pl->agprs = pl->sgprs = -1;
+  pl->tail_variant = -1;
 }
 
 // Registers of the kernel a launch of flavour `flavour` would run (bf16 output).
@@ -104,38 +105,99 @@ inline void fill_registers(const VariantDesc& v, int flavour, gemm_w4a4_plan_t* 
   }
 }
 
-// The solver's choice among compiled instances: for each, the rounds the chip
+// The solver's estimate for instance x over `rows` rows: the rounds the chip
 // needs (tiles / (CUs x workgroups resident per CU)) times the time of one
 // round (workgroups on the busiest CU x tile elements x the instance's cost
-// per element); the smallest estimate wins, ties to the earlier instance.
-inline int choose_variant(const VariantDesc* vs, int n, int M, int N) {
-  int best = 0;
-  double best_cost = 0.0;
-  for (int i = 0; i < n; ++i) {
-    const VariantDesc& x = vs[i];
-    const long tiles = long((M + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
-    const long slots = long(kNumCUs) * x.occ;
-    const long rounds = (tiles + slots - 1) / slots;
-    const long per_cu = std::min<long>(x.occ, (tiles + kNumCUs - 1) / kNumCUs);
-    const double cost = double(rounds) * double(per_cu) * x.block_m * x.block_n * x.cost;
-    if (i == 0 || cost < best_cost) {
-      best = i;
-      best_cost = cost;
-    }
-  }
-  return best;
+// per element).
+inline double estimate(const VariantDesc& x, int rows, int N) {
+  const long tiles = long((rows + x.block_m - 1) / x.block_m) * long((N + x.block_n - 1) / x.block_n);
+  const long slots = long(kNumCUs) * x.occ;
+  const long rounds = (tiles + slots - 1) / slots;
+  const long per_cu = std::min<long>(x.occ, (tiles + kNumCUs - 1) / kNumCUs);
+  return double(rounds) * double(per_cu) * x.block_m * x.block_n * x.cost;
 }
 
-// Problem-size part of a plan for instance `v` (index `idx`).
-inline int plan_for(const VariantDesc& v, int idx, int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
+// The solver's choice among compiled instances: the smallest estimate of one
+// instance over all M rows (ties to the earlier instance), or of a main
+// instance over its first M1 rows followed by a second launch of a tail
+// instance over the last M - M1 rows. M1 is a whole number of the main
+// instance's tile rows: those of its whole rounds (k times the tile rows one
+// round holds), or all of its whole tile rows when M is not a multiple of
+// its BM. The tail instance's BM divides the main one's, so its first tile
+// row M1 / BM_tail is whole. At M = 17 x 256 rows this runs 16 tile rows of
+// 256 x 192 in one round and the 17th on 64-row tiles, instead of a second
+// round for 16 tiles or a smaller tile everywhere.
+//
+// The estimate has no K: it counts rounds of k-loops. A second launch adds
+// what a launch costs besides its k-loop (ring fill, epilogue, the store of
+// its tiles), about `launch_stages` k-stages of a full round of instance 0.
+// A split is taken only when its estimate plus that share of a round of
+// K/128 stages is below the best single launch.
+struct Choice {
+  int main, tail;   // instances; tail -1: one launch over all M rows
+  int main_rows;    // rows of the main launch (M when there is no tail)
+};
+inline Choice choose_plan(const VariantDesc* vs, int n, int M, int N, int K, double launch_stages) {
+  Choice best{0, -1, M};
+  double best_cost = estimate(vs[0], M, N);
+  for (int i = 1; i < n; ++i) {
+    const double c = estimate(vs[i], M, N);
+    if (c < best_cost) {
+      best = Choice{i, -1, M};
+      best_cost = c;
+    }
+  }
+  Choice split{0, -1, M};
+  double split_cost = 0.0;
+  auto consider = [&](int i, int m1) {
+    if (m1 <= 0 || m1 >= M) return;
+    for (int j = 0; j < n; ++j) {
+      if (vs[i].block_m % vs[j].block_m != 0) continue;
+      const double c = estimate(vs[i], m1, N) + estimate(vs[j], M - m1, N);
+      if (split.tail < 0 || c < split_cost) {
+        split = Choice{i, j, m1};
+        split_cost = c;
+      }
+    }
+  };
+  for (int i = 0; i < n; ++i) {
+    const VariantDesc& x = vs[i];
+    consider(i, M / x.block_m * x.block_m);
+    const long round_rows = long(kNumCUs) * x.occ / ((N + x.block_n - 1) / x.block_n);   // tile rows a round holds
+    for (long k = 1; round_rows > 0 && k <= 64 && k * round_rows * x.block_m < M; ++k)
+      consider(i, int(k * round_rows * x.block_m));
+  }
+  const double round0 = double(vs[0].occ) * vs[0].block_m * vs[0].block_n * vs[0].cost;
+  const double k_stages = double((K + vs[0].block_k - 1) / vs[0].block_k);
+  return split.tail >= 0 && split_cost + launch_stages / k_stages * round0 < best_cost ? split : best;
+}
+
+// Problem-size part of a plan for instance `v` (index `idx`) over the first
+// `rows` of the M rows (all of them, or a split's main launch).
+inline int plan_for(const VariantDesc& v, int idx, int rows, int N, int K, int R, gemm_w4a4_plan_t* pl) {
   fill_static(v, idx, pl);
-  pl->tiles_m = (M + v.block_m - 1) / v.block_m;
+  pl->tiles_m = (rows + v.block_m - 1) / v.block_m;
   pl->tiles_n = (N + v.block_n - 1) / v.block_n;
   const long grid = long(pl->tiles_m) * pl->tiles_n;
   if (grid > 0x7fffffffL) return GEMM_W4A4_EINVAL;
   pl->grid = int(grid);
   pl->k_stages = (K + v.block_k - 1) / v.block_k;
   pl->lora_steps = (R + 15) / 16;
+  pl->tail_variant = -1;
+  pl->tail_rows = pl->tail_block_m = pl->tail_block_n = pl->tail_grid = 0;
+  return GEMM_W4A4_OK;
+}
+
+// The plan of a solver choice `c` (its tail fields filled when it splits).
+inline int plan_choice(const VariantDesc* vs, const Choice& c, int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
+  const int rc = plan_for(vs[c.main], c.main, c.main_rows, N, K, R, pl);
+  if (rc != GEMM_W4A4_OK || c.tail < 0) return rc;
+  const VariantDesc& t = vs[c.tail];
+  pl->tail_variant = c.tail;
+  pl->tail_rows = M - c.main_rows;
+  pl->tail_block_m = t.block_m;
+  pl->tail_block_n = t.block_n;
+  pl->tail_grid = (pl->tail_rows + t.block_m - 1) / t.block_m * ((N + t.block_n - 1) / t.block_n);
   return GEMM_W4A4_OK;
 }
 
@@ -169,7 +231,9 @@ inline int check_call(const CallArgs& a, int block) {
   return GEMM_W4A4_OK;
 }
 
-inline int launch_kernel(const void* kernel, const gemm_w4a4_plan_t& pl, const CallArgs& a) {
+// One launch of `kernel` (instance v) over tile rows [tm0, tm0 + tiles_m) of
+// its BM rows.
+inline int launch_kernel(const void* kernel, const VariantDesc& v, int tiles_m, int tm0, const CallArgs& a) {
   Params prm;
   prm.act = a.act;
   prm.ascales = a.ascales;
@@ -184,12 +248,26 @@ inline int launch_kernel(const void* kernel, const gemm_w4a4_plan_t& pl, const C
   prm.N = a.N;
   prm.K = a.K;
   prm.R = a.R;
-  prm.tiles_m = pl.tiles_m;
-  prm.tiles_n = pl.tiles_n;
+  prm.tiles_m = tiles_m;
+  prm.tiles_n = (a.N + v.block_n - 1) / v.block_n;
+  prm.tm0 = tm0;
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(kernel, dim3(pl.grid), dim3(pl.threads), args, 0,
+  const hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(long(tiles_m) * prm.tiles_n)), dim3(v.threads), args, 0,
                                        static_cast<hipStream_t>(a.stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}
+
+// The launches of a plan: the main instance, then the tail instance, if any,
+// over the last rows (the same flavour rule; `kernel_of` maps an instance to
+// the kernel of that flavour and output type).
+template <class KernelOf>
+inline int launch_plan(const VariantDesc* vs, const gemm_w4a4_plan_t& pl, const CallArgs& a, KernelOf kernel_of) {
+  const VariantDesc& v = vs[pl.variant];
+  int rc = launch_kernel(kernel_of(v), v, pl.tiles_m, 0, a);
+  if (rc != GEMM_W4A4_OK || pl.tail_variant < 0) return rc;
+  const VariantDesc& t = vs[pl.tail_variant];
+  const int main_rows = a.M - pl.tail_rows;
+  return launch_kernel(kernel_of(t), t, (pl.tail_rows + t.block_m - 1) / t.block_m, main_rows / t.block_m, a);
 }
 
 }  // namespace w4a4

@@ -165,6 +165,17 @@ typedef struct {
   int regs_limit;     /* VGPR + AGPR a lane may hold at this occupancy (512 per SIMD lane, shared) */
   int k_groups;       /* waves sharing each wave tile, splitting every stage's k-steps between them
                          (threads = 64 * waves_m * waves_n * k_groups) */
+  /* A split plan (the solver's choice only, tail_variant >= 0): the fields
+   * above describe a first launch over the first M - tail_rows rows (whole
+   * tile rows: tiles_m * block_m of them), and a second launch of instance
+   * tail_variant, whose block_m divides the first one's, covers the last
+   * tail_rows rows in tail_grid workgroups. Both run on the call's stream, in order, on
+   * disjoint output rows. Not split: tail_variant -1, the others 0. */
+  int tail_variant;
+  int tail_rows;
+  int tail_block_m;
+  int tail_block_n;
+  int tail_grid;
 } gemm_w4a4_plan_t;
 
 /* Fill *plan for (M, N, K, R). Returns GEMM_W4A4_OK or GEMM_W4A4_EINVAL

@@ -23,6 +23,12 @@ int main(void) {
   check(pl.block_m * pl.tiles_m >= 4096 && pl.block_n * pl.tiles_n >= 3072, "plan covers M and N");
   check(pl.grid == pl.tiles_m * pl.tiles_n && pl.k_stages * pl.block_k >= 3072, "grid and k stages");
   check(pl.lds_bytes > 0 && pl.lds_bytes <= pl.lds_limit, "LDS within the limit");
+  check(pl.tail_variant == -1 && pl.tail_rows == 0, "4096 rows: one launch");
+  check(gemm_w4a4_plan(4352, 3072, 3840, 128, &pl) == GEMM_W4A4_OK && pl.tail_variant >= 0 &&
+            pl.block_m * pl.tiles_m + pl.tail_rows == 4352 && pl.block_m % pl.tail_block_m == 0 &&
+            pl.tail_grid == (pl.tail_rows + pl.tail_block_m - 1) / pl.tail_block_m *
+                                ((3072 + pl.tail_block_n - 1) / pl.tail_block_n),
+        "4352 rows: whole tile rows, then a tail launch over the rest");
   check(gemm_w4a4_plan(4096, 3072, 3000, 32, &pl) == GEMM_W4A4_EINVAL, "K % 16 != 0 rejected");
   check(gemm_mxfp4_plan(64, 64, 48, 0, &pl) == GEMM_W4A4_EINVAL, "MXFP4 K % 32 != 0 rejected");
 
@@ -46,5 +52,8 @@ int main(void) {
                        (const uint8_t*)16, (const float*)16, (const float*)16, NULL, NULL,
                        (uint16_t*)4096, 16, 16, 32, GEMM_W4A4_MAX_R + 1, NULL) == GEMM_W4A4_EINVAL,
         "R past the maximum rejected");
+  /* the struct sizes, for the Python binding's mirror of them */
+  printf("sizeof gemm_w4a4_plan_t %d\n", (int)sizeof(gemm_w4a4_plan_t));
+  printf("sizeof quantize_w4a4_plan_t %d\n", (int)sizeof(quantize_w4a4_plan_t));
   return failures == 0 ? 0 : 1;
 }

@@ -24,4 +24,11 @@ def test_c_program_uses_the_c_abi(tmp_path):
     assert res.returncode == 0, res.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
-    assert "FAIL" not in run.stdout and run.stdout.count("ok") >= 12, run.stdout
+    assert "FAIL" not in run.stdout and run.stdout.count("ok") >= 14, run.stdout
+    # the binding's ctypes mirrors of the plan structs have the C layout's size
+    import ctypes
+
+    from bit_quantized_gemm_amd._native import Plan, QuantizePlan
+    sizes = dict(line.rsplit(" ", 1) for line in run.stdout.splitlines() if line.startswith("sizeof"))
+    assert int(sizes["sizeof gemm_w4a4_plan_t"]) == ctypes.sizeof(Plan)
+    assert int(sizes["sizeof quantize_w4a4_plan_t"]) == ctypes.sizeof(QuantizePlan)

@@ -451,22 +451,26 @@ def test_concurrent_streams():
         assert torch.equal(oa, ra) and torch.equal(ob, rb)
 
 
-# shapes whose plan is the 256x128 instance (more than one round of 128x128
-# tiles), with edges in m and n: the fast flavour (M % 8 == 0), the general
-# one through M % 8 != 0, and through K % 32 != 0
+# the 256x128 instance forced over more than one round of 128x128 tiles, with
+# edges in m and n: the fast flavour (M % 8 == 0), the general one through
+# M % 8 != 0, and through K % 32 != 0 (the solver may split these shapes)
 TILE_256x128 = [(4320, 3064, 384, 40), (4316, 3064, 384, 40), (4300, 3000, 272, 24)]
 
 
 @pytest.mark.parametrize("shape", TILE_256x128, ids=["x".join(map(str, s)) for s in TILE_256x128])
 def test_256x128_instance(shape):
     M, N, K, R = shape
-    plan = w4.plan(*shape)
-    assert (plan["block_m"], plan["block_n"]) == (256, 128)
-    _say(f"case: 256x128 instance, M={M} N={N} K={K} R={R}, every element")
+    v = [i for i, d in enumerate(w4.variants("nvfp4")) if (d["block_m"], d["block_n"]) == (256, 128)][0]
+    _say(f"case: 256x128 instance (variant {v}), M={M} N={N} K={K} R={R}, every element")
     x = synthetic.custom_inputs(M, N, K, R, seed=M + N + K + R)
-    got = run_gpu(x)
+    d = to_device(x)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    rc = w4.run_raw("nvfp4", False, v, *[d[k].data_ptr() for k in ARGS], out.data_ptr(), M, N, K, R,
+                    torch.cuda.current_stream().cuda_stream)
+    assert rc == w4.OK, rc
+    torch.cuda.synchronize()
     y, T = full_reference(x)
-    assert_parity(got, y, T, f"256x128 {shape}")
+    assert_parity(out.view(torch.int16).cpu().numpy().view(np.uint16), y, T, f"256x128 {shape}")
 
 
 # token counts that are not a multiple of 8 on the large tiles: the fast
@@ -627,3 +631,39 @@ def test_prefetched_lora_chunk_partial_rank(shape, dtype):
     got = run_gpu(x)
     y, T = full_reference(x)
     assert_parity(got, y, T, f"side chunk R={R} {dtype}", dtype)
+
+
+# Split plans: the solver runs whole rounds of one instance over the first
+# rows and a second launch of another over the rest (M = 4096 + 100 and
+# 4096 + 257 rows at N = 3072, where 16 tile rows of 256 x 192 fill one
+# round; K long enough that the second launch pays for itself): both
+# launches' rows, edge tiles past M in the tail, the act-scale window flavour
+# in both launches (M % 8 != 0), MXFP4 (whose tail instance takes another
+# flavour than its main one at M % 4 != 0), fp16 output. Every element of the
+# first 64 rows, of the main launch's last tile row and of every tail row.
+SPLIT = [("nvfp4", "bf16", (4196, 3072, 3584, 32)), ("nvfp4", "bf16", (4353, 3072, 3840, 16)),
+         ("nvfp4", "f16", (4196, 3072, 3584, 32)), ("mxfp4", "bf16", (4196, 3072, 10240, 32)),
+         ("mxfp4", "bf16", (4353, 3072, 10240, 16))]
+
+
+@pytest.mark.parametrize("fmt,dtype,shape", SPLIT, ids=[f"{f}-{d}-" + "x".join(map(str, s)) for f, d, s in SPLIT])
+def test_split_plan(fmt, dtype, shape):
+    M, N, K, R = shape
+    p = w4.plan(M, N, K, R, fmt=fmt)
+    m1 = p["tiles_m"] * p["block_m"]
+    _say(f"case: {fmt} split plan M={M} N={N} K={K} R={R} {dtype}: v{p['variant']} over "
+         f"{m1} rows, v{p['tail_variant']} over the last {p['tail_rows']}")
+    assert p["tail_variant"] >= 0 and m1 + p["tail_rows"] == M
+    x = synthetic.custom_inputs(M, N, K, R, seed=M + R, dtype=dtype, fmt=fmt)
+    x["dtype"] = dtype
+    d = to_device(x)
+    half = torch.float16 if dtype == "f16" else torch.bfloat16
+    fn = w4.gemm_mxfp4 if fmt == "mxfp4" else w4.gemm_w4a4
+    out = fn(d["act"], d["ascales"], d["wgt"], d["wscales"], d["wcscale"], d["bias"],
+             d["lora_act_in"], d["lora_up"], dtype=half)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(64), np.arange(m1 - p["block_m"], M)])
+    refrows = ref.reference_rows_mx if fmt == "mxfp4" else ref.reference_rows
+    y, T = refrows(x, rows)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    assert_parity(got, y, T, f"{fmt} split {shape} {dtype}, {rows.size} rows", dtype)
