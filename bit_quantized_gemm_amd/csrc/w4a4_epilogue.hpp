@@ -349,7 +349,9 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   wait_vm_lgkm0<63>();
   wg_barrier();
 
-  // LDS -> HBM in 16-byte pieces of whole output rows (8 columns each).
+  // LDS -> HBM in 16-byte pieces of whole output rows (8 columns each), as
+  // non-temporal stores: the output is not read again by this launch, and
+  // keeping it out of the way of the operands in L2 measured 1-2 % faster.
   constexpr int PIECES_PER_ROW = C::BN / 8;
   constexpr int PIECES = C::BM * PIECES_PER_ROW;
   static_assert(PIECES % C::THREADS == 0, "whole store rounds");
@@ -366,7 +368,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
       const int row = m0 + rl;
       if (row >= M) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
-      *reinterpret_cast<u32x4*>(p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl)) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl)));
     }
     return;
   }
@@ -380,7 +382,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rl * OUT_STRIDE + cl * 2);
     uint16_t* dst = p.out + uint32_t(row) * uint32_t(N) + uint32_t(n0 + cl);
     if (vec_ok && left >= 8) {
-      *reinterpret_cast<u32x4*>(dst) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
