@@ -577,7 +577,9 @@ def main() -> int:
                    "lora_place": plan["lora_place"], "solver_choice": a.variant < 0,
                    "tail": (None if plan["tail_variant"] < 0 else
                             f"{plan['tail_block_m']}x{plan['tail_block_n']} (variant {plan['tail_variant']}) over "
-                            f"the last {plan['tail_rows']} rows, grid {plan['tail_grid']}, a second launch")},
+                            f"the last {plan['tail_rows']} rows, grid {plan['tail_grid']}"
+                            + (f", its K in {plan['tail_splits']} slices added by a reduction, both before"
+                               if plan["tail_splits"] > 1 else ", a second launch"))},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),

@@ -27,7 +27,7 @@ _PLAN_FIELDS = ("variant", "block_m", "block_n", "block_k", "stages", "waves_m",
                 "grid", "k_stages", "lora_steps", "occupancy", "policy", "lora_place",
                 "lds_ring_bytes", "lds_side_bytes", "flavour", "vgprs", "agprs", "sgprs",
                 "regs_limit", "k_groups", "tail_variant", "tail_rows", "tail_block_m", "tail_block_n",
-                "tail_grid")
+                "tail_grid", "tail_splits")
 
 
 _QPLAN_FIELDS = ("variant", "wide", "rank_tiles", "rows", "threads", "lds_bytes", "row_blocks", "k_slices",

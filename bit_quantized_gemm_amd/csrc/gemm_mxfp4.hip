@@ -66,7 +66,10 @@ constexpr bool kAwinRoom = C::KBLK * (C::BM + 4 + C::BN) <= C::SCALE_ROUNDS * C:
 // of BM + 4 bytes from the 4-byte boundary at or below its first byte, so
 // that its 4-byte DMA pieces stay aligned when M % 4 != 0; the reader adds the
 // row's offset into its window (see act_window).
-template <class C, bool GENERAL, bool F16, bool AWIN = false>
+// PART (fast flavour without windows, K % 128 == 0): workgroup (tile,
+// blockIdx.y) runs slice blockIdx.y of gridDim.y of the tile's K stages and
+// stores float32 sums (see epilogue); split_k_reduce adds the slices.
+template <class C, bool GENERAL, bool F16, bool AWIN = false, bool PART = false>
 __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mxfp4_kernel(
     const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
@@ -96,8 +99,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = (p.tm0 + tm) * C::BM, n0 = tn * C::BN;
-  const int M = p.M, N = p.N, K = p.K;
-  const int rowbytes = K >> 1;
+  const int M = p.M, N = p.N;
+  const int rowbytes = p.K >> 1;             // packed row stride
+  // the stages [ks0, ks1) this workgroup runs: all, or its K slice; the
+  // operand pointers start at the first of them
+  static_assert(!PART || (!GENERAL && !AWIN), "K slices run on the fast flavour");
+  const int nst_all = (p.K + C::BK - 1) / C::BK;
+  const int ks0 = PART ? int(blockIdx.y) * nst_all / int(gridDim.y) : 0;
+  const int ks1 = PART ? (int(blockIdx.y) + 1) * nst_all / int(gridDim.y) : nst_all;
+  const uint8_t* const act = p.act + (PART ? size_t(ks0) * C::ROW_BYTES : 0);
+  const uint8_t* const wgt = p.wgt + (PART ? size_t(ks0) * C::ROW_BYTES : 0);
+  const uint8_t* const ascales = p.ascales + (PART ? size_t(ks0) * C::KBLK * size_t(M) : 0);
+  const uint8_t* const wscales = p.wscales + (PART ? size_t(ks0) * C::KBLK * size_t(N) : 0);
+  const int K = PART ? (ks1 - ks0) * C::BK : p.K;   // k of this workgroup
+  const int kbytes = K >> 1;                 // packed bytes of a row it reads
   const int KB = K >> 5;                     // scale blocks along k
   const int nst = (K + C::BK - 1) / C::BK;
   const int last = nst - 1;
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   // packed region holds the bytes of data chunk cp ^ swz(row) of its row.
   const int dma_row0 = tid * 16 / C::ROW_BYTES;
   const uint32_t dma_inrow = uint32_t(((tid & 3) ^ swz(dma_row0)) * 16);
-  const int full_stages = rowbytes / C::ROW_BYTES;
+  const int full_stages = kbytes / C::ROW_BYTES;
   auto dma_packed = [&](int st, int buf, int u) __attribute__((always_inline)) {
     uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
     const bool is_b = u >= A_ROUNDS;
@@ -115,9 +130,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     const uint32_t k0 = uint32_t(st * C::ROW_BYTES);
     // pieces past the row end (partial last stage only) re-read the row start;
     // their 32-blocks are masked to zero where the operands are used
-    const uint32_t kin = (st >= full_stages && dma_inrow + k0 + 16 > uint32_t(rowbytes)) ? 0u : k0 + dma_inrow;
+    const uint32_t kin = (st >= full_stages && dma_inrow + k0 + 16 > uint32_t(kbytes)) ? 0u : k0 + dma_inrow;
     const int row = min((is_b ? n0 : m0) + dma_row0 + ur * ROWS_PER_ROUND, (is_b ? N : M) - 1);
-    const uint8_t* src = (is_b ? p.wgt : p.act) + (uint32_t(row) * uint32_t(rowbytes) + kin);
+    const uint8_t* src = (is_b ? wgt : act) + (uint32_t(row) * uint32_t(rowbytes) + kin);
     dma<16>(src, stage + (u * C::THREADS + wave_u * 64) * 16);
   };
   // ---- act-scale windows (AWIN). Row stride of the act scales in LDS: BM,
@@ -150,13 +165,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
     if (o < C::KBLK * SW) {
       const int kb = min(st * C::KBLK + o / SW, KB - 1);
       if constexpr (AWIN)
-        src = p.ascales + act_window(kb) + uint32_t(o % SW);
+        src = ascales + act_window(kb) + uint32_t(o % SW);
       else
-        src = p.ascales + uint32_t(kb) * uint32_t(M) + uint32_t(min(m0 + o % C::BM, M - 4));
+        src = ascales + uint32_t(kb) * uint32_t(M) + uint32_t(min(m0 + o % C::BM, M - 4));
     } else {
       const int ob = min(o - C::KBLK * SW, C::KBLK * C::BN - 4);
       const int kb = min(st * C::KBLK + ob / C::BN, KB - 1);
-      src = p.wscales + uint32_t(kb) * uint32_t(N) + uint32_t(min(n0 + ob % C::BN, N - 4));
+      src = wscales + uint32_t(kb) * uint32_t(N) + uint32_t(min(n0 + ob % C::BN, N - 4));
     }
     dma<4>(src, stage + C::SA_OFF + (v * C::THREADS + wave_u * 64) * 4);
   };
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
       return b0 | (b1 << 8);
     } else {
       const bool is_a = t < C::MI;
-      const uint8_t* src = is_a ? p.ascales : p.wscales;
+      const uint8_t* src = is_a ? ascales : wscales;
       const int nrows = is_a ? M : N;
       const int row = min((is_a ? m0 + ra + 32 * t : n0 + rb + 32 * (t - C::MI)), nrows - 1);
       const int kb0 = min(st * C::KBLK + g, KB - 1), kb1 = min(st * C::KBLK + 2 + g, KB - 1);
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_mx
   }
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
-  epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0, epi_regs);
+  epilogue<C, GENERAL, F16, PART>(acc, p, smem, tid, m0, n0, epi_regs);
 }
 
 // ------------------------------------------------------------------ host side
@@ -314,6 +329,19 @@ static constexpr int kNumMxVariants = int(sizeof(kMxVariants) / sizeof(kMxVarian
 // 256x192 tiles: a 4096x3072 launch over one stage (K = 128) takes about
 // 10.6 us against 0.78 us per added stage.
 static constexpr double kMxLaunchStages = 12.7;
+// The instance compiled with K-sliced workgroups (128x128), as the tail of a
+// split plan, its kernels [F16] and the reduction.
+static constexpr int kMxPartVariant = 1;
+static const void* const kMxPartKernel[2] = {
+    reinterpret_cast<const void*>(gemm_mxfp4_kernel<MxCfg128x128, false, false, false, true>),
+    reinterpret_cast<const void*>(gemm_mxfp4_kernel<MxCfg128x128, false, true, false, true>)};
+static const void* const kMxReduceKernel[2] = {reinterpret_cast<const void*>(split_k_reduce<false>),
+                                               reinterpret_cast<const void*>(split_k_reduce<true>)};
+// K slices need whole stages, N % 8 == 0 and the fast flavour without act-scale
+// windows on the 128-row tail (M % 4 == 0).
+static bool mx_slices_ok(int M, int N, int K, int R) {
+  return K % 128 == 0 && N % 8 == 0 && M % 4 == 0 && (R == 0 || R % 8 == 0);
+}
 
 // K a multiple of the 32-wide scale block; every tensor below 2^31 bytes.
 static bool mx_sizes_ok(int M, int N, int K, int R) {
@@ -335,7 +363,9 @@ static int mx_flavour(const VariantDesc& v, int M, int N, int K, int R, uintptr_
 
 int mx_plan(int variant, int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
   if (!pl || !mx_sizes_ok(M, N, K, R) || variant < -1 || variant >= kNumMxVariants) return GEMM_W4A4_EINVAL;
-  const Choice c = variant >= 0 ? Choice{variant, -1, M} : choose_plan(kMxVariants, kNumMxVariants, M, N, K, kMxLaunchStages);
+  const Choice c = variant >= 0 ? Choice{variant, -1, M, 1}
+                                 : choose_plan(kMxVariants, kNumMxVariants, M, N, K, kMxLaunchStages,
+                                               mx_slices_ok(M, N, K, R) ? kMxPartVariant : -1);
   const int rc = plan_choice(kMxVariants, c, M, N, K, R, pl);
   if (rc == GEMM_W4A4_OK) fill_registers(kMxVariants[c.main], mx_flavour(kMxVariants[c.main], M, N, K, R, 0, 0), pl);
   return rc;
@@ -353,6 +383,13 @@ int mx_run(int variant, bool f16, const CallArgs& a) {
   const uintptr_t lora = a.R > 0 ? (uintptr_t(a.lora_act_in) | uintptr_t(a.lora_up)) : 0u;
   return launch_plan(kMxVariants, pl, a, [&](const VariantDesc& v) {
     return v.kernel[f16 ? 1 : 0][mx_flavour(v, a.M, a.N, a.K, a.R, scales, lora)];
+  }, [&](int rows, int splits, int row0) -> int {
+    // the fast flavour without windows on the tail instance, and 16-byte
+    // aligned float32 sums in the output
+    const VariantDesc& t = kMxVariants[kMxPartVariant];
+    if (mx_flavour(t, a.M, a.N, a.K, a.R, scales, lora) != 1 || (uintptr_t(a.out) & 15u) != 0)
+      return GEMM_W4A4_EINVAL;
+    return launch_slices(kMxPartKernel[f16 ? 1 : 0], kMxReduceKernel[f16 ? 1 : 0], t, rows, splits, row0, a);
   });
 }
 

@@ -129,7 +129,10 @@ __device__ __forceinline__ u32x2 window_bytes(u32x3_a4 v, uint32_t pos) {
 // 8 bytes), scales byte by byte at the edges, LoRA operands element by element.
 // F16 selects the 16-bit type of the LoRA operands and of the output:
 // IEEE binary16 (true) or bfloat16 (false); both round to nearest even.
-template <class C, bool GENERAL, bool F16, bool ABYTE>
+// PART (fast flavour, K % 128 == 0): workgroup (tile, blockIdx.y) runs slice
+// blockIdx.y of gridDim.y of the tile's K stages and stores float32 sums to
+// p.part (see epilogue); split_k_reduce adds the slices.
+template <class C, bool GENERAL, bool F16, bool ABYTE, bool PART = false>
 __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4a4_kernel(
     const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
@@ -149,8 +152,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = (p.tm0 + tm) * C::BM, n0 = tn * C::BN;
-  const int M = p.M, N = p.N, K = p.K;
-  const int rowbytes = K >> 1;
+  const int M = p.M, N = p.N;
+  const int rowbytes = p.K >> 1;           // packed row stride
+  // the stages [ks0, ks1) this workgroup runs: all, or its K slice; the
+  // operand pointers start at the first of them
+  static_assert(!PART || (!GENERAL && !ABYTE), "K slices run on the fast flavour");
+  const int nst_all = (p.K + C::BK - 1) / C::BK;
+  const int ks0 = PART ? int(blockIdx.y) * nst_all / int(gridDim.y) : 0;
+  const int ks1 = PART ? (int(blockIdx.y) + 1) * nst_all / int(gridDim.y) : nst_all;
+  const uint8_t* const act = p.act + (PART ? size_t(ks0) * C::ROW_BYTES : 0);
+  const uint8_t* const wgt = p.wgt + (PART ? size_t(ks0) * C::ROW_BYTES : 0);
+  const uint8_t* const ascales = p.ascales + (PART ? size_t(ks0) * C::KBLK * size_t(M) : 0);
+  const uint8_t* const wscales = p.wscales + (PART ? size_t(ks0) * C::KBLK * size_t(N) : 0);
+  const int K = PART ? (ks1 - ks0) * C::BK : p.K;   // k of this workgroup
+  const int kbytes = K >> 1;               // packed bytes of a row it reads
   const int KB = K >> 4;                   // scale blocks along k
   const int nst = (K + C::BK - 1) / C::BK;
 
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const uint32_t dma_b0 = uint32_t(n0 + dma_row0) * uint32_t(rowbytes) + dma_inrow;
   const uint32_t dma_round = uint32_t(ROWS_PER_ROUND) * uint32_t(rowbytes);
 
-  const int full_stages = rowbytes / C::ROW_BYTES;   // stages lying entirely inside K
+  const int full_stages = kbytes / C::ROW_BYTES;   // stages lying entirely inside K
   // Round u of stage `st`'s packed bytes into ring slot `buf` % STAGES.
   auto dma_part = [&](int st, int buf, int u) __attribute__((always_inline)) {
     uint8_t* stage = smem + (buf % C::STAGES) * C::STAGE_BYTES;
@@ -189,7 +204,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
           SAME_INROW ? dma_inrow
                      : uint32_t(((dma_cp ^ swz(dma_row0 + ur * ROWS_PER_ROUND)) * 16) +
                                 dma_pc * DMA_BYTES);
-      const bool tail = tail_stage && inrow + k0 + DMA_BYTES > uint32_t(rowbytes);
+      const bool tail = tail_stage && inrow + k0 + DMA_BYTES > uint32_t(kbytes);
       const uint32_t kin = tail ? 0u : k0 + inrow;
       uint32_t row_off;
       if (is_b ? dma_b_inside : dma_a_inside) {
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
         const int row = (is_b ? n0 : m0) + dma_row0 + ur * ROWS_PER_ROUND;
         row_off = uint32_t(min(row, (is_b ? N : M) - 1)) * uint32_t(rowbytes);
       }
-      const uint8_t* src = (is_b ? p.wgt : p.act) + (row_off + kin);
+      const uint8_t* src = (is_b ? wgt : act) + (row_off + kin);
       dma<DMA_BYTES>(src, stage + (u * C::THREADS + wave_u * 64) * DMA_BYTES);
     }
   };
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   const int s_rows8 = (s_is_a ? C::BM : C::BN) / 8;
   const int s_kp = s_idx / s_rows8;
   const int s_r8 = (s_idx % s_rows8) * 8;
-  const uint8_t* s_src = s_is_a ? p.ascales : p.wscales;
+  const uint8_t* s_src = s_is_a ? ascales : wscales;
   const int s_rows = s_is_a ? M : N;
   const int s_r0 = (s_is_a ? m0 : n0) + s_r8;
   const int s_off = (s_is_a ? C::SA_OFF : C::SB_OFF) +
@@ -605,7 +620,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
   wait_vm_lgkm0<0>();   // drain the prefetches past the last stage
 
   if constexpr (C::KG == 1) {
-    epilogue<C, GENERAL, F16>(acc, p, smem, tid, m0, n0, epi_regs);
+    epilogue<C, GENERAL, F16, PART>(acc, p, smem, tid, m0, n0, epi_regs);
   } else {
     // k-group kg keeps m-tiles [kg MIH, (kg+1) MIH) of the wave tile and adds
     // its partner's partial sums of them; it hands the other half to the
@@ -649,7 +664,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC * C::THREADS / 256) void gemm_w4
     if (kg == 0) exchange.template operator()<0>();
     else exchange.template operator()<1>();
     __syncthreads();   // the epilogue reuses the ring
-    epilogue<E, GENERAL, F16>(kept, p, smem, tid, m0, n0, epi_regs);
+    epilogue<E, GENERAL, F16, PART>(kept, p, smem, tid, m0, n0, epi_regs);
   }
 }
 
@@ -689,6 +704,18 @@ static constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0])
 // 256x192 tiles: a 4096x3072 launch over one stage (K = 128) takes about
 // 11.7 us against 2.14 us per added stage.
 static constexpr double kLaunchStages = 4.4;
+// The instance compiled with K-sliced workgroups (the 64x192 k-group tile),
+// as the tail of a split plan, and those kernels [F16].
+static constexpr int kPartVariant = 4;
+static const void* const kPartKernel[2] = {
+    reinterpret_cast<const void*>(gemm_w4a4_kernel<Cfg64x192K, false, false, false, true>),
+    reinterpret_cast<const void*>(gemm_w4a4_kernel<Cfg64x192K, false, true, false, true>)};
+static const void* const kReduceKernel[2] = {reinterpret_cast<const void*>(split_k_reduce<false>),
+                                             reinterpret_cast<const void*>(split_k_reduce<true>)};
+// K slices need the fast flavour with 8-row act scales and whole stages.
+static bool slices_ok(int M, int N, int K, int R) {
+  return K % 128 == 0 && N % 8 == 0 && M % 8 == 0 && (R == 0 || R % 8 == 0);
+}
 
 // Size rules. Besides the operator's own (K a multiple of the 16-wide scale
 // block), every tensor must stay below 2^31 bytes: the kernels address them
@@ -717,7 +744,9 @@ static int nv_flavour(int M, int N, int K, int R, uintptr_t ascales, uintptr_t w
 
 int nv_plan(int variant, int M, int N, int K, int R, gemm_w4a4_plan_t* pl) {
   if (!pl || !sizes_ok(M, N, K, R) || variant < -1 || variant >= kNumVariants) return GEMM_W4A4_EINVAL;
-  const Choice c = variant >= 0 ? Choice{variant, -1, M} : choose_plan(kVariants, kNumVariants, M, N, K, kLaunchStages);
+  const Choice c = variant >= 0 ? Choice{variant, -1, M, 1}
+                                 : choose_plan(kVariants, kNumVariants, M, N, K, kLaunchStages,
+                                               slices_ok(M, N, K, R) ? kPartVariant : -1);
   const int rc = plan_choice(kVariants, c, M, N, K, R, pl);
   if (rc == GEMM_W4A4_OK) fill_registers(kVariants[c.main], nv_flavour(M, N, K, R, 0, 0, 0), pl);
   return rc;
@@ -733,7 +762,14 @@ int nv_run(int variant, bool f16, const CallArgs& a) {
   if (rc != GEMM_W4A4_OK) return rc;
   const int flavour = nv_flavour(a.M, a.N, a.K, a.R, uintptr_t(a.ascales), uintptr_t(a.wscales),
                                  a.R > 0 ? (uintptr_t(a.lora_act_in) | uintptr_t(a.lora_up)) : 0u);
-  return launch_plan(kVariants, pl, a, [&](const VariantDesc& v) { return v.kernel[f16 ? 1 : 0][flavour]; });
+  auto sliced = [&](int rows, int splits, int row0) -> int {
+    // the fast flavour with 8-row act scales (flavour 1), and 16-byte aligned
+    // float32 sums in the output
+    if (flavour != 1 || (uintptr_t(a.out) & 15u) != 0) return GEMM_W4A4_EINVAL;
+    return launch_slices(kPartKernel[f16 ? 1 : 0], kReduceKernel[f16 ? 1 : 0], kVariants[kPartVariant], rows, splits,
+                         row0, a);
+  };
+  return launch_plan(kVariants, pl, a, [&](const VariantDesc& v) { return v.kernel[f16 ? 1 : 0][flavour]; }, sliced);
 }
 
 }  // namespace w4a4

@@ -31,6 +31,8 @@ struct Params {
   int M, N, K, R;
   int tiles_m, tiles_n;   // tile rows and columns of this launch
   int tm0;                // its first tile row (in this instance's BM rows) within the M rows
+  float* part;            // a K-sliced launch: fp32 sums, [gridDim.y slices][part_rows][N]
+  int part_row0, part_rows;   // the output rows those sums cover
 };
 
 // 16-byte chunk c of a 64-byte row is stored at chunk position c ^ swz(row).

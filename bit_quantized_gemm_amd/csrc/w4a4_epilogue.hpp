@@ -90,7 +90,10 @@ __device__ __forceinline__ void epilogue_prefetch(const Params& p, uint8_t* smem
 // in 16-byte pieces; F16: LoRA operands and output in binary16, else bfloat16.
 // The LDS ring (C::RING_BYTES) is dead when this runs and is reused; the side
 // region, if any, holds what epilogue_prefetch brought in.
-template <class C, bool GENERAL, bool F16>
+// PART: the launch is one K slice (blockIdx.y) of the tile: its sums times
+// wcscale (slice 0 also adds bias and the LoRA term) are stored in float32 to
+// p.part instead of the output; a reduction adds the slices.
+template <class C, bool GENERAL, bool F16, bool PART = false>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Params& p, uint8_t* smem,
                                          const int tid, const int m0, const int n0,
                                          const EpiRegs& regs) {
@@ -100,6 +103,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   const int wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int M = p.M, N = p.N, R = p.R;
+  const bool first = !PART || blockIdx.y == 0;   // the slice that adds bias and LoRA
 
   // ---------------- epilogue: *wcscale + bias, + LoRA (same accumulators), bf16 store
   // The first of this lane's four consecutive output columns in (tile j, group q).
@@ -238,7 +242,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
     }
   };
 
-  const int nchunks = (R + RC - 1) / RC;
+  const int nchunks = first ? (R + RC - 1) / RC : 0;
   if (nchunks > 0) {
     if constexpr (!PRE) {
       la_load(0);
@@ -271,6 +275,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
         w = col4(p.wcscale, j, q);
         b = col4(p.bias, j, q);
       }
+      if (!first) b = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -314,6 +319,42 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
 #pragma unroll
         for (int i = 0; i < C::MI; ++i) acc[j][i] = lora_mfma<F16>(lu[j], la[i], acc[j][i]);
     }
+  }
+
+  if constexpr (PART) {
+    // float32 sums of this slice, staged through LDS as whole rows, then
+    // stored as 16-byte pieces of rows of p.part (N % 4 == 0, 16-byte aligned)
+    wait_vm_lgkm0<0>();
+    wg_barrier();
+    constexpr int F_STRIDE = C::BN * 4 + 16;
+    static_assert(C::BM * F_STRIDE <= C::RING_BYTES, "float32 tile must fit in the ring");
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) {
+          const int ml = wm * C::TM + 32 * i + l32;
+          const int nl = wn * C::TN + 32 * j + 8 * q + 4 * g;
+          *reinterpret_cast<f32x4*>(smem + ml * F_STRIDE + nl * 4) =
+              f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+        }
+    wait_vm_lgkm0<63>();
+    wg_barrier();
+    constexpr int F_PER_ROW = C::BN / 4;
+    constexpr int F_PIECES = C::BM * F_PER_ROW;
+    static_assert(F_PIECES % C::THREADS == 0, "whole store rounds");
+    float* const dst = p.part + size_t(blockIdx.y) * size_t(p.part_rows) * size_t(N);
+#pragma unroll
+    for (int u = 0; u < F_PIECES / C::THREADS; ++u) {
+      const int piece = u * C::THREADS + tid;
+      const int rl = piece / F_PER_ROW, cl = (piece % F_PER_ROW) * 4;
+      const int row = m0 + rl, col = n0 + cl;
+      if (row >= M || col >= N) continue;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(smem + rl * F_STRIDE + cl * 4);
+      *reinterpret_cast<f32x4*>(dst + size_t(row - p.part_row0) * size_t(N) + size_t(col)) = v;
+    }
+    return;
   }
 
   // bf16 (round to nearest even), staged through LDS: the tile is row-major
@@ -389,6 +430,32 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
       for (int e = 0; e < 8; ++e)
         if (e < left) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
     }
+  }
+}
+
+// The slices of a K-sliced launch added: part holds S planes of rows x N
+// float32 sums (slice 0 carries bias and the LoRA term), summed in slice
+// order and rounded to the output type (nearest even) into output rows
+// row0 .. row0 + rows - 1. One thread per four consecutive outputs
+// (N % 4 == 0, out 8-byte aligned).
+template <bool F16>
+__global__ __launch_bounds__(256) void split_k_reduce(const float* part, uint16_t* out, int rows, int N, int S,
+                                                      int row0) {
+  const uint32_t q = blockIdx.x * 256u + threadIdx.x;
+  if (q >= uint32_t(rows) * uint32_t(N >> 2)) return;
+  const size_t plane = size_t(rows) * size_t(N);
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + size_t(q) * 4);
+  for (int k = 1; k < S; ++k) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(part + size_t(k) * plane + size_t(q) * 4);
+    v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+  }
+  uint16_t* dst = out + size_t(row0) * size_t(N) + size_t(q) * 4;
+  if constexpr (F16) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<f16x4*>(dst) = f16x4{_Float16(v[0]), _Float16(v[1]), _Float16(v[2]), _Float16(v[3])};
+  } else {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{__bf16(v[0]), __bf16(v[1]), __bf16(v[2]), __bf16(v[3])};
   }
 }
 

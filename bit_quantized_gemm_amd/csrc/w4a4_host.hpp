@@ -93,6 +93,7 @@ inline void fill_static(const VariantDesc& v, int idx, gemm_w4a4_plan_t* pl) {
   pl->flavour = -1;
   pl->vgprs = pl->agprs = pl->sgprs = -1;
   pl->tail_variant = -1;
+  pl->tail_splits = 1;
 }
 
 // Registers of the kernel a launch of flavour `flavour` would run (bf16 output).
@@ -128,36 +129,50 @@ inline double estimate(const VariantDesc& x, int rows, int N) {
 // 256 x 192 in one round and the 17th on 64-row tiles, instead of a second
 // round for 16 tiles or a smaller tile everywhere.
 //
-// The estimate has no K: it counts rounds of k-loops. A second launch adds
-// what a launch costs besides its k-loop (ring fill, epilogue, the store of
-// its tiles), about `launch_stages` k-stages of a full round of instance 0.
-// A split is taken only when its estimate plus that share of a round of
-// K/128 stages is below the best single launch.
+// The estimate has no K: it counts rounds of k-loops. Every launch past the
+// first adds what a launch costs besides its k-loop (ring fill, epilogue, the
+// store of its tiles), about `launch_stages` k-stages of a full round of
+// instance 0, so each candidate pays that share of a round of K/128 stages
+// per extra launch.
+//
+// K slices: when `part` (an instance compiled with K-sliced workgroups, -1
+// for none) is the tail instance, the tail may instead run its K in S slices
+// over S times the workgroups (one round), writing float32 sums that a
+// reduction launch adds. Its rows take 1/S of the tail's estimate and two
+// extra launches. The sums live in the main launch's rows of the output,
+// which that launch, enqueued after the reduction, overwrites, so a slice
+// count needs S x tail rows x 4 bytes <= M1 x 2 bytes; 2 <= S <= 8, and every
+// slice keeps at least two stages.
 struct Choice {
   int main, tail;   // instances; tail -1: one launch over all M rows
   int main_rows;    // rows of the main launch (M when there is no tail)
+  int splits;       // K slices of the tail (1: the tail runs whole)
 };
-inline Choice choose_plan(const VariantDesc* vs, int n, int M, int N, int K, double launch_stages) {
-  Choice best{0, -1, M};
+inline Choice choose_plan(const VariantDesc* vs, int n, int M, int N, int K, double launch_stages, int part) {
+  const double round0 = double(vs[0].occ) * vs[0].block_m * vs[0].block_n * vs[0].cost;
+  const int nst = (K + vs[0].block_k - 1) / vs[0].block_k;
+  const double launch = launch_stages / double(nst) * round0;   // one extra launch
+  Choice best{0, -1, M, 1};
   double best_cost = estimate(vs[0], M, N);
-  for (int i = 1; i < n; ++i) {
-    const double c = estimate(vs[i], M, N);
-    if (c < best_cost) {
-      best = Choice{i, -1, M};
-      best_cost = c;
+  auto take = [&](const Choice& c, double cost) {
+    if (cost < best_cost) {
+      best = c;
+      best_cost = cost;
     }
-  }
-  Choice split{0, -1, M};
-  double split_cost = 0.0;
+  };
+  for (int i = 1; i < n; ++i) take(Choice{i, -1, M, 1}, estimate(vs[i], M, N));
   auto consider = [&](int i, int m1) {
     if (m1 <= 0 || m1 >= M) return;
+    const double main = estimate(vs[i], m1, N);
     for (int j = 0; j < n; ++j) {
       if (vs[i].block_m % vs[j].block_m != 0) continue;
-      const double c = estimate(vs[i], m1, N) + estimate(vs[j], M - m1, N);
-      if (split.tail < 0 || c < split_cost) {
-        split = Choice{i, j, m1};
-        split_cost = c;
-      }
+      const int rows = M - m1;
+      const double tail = estimate(vs[j], rows, N);
+      take(Choice{i, j, m1, 1}, main + tail + launch);
+      if (j != part) continue;
+      const long tiles = long((rows + vs[j].block_m - 1) / vs[j].block_m) * ((N + vs[j].block_n - 1) / vs[j].block_n);
+      const long fit = std::min<long>({8, long(kNumCUs) * vs[j].occ / tiles, long(nst) / 2, long(m1) / (2L * rows)});
+      if (fit >= 2) take(Choice{i, j, m1, int(fit)}, main + tail / double(fit) + 2.0 * launch);
     }
   };
   for (int i = 0; i < n; ++i) {
@@ -167,9 +182,7 @@ inline Choice choose_plan(const VariantDesc* vs, int n, int M, int N, int K, dou
     for (long k = 1; round_rows > 0 && k <= 64 && k * round_rows * x.block_m < M; ++k)
       consider(i, int(k * round_rows * x.block_m));
   }
-  const double round0 = double(vs[0].occ) * vs[0].block_m * vs[0].block_n * vs[0].cost;
-  const double k_stages = double((K + vs[0].block_k - 1) / vs[0].block_k);
-  return split.tail >= 0 && split_cost + launch_stages / k_stages * round0 < best_cost ? split : best;
+  return best;
 }
 
 // Problem-size part of a plan for instance `v` (index `idx`) over the first
@@ -185,6 +198,7 @@ inline int plan_for(const VariantDesc& v, int idx, int rows, int N, int K, int R
   pl->lora_steps = (R + 15) / 16;
   pl->tail_variant = -1;
   pl->tail_rows = pl->tail_block_m = pl->tail_block_n = pl->tail_grid = 0;
+  pl->tail_splits = 1;
   return GEMM_W4A4_OK;
 }
 
@@ -197,7 +211,8 @@ inline int plan_choice(const VariantDesc* vs, const Choice& c, int M, int N, int
   pl->tail_rows = M - c.main_rows;
   pl->tail_block_m = t.block_m;
   pl->tail_block_n = t.block_n;
-  pl->tail_grid = (pl->tail_rows + t.block_m - 1) / t.block_m * ((N + t.block_n - 1) / t.block_n);
+  pl->tail_splits = c.splits;
+  pl->tail_grid = (pl->tail_rows + t.block_m - 1) / t.block_m * ((N + t.block_n - 1) / t.block_n) * c.splits;
   return GEMM_W4A4_OK;
 }
 
@@ -233,7 +248,8 @@ inline int check_call(const CallArgs& a, int block) {
 
 // One launch of `kernel` (instance v) over tile rows [tm0, tm0 + tiles_m) of
 // its BM rows.
-inline int launch_kernel(const void* kernel, const VariantDesc& v, int tiles_m, int tm0, const CallArgs& a) {
+inline int launch_kernel(const void* kernel, const VariantDesc& v, int tiles_m, int tm0, const CallArgs& a,
+                         int splits = 1, int part_rows = 0) {
   Params prm;
   prm.act = a.act;
   prm.ascales = a.ascales;
@@ -251,22 +267,57 @@ inline int launch_kernel(const void* kernel, const VariantDesc& v, int tiles_m, 
   prm.tiles_m = tiles_m;
   prm.tiles_n = (a.N + v.block_n - 1) / v.block_n;
   prm.tm0 = tm0;
+  // K slices: float32 sums over the rows before this launch's (see choose_plan)
+  prm.part = splits > 1 ? reinterpret_cast<float*>(a.out) : nullptr;
+  prm.part_row0 = tm0 * v.block_m;
+  prm.part_rows = part_rows;
   void* args[] = {&prm};
-  const hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(long(tiles_m) * prm.tiles_n)), dim3(v.threads), args, 0,
-                                       static_cast<hipStream_t>(a.stream));
+  const hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(long(tiles_m) * prm.tiles_n), unsigned(splits)),
+                                       dim3(v.threads), args, 0, static_cast<hipStream_t>(a.stream));
   return e == hipSuccess ? GEMM_W4A4_OK : GEMM_W4A4_ELAUNCH;
+}
+
+// A K-sliced tail: `part_kernel` (instance t, K-sliced workgroups) over the
+// last `rows` rows in `splits` slices, its float32 sums in the output's first
+// rows, then `reduce_kernel` (split_k_reduce of the output type) adding them
+// into rows row0 .. row0 + rows - 1.
+inline int launch_slices(const void* part_kernel, const void* reduce_kernel, const VariantDesc& t, int rows, int splits,
+                         int row0, const CallArgs& a) {
+  if (launch_kernel(part_kernel, t, (rows + t.block_m - 1) / t.block_m, row0 / t.block_m, a, splits, rows) !=
+      GEMM_W4A4_OK)
+    return GEMM_W4A4_ELAUNCH;
+  const long groups = long(rows) * (a.N / 4);
+  const float* part = reinterpret_cast<const float*>(a.out);
+  uint16_t* out = a.out;
+  int n = a.N, s = splits, r0 = row0, nr = rows;
+  void* args[] = {&part, &out, &nr, &n, &s, &r0};
+  return hipLaunchKernel(reduce_kernel, dim3(unsigned((groups + 255) / 256)), dim3(256), args, 0,
+                         static_cast<hipStream_t>(a.stream)) == hipSuccess
+             ? GEMM_W4A4_OK
+             : GEMM_W4A4_ELAUNCH;
 }
 
 // The launches of a plan: the main instance, then the tail instance, if any,
 // over the last rows (the same flavour rule; `kernel_of` maps an instance to
-// the kernel of that flavour and output type).
-template <class KernelOf>
-inline int launch_plan(const VariantDesc* vs, const gemm_w4a4_plan_t& pl, const CallArgs& a, KernelOf kernel_of) {
+// the kernel of that flavour and output type). A K-sliced tail runs first:
+// `sliced(rows, splits, row0)` enqueues its slices and their reduction, which
+// use the main launch's rows of the output as scratch; the main launch then
+// overwrites them. `sliced` returns GEMM_W4A4_EINVAL when the call's pointers
+// do not allow slices; the tail then runs whole.
+template <class KernelOf, class Sliced>
+inline int launch_plan(const VariantDesc* vs, const gemm_w4a4_plan_t& pl, const CallArgs& a, KernelOf kernel_of,
+                       Sliced sliced) {
   const VariantDesc& v = vs[pl.variant];
-  int rc = launch_kernel(kernel_of(v), v, pl.tiles_m, 0, a);
-  if (rc != GEMM_W4A4_OK || pl.tail_variant < 0) return rc;
-  const VariantDesc& t = vs[pl.tail_variant];
   const int main_rows = a.M - pl.tail_rows;
+  bool tail_done = false;
+  if (pl.tail_variant >= 0 && pl.tail_splits > 1) {
+    const int rc = sliced(pl.tail_rows, pl.tail_splits, main_rows);
+    if (rc == GEMM_W4A4_ELAUNCH) return rc;
+    tail_done = rc == GEMM_W4A4_OK;
+  }
+  int rc = launch_kernel(kernel_of(v), v, pl.tiles_m, 0, a);
+  if (rc != GEMM_W4A4_OK || pl.tail_variant < 0 || tail_done) return rc;
+  const VariantDesc& t = vs[pl.tail_variant];
   return launch_kernel(kernel_of(t), t, (pl.tail_rows + t.block_m - 1) / t.block_m, main_rows / t.block_m, a);
 }
 

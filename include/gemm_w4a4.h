@@ -176,6 +176,15 @@ typedef struct {
   int tail_block_m;
   int tail_block_n;
   int tail_grid;
+  /* K slices of the tail launch (1: it runs whole). Above 1, its workgroups
+   * (tail_grid of them, counted with the slices) each run one slice of K and
+   * write float32 sums into the first tail_splits * tail_rows * 2 rows of out,
+   * rows the first launch writes later; a reduction launch adds the slices
+   * into the last tail_rows rows. The three launches run on the call's stream
+   * in the order slices, reduction, first launch; the call allocates nothing.
+   * When the call's pointers do not allow the fast flavour the tail runs
+   * whole, after the first launch. */
+  int tail_splits;
 } gemm_w4a4_plan_t;
 
 /* Fill *plan for (M, N, K, R). Returns GEMM_W4A4_OK or GEMM_W4A4_EINVAL

@@ -26,8 +26,9 @@ int main(void) {
   check(pl.tail_variant == -1 && pl.tail_rows == 0, "4096 rows: one launch");
   check(gemm_w4a4_plan(4352, 3072, 3840, 128, &pl) == GEMM_W4A4_OK && pl.tail_variant >= 0 &&
             pl.block_m * pl.tiles_m + pl.tail_rows == 4352 && pl.block_m % pl.tail_block_m == 0 &&
+            pl.tail_splits >= 1 &&
             pl.tail_grid == (pl.tail_rows + pl.tail_block_m - 1) / pl.tail_block_m *
-                                ((3072 + pl.tail_block_n - 1) / pl.tail_block_n),
+                                ((3072 + pl.tail_block_n - 1) / pl.tail_block_n) * pl.tail_splits,
         "4352 rows: whole tile rows, then a tail launch over the rest");
   check(gemm_w4a4_plan(4096, 3072, 3000, 32, &pl) == GEMM_W4A4_EINVAL, "K % 16 != 0 rejected");
   check(gemm_mxfp4_plan(64, 64, 48, 0, &pl) == GEMM_W4A4_EINVAL, "MXFP4 K % 32 != 0 rejected");

@@ -217,9 +217,11 @@ def test_solver_lds_matches_code_objects():
     # mangled tile configurations: w4a4::TileCfg (NVFP4) and w4a4::MxTileCfg (MXFP4)
     # instances per tile: NVFP4 {general, fast, fast with byte-wise act
     # scales} x {bf16, fp16}; MXFP4 {general, fast} x {bf16, fp16}, plus fast
-    # with act-scale windows where the 256-row tile's scale rounds have room
-    cases = [(v, "7TileCfgI", 6) for v in w4.variants("nvfp4")] + \
-            [(v, "9MxTileCfgI", 6 if v["block_m"] == 256 else 4) for v in w4.variants("mxfp4")]
+    # with act-scale windows where the 256-row tile's scale rounds have room;
+    # the 64x192 k-group tile (NVFP4) and the 128x128 tile (MXFP4) also in K
+    # slices (fast, bf16 and fp16)
+    cases = [(v, "7TileCfgI", 8 if (v["block_m"], v["k_groups"]) == (64, 2) else 6) for v in w4.variants("nvfp4")] + \
+            [(v, "9MxTileCfgI", 6 if v["block_m"] == 256 else 6) for v in w4.variants("mxfp4")]
     for v, tag, count in cases:
         key = tag + "Li%dELi%dELi%dELi%dELi%dELi%dE" % (v["block_m"], v["block_n"], v["waves_m"],
                                                        v["waves_n"], v["occupancy"], v["policy"])

@@ -639,11 +639,17 @@ def test_prefetched_lora_chunk_partial_rank(shape, dtype):
 # round; K long enough that the second launch pays for itself): both
 # launches' rows, edge tiles past M in the tail, the act-scale window flavour
 # in both launches (M % 8 != 0), MXFP4 (whose tail instance takes another
-# flavour than its main one at M % 4 != 0), fp16 output. Every element of the
-# first 64 rows, of the main launch's last tile row and of every tail row.
+# flavour than its main one at M % 4 != 0), fp16 output; tails whose K runs
+# in slices (M % 8 == 0, K % 128 == 0: float32 sums in the output's first
+# rows, then a reduction) with and without LoRA, and at R > 128 (LoRA in
+# slice 0 over several chunks). Every element of the first 64 rows, of the
+# main launch's last tile row and of every tail row.
 SPLIT = [("nvfp4", "bf16", (4196, 3072, 3584, 32)), ("nvfp4", "bf16", (4353, 3072, 3840, 16)),
          ("nvfp4", "f16", (4196, 3072, 3584, 32)), ("mxfp4", "bf16", (4196, 3072, 10240, 32)),
-         ("mxfp4", "bf16", (4353, 3072, 10240, 16))]
+         ("mxfp4", "bf16", (4353, 3072, 10240, 16)),
+         ("nvfp4", "bf16", (4224, 3072, 3840, 32)), ("nvfp4", "f16", (4224, 3072, 3840, 32)),
+         ("nvfp4", "bf16", (4352, 3072, 3840, 0)), ("nvfp4", "bf16", (4352, 3072, 2816, 136)),
+         ("mxfp4", "f16", (4224, 3072, 10240, 32)), ("mxfp4", "bf16", (4352, 3072, 10240, 0))]
 
 
 @pytest.mark.parametrize("fmt,dtype,shape", SPLIT, ids=[f"{f}-{d}-" + "x".join(map(str, s)) for f, d, s in SPLIT])
@@ -652,7 +658,7 @@ def test_split_plan(fmt, dtype, shape):
     p = w4.plan(M, N, K, R, fmt=fmt)
     m1 = p["tiles_m"] * p["block_m"]
     _say(f"case: {fmt} split plan M={M} N={N} K={K} R={R} {dtype}: v{p['variant']} over "
-         f"{m1} rows, v{p['tail_variant']} over the last {p['tail_rows']}")
+         f"{m1} rows, v{p['tail_variant']} over the last {p['tail_rows']} in {p['tail_splits']} K slices")
     assert p["tail_variant"] >= 0 and m1 + p["tail_rows"] == M
     x = synthetic.custom_inputs(M, N, K, R, seed=M + R, dtype=dtype, fmt=fmt)
     x["dtype"] = dtype
@@ -667,3 +673,29 @@ def test_split_plan(fmt, dtype, shape):
     y, T = refrows(x, rows)
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
     assert_parity(got, y, T, f"{fmt} split {shape} {dtype}, {rows.size} rows", dtype)
+
+
+# A K-sliced tail whose call does not allow slices (the output 8 bytes off
+# 16-byte alignment: no float32 sums in it) runs whole, after the main
+# launch; the same call on an aligned output slices. Both formats, on every
+# element of the boundary rows.
+@pytest.mark.parametrize("fmt,shape", [("nvfp4", (4224, 3072, 3840, 32)), ("mxfp4", (4224, 3072, 10240, 32))])
+def test_sliced_tail_falls_back_on_unaligned_out(fmt, shape):
+    M, N, K, R = shape
+    p = w4.plan(M, N, K, R, fmt=fmt)
+    assert p["tail_splits"] > 1
+    x = synthetic.custom_inputs(M, N, K, R, seed=77, fmt=fmt)
+    d = to_device(x)
+    rows = np.concatenate([np.arange(64), np.arange(p["tiles_m"] * p["block_m"] - p["block_m"], M)])
+    refrows = ref.reference_rows_mx if fmt == "mxfp4" else ref.reference_rows
+    y, T = refrows(x, rows)
+    for off in (0, 4):
+        _say(f"case: {fmt} K-sliced tail, output offset {2 * off} bytes")
+        buf = torch.empty(M * N + 8, dtype=torch.bfloat16, device=DEV)
+        out = buf[off:off + M * N].view(M, N)
+        rc = w4.run_raw(fmt, False, -1, *[d[k].data_ptr() for k in ARGS], out.data_ptr(), M, N, K, R,
+                        torch.cuda.current_stream().cuda_stream)
+        assert rc == w4.OK, rc
+        torch.cuda.synchronize()
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+        assert_parity(got, y, T, f"{fmt} K-sliced tail, offset {2 * off}", "bf16")
