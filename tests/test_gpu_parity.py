@@ -425,6 +425,43 @@ def test_hip_graph_capture_and_replay(fmt):
     assert_parity(eager.view(np.uint16), refn(*a), tmag(*a), f"graph {fmt}")
 
 
+@pytest.mark.parametrize("fmt,shape", [("nvfp4", (4224, 3072, 3840, 32)), ("mxfp4", (4224, 3072, 10240, 32))])
+def test_hip_graph_sliced_tail(fmt, shape):
+    """A split plan whose tail runs its K in slices (three launches, float32
+    sums in the output's first rows) captured into a HIP graph: every replay
+    gives the eager bytes, with eager work and synchronisations in between;
+    the boundary rows match the oracle."""
+    M, N, K, R = shape
+    p = w4.plan(M, N, K, R, fmt=fmt)
+    assert p["tail_splits"] > 1
+    _say(f"case: HIP graph of a K-sliced tail plan, {fmt}, {shape}")
+    x = synthetic.custom_inputs(M, N, K, R, seed=92, fmt=fmt)
+    d = to_device(x)
+    call = w4.gemm_mxfp4 if fmt == "mxfp4" else w4.gemm_w4a4
+    args = [d[k] for k in ARGS]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(*args, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.view(torch.int16).cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(*args, out=out)
+    for rep in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), eager), rep
+    rows = np.concatenate([np.arange(64), np.arange(p["tiles_m"] * p["block_m"] - p["block_m"], M)])
+    refrows = ref.reference_rows_mx if fmt == "mxfp4" else ref.reference_rows
+    y, T = refrows(x, rows)
+    assert_parity(eager.view(np.uint16)[rows], y, T, f"graph sliced {fmt}")
+
+
 def test_concurrent_streams():
     """Two calls on two streams at once (different shapes, both formats)
     give the same bytes as the same calls made one after the other."""
