@@ -68,8 +68,11 @@ enum {
  * stream: a hipStream_t passed as void*; NULL selects the null stream.
  *
  * Every out[m][n] with m < M, n < N is overwritten; nothing else is written
- * and no input is modified. Results are deterministic: the same inputs give
- * the same bytes on every call (no atomics, no split-K). E4M3 NaN scale bytes
+ * and no input is modified. A plan whose tail runs its K in slices (see
+ * gemm_w4a4_plan_t) first keeps the slices' float32 sums in out's first
+ * rows; every element holds its result once the call's work on the stream
+ * has finished. Results are deterministic: the same inputs give the same
+ * bytes on every call (no atomics; slices are added in a fixed order). E4M3 NaN scale bytes
  * (0x7F, 0xFF) propagate NaN into every output their block touches.
  * Returns GEMM_W4A4_OK or one of the negative codes above.
  */
