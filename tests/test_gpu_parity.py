@@ -462,6 +462,29 @@ def test_hip_graph_sliced_tail(fmt, shape):
     assert_parity(eager.view(np.uint16)[rows], y, T, f"graph sliced {fmt}")
 
 
+def test_concurrent_sliced_tails():
+    """Two K-sliced split plans on two streams at once, each keeping its
+    float32 sums in its own output: the same bytes as one after the other."""
+    M, N, K, R = 4224, 3072, 3840, 32
+    assert w4.plan(M, N, K, R)["tail_splits"] > 1
+    _say(f"case: two K-sliced tail plans on two streams, {M}x{N}x{K} R={R}")
+    ds = [to_device(synthetic.custom_inputs(M, N, K, R, seed=s)) for s in (93, 94)]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for _ in ds]
+    for d, o in zip(ds, outs):
+        w4.gemm_w4a4(*[d[k] for k in ARGS], out=o)
+    torch.cuda.synchronize()
+    ref_bytes = [o.clone() for o in outs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        for d, o, st in zip(ds, outs, streams):
+            w4.gemm_w4a4(*[d[k] for k in ARGS], out=o, stream=st)
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, r) for o, r in zip(outs, ref_bytes))
+
+
 def test_concurrent_streams():
     """Two calls on two streams at once (different shapes, both formats)
     give the same bytes as the same calls made one after the other."""
