@@ -91,8 +91,9 @@ __device__ __forceinline__ void epilogue_prefetch(const Params& p, uint8_t* smem
 // The LDS ring (C::RING_BYTES) is dead when this runs and is reused; the side
 // region, if any, holds what epilogue_prefetch brought in.
 // PART: the launch is one K slice (blockIdx.y) of the tile: its sums times
-// wcscale (slice 0 also adds bias and the LoRA term) are stored in float32 to
-// p.part instead of the output; a reduction adds the slices.
+// wcscale, plus its share of the LoRA term's rank chunks (slice 0 also adds
+// bias), are stored in float32 to p.part instead of the output; a reduction
+// adds the slices.
 template <class C, bool GENERAL, bool F16, bool PART = false>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Params& p, uint8_t* smem,
                                          const int tid, const int m0, const int n0,
@@ -103,7 +104,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   const int wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int M = p.M, N = p.N, R = p.R;
-  const bool first = !PART || blockIdx.y == 0;   // the slice that adds bias and LoRA
+  const bool first = !PART || blockIdx.y == 0;   // the slice that adds bias
 
   // ---------------- epilogue: *wcscale + bias, + LoRA (same accumulators), bf16 store
   // The first of this lane's four consecutive output columns in (tile j, group q).
@@ -242,11 +243,14 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
     }
   };
 
-  const int nchunks = first ? (R + RC - 1) / RC : 0;
-  if (nchunks > 0) {
-    if constexpr (!PRE) {
-      la_load(0);
-      lu_load(0);
+  // K slices share the LoRA term: slice s takes rank chunks s, s + S, ...
+  // (the term is a sum over chunks), so no slice waits on all of them.
+  const int nchunks = (R + RC - 1) / RC;
+  const int c0 = PART ? int(blockIdx.y) : 0, cstep = PART ? int(gridDim.y) : 1;
+  if (c0 < nchunks) {
+    if (!PRE || c0 != 0) {
+      la_load(c0 * RC);
+      lu_load(c0 * RC);
     }
   }
 
@@ -290,13 +294,13 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[C::NI][C::MI], const Para
   const int la_row = wm * C::TM + l32;   // + 32i: the same swizzle
   const uint32_t la_rd = PRE ? LA_OFF + la_row * 64 : LA_OFF + la_row * LR_STRIDE + g * 16;
   const uint32_t lu_rd = LU_OFF + (wn * C::TN + l32) * LR_STRIDE + g * 16;
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = c0; c < nchunks; c += cstep) {
     wait_vm_lgkm0<0>();
     wg_barrier();   // every wave is done with the ring / the previous chunk
     lora_store(c * RC);
-    if (c + 1 < nchunks) {
-      la_load((c + 1) * RC);
-      lu_load((c + 1) * RC);
+    if (c + cstep < nchunks) {
+      la_load((c + cstep) * RC);
+      lu_load((c + cstep) * RC);
     }
     wait_vm_lgkm0<63>();
     wg_barrier();
