@@ -1,8 +1,8 @@
 /*
  * w4a4_probes.h — C ABI of libw4a4_probes.so: measurement aids that sit beside
  * the fused W4A4 GEMM library (include/gemm_w4a4.h) but are not part of the
- * operator. They give the figures the operator's performance is judged
- * against: the attainable rate of each matrix instruction under full-chip
+ * operator. They give the figures the operator's performance is compared
+ * with: the attainable rate of each matrix instruction under full-chip
  * load, and the two candidate ways of running NVFP4's block-scaled product on
  * gfx950's matrix cores.
  *
